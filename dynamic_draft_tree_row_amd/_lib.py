@@ -1,0 +1,100 @@
+"""ctypes view of the C ABI in include/ddt.h (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libddt.so")
+
+DDT_OK, DDT_EINVAL, DDT_EDTYPE, DDT_ECAPACITY, DDT_EWORKSPACE, DDT_ELAUNCH = range(6)
+DDT_F32, DDT_BF16 = 0, 1
+MAX_K, MAX_DEPTH, MAX_FRONT, MAX_NODES, MAX_VERIFY, MAX_CHUNKS = 32, 11, 32, 4096, 255, 64
+
+P = C.c_void_p
+i32, i64, f32, sz = C.c_int32, C.c_int64, C.c_float, C.c_size_t
+
+
+class Tree(C.Structure):
+    _fields_ = [("B", i32), ("cap", i32), ("D_max", i32), ("R_max", i32),
+                ("token", P), ("parent", P), ("depth", P), ("eslot", P), ("key", P),
+                ("S", P), ("logc", P), ("rmax", P), ("rsp", P), ("n_nodes", P),
+                ("layer_base", P), ("n_front", P), ("frontier", P), ("active", P),
+                ("k_draft", P), ("cont", P), ("widths", P), ("cast_state", P)]
+
+
+class Flat(C.Structure):
+    _fields_ = [("B", i32), ("P", i32), ("W", i32), ("Dp", i32), ("L", i32),
+                ("node", P), ("token", P), ("parent", P), ("pos", P), ("mask", P),
+                ("retrieve", P), ("n_leaves", P), ("m", P)]
+
+
+class Logits(C.Structure):
+    _fields_ = [("data", P), ("dtype", C.c_int), ("V", C.c_int), ("s0", i64), ("s1", i64)]
+
+
+class Cast(C.Structure):
+    _fields_ = [("S_T", P), ("S_D", P), ("L", C.c_int), ("M", C.c_int), ("N", C.c_int),
+                ("C1", P), ("C2", f32), ("C3", P), ("R", C.c_int), ("ctx_verify", C.c_int)]
+
+
+class Gate(C.Structure):
+    _fields_ = [("n_ck", C.c_int), ("ck_depth", C.c_int * 4), ("tau", f32 * 4),
+                ("k_draft", C.c_int * 4), ("K_max", C.c_int)]
+
+
+# exported name -> (restype, argtypes)
+SIGNATURES = {
+    "ddt_strerror": (C.c_char_p, [C.c_int]),
+    "ddt_chunk_elems": (C.c_int, [C.c_int]),
+    "ddt_workspace_bytes": (sz, [C.c_int, C.c_int, C.c_int, C.c_int]),
+    "ddt_tree_bytes": (sz, [C.c_int, C.c_int, C.c_int, C.c_int]),
+    "ddt_tree_bind": (C.c_int, [C.POINTER(Tree), P, sz, C.c_int, C.c_int, C.c_int, C.c_int]),
+    "ddt_flat_bytes": (sz, [C.c_int, C.c_int, C.c_int]),
+    "ddt_flat_bind": (C.c_int, [C.POINTER(Flat), P, sz, C.c_int, C.c_int, C.c_int]),
+    "ddt_tree_expand": (C.c_int, [C.POINTER(Tree), C.c_int, P, C.POINTER(Logits), C.c_int,
+                                  C.c_int, C.POINTER(Cast), C.POINTER(Gate), P, sz, P]),
+    "ddt_tree_rerank": (C.c_int, [C.POINTER(Tree), C.c_int, C.POINTER(Cast), C.c_int, P, P, P]),
+    "ddt_succ_gather": (C.c_int, [C.POINTER(Tree), P, i64, C.c_int, C.c_int, C.c_int, C.c_int,
+                                  C.c_int, C.c_int, P, P, P]),
+    "ddt_tree_build_mask": (C.c_int, [C.POINTER(Tree), P, P, C.c_int, C.POINTER(Flat), P, P]),
+    "ddt_tree_verify": (C.c_int, [C.POINTER(Tree), C.POINTER(Flat), C.POINTER(Logits),
+                                  C.POINTER(Logits), i64, P, P, C.c_int, P, P, P, P, P, P, sz, P]),
+    "ddt_succ_update": (C.c_int, [P, i64, C.c_int, C.c_int, C.POINTER(Flat), P, C.c_int,
+                                  C.POINTER(Logits), P, sz, P]),
+    "ddt_row_topk": (C.c_int, [C.POINTER(Logits), C.c_int, C.c_int, C.c_int, P, P, P, P, P, sz, P]),
+}
+
+_lib = None
+
+
+class DDTError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed with status {status}: {strerror(status)}")
+        self.status = status
+
+
+def load(path: str = LIB_PATH):
+    """Load libddt.so.  Raises if it has not been built: there is no fallback."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m dynamic_draft_tree_row_amd.build_lib` (hipcc, gfx950)")
+    lib = C.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def strerror(status: int) -> str:
+    return load().ddt_strerror(status).decode()
+
+
+def check(fn: str, status: int) -> None:
+    if status != DDT_OK:
+        raise DDTError(fn, status)

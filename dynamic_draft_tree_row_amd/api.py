@@ -1,0 +1,230 @@
+"""Thin torch-facing wrappers over the C ABI (include/ddt.h).
+
+Torch only provides device memory and the stream; every step of the round runs
+in the library's HIP kernels.  Names follow the C calls without the ``ddt_``
+prefix.  All tensors must live on the same ROCm device.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+from . import _lib as L
+
+_DT = {torch.float32: L.DDT_F32, torch.bfloat16: L.DDT_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None, device=None):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return C.c_void_p(s.cuda_stream)
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+    return _DT[t.dtype]
+
+
+def logits_desc(x: torch.Tensor) -> L.Logits:
+    """Descriptor of a [n0][n1][V] logit tensor with unit stride along V."""
+    if x.dim() != 3 or x.stride(2) != 1:
+        raise ValueError("logits must be 3-D [n0][n1][V] with contiguous rows")
+    return L.Logits(C.c_void_p(x.data_ptr()), dtype_code(x), x.shape[2], x.stride(0), x.stride(1))
+
+
+def chunk_elems(dtype) -> int:
+    return L.load().ddt_chunk_elems(_DT[dtype] if isinstance(dtype, torch.dtype) else dtype)
+
+
+def workspace_bytes(rows: int, V: int, dtype, K: int) -> int:
+    code = _DT[dtype] if isinstance(dtype, torch.dtype) else dtype
+    return int(L.load().ddt_workspace_bytes(rows, V, code, K))
+
+
+class _Carved:
+    """A caller-owned device buffer carved into typed views by the library."""
+
+    def _view(self, ptr: int, dtype, shape):
+        off = ptr - self.buf.data_ptr()
+        n = 1
+        for s in shape:
+            n *= s
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        return self.buf[off:off + nbytes].view(dtype).view(*shape)
+
+
+class DeviceTree(_Carved):
+    """Tree state for B rows of at most `cap` nodes (include/ddt.h, ddt_tree)."""
+
+    def __init__(self, B: int, cap: int, D_max: int, R_max: int, device="cuda"):
+        lib = L.load()
+        nbytes = int(lib.ddt_tree_bytes(B, cap, D_max, R_max))
+        if nbytes == 0:
+            raise ValueError("invalid tree sizes")
+        self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        self.c = L.Tree()
+        L.check("ddt_tree_bind", lib.ddt_tree_bind(C.byref(self.c), C.c_void_p(self.buf.data_ptr()),
+                                                   nbytes, B, cap, D_max, R_max))
+        self.B, self.cap, self.D_max, self.R_max = B, cap, D_max, R_max
+        c = self.c
+        v = self._view
+        self.token = v(c.token, torch.int32, (B, cap))
+        self.parent = v(c.parent, torch.int32, (B, cap))
+        self.depth = v(c.depth, torch.int32, (B, cap))
+        self.eslot = v(c.eslot, torch.int32, (B, cap))
+        self.key = v(c.key, torch.int64, (B, cap))
+        self.S = v(c.S, torch.float32, (B, cap))
+        self.logc = v(c.logc, torch.float32, (B, cap))
+        self.rmax = v(c.rmax, torch.float32, (B, D_max, R_max))
+        self.rsp = v(c.rsp, torch.float32, (B, D_max, R_max))
+        self.n_nodes = v(c.n_nodes, torch.int32, (B,))
+        self.n_front = v(c.n_front, torch.int32, (B,))
+        self.frontier = v(c.frontier, torch.int32, (B, R_max))
+        self.active = v(c.active, torch.int32, (B,))
+        self.k_draft = v(c.k_draft, torch.int32, (B,))
+        self.cont = v(c.cont, torch.int32, (1,))
+        self.widths = v(c.widths, torch.int32, (D_max,))
+
+
+class DeviceFlat(_Carved):
+    """Flattened tree buffers (include/ddt.h, ddt_flat)."""
+
+    def __init__(self, B: int, m_max: int, Dp: int, device="cuda"):
+        lib = L.load()
+        nbytes = int(lib.ddt_flat_bytes(B, m_max, Dp))
+        if nbytes == 0:
+            raise ValueError("invalid flat sizes")
+        self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        self.c = L.Flat()
+        L.check("ddt_flat_bind", lib.ddt_flat_bind(C.byref(self.c), C.c_void_p(self.buf.data_ptr()),
+                                                   nbytes, B, m_max, Dp))
+        c = self.c
+        self.B, self.P, self.W, self.Dp, self.L = c.B, c.P, c.W, c.Dp, c.L
+        v = self._view
+        P, W = c.P, c.W
+        self.node = v(c.node, torch.int32, (B, P))
+        self.token = v(c.token, torch.int32, (B, P))
+        self.parent = v(c.parent, torch.int32, (B, P))
+        self.pos = v(c.pos, torch.int32, (B, P))
+        self.mask = v(c.mask, torch.int32, (B, P, W))
+        self.retrieve = v(c.retrieve, torch.int32, (B, c.L, Dp + 1))
+        self.n_leaves = v(c.n_leaves, torch.int32, (B,))
+        self.m = v(c.m, torch.int32, (B,))
+
+
+@dataclass
+class CastParams:
+    """CAST tables and thresholds on the device (include/ddt.h, ddt_cast)."""
+    S_T: torch.Tensor          # fp32 [M][N+1]
+    S_D: torch.Tensor          # fp32 [M][N+1]
+    L: int
+    C1: torch.Tensor           # fp32 [D_max]
+    C2: float
+    C3: torch.Tensor           # fp32 [B]
+    R: int
+    ctx_verify: int = 0
+
+    def struct(self) -> L.Cast:
+        M, N1 = self.S_T.shape
+        return L.Cast(_ptr(self.S_T), _ptr(self.S_D), self.L, M, N1 - 1, _ptr(self.C1),
+                      float(self.C2), _ptr(self.C3), self.R, self.ctx_verify)
+
+
+@dataclass
+class GraftGate:
+    ck_depth: Sequence[int]
+    tau: Sequence[float]
+    k_draft: Sequence[int]
+    K_max: int
+
+    def struct(self) -> L.Gate:
+        g = L.Gate()
+        g.n_ck = len(self.ck_depth)
+        for i, (d, t, k) in enumerate(zip(self.ck_depth, self.tau, self.k_draft)):
+            g.ck_depth[i], g.tau[i], g.k_draft[i] = d, t, k
+        g.K_max = self.K_max
+        return g
+
+
+def tree_expand(tree: DeviceTree, layer: int, root_tok: torch.Tensor, logits: torch.Tensor,
+                K_n: int, K_e: int, ws: torch.Tensor, cast: Optional[CastParams] = None,
+                gate: Optional[GraftGate] = None, stream=None) -> None:
+    d = logits_desc(logits)
+    cs = C.byref(cast.struct()) if cast is not None else None
+    gs = C.byref(gate.struct()) if gate is not None else None
+    L.check("ddt_tree_expand", L.load().ddt_tree_expand(
+        C.byref(tree.c), layer, _ptr(root_tok), C.byref(d), K_n, K_e, cs, gs, _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream, logits.device)))
+
+
+def tree_rerank(tree: DeviceTree, m_max: int, sel: torch.Tensor, m_out: torch.Tensor,
+                cast: Optional[CastParams] = None, use_k_draft: bool = False, stream=None) -> None:
+    cs = C.byref(cast.struct()) if cast is not None else None
+    L.check("ddt_tree_rerank", L.load().ddt_tree_rerank(
+        C.byref(tree.c), m_max, cs, int(use_k_draft), _ptr(sel), _ptr(m_out),
+        _stream(stream, sel.device)))
+
+
+def succ_gather(tree: DeviceTree, M: torch.Tensor, k_succ: int, tpl_depth: int, tpl_width: int,
+                K_max: int, m_max: int, sel: torch.Tensor, m_out: torch.Tensor, shared: bool = False,
+                stream=None) -> None:
+    V = M.shape[-2]
+    bstride = 0 if shared else V * k_succ
+    L.check("ddt_succ_gather", L.load().ddt_succ_gather(
+        C.byref(tree.c), _ptr(M), bstride, V, k_succ, tpl_depth, tpl_width, K_max, m_max,
+        _ptr(sel), _ptr(m_out), _stream(stream, M.device)))
+
+
+def tree_build_mask(tree: DeviceTree, sel: torch.Tensor, m: torch.Tensor, prefix_len: int,
+                    flat: DeviceFlat, dense: Optional[torch.Tensor] = None, stream=None) -> None:
+    L.check("ddt_tree_build_mask", L.load().ddt_tree_build_mask(
+        C.byref(tree.c), _ptr(sel), _ptr(m), prefix_len, C.byref(flat.c), _ptr(dense),
+        _stream(stream, sel.device)))
+
+
+def tree_verify(tree: DeviceTree, flat: DeviceFlat, target: torch.Tensor,
+                draft_arena: Optional[torch.Tensor], temperature: torch.Tensor,
+                uniforms: torch.Tensor, accept_len: torch.Tensor, accept_path: torch.Tensor,
+                next_token: torch.Tensor, ws: torch.Tensor, k_top: int = 0,
+                row_topk: Optional[torch.Tensor] = None, row_argmax: Optional[torch.Tensor] = None,
+                stream=None) -> None:
+    """target: [B][P][V]; draft_arena: [D][B][R][V] (layer-major) or None."""
+    td = logits_desc(target)
+    if draft_arena is not None:
+        dd = logits_desc(draft_arena[0])
+        dref, dls = C.byref(dd), draft_arena.stride(0)
+    else:
+        dref, dls = None, 0
+    L.check("ddt_tree_verify", L.load().ddt_tree_verify(
+        C.byref(tree.c), C.byref(flat.c), C.byref(td), dref, dls, _ptr(temperature),
+        _ptr(uniforms), k_top, _ptr(row_topk), _ptr(row_argmax), _ptr(accept_len),
+        _ptr(accept_path), _ptr(next_token), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream, target.device)))
+
+
+def succ_update(M: torch.Tensor, flat: DeviceFlat, k_succ: int, row_topk: Optional[torch.Tensor] = None,
+                k_top: int = 0, target: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                shared: bool = False, stream=None) -> None:
+    V = M.shape[-2]
+    bstride = 0 if shared else V * k_succ
+    td = C.byref(logits_desc(target)) if target is not None else None
+    wsz = ws.numel() * ws.element_size() if ws is not None else 0
+    L.check("ddt_succ_update", L.load().ddt_succ_update(
+        _ptr(M), bstride, V, k_succ, C.byref(flat.c), _ptr(row_topk), k_top, td, _ptr(ws), wsz,
+        _stream(stream, M.device)))
+
+
+def row_topk(x: torch.Tensor, K: int, ws: torch.Tensor, ids: Optional[torch.Tensor] = None,
+             logc: Optional[torch.Tensor] = None, rmax: Optional[torch.Tensor] = None,
+             rsp: Optional[torch.Tensor] = None, stream=None) -> None:
+    d = logits_desc(x)
+    L.check("ddt_row_topk", L.load().ddt_row_topk(
+        C.byref(d), x.shape[0], x.shape[1], K, _ptr(ids), _ptr(logc), _ptr(rmax), _ptr(rsp),
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream, x.device)))

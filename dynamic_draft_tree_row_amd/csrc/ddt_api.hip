@@ -1,0 +1,368 @@
+// C ABI of the draft-tree library: argument checks on the host, then kernel
+// launches on the caller's stream.  No allocation, no synchronisation.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include "../../include/ddt.h"
+#include "ddt_device.hpp"
+#include "ddt_rowreduce.hpp"
+#include "ddt_tree_kernels.hpp"
+
+namespace {
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline int chunk_elems(int dtype) {
+    return dtype == DDT_BF16 ? RRShape<true>::CH : RRShape<false>::CH;
+}
+
+inline int chunks_of(int V, int dtype) { return (V + chunk_elems(dtype) - 1) / chunk_elems(dtype); }
+
+inline size_t ws_need(long long rows, int V, int dtype, int K) {
+    return (size_t)rows * (size_t)chunks_of(V, dtype) * (size_t)rr_ps(K) * 4u;
+}
+
+inline int launched() { return hipGetLastError() == hipSuccess ? DDT_OK : DDT_ELAUNCH; }
+
+inline bool logits_ok(const ddt_logits* x) {
+    return x != nullptr && x->data != nullptr && x->V >= 1 && x->s0 >= 0 && x->s1 >= 0;
+}
+
+int check_tree(const ddt_tree* t) {
+    if (t == nullptr || t->token == nullptr || t->parent == nullptr || t->depth == nullptr ||
+        t->eslot == nullptr || t->key == nullptr || t->S == nullptr || t->logc == nullptr ||
+        t->rmax == nullptr || t->rsp == nullptr || t->n_nodes == nullptr ||
+        t->layer_base == nullptr || t->n_front == nullptr || t->frontier == nullptr ||
+        t->active == nullptr || t->k_draft == nullptr || t->cont == nullptr ||
+        t->widths == nullptr || t->cast_state == nullptr)
+        return DDT_EINVAL;
+    if (t->B < 1 || t->cap < 2 || t->D_max < 1 || t->R_max < 1) return DDT_EINVAL;
+    if (t->cap > DDT_MAX_NODES || t->D_max > DDT_MAX_DEPTH || t->R_max > DDT_MAX_FRONT)
+        return DDT_ECAPACITY;
+    return DDT_OK;
+}
+
+int check_flat(const ddt_flat* f, int B) {
+    if (f == nullptr || f->node == nullptr || f->token == nullptr || f->parent == nullptr ||
+        f->pos == nullptr || f->mask == nullptr || f->retrieve == nullptr ||
+        f->n_leaves == nullptr || f->m == nullptr)
+        return DDT_EINVAL;
+    if (f->B != B || f->P < 1 || f->W != (f->P + 31) / 32 || f->Dp < 0 || f->L < 1)
+        return DDT_EINVAL;
+    if (f->P > DDT_MAX_VERIFY + 1 || f->Dp > DDT_MAX_DEPTH) return DDT_ECAPACITY;
+    return DDT_OK;
+}
+
+int check_cast(const ddt_cast* c, int B) {
+    if (c->S_T == nullptr || c->S_D == nullptr || c->C1 == nullptr || c->C3 == nullptr)
+        return DDT_EINVAL;
+    if (c->L < 1 || c->M < 1 || c->N < 1 || c->R < 1 || c->R > 8 || c->ctx_verify < 0)
+        return DDT_EINVAL;
+    if (B > 64) return DDT_ECAPACITY;
+    return DDT_OK;
+}
+
+template <class T>
+inline T* carve(char*& p, size_t n) {
+    T* r = (T*)p;
+    p += align256(n * sizeof(T));
+    return r;
+}
+
+int launch_partials(const ddt_logits* x, int n0, int n1, const int32_t* count, int count_add,
+                    int K, void* ws, hipStream_t s) {
+    RowSrc rs;
+    rs.base = x->data; rs.s0 = x->s0; rs.s1 = x->s1; rs.n1 = n1;
+    rs.count = count; rs.count_add = count_add;
+    const int chunks = chunks_of(x->V, x->dtype);
+    const long long blocks = (long long)n0 * n1 * chunks;
+    if (blocks <= 0) return DDT_OK;
+    if (x->dtype == DDT_BF16)
+        hipLaunchKernelGGL(k_row_partial<true>, dim3((unsigned)blocks), dim3(RR_NT), 0, s, rs, x->V,
+                           chunks, K, (uint32_t*)ws);
+    else
+        hipLaunchKernelGGL(k_row_partial<false>, dim3((unsigned)blocks), dim3(RR_NT), 0, s, rs,
+                           x->V, chunks, K, (uint32_t*)ws);
+    return launched();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ddt_strerror(int status) {
+    switch (status) {
+        case DDT_OK: return "ok";
+        case DDT_EINVAL: return "invalid argument (null pointer or inconsistent size/stride)";
+        case DDT_EDTYPE: return "unknown logit dtype";
+        case DDT_ECAPACITY: return "size exceeds a documented limit";
+        case DDT_EWORKSPACE: return "workspace too small";
+        case DDT_ELAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int ddt_chunk_elems(int dtype) {
+    if (dtype != DDT_F32 && dtype != DDT_BF16) return -1;
+    return chunk_elems(dtype);
+}
+
+size_t ddt_workspace_bytes(int rows, int V, int dtype, int K) {
+    if (rows < 0 || V < 1 || K < 1 || (dtype != DDT_F32 && dtype != DDT_BF16)) return 0;
+    return ws_need(rows, V, dtype, K);
+}
+
+size_t ddt_tree_bytes(int B, int cap, int D_max, int R_max) {
+    if (B < 1 || cap < 1 || D_max < 1 || R_max < 1) return 0;
+    const size_t bc = (size_t)B * cap;
+    size_t n = 0;
+    n += 4 * align256(bc * 4);                                 // token parent depth eslot
+    n += align256(bc * 8);                                     // key
+    n += 2 * align256(bc * 4);                                 // S logc
+    n += 2 * align256((size_t)B * D_max * R_max * 4);          // rmax rsp
+    n += 5 * align256((size_t)B * 4);                          // n_nodes layer_base n_front active k_draft
+    n += align256((size_t)B * R_max * 4);                      // frontier
+    n += align256(4);                                          // cont
+    n += align256((size_t)D_max * 4);                          // widths
+    n += align256(16 * 8);                                     // cast_state
+    return n;
+}
+
+int ddt_tree_bind(ddt_tree* t, void* base, size_t bytes, int B, int cap, int D_max, int R_max) {
+    if (t == nullptr || base == nullptr) return DDT_EINVAL;
+    if (((uintptr_t)base & 255u) != 0) return DDT_EINVAL;
+    if (B < 1 || cap < 2 || D_max < 1 || R_max < 1) return DDT_EINVAL;
+    if (cap > DDT_MAX_NODES || D_max > DDT_MAX_DEPTH || R_max > DDT_MAX_FRONT) return DDT_ECAPACITY;
+    if (bytes < ddt_tree_bytes(B, cap, D_max, R_max)) return DDT_EWORKSPACE;
+    const size_t bc = (size_t)B * cap;
+    char* p = (char*)base;
+    t->B = B; t->cap = cap; t->D_max = D_max; t->R_max = R_max;
+    t->token = carve<int32_t>(p, bc);
+    t->parent = carve<int32_t>(p, bc);
+    t->depth = carve<int32_t>(p, bc);
+    t->eslot = carve<int32_t>(p, bc);
+    t->key = carve<uint64_t>(p, bc);
+    t->S = carve<float>(p, bc);
+    t->logc = carve<float>(p, bc);
+    t->rmax = carve<float>(p, (size_t)B * D_max * R_max);
+    t->rsp = carve<float>(p, (size_t)B * D_max * R_max);
+    t->n_nodes = carve<int32_t>(p, B);
+    t->layer_base = carve<int32_t>(p, B);
+    t->n_front = carve<int32_t>(p, B);
+    t->active = carve<int32_t>(p, B);
+    t->k_draft = carve<int32_t>(p, B);
+    t->frontier = carve<int32_t>(p, (size_t)B * R_max);
+    t->cont = carve<int32_t>(p, 1);
+    t->widths = carve<int32_t>(p, D_max);
+    t->cast_state = carve<double>(p, 16);
+    return DDT_OK;
+}
+
+size_t ddt_flat_bytes(int B, int m_max, int Dp) {
+    if (B < 1 || m_max < 0 || Dp < 0) return 0;
+    const size_t P = (size_t)m_max + 1, W = (P + 31) / 32, L = m_max > 1 ? m_max : 1;
+    size_t n = 4 * align256((size_t)B * P * 4);
+    n += align256((size_t)B * P * W * 4);
+    n += align256((size_t)B * L * (Dp + 1) * 4);
+    n += 2 * align256((size_t)B * 4);
+    return n;
+}
+
+int ddt_flat_bind(ddt_flat* f, void* base, size_t bytes, int B, int m_max, int Dp) {
+    if (f == nullptr || base == nullptr || B < 1 || m_max < 0 || Dp < 0) return DDT_EINVAL;
+    if (((uintptr_t)base & 255u) != 0) return DDT_EINVAL;
+    if (m_max > DDT_MAX_VERIFY || Dp > DDT_MAX_DEPTH) return DDT_ECAPACITY;
+    if (bytes < ddt_flat_bytes(B, m_max, Dp)) return DDT_EWORKSPACE;
+    const size_t P = (size_t)m_max + 1, W = (P + 31) / 32, L = m_max > 1 ? m_max : 1;
+    char* p = (char*)base;
+    f->B = B; f->P = (int)P; f->W = (int)W; f->Dp = Dp; f->L = (int)L;
+    f->node = carve<int32_t>(p, B * P);
+    f->token = carve<int32_t>(p, B * P);
+    f->parent = carve<int32_t>(p, B * P);
+    f->pos = carve<int32_t>(p, B * P);
+    f->mask = carve<uint32_t>(p, B * P * W);
+    f->retrieve = carve<int32_t>(p, B * L * (Dp + 1));
+    f->n_leaves = carve<int32_t>(p, B);
+    f->m = carve<int32_t>(p, B);
+    return DDT_OK;
+}
+
+int ddt_tree_expand(const ddt_tree* t, int layer, const int32_t* root_tok, const ddt_logits* logits,
+                    int K_n, int K_e, const ddt_cast* cast, const ddt_graft_gate* gate, void* ws,
+                    size_t ws_bytes, void* stream) {
+    int st = check_tree(t);
+    if (st) return st;
+    if (!logits_ok(logits) || ws == nullptr) return DDT_EINVAL;
+    if (logits->dtype != DDT_F32 && logits->dtype != DDT_BF16) return DDT_EDTYPE;
+    if (layer < 1 || layer > t->D_max) return DDT_EINVAL;
+    if (layer == 1 && root_tok == nullptr) return DDT_EINVAL;
+    if (K_n < 1 || K_e < 1 || K_n > logits->V) return DDT_EINVAL;
+    if (K_n > DDT_MAX_K || K_e > t->R_max) return DDT_ECAPACITY;
+    if (t->R_max * K_n > AT_SORT) return DDT_ECAPACITY;
+    if (chunks_of(logits->V, logits->dtype) > DDT_MAX_CHUNKS) return DDT_ECAPACITY;
+    if ((long long)1 + K_n + (long long)(t->D_max - 1) * K_e * K_n > t->cap) return DDT_ECAPACITY;
+    if (cast != nullptr && gate != nullptr) return DDT_EINVAL;
+    if (cast != nullptr && (st = check_cast(cast, t->B))) return st;
+    if (cast != nullptr && K_e > cast->N) return DDT_EINVAL;
+    if (gate != nullptr && (gate->n_ck < 0 || gate->n_ck > 4 || gate->K_max < 1)) return DDT_EINVAL;
+    const int R = layer == 1 ? 1 : t->R_max;
+    if (ws_bytes < ws_need((long long)t->B * t->R_max, logits->V, logits->dtype, K_n))
+        return DDT_EWORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+
+    st = launch_partials(logits, t->B, R, layer == 1 ? nullptr : t->n_front, 0, K_n, ws, s);
+    if (st) return st;
+
+    AttachArgs a;
+    a.t = *t; a.part = (const uint32_t*)ws; a.root_tok = root_tok; a.layer = layer; a.R = R;
+    a.chunks = chunks_of(logits->V, logits->dtype); a.K_n = K_n; a.K_e = K_e;
+    a.ck = 0; a.kd_ck = 0; a.tau = 0.f; a.gate_on = gate != nullptr; a.K_max = gate ? gate->K_max : 0;
+    if (gate != nullptr)
+        for (int i = 0; i < gate->n_ck; ++i)
+            if (gate->ck_depth[i] == layer) { a.ck = 1; a.kd_ck = gate->k_draft[i]; a.tau = gate->tau[i]; }
+    hipLaunchKernelGGL(k_attach, dim3(t->B), dim3(AT_NT), 0, s, a);
+    if ((st = launched())) return st;
+
+    if (cast != nullptr) {
+        CastArgs c;
+        c.t = *t; c.c = *cast; c.layer = layer; c.K_e = K_e;
+        hipLaunchKernelGGL(k_cast, dim3(1), dim3(CS_NT), 0, s, c);
+        if ((st = launched())) return st;
+    }
+    return DDT_OK;
+}
+
+int ddt_tree_rerank(const ddt_tree* t, int m_max, const ddt_cast* cast, int use_k_draft,
+                    int32_t* sel, int32_t* m_out, void* stream) {
+    int st = check_tree(t);
+    if (st) return st;
+    if (sel == nullptr || m_out == nullptr || m_max < 0) return DDT_EINVAL;
+    if (m_max > DDT_MAX_VERIFY) return DDT_ECAPACITY;
+    if (cast != nullptr && (st = check_cast(cast, t->B))) return st;
+    if (cast != nullptr && m_max > cast->N) return DDT_EINVAL;
+    RerankArgs a;
+    a.t = *t;
+    if (cast) a.c = *cast; else memset(&a.c, 0, sizeof(a.c));
+    a.cast_on = cast != nullptr; a.use_k_draft = use_k_draft != 0; a.m_max = m_max;
+    a.sel = sel; a.m_out = m_out;
+    hipLaunchKernelGGL(k_rerank, dim3(t->B), dim3(RK_NT), 0, (hipStream_t)stream, a);
+    return launched();
+}
+
+int ddt_succ_gather(const ddt_tree* t, const int32_t* M, int64_t M_bstride, int V, int k_succ,
+                    int tpl_depth, int tpl_width, int K_max, int m_max, int32_t* sel,
+                    int32_t* m_out, void* stream) {
+    int st = check_tree(t);
+    if (st) return st;
+    if (M == nullptr || sel == nullptr || m_out == nullptr || V < 1 || M_bstride < 0) return DDT_EINVAL;
+    if (k_succ < 1 || tpl_depth < 1 || tpl_width < 1 || K_max < 1) return DDT_EINVAL;
+    if (tpl_width > k_succ || tpl_width > 32) return DDT_EINVAL;
+    if (tpl_depth > DDT_MAX_DEPTH || K_max > DDT_MAX_VERIFY) return DDT_ECAPACITY;
+    if (m_max < K_max) return DDT_EINVAL;
+    GatherArgs a;
+    a.t = *t; a.M = M; a.M_bstride = M_bstride; a.V = V; a.k_succ = k_succ; a.depth = tpl_depth;
+    a.width = tpl_width; a.K_max = K_max; a.m_cap = m_max; a.sel = sel; a.m_out = m_out;
+    hipLaunchKernelGGL(k_succ_gather, dim3(t->B), dim3(64), 0, (hipStream_t)stream, a);
+    return launched();
+}
+
+int ddt_tree_build_mask(const ddt_tree* t, const int32_t* sel, const int32_t* m, int prefix_len,
+                        const ddt_flat* f, uint8_t* dense, void* stream) {
+    int st = check_tree(t);
+    if (st) return st;
+    if ((st = check_flat(f, t->B))) return st;
+    if (sel == nullptr || m == nullptr || prefix_len < 0) return DDT_EINVAL;
+    if (f->P > MK_NT || f->W > 8) return DDT_ECAPACITY;
+    MaskArgs a;
+    a.t = *t; a.f = *f; a.sel = sel; a.m = m; a.prefix = prefix_len; a.dense = dense;
+    hipLaunchKernelGGL(k_build_mask, dim3(t->B), dim3(MK_NT), 0, (hipStream_t)stream, a);
+    return launched();
+}
+
+int ddt_tree_verify(const ddt_tree* t, const ddt_flat* f, const ddt_logits* target,
+                    const ddt_logits* draft, int64_t draft_layer_stride, const float* temperature,
+                    const float* uniforms, int k_top, int32_t* row_topk, int32_t* row_argmax,
+                    int32_t* accept_len, int32_t* accept_path, int32_t* next_token, void* ws,
+                    size_t ws_bytes, void* stream) {
+    int st = check_tree(t);
+    if (st) return st;
+    if ((st = check_flat(f, t->B))) return st;
+    if (!logits_ok(target) || temperature == nullptr || uniforms == nullptr || ws == nullptr ||
+        accept_len == nullptr || accept_path == nullptr || next_token == nullptr)
+        return DDT_EINVAL;
+    if (target->dtype != DDT_F32 && target->dtype != DDT_BF16) return DDT_EDTYPE;
+    if (draft != nullptr && (!logits_ok(draft) || draft->dtype != target->dtype ||
+                             draft->V != target->V || draft_layer_stride < 0))
+        return DDT_EINVAL;
+    if (k_top < 0 || k_top > DDT_MAX_K || k_top > target->V) return DDT_ECAPACITY;
+    if (k_top > 0 && row_topk == nullptr) return DDT_EINVAL;
+    if (f->P > MK_NT) return DDT_ECAPACITY;
+    if (chunks_of(target->V, target->dtype) > DDT_MAX_CHUNKS) return DDT_ECAPACITY;
+    if ((target->V + VF_TILE - 1) / VF_TILE > VF_MAXTILES) return DDT_ECAPACITY;
+    const int Kp = k_top > 0 ? k_top : 1;
+    if (ws_bytes < ws_need((long long)t->B * f->P, target->V, target->dtype, Kp))
+        return DDT_EWORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    st = launch_partials(target, t->B, f->P, f->m, 1, Kp, ws, s);
+    if (st) return st;
+    VerifyArgs a;
+    a.t = *t; a.f = *f; a.part = (const uint32_t*)ws;
+    a.chunks = chunks_of(target->V, target->dtype); a.Kp = Kp;
+    a.tgt = target->data; a.bf16 = target->dtype == DDT_BF16; a.V = target->V;
+    a.ts0 = target->s0; a.ts1 = target->s1;
+    a.drf = draft ? draft->data : nullptr; a.dl = draft_layer_stride;
+    a.ds0 = draft ? draft->s0 : 0; a.ds1 = draft ? draft->s1 : 0;
+    a.temperature = temperature; a.U = uniforms; a.k_top = k_top; a.row_topk = row_topk;
+    a.row_argmax = row_argmax; a.accept_len = accept_len; a.accept_path = accept_path;
+    a.next_token = next_token;
+    hipLaunchKernelGGL(k_verify, dim3(t->B), dim3(VF_NT), 0, s, a);
+    return launched();
+}
+
+int ddt_succ_update(int32_t* M, int64_t M_bstride, int V, int k_succ, const ddt_flat* f,
+                    const int32_t* row_topk, int k_top, const ddt_logits* target, void* ws,
+                    size_t ws_bytes, void* stream) {
+    if (M == nullptr || f == nullptr || V < 1 || M_bstride < 0) return DDT_EINVAL;
+    int st = check_flat(f, f->B);
+    if (st) return st;
+    if (k_succ < 1 || k_succ > DDT_MAX_K) return DDT_ECAPACITY;
+    hipStream_t s = (hipStream_t)stream;
+    UpdateArgs a;
+    a.f = *f; a.M = M; a.M_bstride = M_bstride; a.V = V; a.k_succ = k_succ; a.B = f->B;
+    a.shared = M_bstride == 0 && f->B > 1;
+    a.row_topk = row_topk; a.k_top = k_top; a.part = nullptr; a.chunks = 0; a.Kp = k_succ;
+    if (row_topk != nullptr) {
+        if (k_top < k_succ) return DDT_EINVAL;
+    } else {
+        if (!logits_ok(target) || ws == nullptr || target->V != V) return DDT_EINVAL;
+        if (target->dtype != DDT_F32 && target->dtype != DDT_BF16) return DDT_EDTYPE;
+        if (chunks_of(V, target->dtype) > DDT_MAX_CHUNKS) return DDT_ECAPACITY;
+        if (ws_bytes < ws_need((long long)f->B * f->P, V, target->dtype, k_succ)) return DDT_EWORKSPACE;
+        st = launch_partials(target, f->B, f->P, f->m, 1, k_succ, ws, s);
+        if (st) return st;
+        a.part = (const uint32_t*)ws; a.chunks = chunks_of(V, target->dtype);
+    }
+    hipLaunchKernelGGL(k_succ_update, dim3(a.shared ? 1 : f->B), dim3(UP_NT), 0, s, a);
+    return launched();
+}
+
+int ddt_row_topk(const ddt_logits* x, int n0, int n1, int K, int32_t* ids, float* logc, float* rmax,
+                 float* rsp, void* ws, size_t ws_bytes, void* stream) {
+    if (!logits_ok(x) || ws == nullptr || n0 < 0 || n1 < 0) return DDT_EINVAL;
+    if (x->dtype != DDT_F32 && x->dtype != DDT_BF16) return DDT_EDTYPE;
+    if (K < 1 || K > x->V) return DDT_EINVAL;
+    if (K > DDT_MAX_K || chunks_of(x->V, x->dtype) > DDT_MAX_CHUNKS) return DDT_ECAPACITY;
+    const long long rows = (long long)n0 * n1;
+    if (ws_bytes < ws_need(rows, x->V, x->dtype, K)) return DDT_EWORKSPACE;
+    if (rows == 0) return DDT_OK;
+    hipStream_t s = (hipStream_t)stream;
+    int st = launch_partials(x, n0, n1, nullptr, 0, K, ws, s);
+    if (st) return st;
+    RowFinishArgs a;
+    a.part = (const uint32_t*)ws; a.rows = (int)rows; a.chunks = chunks_of(x->V, x->dtype); a.K = K;
+    a.ids = ids; a.logc = logc; a.rmax = rmax; a.rsp = rsp;
+    hipLaunchKernelGGL(k_row_finish, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
+    return launched();
+}
+
+}  // extern "C"

@@ -1,0 +1,892 @@
+// Tree kernels: attach + frontier, CAST width/depth, rerank, retrieval graft,
+// flatten + mask, accept walk, successor refresh.  One workgroup per batch row
+// unless noted; every index derived from device state is bounded by the
+// capacities passed in, so corrupt state cannot push an access out of range.
+#pragma once
+#include "ddt_device.hpp"
+#include "ddt_rowreduce.hpp"
+#include "../../include/ddt.h"
+
+// ---------------------------------------------------------------------------
+// attach: merge the layer's row partials, create children, pick the frontier
+// ---------------------------------------------------------------------------
+//
+// EAGLE-2 explainer, expansion section: every expanded node gets its draft
+// row's top-K_n tokens as children, value(child) = value(parent) x
+// confidence(child), kept here as S_child = S_parent + log c in fp32 (Graft
+// review step 1, S_{d,j} recursion).  The next frontier is the best K_e of
+// the newest layer by value (ties: canonical key).  Graft review step 1: at a
+// checkpoint depth the row stops unless exp(max S of the layer) > tau.
+
+struct AttachArgs {
+    ddt_tree t;
+    const uint32_t* part;
+    const int32_t* root_tok;
+    int layer, R, chunks, K_n, K_e;
+    int ck, kd_ck, K_max, gate_on;  // ck: 1 if this layer is a Graft checkpoint
+    float tau;
+};
+
+#define AT_NT 256
+#define AT_SORT 1024
+
+__global__ __launch_bounds__(AT_NT) void k_attach(AttachArgs a) {
+    const ddt_tree& t = a.t;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int cap = t.cap;
+    __shared__ float s_M[DDT_MAX_FRONT], s_S[DDT_MAX_FRONT];
+    __shared__ int s_par[DDT_MAX_FRONT];
+    __shared__ uint64_t s_key[DDT_MAX_FRONT * DDT_MAX_K];
+    __shared__ uint32_t srt_a[AT_SORT];
+    __shared__ uint64_t srt_b[AT_SORT];
+    __shared__ int32_t srt_i[AT_SORT];
+    __shared__ int s_Rd, s_base;
+
+    int32_t* tok = t.token + (size_t)b * cap;
+    int32_t* par = t.parent + (size_t)b * cap;
+    int32_t* dep = t.depth + (size_t)b * cap;
+    int32_t* esl = t.eslot + (size_t)b * cap;
+    uint64_t* key = t.key + (size_t)b * cap;
+    float* S = t.S + (size_t)b * cap;
+    float* lc = t.logc + (size_t)b * cap;
+
+    if (tid == 0) {
+        int Rd, base;
+        if (a.layer == 1) {
+            tok[0] = a.root_tok[b]; par[0] = -1; dep[0] = 0; esl[0] = -1; key[0] = 0ull;
+            S[0] = 0.f; lc[0] = 0.f;
+            t.frontier[(size_t)b * t.R_max] = 0;
+            t.active[b] = 1;
+            t.k_draft[b] = a.gate_on ? a.K_max : 0;
+            Rd = 1; base = 1;
+        } else {
+            Rd = min(max(t.n_front[b], 0), a.R);
+            base = t.n_nodes[b];
+            if (base < 1 || base + Rd * a.K_n > cap) Rd = 0;      // capacity guard
+        }
+        s_Rd = Rd; s_base = base;
+    }
+    __syncthreads();
+    const int Rd = s_Rd, base = s_base;
+    if (a.layer == 1 && tid == 0) t.n_nodes[b] = 1;
+    if (Rd == 0) {
+        if (tid == 0) t.n_front[b] = 0;
+        return;
+    }
+    for (int j = tid; j < Rd; j += AT_NT) {
+        const int u = a.layer == 1 ? 0 : t.frontier[(size_t)b * t.R_max + j];
+        s_par[j] = (u >= 0 && u < base) ? u : 0;
+    }
+    // merge row partials: one wave per frontier slot
+    for (int j = wid; j < Rd; j += AT_NT / 64) {
+        float M, Sp;
+        const uint32_t* p = a.part + ((size_t)(b * a.R + j) * a.chunks) * rr_ps(a.K_n);
+        const uint64_t mine = merge_row_wave(p, a.chunks, a.K_n, M, Sp);
+        if (lane < a.K_n) s_key[j * a.K_n + lane] = mine;
+        if (lane == 0) { s_M[j] = M; s_S[j] = Sp; }
+    }
+    __syncthreads();
+    const int count = Rd * a.K_n;
+    const int n2 = next_pow2(count);
+    for (int q = tid; q < n2; q += AT_NT) {
+        if (q < count) {
+            const int j = q / a.K_n, r = q - j * a.K_n;
+            const int u = s_par[j];
+            const uint64_t kk = s_key[j * a.K_n + r];
+            const float l1p = log1pf(s_S[j]);
+            const float logc = (vkey_val(kk) - s_M[j]) - l1p;
+            const float Sv = S[u] + logc;
+            const int du = dep[u];
+            const uint64_t nk = key_child(key[u], du, r, 0);
+            const int node = base + q;
+            tok[node] = vkey_id(kk); par[node] = u; dep[node] = du + 1; esl[node] = -1;
+            S[node] = Sv; lc[node] = logc; key[node] = nk;
+            srt_a[q] = ~ord_f32(Sv); srt_b[q] = nk; srt_i[q] = node;
+            if (r == 0) {
+                esl[u] = j;
+                const size_t ri = ((size_t)b * t.D_max + (a.layer - 1)) * t.R_max + j;
+                t.rmax[ri] = s_M[j];
+                t.rsp[ri] = s_S[j];
+            }
+        } else {
+            srt_a[q] = 0xFFFFFFFFu; srt_b[q] = ~0ull; srt_i[q] = -1;
+        }
+    }
+    __syncthreads();
+    bitonic_sort_lds<AT_NT>(srt_a, srt_b, srt_i, n2);
+    const int nkeep = min(count, t.R_max);
+    for (int k = tid; k < nkeep; k += AT_NT) t.frontier[(size_t)b * t.R_max + k] = srt_i[k];
+    if (tid == 0) {
+        t.n_nodes[b] = base + count;
+        t.layer_base[b] = base;
+        int nf = min(a.K_e, count);
+        if (a.layer >= t.D_max) nf = 0;
+        if (a.ck) {
+            const float smax = unord_f32(~srt_a[0]);
+            if (!(expf(smax) > a.tau)) {       // g_d = 1[c_d > tau_d]
+                t.active[b] = 0;
+                t.k_draft[b] = a.kd_ck;
+                nf = 0;
+            }
+        }
+        t.n_front[b] = nf;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// CAST width and depth for the whole batch (one workgroup)
+// ---------------------------------------------------------------------------
+//
+// CAST notes, key design 2: width n_i = anchor scan of the batch-averaged
+// cumulative utility u_k of the layer's sorted values e^S against the cost
+// c_k = S_D[sel(ctx)][k] / S_T[sel(ctx)][1] and threshold C1[i].  Key design
+// 3: FIFO A of the last R gain ratios u_n(i)/u_n(i-1), initially {1}; grow
+// another layer iff mean(A) * u_n / c_n >= C2 (and the depth cap allows).
+// Key design 1: select(c) = min(floor(c/L), M-1) (the printed max is read as
+// min).  State lives in t.cast_state: [0..7] FIFO, [8] length, [9] previous
+// u_n, [10] context (tree tokens fed so far).
+
+struct CastArgs {
+    ddt_tree t;
+    ddt_cast c;
+    int layer, K_e;
+};
+
+#define CS_NT 256
+
+__device__ __forceinline__ int cast_sel_row(long long c, int L, int M) {
+    long long r = c / L;
+    return (int)(r < M - 1 ? r : M - 1);
+}
+
+// keep 1, move the anchor to k while the average marginal from it reaches C
+__device__ int anchor_scan_dev(const double* u, const double* c, double C, int kmax) {
+    if (kmax <= 0) return 0;
+    int a = 1;
+    for (int k = 2; k <= kmax; ++k) {
+        const double du = u[k] - u[a], dc = c[k] - c[a];
+        if (dc > 0.0) {
+            if (du / dc >= C) a = k;
+        } else if (du > 0.0) {
+            a = k;
+        }
+    }
+    return a;
+}
+
+__global__ __launch_bounds__(CS_NT) void k_cast(CastArgs a) {
+    const ddt_tree& t = a.t;
+    const int tid = threadIdx.x, B = t.B;
+    __shared__ double s_v[64 * DDT_MAX_FRONT];
+    __shared__ double s_col[DDT_MAX_FRONT + 1];
+    __shared__ double u[DDT_MAX_FRONT + 1], c[DDT_MAX_FRONT + 1];
+    __shared__ int s_kcap, s_n, s_go;
+    double* st = t.cast_state;
+    if (tid == 0) {
+        if (a.layer == 1) {
+            st[0] = 1.0;
+            for (int i = 1; i < 8; ++i) st[i] = 0.0;
+            st[8] = 1.0; st[9] = -1.0; st[10] = 0.0;
+            t.cont[0] = 1;
+        }
+        s_go = t.cont[0];
+        int kc = a.K_e;
+        for (int b = 0; b < B; ++b) kc = min(kc, t.n_nodes[b] - t.layer_base[b]);
+        s_kcap = max(0, min(kc, t.R_max));
+    }
+    __syncthreads();
+    if (!s_go) {
+        for (int b = tid; b < B; b += CS_NT) t.n_front[b] = 0;
+        return;
+    }
+    const int kcap = s_kcap;
+    for (int q = tid; q < B * kcap; q += CS_NT) {
+        const int b = q / kcap, k = q - b * kcap;
+        const int node = t.frontier[(size_t)b * t.R_max + k];
+        const int nn = min(max(node, 0), t.cap - 1);
+        s_v[q] = exp((double)t.S[(size_t)b * t.cap + nn]);
+    }
+    __syncthreads();
+    for (int k = tid; k < kcap; k += CS_NT) {
+        double sum = 0.0;
+        for (int b = 0; b < B; ++b) sum += s_v[b * kcap + k];
+        s_col[k] = sum;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        u[0] = 0.0; c[0] = 0.0;
+        const int ctx = (int)st[10];
+        const int row = cast_sel_row(ctx, a.c.L, a.c.M);
+        const float* SD = a.c.S_D + (size_t)row * (a.c.N + 1);
+        const float* ST = a.c.S_T + (size_t)row * (a.c.N + 1);
+        for (int k = 1; k <= kcap; ++k) {
+            u[k] = u[k - 1] + s_col[k - 1] / (double)B;
+            c[k] = (double)SD[k] / (double)ST[1];
+        }
+        const int n = anchor_scan_dev(u, c, (double)a.c.C1[a.layer - 1], kcap);
+        int len = (int)st[8];
+        if (st[9] >= 0.0) {                        // push the previous layer's gain ratio
+            const double phi = st[9] > 0.0 ? u[n] / st[9] : 0.0;
+            if (len < 8) st[len++] = phi;
+            if (len > a.c.R) {
+                for (int i = 1; i < len; ++i) st[i - 1] = st[i];
+                --len;
+            }
+        }
+        st[8] = (double)len;
+        double mean = 0.0;
+        for (int i = 0; i < len; ++i) mean += st[i];
+        mean /= (double)len;
+        const double score = n > 0 ? mean * u[n] / c[n] : 0.0;
+        const bool stop = (a.layer >= t.D_max) || !(score >= (double)a.c.C2);
+        st[9] = u[n];
+        st[10] = (double)(ctx + n);
+        t.widths[a.layer - 1] = n;
+        t.cont[0] = stop ? 0 : 1;
+        s_n = stop ? 0 : n;
+    }
+    __syncthreads();
+    for (int b = tid; b < B; b += CS_NT) t.n_front[b] = s_n;
+}
+
+// ---------------------------------------------------------------------------
+// rerank: top-m of all non-root nodes by (S desc, key asc)
+// ---------------------------------------------------------------------------
+//
+// EAGLE-2 explainer, reranking section: every candidate node is ranked by
+// value, the top m are verified; a child never outranks its parent and equal
+// values go to the shallower node, so the set is a connected subtree.  CAST
+// key design 4: m per row by the anchor scan of the sorted cumulative values
+// against the verify cost.  Graft: m = the row's k_draft.
+
+struct RerankArgs {
+    ddt_tree t;
+    ddt_cast c;
+    int cast_on, use_k_draft, m_max;
+    int32_t* sel;
+    int32_t* m_out;
+};
+
+#define RK_NT 1024
+#define RK_SORT DDT_MAX_NODES
+
+__global__ __launch_bounds__(RK_NT) void k_rerank(RerankArgs a) {
+    const ddt_tree& t = a.t;
+    const int b = blockIdx.x, tid = threadIdx.x;
+    __shared__ uint32_t sa[RK_SORT];
+    __shared__ uint64_t sb[RK_SORT];
+    __shared__ int32_t si[RK_SORT];
+    __shared__ double s_v[DDT_MAX_VERIFY + 1];
+    __shared__ double u[DDT_MAX_VERIFY + 1], c[DDT_MAX_VERIFY + 1];
+    __shared__ int s_m;
+    const int nn = min(max(t.n_nodes[b], 1), t.cap);
+    const int N = nn - 1;
+    const int n2 = next_pow2(N > 0 ? N : 1);
+    const float* S = t.S + (size_t)b * t.cap;
+    const uint64_t* key = t.key + (size_t)b * t.cap;
+    for (int q = tid; q < n2; q += RK_NT) {
+        if (q < N) {
+            sa[q] = ~ord_f32(S[1 + q]); sb[q] = key[1 + q]; si[q] = 1 + q;
+        } else {
+            sa[q] = 0xFFFFFFFFu; sb[q] = ~0ull; si[q] = -1;
+        }
+    }
+    __syncthreads();
+    bitonic_sort_lds<RK_NT>(sa, sb, si, n2);
+    const int kmax = min(a.m_max, N);
+    if (a.cast_on) {
+        for (int k = tid; k < kmax; k += RK_NT) s_v[k] = exp((double)unord_f32(~sa[k]));
+        __syncthreads();
+        if (tid == 0) {
+            u[0] = 0.0; c[0] = 0.0;
+            const int row = cast_sel_row(a.c.ctx_verify, a.c.L, a.c.M);
+            const float* ST = a.c.S_T + (size_t)row * (a.c.N + 1);
+            for (int k = 1; k <= kmax; ++k) {
+                u[k] = u[k - 1] + s_v[k - 1];
+                c[k] = (double)ST[k] / (double)ST[1];
+            }
+            s_m = anchor_scan_dev(u, c, (double)a.c.C3[b], kmax);
+        }
+    } else if (tid == 0) {
+        s_m = a.use_k_draft ? min(max(t.k_draft[b], 0), kmax) : kmax;
+    }
+    __syncthreads();
+    const int m = s_m;
+    int32_t* sel = a.sel + (size_t)b * (a.m_max + 1);
+    for (int k = tid; k <= a.m_max; k += RK_NT) sel[k] = k == 0 ? 0 : (k <= m ? si[k - 1] : -1);
+    if (tid == 0) a.m_out[b] = m;
+}
+
+// ---------------------------------------------------------------------------
+// Graft retrieval graft: template envelope by successor-matrix row lookups
+// ---------------------------------------------------------------------------
+//
+// Graft review step 2: root-centred retrieval, x_u = M[x_parent(u), r_u].
+// Template (reading of "depth x width"): `width` chains under the root; chain
+// c starts with successor c of the root token and continues with successor 0
+// of its own last token; level-major order, the first K_ret = K_max - m kept.
+
+struct GatherArgs {
+    ddt_tree t;
+    const int32_t* M;
+    int64_t M_bstride;
+    int V, k_succ, depth, width, K_max, m_cap;
+    int32_t* sel;
+    int32_t* m_out;
+};
+
+__global__ __launch_bounds__(64) void k_succ_gather(GatherArgs a) {
+    const ddt_tree& t = a.t;
+    const int b = blockIdx.x, c = threadIdx.x;
+    __shared__ int s_kret, s_base, s_m;
+    if (c == 0) {
+        const int m = min(max(a.m_out[b], 0), a.K_max);
+        int kret = a.K_max - m;
+        const int base = min(max(t.n_nodes[b], 1), t.cap);
+        kret = min(kret, min(t.cap - base, a.depth * a.width));
+        s_kret = max(kret, 0); s_base = base; s_m = m;
+    }
+    __syncthreads();
+    const int kret = s_kret, base = s_base, m = s_m;
+    const size_t o = (size_t)b * t.cap;
+    const int32_t* Mb = a.M + (size_t)b * a.M_bstride;
+    int32_t* sel = a.sel + (size_t)b * (a.m_cap + 1);
+    if (c < a.width) {
+        int prev = 0;                              // parent node (root for level 1)
+        int ptok = t.token[o];
+        for (int lvl = 1; lvl <= a.depth; ++lvl) {
+            const int idx = (lvl - 1) * a.width + c;
+            if (idx >= kret) break;
+            const int r = lvl == 1 ? c : 0;
+            const int pt = min(max(ptok, 0), a.V - 1);
+            const int tk = Mb[(size_t)pt * a.k_succ + r];
+            const int node = base + idx;
+            t.token[o + node] = tk;
+            t.parent[o + node] = prev;
+            t.depth[o + node] = lvl;
+            t.eslot[o + node] = -1;
+            t.key[o + node] = key_child(lvl == 1 ? 0ull : t.key[o + prev], lvl - 1, r, 1);
+            t.S[o + node] = -INFINITY;
+            t.logc[o + node] = -INFINITY;
+            if (1 + m + idx <= a.m_cap) sel[1 + m + idx] = node;
+            prev = node;
+            ptok = tk;
+        }
+    }
+    __syncthreads();
+    if (c == 0) {
+        t.n_nodes[b] = base + kret;
+        a.m_out[b] = min(m + kret, a.m_cap);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// flatten + ancestor mask + position ids + retrieve paths
+// ---------------------------------------------------------------------------
+//
+// EAGLE-2 explainer, reranking section (flatten to a 1-D list, mask by the
+// tree) and engineering difficulty one (mask by parent relation, never by
+// linear position); Graft review step 3 (tree position ids, ancestor mask,
+// candidate path indices).  Flat order: ascending canonical key.
+
+struct MaskArgs {
+    ddt_tree t;
+    ddt_flat f;
+    const int32_t* sel;
+    const int32_t* m;
+    int prefix;
+    uint8_t* dense;
+};
+
+#define MK_NT 256
+
+__global__ __launch_bounds__(MK_NT) void k_build_mask(MaskArgs a) {
+    const ddt_tree& t = a.t;
+    const ddt_flat& f = a.f;
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const int P = f.P, W = f.W, Dp = f.Dp;
+    __shared__ uint32_t sa[MK_NT];
+    __shared__ uint64_t sb[MK_NT];
+    __shared__ int32_t si[MK_NT];
+    __shared__ int16_t s_map[DDT_MAX_NODES];
+    __shared__ int s_fp[MK_NT], s_dep[MK_NT], s_hc[MK_NT], s_lidx[MK_NT];
+    __shared__ int s_nl;
+    const int m = min(max(a.m[b], 0), P - 1);
+    const int n = m + 1;
+    const int n2 = next_pow2(P);
+    const size_t o = (size_t)b * t.cap;
+    const int32_t* sel = a.sel + (size_t)b * P;
+    for (int q = tid; q < n2; q += MK_NT) {
+        int node = q < n ? sel[q] : -1;
+        if (node < 0 || node >= t.cap) node = -1;
+        sa[q] = 0u;
+        sb[q] = node >= 0 ? t.key[o + node] : ~0ull;
+        si[q] = node;
+    }
+    for (int q = tid; q < DDT_MAX_NODES; q += MK_NT) s_map[q] = -1;
+    __syncthreads();
+    bitonic_sort_lds<MK_NT>(sa, sb, si, n2);
+    for (int i = tid; i < n; i += MK_NT) if (si[i] >= 0) s_map[si[i]] = (int16_t)i;
+    __syncthreads();
+    const size_t fo = (size_t)b * P;
+    for (int i = tid; i < P; i += MK_NT) {
+        int node = -1, tk = -1, fp = -1, d = 0;
+        if (i < n && si[i] >= 0) {
+            node = si[i];
+            tk = t.token[o + node];
+            const int pn = t.parent[o + node];
+            fp = (pn >= 0 && pn < t.cap) ? s_map[pn] : -1;
+            d = t.depth[o + node];
+        }
+        f.node[fo + i] = node;
+        f.token[fo + i] = tk;
+        f.parent[fo + i] = fp;
+        f.pos[fo + i] = a.prefix + d;
+        s_fp[i] = fp; s_dep[i] = d; s_hc[i] = 0;
+    }
+    __syncthreads();
+    for (int i = tid; i < P; i += MK_NT) {
+        const int cols = a.prefix + P;
+        uint8_t* dr = a.dense != nullptr ? a.dense + ((size_t)b * P + i) * cols : nullptr;
+        if (dr != nullptr)
+            for (int col = 0; col < a.prefix; ++col) dr[col] = 1;
+        for (int k = 0; k < W; ++k) {
+            uint32_t word = 0u;
+            int j = i, guard = 0;
+            while (j >= 0 && guard++ <= DDT_MAX_DEPTH + 1) {
+                if ((j >> 5) == k) word |= 1u << (j & 31);
+                j = (i < n) ? s_fp[j] : -1;
+            }
+            f.mask[(fo + i) * W + k] = word;
+            if (dr != nullptr)
+                for (int e = 0; e < 32 && k * 32 + e < P; ++e)
+                    dr[a.prefix + k * 32 + e] = (uint8_t)((word >> e) & 1u);
+        }
+        if (i >= 1 && i < n && s_fp[i] >= 0) s_hc[s_fp[i]] = 1;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int c = 0;
+        for (int i = 0; i < n; ++i) {
+            if (!s_hc[i]) s_lidx[i] = c++;
+            else s_lidx[i] = -1;
+        }
+        s_nl = c;
+        f.n_leaves[b] = c;
+        f.m[b] = m;
+    }
+    __syncthreads();
+    const int L = f.L;
+    int32_t* ret = f.retrieve + (size_t)b * L * (Dp + 1);
+    for (int i = tid; i < n; i += MK_NT) {
+        const int li = s_lidx[i];
+        if (li < 0 || li >= L) continue;
+        int32_t* row = ret + (size_t)li * (Dp + 1);
+        const int d = min(s_dep[i], Dp);
+        for (int s = d + 1; s <= Dp; ++s) row[s] = -1;
+        int j = i;
+        for (int s = d; s >= 0; --s) {
+            row[s] = j;
+            j = j >= 0 ? s_fp[j] : -1;
+        }
+    }
+    for (int q = s_nl * (Dp + 1) + tid; q < L * (Dp + 1); q += MK_NT) ret[q] = -1;
+}
+
+// ---------------------------------------------------------------------------
+// accept walk
+// ---------------------------------------------------------------------------
+//
+// EAGLE-2 explainer: at T = 0 acceptance is an argmax match along candidate
+// paths (losslessness section); at T > 0 a drafted token x is accepted with
+// probability min(1, p(x)/q(x)) and a rejection resamples from
+// norm(max(0, p - q)) (ledger section).  Tree reading: siblings are tried in
+// flat order with the residual carried between them.
+
+struct VerifyArgs {
+    ddt_tree t;
+    ddt_flat f;
+    const uint32_t* part;
+    int chunks, Kp;
+    const void* tgt;
+    int bf16, V;
+    int64_t ts0, ts1;
+    const void* drf;
+    int64_t dl, ds0, ds1;
+    const float* temperature;
+    const float* U;
+    int k_top;
+    int32_t* row_topk;
+    int32_t* row_argmax;
+    int32_t* accept_len;
+    int32_t* accept_path;
+    int32_t* next_token;
+};
+
+#define VF_NT 256
+#define VF_TILE 512            // one wave x 8 elements
+#define VF_MAXTILES 1024       // V <= 524288
+
+__device__ __forceinline__ float ld_logit(const void* base, int bf16, int64_t i) {
+    return bf16 ? __uint_as_float((uint32_t)((const uint16_t*)base)[i] << 16) : ((const float*)base)[i];
+}
+
+struct WalkState {
+    const void* trow;
+    const void* drow;
+    int bf16;
+    float Mt, Md, invT;
+    double Zt, Zd;
+    int k;
+    const double* Zs;
+};
+
+// residual chain value p_k(v) and draft q(v) of one vocabulary entry
+__device__ __forceinline__ void walk_pq(const WalkState& w, int v, double& p, double& q) {
+    const float tv = ld_logit(w.trow, w.bf16, v), dv = ld_logit(w.drow, w.bf16, v);
+    p = (double)expf((tv - w.Mt) * w.invT) / w.Zt;
+    q = (double)expf((dv - w.Md) * w.invT) / w.Zd;
+    for (int r = 0; r < w.k; ++r) {
+        const double z = w.Zs[r];
+        if (z > 0.0) p = fmax(0.0, p - q) / z;
+    }
+}
+
+__global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
+    const ddt_tree& t = a.t;
+    const ddt_flat& f = a.f;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int P = f.P, Dp = f.Dp;
+    __shared__ int s_am[MK_NT];
+    __shared__ float s_M[MK_NT], s_S[MK_NT];
+    __shared__ int s_fp[MK_NT], s_ft[MK_NT];
+    __shared__ double s_tile[VF_MAXTILES];
+    __shared__ double s_Zs[DDT_MAX_K + 1];
+    __shared__ double s_red[VF_NT / 64];
+    __shared__ int s_path[DDT_MAX_DEPTH + 2];
+    __shared__ int s_ch[MK_NT];
+    __shared__ int s_nch, s_u, s_len, s_done, s_acc, s_next;
+    __shared__ unsigned long long s_best;
+    const int m = min(max(f.m[b], 0), P - 1);
+    const int n = m + 1;
+    const size_t fo = (size_t)b * P;
+
+    for (int i = wid; i < n; i += VF_NT / 64) {
+        float M, Sp;
+        const uint32_t* p = a.part + ((size_t)(b * P + i) * a.chunks) * rr_ps(a.Kp);
+        const uint64_t mine = merge_row_wave(p, a.chunks, a.Kp, M, Sp);
+        const int am = __shfl(vkey_id(mine), 0);
+        if (lane == 0) {
+            s_am[i] = am; s_M[i] = M; s_S[i] = Sp;
+            if (a.row_argmax) a.row_argmax[fo + i] = am;
+        }
+        if (a.row_topk && lane < a.k_top) a.row_topk[(fo + i) * a.k_top + lane] = vkey_id(mine);
+    }
+    for (int i = tid; i < P; i += VF_NT) {
+        s_fp[i] = i < n ? f.parent[fo + i] : -1;
+        s_ft[i] = i < n ? f.token[fo + i] : -1;
+    }
+    if (tid == 0) s_best = 0ull;
+    __syncthreads();
+    const float T = a.temperature[b];
+    int32_t* apath = a.accept_path + (size_t)b * (Dp + 1);
+
+    if (!(T > 0.f)) {
+        // greedy: longest matching prefix over the candidate paths
+        const int L = min(f.n_leaves[b], f.L);
+        const int32_t* ret = f.retrieve + (size_t)b * f.L * (Dp + 1);
+        unsigned long long best = 0ull;
+        for (int l = tid; l < L; l += VF_NT) {
+            const int32_t* path = ret + (size_t)l * (Dp + 1);
+            int len = 0;
+            for (int s = 1; s <= Dp; ++s) {
+                const int j = path[s], pj = path[s - 1];
+                if (j < 0 || j >= n || pj < 0 || pj >= n) break;
+                if (s_ft[j] == s_am[pj]) len = s;
+                else break;
+            }
+            const unsigned long long k = ((unsigned long long)len << 32) | (unsigned)(0x7FFFFFFF - l);
+            best = k > best ? k : best;
+        }
+        best = wave_max_u64(best);
+        if (lane == 0) atomicMax(&s_best, best);
+        __syncthreads();
+        if (tid == 0) {
+            if (s_best == 0ull) {                      // no candidate path: root only
+                for (int s = 0; s <= Dp; ++s) apath[s] = s == 0 ? 0 : -1;
+                a.accept_len[b] = 0;
+                a.next_token[b] = s_am[0];
+            } else {
+                const int len = (int)(s_best >> 32);
+                const int l = 0x7FFFFFFF - (int)(s_best & 0xFFFFFFFFu);
+                const int32_t* path = ret + (size_t)l * (Dp + 1);
+                for (int s = 0; s <= Dp; ++s) apath[s] = s <= len ? path[s] : -1;
+                a.accept_len[b] = len;
+                a.next_token[b] = s_am[path[len]];
+            }
+        }
+        return;
+    }
+
+    // T > 0: sibling walk with residual resampling
+    const float invT = 1.f / T;
+    const float* Ub = a.U + fo * 2;
+    if (tid == 0) { s_u = 0; s_len = 0; s_path[0] = 0; s_done = 0; }
+    __syncthreads();
+    while (true) {
+        const int u = s_u;
+        if (tid == 0) {
+            int c = 0;
+            for (int i = u + 1; i < n; ++i) if (s_fp[i] == u) s_ch[c++] = i;
+            s_nch = c;
+        }
+        __syncthreads();
+        const int nch = s_nch;
+        const int unode = f.node[fo + u];
+        const int uslot = (unode >= 0 && unode < t.cap) ? t.eslot[(size_t)b * t.cap + unode] : -1;
+        const int udep = (unode >= 0 && unode < t.cap) ? t.depth[(size_t)b * t.cap + unode] : 0;
+        WalkState w;
+        w.bf16 = a.bf16;
+        w.trow = a.bf16 ? (const void*)((const uint16_t*)a.tgt + b * a.ts0 + u * a.ts1)
+                        : (const void*)((const float*)a.tgt + b * a.ts0 + u * a.ts1);
+        w.invT = invT;
+        w.Mt = s_M[u];
+        w.k = 0;
+        w.Zs = s_Zs;
+        const bool has_q = nch > 0 && uslot >= 0 && a.drf != nullptr && udep < t.D_max;
+        if (has_q) {
+            const int64_t doff = (int64_t)udep * a.dl + (int64_t)b * a.ds0 + (int64_t)uslot * a.ds1;
+            w.drow = a.bf16 ? (const void*)((const uint16_t*)a.drf + doff)
+                            : (const void*)((const float*)a.drf + doff);
+            const size_t ri = ((size_t)b * t.D_max + udep) * t.R_max + uslot;
+            w.Md = t.rmax[ri];
+        } else {
+            w.drow = w.trow;
+            w.Md = w.Mt;
+        }
+        // normalisers of p and q at this temperature
+        if (T == 1.f) {
+            w.Zt = 1.0 + (double)s_S[u];
+            w.Zd = has_q ? 1.0 + (double)t.rsp[((size_t)b * t.D_max + udep) * t.R_max + uslot] : 1.0;
+        } else {
+            double zt = 0.0, zd = 0.0;
+            for (int v = tid; v < a.V; v += VF_NT) {
+                zt += (double)expf((ld_logit(w.trow, w.bf16, v) - w.Mt) * invT);
+                if (has_q) zd += (double)expf((ld_logit(w.drow, w.bf16, v) - w.Md) * invT);
+            }
+            zt = wave_sum_f64(zt); zd = wave_sum_f64(zd);
+            __syncthreads();
+            if (lane == 0) s_red[wid] = zt;
+            __syncthreads();
+            double tz = 0.0;
+            for (int q = 0; q < VF_NT / 64; ++q) tz += s_red[q];
+            __syncthreads();
+            if (lane == 0) s_red[wid] = zd;
+            __syncthreads();
+            double dz = 0.0;
+            for (int q = 0; q < VF_NT / 64; ++q) dz += s_red[q];
+            w.Zt = tz; w.Zd = has_q ? dz : 1.0;
+        }
+        int accepted = -1;
+        if (has_q) {
+            for (int ci = 0; ci < nch; ++ci) {
+                const int c = s_ch[ci];
+                if (tid == 0) {
+                    const int x = min(max(s_ft[c], 0), a.V - 1);
+                    double p, q;
+                    walk_pq(w, x, p, q);
+                    const double ratio = q > 0.0 ? p / q : INFINITY;
+                    s_acc = ((double)Ub[2 * c] < ratio) ? 1 : 0;
+                }
+                __syncthreads();
+                if (s_acc) { accepted = c; break; }
+                // rejection: Z = sum_v max(0, p_k(v) - q(v))
+                double z = 0.0;
+                for (int v = tid; v < a.V; v += VF_NT) {
+                    double p, q;
+                    walk_pq(w, v, p, q);
+                    z += fmax(0.0, p - q);
+                }
+                z = wave_sum_f64(z);
+                if (lane == 0) s_red[wid] = z;
+                __syncthreads();
+                if (tid == 0) {
+                    double zz = 0.0;
+                    for (int q = 0; q < VF_NT / 64; ++q) zz += s_red[q];
+                    s_Zs[w.k] = zz;
+                }
+                __syncthreads();
+                w.k = min(w.k + 1, DDT_MAX_K);
+            }
+        }
+        if (accepted >= 0) {
+            if (tid == 0) { s_u = accepted; s_path[++s_len] = accepted; }
+            __syncthreads();
+            continue;
+        }
+        // emission from the current p by inverse CDF with U[u][1]
+        const int ntiles = (a.V + VF_TILE - 1) / VF_TILE;
+        for (int tile = wid; tile < ntiles; tile += VF_NT / 64) {
+            double ls = 0.0;
+            for (int e = 0; e < 8; ++e) {
+                const int v = tile * VF_TILE + lane * 8 + e;
+                if (v < a.V) { double p, q; walk_pq(w, v, p, q); ls += p; }
+            }
+            ls = wave_sum_f64(ls);
+            if (lane == 0) s_tile[tile] = ls;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            double tot = 0.0;
+            for (int i = 0; i < ntiles; ++i) tot += s_tile[i];
+            const double thr = (double)Ub[2 * u + 1] * tot;
+            double acc = 0.0;
+            int ts = -1;
+            for (int i = 0; i < ntiles; ++i) {
+                if (acc + s_tile[i] > thr) { ts = i; break; }
+                acc += s_tile[i];
+            }
+            if (ts < 0) { ts = ntiles - 1; acc -= s_tile[ts]; }
+            s_red[0] = acc; s_red[1] = thr;
+            s_next = ts;
+        }
+        __syncthreads();
+        if (wid == 0) {
+            const int tile = s_next;
+            const double base = s_red[0], thr = s_red[1];
+            double pv[8], ls = 0.0;
+            for (int e = 0; e < 8; ++e) {
+                const int v = tile * VF_TILE + lane * 8 + e;
+                double p = 0.0, q;
+                if (v < a.V) walk_pq(w, v, p, q);
+                pv[e] = p; ls += p;
+            }
+            // exclusive prefix over lanes, in lane order
+            double incl = ls;
+            for (int d = 1; d < 64; d <<= 1) {
+                const double o = __shfl_up(incl, d);
+                if (lane >= d) incl += o;
+            }
+            const double excl = incl - ls;
+            // first element whose running sum exceeds thr; fall back to the last positive
+            int hit = 0x7FFFFFFF, lastpos = -1;
+            double run = base + excl;
+            for (int e = 0; e < 8; ++e) {
+                const int v = tile * VF_TILE + lane * 8 + e;
+                run += pv[e];
+                if (v < a.V && pv[e] > 0.0) {
+                    if (run > thr && hit == 0x7FFFFFFF) hit = v;
+                    lastpos = v;
+                }
+            }
+            hit = wave_min_i32(hit);
+            int lp = lastpos;
+            for (int d = 32; d >= 1; d >>= 1) lp = max(lp, __shfl_xor(lp, d));
+            if (lane == 0) s_next = hit != 0x7FFFFFFF ? hit : (lp >= 0 ? lp : 0);
+        }
+        __syncthreads();
+        break;
+    }
+    if (tid == 0) {
+        const int len = s_len;
+        for (int s = 0; s <= Dp; ++s) apath[s] = s <= len ? s_path[s] : -1;
+        a.accept_len[b] = len;
+        a.next_token[b] = s_next;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// successor-matrix refresh
+// ---------------------------------------------------------------------------
+//
+// Graft review step 3: every verified token's row of M is replaced by the
+// top-k of the target's next-token distribution at that position; the later
+// flat position wins on duplicate tokens (reading).  With a shared matrix
+// (M_bstride = 0) one workgroup handles the whole batch so the winner is the
+// last (row, position) pair.
+
+struct UpdateArgs {
+    ddt_flat f;
+    int32_t* M;
+    int64_t M_bstride;
+    int V, k_succ, k_top, B, shared;
+    const int32_t* row_topk;     // [B][P][k_top], or NULL to merge partials
+    const uint32_t* part;
+    int chunks, Kp;
+};
+
+#define UP_NT 256
+
+__global__ __launch_bounds__(UP_NT) void k_succ_update(UpdateArgs a) {
+    const ddt_flat& f = a.f;
+    const int P = f.P;
+    const int b0 = a.shared ? 0 : blockIdx.x, b1 = a.shared ? a.B : blockIdx.x + 1;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    for (int b = b0; b < b1; ++b) {
+        const int m = min(max(f.m[b], 0), P - 1);
+        const size_t fo = (size_t)b * P;
+        int32_t* Mb = a.M + (size_t)b * a.M_bstride;
+        if (a.row_topk != nullptr) {
+            for (int i = 1 + tid; i <= m; i += UP_NT) {
+                const int tk = f.token[fo + i];
+                if (tk < 0 || tk >= a.V) continue;
+                bool last = true;
+                for (int j = i + 1; j <= m && last; ++j) last = f.token[fo + j] != tk;
+                for (int bb = b + 1; a.shared && bb < a.B && last; ++bb) {
+                    const int mm = min(max(f.m[bb], 0), P - 1);
+                    for (int j = 1; j <= mm && last; ++j) last = f.token[(size_t)bb * P + j] != tk;
+                }
+                if (!last) continue;
+                for (int c = 0; c < a.k_succ; ++c)
+                    Mb[(size_t)tk * a.k_succ + c] = a.row_topk[(fo + i) * a.k_top + c];
+            }
+        } else {
+            for (int i = 1 + wid; i <= m; i += UP_NT / 64) {
+                const int tk = f.token[fo + i];
+                if (tk < 0 || tk >= a.V) continue;
+                bool last = true;
+                for (int j = i + 1; j <= m && last; ++j) last = f.token[fo + j] != tk;
+                for (int bb = b + 1; a.shared && bb < a.B && last; ++bb) {
+                    const int mm = min(max(f.m[bb], 0), P - 1);
+                    for (int j = 1; j <= mm && last; ++j) last = f.token[(size_t)bb * P + j] != tk;
+                }
+                float M, Sp;
+                const uint32_t* p = a.part + ((size_t)(b * P + i) * a.chunks) * rr_ps(a.Kp);
+                const uint64_t mine = merge_row_wave(p, a.chunks, a.Kp, M, Sp);
+                if (last && lane < a.k_succ) Mb[(size_t)tk * a.k_succ + lane] = vkey_id(mine);
+            }
+        }
+        if (a.shared) __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// standalone row top-k: merge partials into ids / log confidences
+// ---------------------------------------------------------------------------
+
+struct RowFinishArgs {
+    const uint32_t* part;
+    int rows, chunks, K;
+    int32_t* ids;
+    float* logc;
+    float* rmax;
+    float* rsp;
+};
+
+__global__ __launch_bounds__(256) void k_row_finish(RowFinishArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= a.rows) return;
+    float M, Sp;
+    const uint32_t* p = a.part + (size_t)row * a.chunks * rr_ps(a.K);
+    const uint64_t mine = merge_row_wave(p, a.chunks, a.K, M, Sp);
+    if (lane < a.K) {
+        if (a.ids) a.ids[(size_t)row * a.K + lane] = vkey_id(mine);
+        if (a.logc)
+            a.logc[(size_t)row * a.K + lane] = mine ? (vkey_val(mine) - M) - log1pf(Sp) : -INFINITY;
+    }
+    if (lane == 0) {
+        if (a.rmax) a.rmax[row] = M;
+        if (a.rsp) a.rsp[row] = Sp;
+    }
+}
