@@ -1,0 +1,360 @@
+#!/usr/bin/env python3
+"""Draft-tree round throughput on one MI355X.
+
+A step is one full speculative-decoding round of the hot path on the CAST
+workload (B=8, V=128256, bf16 draft and target logits, depth 8, expand 10,
+60 verify tokens, CAST width / depth / verify-count selection, greedy verify):
+8 ddt_tree_expand layers, ddt_tree_rerank, ddt_tree_build_mask and
+ddt_tree_verify.  Inputs are seeded synthetic logits resident in HBM before the
+timed region, in a ring of rounds whose distinct logit bytes exceed 1 GB (more
+than twice the 256 MB last-level cache).  Each ring slot's round is captured
+once as a HIP graph (the kernels take every size from device memory, so no host
+synchronisation is needed between layers) and the timed region replays them.
+
+Prints one JSON line.  --gpus above 1 is refused: this build measures one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+SEED = 1002
+PMC_FILE = os.path.join(ROOT, "profiles", "row_reduce_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "dynamic_draft_tree_row_amd", "csrc", "ddt_rowreduce.hpp")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """The few HIP runtime calls the bench needs (events), via ctypes."""
+
+    def __init__(self):
+        self.h = C.CDLL("libamdhip64.so.7")
+        self.h.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.h.hipEventDestroy.argtypes = [C.c_void_p]
+
+    def events(self, n):
+        out = []
+        for _ in range(n):
+            e = C.c_void_p()
+            if self.h.hipEventCreate(C.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e)
+        return out
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = C.c_float()
+        st = self.h.hipEventElapsedTime(C.byref(ms), a, b)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({st})")
+        return ms.value
+
+
+def flat_layout(run, B):
+    """Per flat position: key, depth, expand slot, token, from the library's outputs."""
+    t, f = run.tree, run.flat
+    node = f.node.cpu().numpy()
+    key, dep = t.key.cpu().numpy(), t.depth.cpu().numpy()
+    esl, tok = t.eslot.cpu().numpy(), t.token.cpu().numpy()
+    P = node.shape[1]
+    fk = np.full((B, P), -1, np.int64)
+    fd = np.zeros((B, P), np.int32)
+    fs = np.full((B, P), -1, np.int32)
+    ft = np.full((B, P), -1, np.int32)
+    for b in range(B):
+        ok = node[b] >= 0
+        nv = node[b][ok]
+        fk[b, ok], fd[b, ok], fs[b, ok], ft[b, ok] = key[b, nv], dep[b, nv], esl[b, nv], tok[b, nv]
+    return fk, fd, fs, ft
+
+
+def snapshot(run):
+    return {k: v.clone() for k, v in (
+        ("accept_len", run.accept_len), ("accept_path", run.accept_path),
+        ("next_token", run.next_token), ("token", run.flat.token), ("mask", run.flat.mask),
+        ("m", run.m_out), ("widths", run.tree.widths), ("argmax", run.row_argmax))}
+
+
+def same(a, b) -> bool:
+    import torch
+    return all(torch.equal(a[k], b[k]) for k in a)
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_per_launch(workload: str):
+    """HBM bytes per row-reduction launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source for this workload."""
+    try:
+        d = json.load(open(PMC_FILE))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_sha") != kernel_hash() or d.get("workload") != workload:
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(w, slot, cast_np, seconds):
+    """The oracle as it stands, on one core, on ring slot 0's inputs."""
+    from oracle import ddt_oracle as O
+    def one():
+        O.run_round(B=w.B, V=w.V, dtype=w.dtype, D=w.D, K_e=w.K_e, K_n=w.K_n, m_max=w.m_max,
+                    root_tok=slot["roots_np"], draft_raw=slot["draft_np"],
+                    target_raw_fn=lambda dr, flats: slot["target_np"],
+                    temperature=slot["T_np"], U=slot["U_np"], prefix=w.prefix, cast=cast_np)
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        one()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": n / el, "unit": "rounds/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} rounds of the same workload (ring slot 0, {el:.1f} s, single thread, "
+                      f"float64 numpy; input generation excluded)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--ring", type=int, default=4)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--break-even", action="store_true",
+                    help="CAST at the break-even thresholds C1=1, C2=0.1, C3=0.5")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        log("bench.py measures one GPU only: this build has no multi-GPU path "
+            "(batch rows would shard across GPUs; see the design notes).")
+        sys.exit(2)
+
+    import torch
+    from gen import configs, synth
+    from dynamic_draft_tree_row_amd import _lib, api
+    from dynamic_draft_tree_row_amd.round_driver import RoundRunner, RoundShape
+
+    w = configs.C2
+    if args.break_even:
+        w = configs.Workload(**{**w.__dict__, "cast": configs.CastSpec(**configs.BREAK_EVEN)})
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    lib = _lib.load()
+    hip = Hip()
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def to_dev(raw):
+        if w.dtype == "f32":
+            return torch.from_numpy(np.ascontiguousarray(raw)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    shape = RoundShape(B=w.B, V=w.V, dtype=tdt, D=w.D, K_e=w.K_e, K_n=w.K_n, m=w.m_max,
+                       prefix=w.prefix)
+    run = RoundRunner(shape, dev)
+    S_T, S_D = synth.cost_tables(w)
+    cs = w.cast
+    cast_np = dict(S_T=S_T, S_D=S_D, L=cs.L, M=cs.M, C1=[cs.C1] * w.D, C2=cs.C2,
+                   C3=[cs.C3] * w.B, R=cs.R)
+    f = lambda a: torch.tensor(np.asarray(a, np.float32), device=dev)
+    cast = api.CastParams(S_T=f(S_T), S_D=f(S_D), L=cs.L, C1=f(cast_np["C1"]), C2=cs.C2,
+                          C3=f(cast_np["C3"]), R=cs.R, ctx_verify=w.prefix)
+
+    # ---- inputs resident in HBM: a ring of rounds --------------------------
+    ring = []
+    t0 = time.perf_counter()
+    for r in range(args.ring):
+        d_np = synth.draft_arena(w, SEED, r)
+        slot = dict(draft=to_dev(d_np), roots=torch.from_numpy(synth.root_tokens(w, SEED, r)).to(dev),
+                    T=torch.from_numpy(synth.temperatures(w, SEED, r)).to(dev),
+                    U=torch.from_numpy(synth.uniforms(w, SEED, r)).to(dev))
+        run.draft(slot["draft"], slot["roots"], cast=cast)
+        torch.cuda.synchronize()
+        fk, fd, fs, ft = flat_layout(run, w.B)
+        t_np = synth.target_arena(w, SEED, r, d_np, fk, fd, fs, ft)
+        slot["target"] = to_dev(t_np)
+        if r == 0:
+            slot.update(draft_np=d_np, target_np=t_np, roots_np=synth.root_tokens(w, SEED, r),
+                        T_np=synth.temperatures(w, SEED, r), U_np=synth.uniforms(w, SEED, r))
+        ring.append(slot)
+    ring_bytes = sum(s["draft"].numel() * s["draft"].element_size() +
+                     s["target"].numel() * s["target"].element_size() for s in ring)
+    log(f"ring of {args.ring} rounds, {ring_bytes / 1e9:.2f} GB of logits, "
+        f"generated in {time.perf_counter() - t0:.1f} s")
+
+    def eager(slot):
+        run.draft(slot["draft"], slot["roots"], cast=cast)
+        run.verify(slot["target"], slot["draft"], slot["T"], slot["U"])
+
+    # eager reference outputs and per-round statistics
+    ref, stats = [], []
+    for slot in ring:
+        eager(slot)
+        torch.cuda.synchronize()
+        ref.append(snapshot(run))
+        tree_esl = run.tree.eslot.cpu().numpy()
+        tree_dep = run.tree.depth.cpu().numpy()
+        n_nodes = run.tree.n_nodes.cpu().numpy()
+        rows_per_layer = []
+        for d in range(1, w.D + 1):
+            rows = 0
+            for b in range(w.B):
+                n = int(n_nodes[b])
+                rows += int(((tree_esl[b, :n] >= 0) & (tree_dep[b, :n] == d - 1)).sum())
+            rows_per_layer.append(rows)
+        m = run.m_out.cpu().numpy()
+        acc = run.accept_len.cpu().numpy()
+        stats.append(dict(rows_per_layer=rows_per_layer, verify_rows=int((m + 1).sum()),
+                          walk_rows=int((acc + 1).sum()), m=m.tolist(), accept=acc.tolist(),
+                          widths=run.tree.widths.cpu().numpy().tolist(),
+                          depth=int(max(d for d, r in enumerate(rows_per_layer, 1) if r > 0))))
+
+    # ---- capture one graph per ring slot -----------------------------------
+    graphs = []
+    for slot in ring:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            eager(slot)
+        graphs.append(g)
+    # every replay must reproduce the eager result, with eager work in between
+    for rep in range(3):
+        for i, g in enumerate(graphs):
+            g.replay()
+            torch.cuda.synchronize()
+            if not same(snapshot(run), ref[i]):
+                raise RuntimeError(f"graph replay {rep} of slot {i} differs from the eager round")
+            eager(ring[(i + 1) % len(ring)])
+            torch.cuda.synchronize()
+    log("graph replays match the eager rounds")
+
+    # ---- timed region ------------------------------------------------------
+    K, W, R = args.steps, args.warmup, len(graphs)
+    for i in range(W):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(K):
+        graphs[i % R].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    ms_per_step = wall_s * 1e3 / K
+    log(f"{K} rounds: {ms_per_step * 1e3:.1f} us/round wall, {gpu_ms * 1e3 / K:.1f} us/round GPU events")
+
+    # eager (no graph) rounds for reference
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ne = max(20, K // 4)
+    for i in range(ne):
+        eager(ring[i % R])
+    torch.cuda.synchronize()
+    eager_us = (time.perf_counter() - t0) * 1e6 / ne
+
+    # ---- dominant kernel: the vocabulary-wide row reduction ----------------
+    # Its launches inside the same replays are bracketed by HIP events recorded
+    # on the launching stream (ddt_set_reduce_events); per round: D expand
+    # launches + 1 verify launch.
+    per_round = w.D + 1
+    n_pairs = per_round * R * 4
+    evs = hip.events(2 * n_pairs)
+    arr = (C.c_void_p * len(evs))(*[e.value for e in evs])
+    # Events recorded inside a captured graph are not valid timing events on
+    # this runtime, so the launches are timed in eager rounds enqueued behind a
+    # long device operation: the whole queue is in place before the GPU reaches
+    # it and each event pair brackets its kernel with no host gap.
+    busy = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    lib.ddt_set_reduce_events(arr, n_pairs)
+    for _ in range(40):
+        busy.mul_(1.0)
+    for slot in ring:
+        eager(slot)
+    used = lib.ddt_set_reduce_events(None, 0)
+    assert used == per_round * R, f"expected {per_round * R} bracketed launches, got {used}"
+    del busy
+    torch.cuda.synchronize()
+    durs, nbytes = [], []
+    ebytes = w.V * (2 if w.dtype == "bf16" else 4)
+    for s, st in enumerate(stats):
+        rows = st["rows_per_layer"] + [st["verify_rows"]]
+        for k in range(per_round):
+            i = s * per_round + k
+            durs.append(hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) * 1e-3)
+            nbytes.append(rows[k] * ebytes)
+    durs, nbytes = np.array(durs), np.array(nbytes, dtype=np.float64)
+    achieved = nbytes.sum() / durs.sum() / 1e9
+    big = nbytes >= np.max(nbytes) * 0.5
+    log(f"row reduction: {len(durs)} launches, mean {durs.mean() * 1e6:.2f} us, "
+        f"{nbytes.mean() / 1e6:.2f} MB/launch, {achieved:.0f} GB/s")
+
+    # ---- algorithmic logit bytes per round ----------------------------------
+    expand_bytes = np.mean([sum(s["rows_per_layer"]) for s in stats]) * ebytes
+    walk_bytes = np.mean([s["walk_rows"] for s in stats]) * ebytes
+    allrow_bytes = np.mean([s["verify_rows"] for s in stats]) * ebytes
+    round_s = ms_per_step * 1e-3
+    logit_gbs = (expand_bytes + walk_bytes) / round_s / 1e9
+
+    out = {
+        "metric": "draft-tree rounds/sec and logit HBM GB/s (% of roofline) at B=8, V=128256",
+        "value": round(1.0 / round_s, 2),
+        "unit": "rounds/s",
+        "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "V": w.V, "depth": w.D, "expand_topk": w.K_e,
+                   "node_topk": w.K_n, "m": w.m, "verify": w.verify,
+                   "cast": {"C1": w.cast.C1, "C2": w.cast.C2, "C3": w.cast.C3, "R": w.cast.R,
+                            "cost": "c_k = 0.02k + 1.0"},
+                   "ring_rounds": R, "ring_gb": round(ring_bytes / 1e9, 3), "hip_graph": True},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_per_launch(w.name),
+                     "kernel": "k_row_partial<bf16> (vocab row reduction: max, sigma', top-k)",
+                     "algorithmic_bytes_per_launch": round(float(nbytes.mean()), 1),
+                     "avg_launch_us": round(float(durs.mean() * 1e6), 3),
+                     "launches": int(len(durs)), "timing": "HIP events around each launch, eager rounds queued behind a busy op",
+                     "big_launches_gbs": round(float(nbytes[big].sum() / durs[big].sum() / 1e9), 1)},
+        "logit_gbs": round(logit_gbs, 1),
+        "logit_frac_of_peak": round(logit_gbs / PEAK_HBM_GBS, 4),
+        "detail": {
+            "gpu_event_us_per_round": round(gpu_ms * 1e3 / K, 2),
+            "eager_us_per_round": round(eager_us, 2),
+            "expand_mb_per_round": round(expand_bytes / 1e6, 3),
+            "verify_walk_mb_per_round": round(walk_bytes / 1e6, 3),
+            "verify_allrows_mb_per_round": round(allrow_bytes / 1e6, 3),
+            "allrow_logit_gbs": round((expand_bytes + allrow_bytes) / round_s / 1e9, 1),
+            "cast_widths": stats[0]["widths"][:stats[0]["depth"]],
+            "depth": [s["depth"] for s in stats],
+            "m_per_row": stats[0]["m"], "accept_len": stats[0]["accept"],
+            "mean_tau": round(float(np.mean([np.mean(s["accept"]) + 1 for s in stats])), 3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, ring[0], cast_np, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -63,6 +63,7 @@ SIGNATURES = {
     "ddt_succ_update": (C.c_int, [P, i64, C.c_int, C.c_int, C.POINTER(Flat), P, C.c_int,
                                   C.POINTER(Logits), P, sz, P]),
     "ddt_row_topk": (C.c_int, [C.POINTER(Logits), C.c_int, C.c_int, C.c_int, P, P, P, P, P, sz, P]),
+    "ddt_set_reduce_events": (C.c_int, [C.POINTER(P), C.c_int]),
 }
 
 _lib = None

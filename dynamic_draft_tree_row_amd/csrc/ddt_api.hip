@@ -69,6 +69,10 @@ inline T* carve(char*& p, size_t n) {
     return r;
 }
 
+// timing hook (ddt_set_reduce_events)
+void* const* g_events = nullptr;
+int g_pairs = 0, g_used = 0;
+
 int launch_partials(const ddt_logits* x, int n0, int n1, const int32_t* count, int count_add,
                     int K, void* ws, hipStream_t s) {
     RowSrc rs;
@@ -77,13 +81,20 @@ int launch_partials(const ddt_logits* x, int n0, int n1, const int32_t* count, i
     const int chunks = chunks_of(x->V, x->dtype);
     const long long blocks = (long long)n0 * n1 * chunks;
     if (blocks <= 0) return DDT_OK;
+    const bool timed = g_events != nullptr && g_used < g_pairs;
+    if (timed && hipEventRecord((hipEvent_t)g_events[2 * g_used], s) != hipSuccess) return DDT_ELAUNCH;
     if (x->dtype == DDT_BF16)
         hipLaunchKernelGGL(k_row_partial<true>, dim3((unsigned)blocks), dim3(RR_NT), 0, s, rs, x->V,
                            chunks, K, (uint32_t*)ws);
     else
         hipLaunchKernelGGL(k_row_partial<false>, dim3((unsigned)blocks), dim3(RR_NT), 0, s, rs,
                            x->V, chunks, K, (uint32_t*)ws);
-    return launched();
+    const int st = launched();
+    if (timed) {
+        if (hipEventRecord((hipEvent_t)g_events[2 * g_used + 1], s) != hipSuccess) return DDT_ELAUNCH;
+        ++g_used;
+    }
+    return st;
 }
 
 }  // namespace
@@ -100,6 +111,14 @@ const char* ddt_strerror(int status) {
         case DDT_ELAUNCH: return "kernel launch failed";
         default: return "unknown status";
     }
+}
+
+int ddt_set_reduce_events(void* const* events, int n_pairs) {
+    const int used = g_used;
+    g_events = (events != nullptr && n_pairs > 0) ? events : nullptr;
+    g_pairs = g_events ? n_pairs : 0;
+    g_used = 0;
+    return used;
 }
 
 int ddt_chunk_elems(int dtype) {

@@ -188,6 +188,7 @@ __global__ __launch_bounds__(CS_NT) void k_cast(CastArgs a) {
             for (int i = 1; i < 8; ++i) st[i] = 0.0;
             st[8] = 1.0; st[9] = -1.0; st[10] = 0.0;
             t.cont[0] = 1;
+            for (int i = 0; i < t.D_max; ++i) t.widths[i] = 0;
         }
         s_go = t.cont[0];
         int kc = a.K_e;
@@ -585,6 +586,10 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
     for (int i = tid; i < P; i += VF_NT) {
         s_fp[i] = i < n ? f.parent[fo + i] : -1;
         s_ft[i] = i < n ? f.token[fo + i] : -1;
+        if (i >= n) {                                  // padding positions carry -1
+            if (a.row_argmax) a.row_argmax[fo + i] = -1;
+            for (int k = 0; a.row_topk && k < a.k_top; ++k) a.row_topk[(fo + i) * a.k_top + k] = -1;
+        }
     }
     if (tid == 0) s_best = 0ull;
     __syncthreads();

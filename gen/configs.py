@@ -18,10 +18,20 @@ from typing import Optional, Tuple
 
 @dataclass(frozen=True)
 class CastSpec:
-    """CAST thresholds and cost-table grid (CAST notes, key designs 1-4)."""
-    C1: float = 1.0          # width threshold, same for every layer
-    C2: float = 0.1          # depth threshold
-    C3: float = 0.5          # verify-count threshold (per row)
+    """CAST thresholds and cost-table grid (CAST notes, key designs 1-4).
+
+    With the cost slope lam = 0.02, C1 = 1 is the break-even point (a node must
+    add 0.02 expected accepted tokens to pay for 0.02 of a target forward).  On
+    this synthetic draft distribution (one planted token per row over a
+    128K-token Gaussian tail) break-even never pays for a second branch and the
+    tree collapses to a chain, so the workload uses thresholds 20x lower, at
+    which every width, depth and verify-count decision is exercised within the
+    configured depth-8 / width-10 / 60-token budget.  BREAK_EVEN keeps the
+    break-even setting for comparison.
+    """
+    C1: float = 0.05         # width threshold, same for every layer
+    C2: float = 0.005        # depth threshold
+    C3: float = 0.02         # verify-count threshold (per row)
     R: int = 3               # FIFO length of the depth gain buffer
     L: int = 256             # context grid step of the cost table
     M: int = 16              # context grid rows
@@ -29,6 +39,9 @@ class CastSpec:
     lam: float = 0.02        # closed-form cost slope
     delta: float = 1.0       # closed-form cost intercept
     table: str = "linear"    # "linear" (c_k = lam*k + delta) or "seeded"
+
+
+BREAK_EVEN = dict(C1=1.0, C2=0.1, C3=0.5)
 
 
 @dataclass(frozen=True)

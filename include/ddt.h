@@ -113,7 +113,7 @@ typedef struct ddt_tree {
     int32_t* active;     /* [B] Graft: 1 until the row is pruned */
     int32_t* k_draft;    /* [B] Graft: draft nodes the row keeps (K_max if never pruned) */
     int32_t* cont;       /* [1] CAST: 1 while the batch keeps growing */
-    int32_t* widths;     /* [D_max] CAST: width n_i chosen at layer i */
+    int32_t* widths;     /* [D_max] CAST: width n_i chosen at layer i (0 for layers not built) */
     double* cast_state;  /* [16] CAST per-round state (gain FIFO, utility, context) */
 } ddt_tree;
 
@@ -298,6 +298,7 @@ int ddt_tree_build_mask(const ddt_tree* t /*host*/, const int32_t* sel, const in
  * Nodes without a draft row (retrieval nodes) end the walk at T > 0.
  * row_argmax: [B][P] or NULL.  k_top > 0 with row_topk [B][P][k_top]: top-k
  * ids of every verified row from the same pass (feeds ddt_succ_update).
+ * Both hold -1 at padding positions (past f->m[b]).
  * accept_len [B]; accept_path [B][Dp+1] flat indices root first, -1 padded;
  * next_token [B].  ws >= ddt_workspace_bytes(B*P, V, dtype, max(1,k_top)).
  */
@@ -328,6 +329,17 @@ int ddt_succ_update(int32_t* M, int64_t M_bstride, int V, int k_succ, const ddt_
  */
 int ddt_row_topk(const ddt_logits* x /*host*/, int n0, int n1, int K, int32_t* ids, float* logc,
                  float* rmax, float* rsp, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * ddt_set_reduce_events -- timing hook for the vocabulary-wide row reduction.
+ * While set, the i-th launch of that kernel (any call, any stream), i <
+ * n_pairs, is bracketed by hipEventRecord(events[2i]) before and
+ * hipEventRecord(events[2i+1]) after, on the launching stream; later launches
+ * are not bracketed.  events are hipEvent_t handles created by the caller.
+ * NULL / 0 clears the hook.  Returns the number of launches bracketed since
+ * the previous call.  Process-wide host state; not thread-safe.
+ */
+int ddt_set_reduce_events(void* const* events, int n_pairs);
 
 /* Text for a status code. */
 const char* ddt_strerror(int status);
