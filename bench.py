@@ -141,6 +141,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--break-even", action="store_true",
                     help="CAST at the break-even thresholds C1=1, C2=0.1, C3=0.5")
+    ap.add_argument("--workload", default=None,
+                    help="profile another workload instead (e.g. eagle2_mixed_b64_v128256_bf16; "
+                         "'fixed' = the CAST shape with fixed EAGLE-2 widths)")
     args = ap.parse_args()
     if args.gpus != 1:
         log("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -153,6 +156,12 @@ def main():
     from dynamic_draft_tree_row_amd.round_driver import RoundRunner, RoundShape
 
     w = configs.C2
+    if args.workload == "fixed":
+        w = configs.Workload(**{**w.__dict__, "cast": None, "name": "eagle2_b8_v128256_bf16"})
+    elif args.workload:
+        w = configs.WORKLOADS[args.workload]
+        if w.graft is not None:
+            raise SystemExit("the Graft workload is exercised by the tests, not by this bench")
     if args.break_even:
         w = configs.Workload(**{**w.__dict__, "cast": configs.CastSpec(**configs.BREAK_EVEN)})
     dev = torch.device("cuda", 0)
@@ -169,13 +178,15 @@ def main():
     shape = RoundShape(B=w.B, V=w.V, dtype=tdt, D=w.D, K_e=w.K_e, K_n=w.K_n, m=w.m_max,
                        prefix=w.prefix)
     run = RoundRunner(shape, dev)
-    S_T, S_D = synth.cost_tables(w)
-    cs = w.cast
-    cast_np = dict(S_T=S_T, S_D=S_D, L=cs.L, M=cs.M, C1=[cs.C1] * w.D, C2=cs.C2,
-                   C3=[cs.C3] * w.B, R=cs.R)
-    f = lambda a: torch.tensor(np.asarray(a, np.float32), device=dev)
-    cast = api.CastParams(S_T=f(S_T), S_D=f(S_D), L=cs.L, C1=f(cast_np["C1"]), C2=cs.C2,
-                          C3=f(cast_np["C3"]), R=cs.R, ctx_verify=w.prefix)
+    cast_np, cast = None, None
+    if w.cast is not None:
+        S_T, S_D = synth.cost_tables(w)
+        cs = w.cast
+        cast_np = dict(S_T=S_T, S_D=S_D, L=cs.L, M=cs.M, C1=[cs.C1] * w.D, C2=cs.C2,
+                       C3=[cs.C3] * w.B, R=cs.R)
+        f = lambda a: torch.tensor(np.asarray(a, np.float32), device=dev)
+        cast = api.CastParams(S_T=f(S_T), S_D=f(S_D), L=cs.L, C1=f(cast_np["C1"]), C2=cs.C2,
+                              C3=f(cast_np["C3"]), R=cs.R, ctx_verify=w.prefix)
 
     # ---- inputs resident in HBM: a ring of rounds --------------------------
     ring = []
@@ -323,8 +334,9 @@ def main():
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "V": w.V, "depth": w.D, "expand_topk": w.K_e,
                    "node_topk": w.K_n, "m": w.m, "verify": w.verify,
-                   "cast": {"C1": w.cast.C1, "C2": w.cast.C2, "C3": w.cast.C3, "R": w.cast.R,
-                            "cost": "c_k = 0.02k + 1.0"},
+                   "cast": ({"C1": w.cast.C1, "C2": w.cast.C2, "C3": w.cast.C3, "R": w.cast.R,
+                             "cost": "c_k = 0.02k + 1.0"} if w.cast else None),
+                   "prefix": w.prefix,
                    "ring_rounds": R, "ring_gb": round(ring_bytes / 1e9, 3), "hip_graph": True},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),

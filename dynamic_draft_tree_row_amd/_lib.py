@@ -20,7 +20,7 @@ class Tree(C.Structure):
                 ("token", P), ("parent", P), ("depth", P), ("eslot", P), ("key", P),
                 ("S", P), ("logc", P), ("rmax", P), ("rsp", P), ("n_nodes", P),
                 ("layer_base", P), ("n_front", P), ("frontier", P), ("active", P),
-                ("k_draft", P), ("cont", P), ("widths", P), ("cast_state", P)]
+                ("k_draft", P), ("cont", P), ("widths", P), ("cast_state", P), ("ticket", P)]
 
 
 class Flat(C.Structure):

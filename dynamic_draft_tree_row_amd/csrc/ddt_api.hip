@@ -18,6 +18,19 @@ inline int chunk_elems(int dtype) {
 
 inline int chunks_of(int V, int dtype) { return (V + chunk_elems(dtype) - 1) / chunk_elems(dtype); }
 
+// Chunks per workgroup of the row reduction: one while the grid is small (more
+// workgroups, more bytes in flight), more once there are workgroups to spare.
+inline int tpw_of(long long rows, int V, int dtype) {
+    (void)rows; (void)V; (void)dtype;
+    return 1;
+}
+
+// Partials per row; producer and consumers derive it from the same grid rows.
+inline int groups_of(long long rows, int V, int dtype) {
+    const int t = tpw_of(rows, V, dtype);
+    return (chunks_of(V, dtype) + t - 1) / t;
+}
+
 inline size_t ws_need(long long rows, int V, int dtype, int K) {
     return (size_t)rows * (size_t)chunks_of(V, dtype) * (size_t)rr_ps(K) * 4u;
 }
@@ -34,7 +47,7 @@ int check_tree(const ddt_tree* t) {
         t->rmax == nullptr || t->rsp == nullptr || t->n_nodes == nullptr ||
         t->layer_base == nullptr || t->n_front == nullptr || t->frontier == nullptr ||
         t->active == nullptr || t->k_draft == nullptr || t->cont == nullptr ||
-        t->widths == nullptr || t->cast_state == nullptr)
+        t->widths == nullptr || t->cast_state == nullptr || t->ticket == nullptr)
         return DDT_EINVAL;
     if (t->B < 1 || t->cap < 2 || t->D_max < 1 || t->R_max < 1) return DDT_EINVAL;
     if (t->cap > DDT_MAX_NODES || t->D_max > DDT_MAX_DEPTH || t->R_max > DDT_MAX_FRONT)
@@ -78,17 +91,20 @@ int launch_partials(const ddt_logits* x, int n0, int n1, const int32_t* count, i
     RowSrc rs;
     rs.base = x->data; rs.s0 = x->s0; rs.s1 = x->s1; rs.n1 = n1;
     rs.count = count; rs.count_add = count_add;
-    const int chunks = chunks_of(x->V, x->dtype);
-    const long long blocks = (long long)n0 * n1 * chunks;
+    const long long rows = (long long)n0 * n1;
+    const int tpw = tpw_of(rows, x->V, x->dtype);
+    const int groups = groups_of(rows, x->V, x->dtype);
+    const long long blocks = rows * groups;
     if (blocks <= 0) return DDT_OK;
     const bool timed = g_events != nullptr && g_used < g_pairs;
     if (timed && hipEventRecord((hipEvent_t)g_events[2 * g_used], s) != hipSuccess) return DDT_ELAUNCH;
+    const dim3 grid((unsigned)blocks), blk(RR_NT);
+    uint32_t* part = (uint32_t*)ws;
+    (void)tpw;
     if (x->dtype == DDT_BF16)
-        hipLaunchKernelGGL(k_row_partial<true>, dim3((unsigned)blocks), dim3(RR_NT), 0, s, rs, x->V,
-                           chunks, K, (uint32_t*)ws);
+        hipLaunchKernelGGL((k_row_partial<true, 1>), grid, blk, 0, s, rs, x->V, groups, K, part);
     else
-        hipLaunchKernelGGL(k_row_partial<false>, dim3((unsigned)blocks), dim3(RR_NT), 0, s, rs,
-                           x->V, chunks, K, (uint32_t*)ws);
+        hipLaunchKernelGGL((k_row_partial<false, 1>), grid, blk, 0, s, rs, x->V, groups, K, part);
     const int st = launched();
     if (timed) {
         if (hipEventRecord((hipEvent_t)g_events[2 * g_used + 1], s) != hipSuccess) return DDT_ELAUNCH;
@@ -144,6 +160,7 @@ size_t ddt_tree_bytes(int B, int cap, int D_max, int R_max) {
     n += align256(4);                                          // cont
     n += align256((size_t)D_max * 4);                          // widths
     n += align256(16 * 8);                                     // cast_state
+    n += align256(4);                                          // ticket
     return n;
 }
 
@@ -174,6 +191,7 @@ int ddt_tree_bind(ddt_tree* t, void* base, size_t bytes, int B, int cap, int D_m
     t->cont = carve<int32_t>(p, 1);
     t->widths = carve<int32_t>(p, D_max);
     t->cast_state = carve<double>(p, 16);
+    t->ticket = carve<uint32_t>(p, 1);
     return DDT_OK;
 }
 
@@ -234,20 +252,15 @@ int ddt_tree_expand(const ddt_tree* t, int layer, const int32_t* root_tok, const
 
     AttachArgs a;
     a.t = *t; a.part = (const uint32_t*)ws; a.root_tok = root_tok; a.layer = layer; a.R = R;
-    a.chunks = chunks_of(logits->V, logits->dtype); a.K_n = K_n; a.K_e = K_e;
+    a.chunks = groups_of((long long)t->B * R, logits->V, logits->dtype); a.K_n = K_n; a.K_e = K_e;
     a.ck = 0; a.kd_ck = 0; a.tau = 0.f; a.gate_on = gate != nullptr; a.K_max = gate ? gate->K_max : 0;
+    a.cast_on = cast != nullptr;
+    if (cast) a.c = *cast; else memset(&a.c, 0, sizeof(a.c));
     if (gate != nullptr)
         for (int i = 0; i < gate->n_ck; ++i)
             if (gate->ck_depth[i] == layer) { a.ck = 1; a.kd_ck = gate->k_draft[i]; a.tau = gate->tau[i]; }
     hipLaunchKernelGGL(k_attach, dim3(t->B), dim3(AT_NT), 0, s, a);
     if ((st = launched())) return st;
-
-    if (cast != nullptr) {
-        CastArgs c;
-        c.t = *t; c.c = *cast; c.layer = layer; c.K_e = K_e;
-        hipLaunchKernelGGL(k_cast, dim3(1), dim3(CS_NT), 0, s, c);
-        if ((st = launched())) return st;
-    }
     return DDT_OK;
 }
 
@@ -326,7 +339,7 @@ int ddt_tree_verify(const ddt_tree* t, const ddt_flat* f, const ddt_logits* targ
     if (st) return st;
     VerifyArgs a;
     a.t = *t; a.f = *f; a.part = (const uint32_t*)ws;
-    a.chunks = chunks_of(target->V, target->dtype); a.Kp = Kp;
+    a.chunks = groups_of((long long)t->B * f->P, target->V, target->dtype); a.Kp = Kp;
     a.tgt = target->data; a.bf16 = target->dtype == DDT_BF16; a.V = target->V;
     a.ts0 = target->s0; a.ts1 = target->s1;
     a.drf = draft ? draft->data : nullptr; a.dl = draft_layer_stride;
@@ -359,7 +372,7 @@ int ddt_succ_update(int32_t* M, int64_t M_bstride, int V, int k_succ, const ddt_
         if (ws_bytes < ws_need((long long)f->B * f->P, V, target->dtype, k_succ)) return DDT_EWORKSPACE;
         st = launch_partials(target, f->B, f->P, f->m, 1, k_succ, ws, s);
         if (st) return st;
-        a.part = (const uint32_t*)ws; a.chunks = chunks_of(V, target->dtype);
+        a.part = (const uint32_t*)ws; a.chunks = groups_of((long long)f->B * f->P, V, target->dtype);
     }
     hipLaunchKernelGGL(k_succ_update, dim3(a.shared ? 1 : f->B), dim3(UP_NT), 0, s, a);
     return launched();
@@ -378,7 +391,7 @@ int ddt_row_topk(const ddt_logits* x, int n0, int n1, int K, int32_t* ids, float
     int st = launch_partials(x, n0, n1, nullptr, 0, K, ws, s);
     if (st) return st;
     RowFinishArgs a;
-    a.part = (const uint32_t*)ws; a.rows = (int)rows; a.chunks = chunks_of(x->V, x->dtype); a.K = K;
+    a.part = (const uint32_t*)ws; a.rows = (int)rows; a.chunks = groups_of(rows, x->V, x->dtype); a.K = K;
     a.ids = ids; a.logc = logc; a.rmax = rmax; a.rsp = rsp;
     hipLaunchKernelGGL(k_row_finish, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
     return launched();

@@ -5,6 +5,7 @@
 
 #define DDT_WAVE 64
 #define DDT_LOG2E 1.4426950408889634f
+#define DDT_LOG2E_D 1.4426950408889634074
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 

@@ -7,134 +7,21 @@
 #include "ddt_rowreduce.hpp"
 #include "../../include/ddt.h"
 
-// ---------------------------------------------------------------------------
-// attach: merge the layer's row partials, create children, pick the frontier
-// ---------------------------------------------------------------------------
-//
-// EAGLE-2 explainer, expansion section: every expanded node gets its draft
-// row's top-K_n tokens as children, value(child) = value(parent) x
-// confidence(child), kept here as S_child = S_parent + log c in fp32 (Graft
-// review step 1, S_{d,j} recursion).  The next frontier is the best K_e of
-// the newest layer by value (ties: canonical key).  Graft review step 1: at a
-// checkpoint depth the row stops unless exp(max S of the layer) > tau.
-
-struct AttachArgs {
-    ddt_tree t;
-    const uint32_t* part;
-    const int32_t* root_tok;
-    int layer, R, chunks, K_n, K_e;
-    int ck, kd_ck, K_max, gate_on;  // ck: 1 if this layer is a Graft checkpoint
-    float tau;
-};
-
-#define AT_NT 256
-#define AT_SORT 1024
-
-__global__ __launch_bounds__(AT_NT) void k_attach(AttachArgs a) {
-    const ddt_tree& t = a.t;
-    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int cap = t.cap;
-    __shared__ float s_M[DDT_MAX_FRONT], s_S[DDT_MAX_FRONT];
-    __shared__ int s_par[DDT_MAX_FRONT];
-    __shared__ uint64_t s_key[DDT_MAX_FRONT * DDT_MAX_K];
-    __shared__ uint32_t srt_a[AT_SORT];
-    __shared__ uint64_t srt_b[AT_SORT];
-    __shared__ int32_t srt_i[AT_SORT];
-    __shared__ int s_Rd, s_base;
-
-    int32_t* tok = t.token + (size_t)b * cap;
-    int32_t* par = t.parent + (size_t)b * cap;
-    int32_t* dep = t.depth + (size_t)b * cap;
-    int32_t* esl = t.eslot + (size_t)b * cap;
-    uint64_t* key = t.key + (size_t)b * cap;
-    float* S = t.S + (size_t)b * cap;
-    float* lc = t.logc + (size_t)b * cap;
-
-    if (tid == 0) {
-        int Rd, base;
-        if (a.layer == 1) {
-            tok[0] = a.root_tok[b]; par[0] = -1; dep[0] = 0; esl[0] = -1; key[0] = 0ull;
-            S[0] = 0.f; lc[0] = 0.f;
-            t.frontier[(size_t)b * t.R_max] = 0;
-            t.active[b] = 1;
-            t.k_draft[b] = a.gate_on ? a.K_max : 0;
-            Rd = 1; base = 1;
-        } else {
-            Rd = min(max(t.n_front[b], 0), a.R);
-            base = t.n_nodes[b];
-            if (base < 1 || base + Rd * a.K_n > cap) Rd = 0;      // capacity guard
-        }
-        s_Rd = Rd; s_base = base;
+// Rank of (a, k) among n entries of (sa, sb) in ascending (sa, sb) order: the
+// number of entries that precede it.  Entries are unique (keys differ).
+__device__ __forceinline__ int rank_among(const uint32_t* sa, const uint64_t* sb, int n, uint32_t a,
+                                          uint64_t k) {
+    int r = 0;
+#pragma unroll 8
+    for (int p = 0; p < n; ++p) {
+        const uint32_t ap = sa[p];
+        r += (ap < a) || (ap == a && sb[p] < k);
     }
-    __syncthreads();
-    const int Rd = s_Rd, base = s_base;
-    if (a.layer == 1 && tid == 0) t.n_nodes[b] = 1;
-    if (Rd == 0) {
-        if (tid == 0) t.n_front[b] = 0;
-        return;
-    }
-    for (int j = tid; j < Rd; j += AT_NT) {
-        const int u = a.layer == 1 ? 0 : t.frontier[(size_t)b * t.R_max + j];
-        s_par[j] = (u >= 0 && u < base) ? u : 0;
-    }
-    // merge row partials: one wave per frontier slot
-    for (int j = wid; j < Rd; j += AT_NT / 64) {
-        float M, Sp;
-        const uint32_t* p = a.part + ((size_t)(b * a.R + j) * a.chunks) * rr_ps(a.K_n);
-        const uint64_t mine = merge_row_wave(p, a.chunks, a.K_n, M, Sp);
-        if (lane < a.K_n) s_key[j * a.K_n + lane] = mine;
-        if (lane == 0) { s_M[j] = M; s_S[j] = Sp; }
-    }
-    __syncthreads();
-    const int count = Rd * a.K_n;
-    const int n2 = next_pow2(count);
-    for (int q = tid; q < n2; q += AT_NT) {
-        if (q < count) {
-            const int j = q / a.K_n, r = q - j * a.K_n;
-            const int u = s_par[j];
-            const uint64_t kk = s_key[j * a.K_n + r];
-            const float l1p = log1pf(s_S[j]);
-            const float logc = (vkey_val(kk) - s_M[j]) - l1p;
-            const float Sv = S[u] + logc;
-            const int du = dep[u];
-            const uint64_t nk = key_child(key[u], du, r, 0);
-            const int node = base + q;
-            tok[node] = vkey_id(kk); par[node] = u; dep[node] = du + 1; esl[node] = -1;
-            S[node] = Sv; lc[node] = logc; key[node] = nk;
-            srt_a[q] = ~ord_f32(Sv); srt_b[q] = nk; srt_i[q] = node;
-            if (r == 0) {
-                esl[u] = j;
-                const size_t ri = ((size_t)b * t.D_max + (a.layer - 1)) * t.R_max + j;
-                t.rmax[ri] = s_M[j];
-                t.rsp[ri] = s_S[j];
-            }
-        } else {
-            srt_a[q] = 0xFFFFFFFFu; srt_b[q] = ~0ull; srt_i[q] = -1;
-        }
-    }
-    __syncthreads();
-    bitonic_sort_lds<AT_NT>(srt_a, srt_b, srt_i, n2);
-    const int nkeep = min(count, t.R_max);
-    for (int k = tid; k < nkeep; k += AT_NT) t.frontier[(size_t)b * t.R_max + k] = srt_i[k];
-    if (tid == 0) {
-        t.n_nodes[b] = base + count;
-        t.layer_base[b] = base;
-        int nf = min(a.K_e, count);
-        if (a.layer >= t.D_max) nf = 0;
-        if (a.ck) {
-            const float smax = unord_f32(~srt_a[0]);
-            if (!(expf(smax) > a.tau)) {       // g_d = 1[c_d > tau_d]
-                t.active[b] = 0;
-                t.k_draft[b] = a.kd_ck;
-                nf = 0;
-            }
-        }
-        t.n_front[b] = nf;
-    }
+    return r;
 }
 
 // ---------------------------------------------------------------------------
-// CAST width and depth for the whole batch (one workgroup)
+// CAST width and depth for the whole batch
 // ---------------------------------------------------------------------------
 //
 // CAST notes, key design 2: width n_i = anchor scan of the batch-averaged
@@ -145,14 +32,6 @@ __global__ __launch_bounds__(AT_NT) void k_attach(AttachArgs a) {
 // Key design 1: select(c) = min(floor(c/L), M-1) (the printed max is read as
 // min).  State lives in t.cast_state: [0..7] FIFO, [8] length, [9] previous
 // u_n, [10] context (tree tokens fed so far).
-
-struct CastArgs {
-    ddt_tree t;
-    ddt_cast c;
-    int layer, K_e;
-};
-
-#define CS_NT 256
 
 __device__ __forceinline__ int cast_sel_row(long long c, int L, int M) {
     long long r = c / L;
@@ -174,41 +53,37 @@ __device__ int anchor_scan_dev(const double* u, const double* c, double C, int k
     return a;
 }
 
-__global__ __launch_bounds__(CS_NT) void k_cast(CastArgs a) {
-    const ddt_tree& t = a.t;
+// Run by one whole workgroup of NT threads once every row's layer is attached.
+template <int NT>
+__device__ void cast_layer(const ddt_tree& t, const ddt_cast& cp, int layer, int K_e) {
     const int tid = threadIdx.x, B = t.B;
     __shared__ double s_v[64 * DDT_MAX_FRONT];
     __shared__ double s_col[DDT_MAX_FRONT + 1];
     __shared__ double u[DDT_MAX_FRONT + 1], c[DDT_MAX_FRONT + 1];
-    __shared__ int s_kcap, s_n, s_go;
+    __shared__ int s_kcap, s_n;
     double* st = t.cast_state;
     if (tid == 0) {
-        if (a.layer == 1) {
+        s_kcap = min(K_e, t.R_max);
+        if (layer == 1) {
             st[0] = 1.0;
             for (int i = 1; i < 8; ++i) st[i] = 0.0;
             st[8] = 1.0; st[9] = -1.0; st[10] = 0.0;
-            t.cont[0] = 1;
-            for (int i = 0; i < t.D_max; ++i) t.widths[i] = 0;
         }
-        s_go = t.cont[0];
-        int kc = a.K_e;
-        for (int b = 0; b < B; ++b) kc = min(kc, t.n_nodes[b] - t.layer_base[b]);
-        s_kcap = max(0, min(kc, t.R_max));
     }
+    if (layer == 1)
+        for (int i = tid; i < t.D_max; i += NT) t.widths[i] = 0;
     __syncthreads();
-    if (!s_go) {
-        for (int b = tid; b < B; b += CS_NT) t.n_front[b] = 0;
-        return;
-    }
+    for (int b = tid; b < B; b += NT) atomicMin(&s_kcap, max(0, t.n_nodes[b] - t.layer_base[b]));
+    __syncthreads();
     const int kcap = s_kcap;
-    for (int q = tid; q < B * kcap; q += CS_NT) {
+    for (int q = tid; q < B * kcap; q += NT) {
         const int b = q / kcap, k = q - b * kcap;
         const int node = t.frontier[(size_t)b * t.R_max + k];
         const int nn = min(max(node, 0), t.cap - 1);
         s_v[q] = exp((double)t.S[(size_t)b * t.cap + nn]);
     }
     __syncthreads();
-    for (int k = tid; k < kcap; k += CS_NT) {
+    for (int k = tid; k < kcap; k += NT) {
         double sum = 0.0;
         for (int b = 0; b < B; ++b) sum += s_v[b * kcap + k];
         s_col[k] = sum;
@@ -217,19 +92,19 @@ __global__ __launch_bounds__(CS_NT) void k_cast(CastArgs a) {
     if (tid == 0) {
         u[0] = 0.0; c[0] = 0.0;
         const int ctx = (int)st[10];
-        const int row = cast_sel_row(ctx, a.c.L, a.c.M);
-        const float* SD = a.c.S_D + (size_t)row * (a.c.N + 1);
-        const float* ST = a.c.S_T + (size_t)row * (a.c.N + 1);
+        const int row = cast_sel_row(ctx, cp.L, cp.M);
+        const float* SD = cp.S_D + (size_t)row * (cp.N + 1);
+        const float* ST = cp.S_T + (size_t)row * (cp.N + 1);
         for (int k = 1; k <= kcap; ++k) {
             u[k] = u[k - 1] + s_col[k - 1] / (double)B;
             c[k] = (double)SD[k] / (double)ST[1];
         }
-        const int n = anchor_scan_dev(u, c, (double)a.c.C1[a.layer - 1], kcap);
+        const int n = anchor_scan_dev(u, c, (double)cp.C1[layer - 1], kcap);
         int len = (int)st[8];
         if (st[9] >= 0.0) {                        // push the previous layer's gain ratio
             const double phi = st[9] > 0.0 ? u[n] / st[9] : 0.0;
             if (len < 8) st[len++] = phi;
-            if (len > a.c.R) {
+            if (len > cp.R) {
                 for (int i = 1; i < len; ++i) st[i - 1] = st[i];
                 --len;
             }
@@ -239,15 +114,159 @@ __global__ __launch_bounds__(CS_NT) void k_cast(CastArgs a) {
         for (int i = 0; i < len; ++i) mean += st[i];
         mean /= (double)len;
         const double score = n > 0 ? mean * u[n] / c[n] : 0.0;
-        const bool stop = (a.layer >= t.D_max) || !(score >= (double)a.c.C2);
+        const bool stop = (layer >= t.D_max) || !(score >= (double)cp.C2);
         st[9] = u[n];
         st[10] = (double)(ctx + n);
-        t.widths[a.layer - 1] = n;
+        t.widths[layer - 1] = n;
         t.cont[0] = stop ? 0 : 1;
         s_n = stop ? 0 : n;
     }
     __syncthreads();
-    for (int b = tid; b < B; b += CS_NT) t.n_front[b] = s_n;
+    for (int b = tid; b < B; b += NT) t.n_front[b] = s_n;
+}
+
+// ---------------------------------------------------------------------------
+// attach: merge the layer's row partials, create children, pick the frontier
+// ---------------------------------------------------------------------------
+//
+// EAGLE-2 explainer, expansion section: every expanded node gets its draft
+// row's top-K_n tokens as children, value(child) = value(parent) x
+// confidence(child), kept here as S_child = S_parent + log c in fp32 (Graft
+// review step 1, S_{d,j} recursion).  The next frontier is the best K_e of
+// the newest layer by value (ties: canonical key), found by rank counting.
+// Graft review step 1: at a checkpoint depth the row stops unless
+// exp(max S of the layer) > tau.  With CAST, the last workgroup to finish the
+// layer (device-scope counter) runs the batch-wide width and depth rule.
+
+struct AttachArgs {
+    ddt_tree t;
+    ddt_cast c;
+    const uint32_t* part;
+    const int32_t* root_tok;
+    int layer, R, chunks, K_n, K_e;
+    int ck, kd_ck, K_max, gate_on, cast_on;  // ck: 1 if this layer is a Graft checkpoint
+    float tau;
+};
+
+#define AT_NT 1024
+#define AT_SORT 1024
+
+__global__ __launch_bounds__(AT_NT) void k_attach(AttachArgs a) {
+    const ddt_tree& t = a.t;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int cap = t.cap;
+    __shared__ float s_M[DDT_MAX_FRONT], s_S[DDT_MAX_FRONT];
+    __shared__ int s_par[DDT_MAX_FRONT];
+    __shared__ uint64_t s_key[DDT_MAX_FRONT * DDT_MAX_K];
+    __shared__ uint32_t srt_a[AT_SORT];
+    __shared__ uint64_t srt_b[AT_SORT];
+    __shared__ int s_Rd, s_base, s_last, s_best;
+
+    int32_t* tok = t.token + (size_t)b * cap;
+    int32_t* par = t.parent + (size_t)b * cap;
+    int32_t* dep = t.depth + (size_t)b * cap;
+    int32_t* esl = t.eslot + (size_t)b * cap;
+    uint64_t* key = t.key + (size_t)b * cap;
+    float* S = t.S + (size_t)b * cap;
+    float* lc = t.logc + (size_t)b * cap;
+
+    // each wave merges its frontier slots' partials straight away (rows past
+    // the row's frontier width were not reduced and are ignored below)
+    {
+        const int rd = a.layer == 1 ? 1 : min(max(t.n_front[b], 0), a.R);
+        for (int j = wid; j < rd; j += AT_NT / 64) {
+            float M, Sp;
+            const uint32_t* p = a.part + ((size_t)(b * a.R + j) * a.chunks) * rr_ps(a.K_n);
+            const uint64_t mine = merge_row_wave(p, a.chunks, a.K_n, M, Sp);
+            if (lane < a.K_n) s_key[j * a.K_n + lane] = mine;
+            if (lane == 0) { s_M[j] = M; s_S[j] = Sp; }
+        }
+    }
+    if (tid == 0) {
+        int Rd, base;
+        if (a.layer == 1) {
+            tok[0] = a.root_tok[b]; par[0] = -1; dep[0] = 0; esl[0] = -1; key[0] = 0ull;
+            S[0] = 0.f; lc[0] = 0.f;
+            t.frontier[(size_t)b * t.R_max] = 0;
+            t.active[b] = 1;
+            t.k_draft[b] = a.gate_on ? a.K_max : 0;
+            t.n_nodes[b] = 1;
+            if (a.cast_on && b == 0) t.cont[0] = 1;
+            Rd = 1; base = 1;
+        } else {
+            Rd = min(max(t.n_front[b], 0), a.R);
+            base = t.n_nodes[b];
+            if (base < 1 || base + Rd * a.K_n > cap) Rd = 0;      // capacity guard
+        }
+        s_Rd = Rd; s_base = base;
+    }
+    __syncthreads();
+    const int Rd = s_Rd, base = s_base;
+    if (Rd > 0) {
+        for (int j = tid; j < Rd; j += AT_NT) {
+            const int u = a.layer == 1 ? 0 : t.frontier[(size_t)b * t.R_max + j];
+            s_par[j] = (u >= 0 && u < base) ? u : 0;
+        }
+        __syncthreads();
+        const int count = Rd * a.K_n;
+        for (int q = tid; q < count; q += AT_NT) {
+            const int j = q / a.K_n, r = q - j * a.K_n;
+            const int u = s_par[j];
+            const uint64_t kk = s_key[j * a.K_n + r];
+            const float l1p = log1pf(s_S[j]);
+            const float logc = (vkey_val(kk) - s_M[j]) - l1p;
+            const float Sv = S[u] + logc;
+            const int du = dep[u];
+            const uint64_t nk = key_child(key[u], du, r, 0);
+            const int node = base + q;
+            tok[node] = vkey_id(kk); par[node] = u; dep[node] = du + 1; esl[node] = -1;
+            S[node] = Sv; lc[node] = logc; key[node] = nk;
+            srt_a[q] = ~ord_f32(Sv); srt_b[q] = nk;
+            if (r == 0) {
+                esl[u] = j;
+                const size_t ri = ((size_t)b * t.D_max + (a.layer - 1)) * t.R_max + j;
+                t.rmax[ri] = s_M[j];
+                t.rsp[ri] = s_S[j];
+            }
+        }
+        __syncthreads();
+        // frontier: the first R_max of the layer by (S desc, key asc)
+        for (int q = tid; q < count; q += AT_NT) {
+            const int r = rank_among(srt_a, srt_b, count, srt_a[q], srt_b[q]);
+            if (r < t.R_max) t.frontier[(size_t)b * t.R_max + r] = base + q;
+            if (r == 0) s_best = q;                     // best node of the layer
+        }
+        __syncthreads();
+        if (tid == 0) {
+            t.n_nodes[b] = base + count;
+            t.layer_base[b] = base;
+            int nf = min(a.K_e, count);
+            if (a.layer >= t.D_max) nf = 0;
+            if (a.ck) {
+                const float smax = unord_f32(~srt_a[s_best]);
+                if (!(expf(smax) > a.tau)) {       // g_d = 1[c_d > tau_d]
+                    t.active[b] = 0;
+                    t.k_draft[b] = a.kd_ck;
+                    nf = 0;
+                }
+            }
+            t.n_front[b] = nf;
+        }
+    } else if (tid == 0) {
+        t.n_front[b] = 0;
+    }
+    if (!a.cast_on) return;
+    // the last workgroup of the layer runs CAST for the batch
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(t.ticket, 1u) == gridDim.x - 1;
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    if (tid == 0) atomicExch(t.ticket, 0u);
+    if (t.cont[0]) cast_layer<AT_NT>(t, a.c, a.layer, a.K_e);
+    else
+        for (int bb = tid; bb < t.B; bb += AT_NT) t.n_front[bb] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -256,7 +275,8 @@ __global__ __launch_bounds__(CS_NT) void k_cast(CastArgs a) {
 //
 // EAGLE-2 explainer, reranking section: every candidate node is ranked by
 // value, the top m are verified; a child never outranks its parent and equal
-// values go to the shallower node, so the set is a connected subtree.  CAST
+// values go to the shallower node, so the set is a connected subtree.  Ranks
+// come from counting, not sorting: only positions below m_max are kept.  CAST
 // key design 4: m per row by the anchor scan of the sorted cumulative values
 // against the verify cost.  Graft: m = the row's k_draft.
 
@@ -271,12 +291,26 @@ struct RerankArgs {
 #define RK_NT 1024
 #define RK_SORT DDT_MAX_NODES
 
+// In-LDS bitonic sort of n2 (power of two) 64-bit keys, ascending.
+template <int NT>
+__device__ void bitonic_sort_u64(uint64_t* v, int n2) {
+    for (int k = 2; k <= n2; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int t = threadIdx.x; t < (n2 >> 1); t += NT) {
+                const int i = ((t / j) * (j << 1)) + (t % j);
+                const int l = i + j;
+                const uint64_t x = v[i], y = v[l];
+                if ((x > y) == ((i & k) == 0)) { v[i] = y; v[l] = x; }
+            }
+            __syncthreads();
+        }
+    }
+}
+
 __global__ __launch_bounds__(RK_NT) void k_rerank(RerankArgs a) {
     const ddt_tree& t = a.t;
     const int b = blockIdx.x, tid = threadIdx.x;
-    __shared__ uint32_t sa[RK_SORT];
-    __shared__ uint64_t sb[RK_SORT];
-    __shared__ int32_t si[RK_SORT];
+    __shared__ uint64_t sv[RK_SORT];
     __shared__ double s_v[DDT_MAX_VERIFY + 1];
     __shared__ double u[DDT_MAX_VERIFY + 1], c[DDT_MAX_VERIFY + 1];
     __shared__ int s_m;
@@ -285,18 +319,33 @@ __global__ __launch_bounds__(RK_NT) void k_rerank(RerankArgs a) {
     const int n2 = next_pow2(N > 0 ? N : 1);
     const float* S = t.S + (size_t)b * t.cap;
     const uint64_t* key = t.key + (size_t)b * t.cap;
-    for (int q = tid; q < n2; q += RK_NT) {
-        if (q < N) {
-            sa[q] = ~ord_f32(S[1 + q]); sb[q] = key[1 + q]; si[q] = 1 + q;
-        } else {
-            sa[q] = 0xFFFFFFFFu; sb[q] = ~0ull; si[q] = -1;
+    // sort (value code, node): S descending; equal values tie-broken by node
+    // index first and fixed up to canonical-key order below
+    for (int q = tid; q < n2; q += RK_NT)
+        sv[q] = q < N ? ((uint64_t)~ord_f32(S[1 + q]) << 32) | (uint32_t)(1 + q) : ~0ull;
+    __syncthreads();
+    bitonic_sort_u64<RK_NT>(sv, n2);
+    // runs of equal value (siblings with equal logits, or exact coincidences)
+    // are re-ordered by canonical key by the thread at each run's start
+    for (int q = tid; q < N; q += RK_NT) {
+        const uint32_t hv = (uint32_t)(sv[q] >> 32);
+        if ((q > 0 && (uint32_t)(sv[q - 1] >> 32) == hv) || q + 1 >= N ||
+            (uint32_t)(sv[q + 1] >> 32) != hv)
+            continue;
+        int e = q + 1;
+        while (e < N && (uint32_t)(sv[e] >> 32) == hv) ++e;
+        for (int i = q + 1; i < e; ++i) {           // insertion sort by key
+            const uint64_t x = sv[i];
+            const uint64_t kx = key[(uint32_t)x];
+            int j = i - 1;
+            while (j >= q && key[(uint32_t)sv[j]] > kx) { sv[j + 1] = sv[j]; --j; }
+            sv[j + 1] = x;
         }
     }
     __syncthreads();
-    bitonic_sort_lds<RK_NT>(sa, sb, si, n2);
     const int kmax = min(a.m_max, N);
     if (a.cast_on) {
-        for (int k = tid; k < kmax; k += RK_NT) s_v[k] = exp((double)unord_f32(~sa[k]));
+        for (int k = tid; k < kmax; k += RK_NT) s_v[k] = exp((double)unord_f32(~(uint32_t)(sv[k] >> 32)));
         __syncthreads();
         if (tid == 0) {
             u[0] = 0.0; c[0] = 0.0;
@@ -314,7 +363,8 @@ __global__ __launch_bounds__(RK_NT) void k_rerank(RerankArgs a) {
     __syncthreads();
     const int m = s_m;
     int32_t* sel = a.sel + (size_t)b * (a.m_max + 1);
-    for (int k = tid; k <= a.m_max; k += RK_NT) sel[k] = k == 0 ? 0 : (k <= m ? si[k - 1] : -1);
+    for (int k = tid; k <= a.m_max; k += RK_NT)
+        sel[k] = k == 0 ? 0 : (k <= m ? (int32_t)(uint32_t)sv[k - 1] : -1);
     if (tid == 0) a.m_out[b] = m;
 }
 
@@ -406,44 +456,58 @@ __global__ __launch_bounds__(MK_NT) void k_build_mask(MaskArgs a) {
     const ddt_flat& f = a.f;
     const int b = blockIdx.x, tid = threadIdx.x;
     const int P = f.P, W = f.W, Dp = f.Dp;
-    __shared__ uint32_t sa[MK_NT];
-    __shared__ uint64_t sb[MK_NT];
-    __shared__ int32_t si[MK_NT];
-    __shared__ int16_t s_map[DDT_MAX_NODES];
+    __shared__ uint64_t s_key[MK_NT], s_fkey[MK_NT];
+    __shared__ int32_t s_node[MK_NT], s_fnode[MK_NT];
     __shared__ int s_fp[MK_NT], s_dep[MK_NT], s_hc[MK_NT], s_lidx[MK_NT];
     __shared__ int s_nl;
     const int m = min(max(a.m[b], 0), P - 1);
-    const int n = m + 1;
-    const int n2 = next_pow2(P);
     const size_t o = (size_t)b * t.cap;
     const int32_t* sel = a.sel + (size_t)b * P;
-    for (int q = tid; q < n2; q += MK_NT) {
-        int node = q < n ? sel[q] : -1;
+    // valid selected nodes (the selection is a prefix of sel)
+    for (int q = tid; q < P; q += MK_NT) {
+        int node = q <= m ? sel[q] : -1;
         if (node < 0 || node >= t.cap) node = -1;
-        sa[q] = 0u;
-        sb[q] = node >= 0 ? t.key[o + node] : ~0ull;
-        si[q] = node;
+        s_node[q] = node;
+        s_key[q] = node >= 0 ? t.key[o + node] : ~0ull;
+        s_hc[q] = 0;
     }
-    for (int q = tid; q < DDT_MAX_NODES; q += MK_NT) s_map[q] = -1;
     __syncthreads();
-    bitonic_sort_lds<MK_NT>(sa, sb, si, n2);
-    for (int i = tid; i < n; i += MK_NT) if (si[i] >= 0) s_map[si[i]] = (int16_t)i;
+    const int n = m + 1;
+    // flat index = rank of the key among the selected keys (keys are unique)
+    for (int q = tid; q < n; q += MK_NT) {
+        const uint64_t k = s_key[q];
+        int r = 0;
+#pragma unroll 8
+        for (int p = 0; p < n; ++p) r += s_key[p] < k;
+        s_fkey[r] = k;
+        s_fnode[r] = s_node[q];
+    }
     __syncthreads();
     const size_t fo = (size_t)b * P;
     for (int i = tid; i < P; i += MK_NT) {
         int node = -1, tk = -1, fp = -1, d = 0;
-        if (i < n && si[i] >= 0) {
-            node = si[i];
+        if (i < n && s_fnode[i] >= 0) {
+            node = s_fnode[i];
             tk = t.token[o + node];
             const int pn = t.parent[o + node];
-            fp = (pn >= 0 && pn < t.cap) ? s_map[pn] : -1;
+            if (pn >= 0 && pn < t.cap) {
+                // parent's flat index: binary search of its key in the sorted keys
+                const uint64_t pk = t.key[o + pn];
+                int lo = 0, hi = n;
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (s_fkey[mid] < pk) lo = mid + 1;
+                    else hi = mid;
+                }
+                fp = (lo < n && s_fkey[lo] == pk) ? lo : -1;
+            }
             d = t.depth[o + node];
         }
         f.node[fo + i] = node;
         f.token[fo + i] = tk;
         f.parent[fo + i] = fp;
         f.pos[fo + i] = a.prefix + d;
-        s_fp[i] = fp; s_dep[i] = d; s_hc[i] = 0;
+        s_fp[i] = fp; s_dep[i] = d;
     }
     __syncthreads();
     for (int i = tid; i < P; i += MK_NT) {
@@ -484,10 +548,10 @@ __global__ __launch_bounds__(MK_NT) void k_build_mask(MaskArgs a) {
         if (li < 0 || li >= L) continue;
         int32_t* row = ret + (size_t)li * (Dp + 1);
         const int d = min(s_dep[i], Dp);
-        for (int s = d + 1; s <= Dp; ++s) row[s] = -1;
+        for (int s2 = d + 1; s2 <= Dp; ++s2) row[s2] = -1;
         int j = i;
-        for (int s = d; s >= 0; --s) {
-            row[s] = j;
+        for (int s2 = d; s2 >= 0; --s2) {
+            row[s2] = j;
             j = j >= 0 ? s_fp[j] : -1;
         }
     }
@@ -524,33 +588,86 @@ struct VerifyArgs {
     int32_t* next_token;
 };
 
-#define VF_NT 256
-#define VF_TILE 512            // one wave x 8 elements
-#define VF_MAXTILES 1024       // V <= 524288
+#define VF_NT 1024
+#define VF_TILE 256            // one wave x 4 elements
+#define VF_MAXTILES 2048       // V <= 524288
 
-__device__ __forceinline__ float ld_logit(const void* base, int bf16, int64_t i) {
-    return bf16 ? __uint_as_float((uint32_t)((const uint16_t*)base)[i] << 16) : ((const float*)base)[i];
+// 4 consecutive logits starting at v0 (a multiple of 4); -inf past V
+__device__ __forceinline__ void ld4(const void* row, bool bf16, bool al, int V, int v0, float (&x)[4]) {
+    if (bf16) {
+        const uint16_t* r = (const uint16_t*)row;
+        if (al && v0 + 4 <= V) {
+            const uint2 w = *(const uint2*)(r + v0);
+            x[0] = __uint_as_float(w.x << 16);
+            x[1] = __uint_as_float(w.x & 0xFFFF0000u);
+            x[2] = __uint_as_float(w.y << 16);
+            x[3] = __uint_as_float(w.y & 0xFFFF0000u);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                x[e] = v0 + e < V ? __uint_as_float((uint32_t)r[v0 + e] << 16) : -INFINITY;
+        }
+    } else {
+        const float* r = (const float*)row;
+        if (al && v0 + 4 <= V) {
+            const u32x4 w = *(const u32x4*)(r + v0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) x[q] = __uint_as_float(w[q]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = v0 + e < V ? r[v0 + e] : -INFINITY;
+        }
+    }
 }
 
-struct WalkState {
+__device__ __forceinline__ float ld_logit(const void* row, bool bf16, int v) {
+    return bf16 ? __uint_as_float((uint32_t)((const uint16_t*)row)[v] << 16) : ((const float*)row)[v];
+}
+
+// The walk at one node: p(v) = 2^((t_v - Mt) kT - lzt) is the target softmax at
+// temperature T (kT = log2(e) / T, lzt = log2 of its normaliser), q(v) likewise
+// from the draft row.  After k rejections the residual is
+// p_k = max(0, p - a_k q) / b_k with a_0 = 0, b_0 = 1, a_{k+1} = a_k + b_k and
+// b_{k+1} = F(a_{k+1}) = sum_v max(0, p(v) - a_{k+1} q(v)): the repeated
+// norm(max(0, p_k - q)) written out (an all-zero residual leaves p_k as it
+// was), so each rejection costs one pass over the two rows and no division.
+// Per-element values are fp64: b_k can be small when target and draft are
+// close, and the error of p - a q is amplified by 1 / b_k.
+struct WalkRows {
     const void* trow;
     const void* drow;
-    int bf16;
-    float Mt, Md, invT;
-    double Zt, Zd;
-    int k;
-    const double* Zs;
+    bool bf16, alt, ald;
+    double kT, Mt, Md, lzt, lzd;
 };
 
-// residual chain value p_k(v) and draft q(v) of one vocabulary entry
-__device__ __forceinline__ void walk_pq(const WalkState& w, int v, double& p, double& q) {
-    const float tv = ld_logit(w.trow, w.bf16, v), dv = ld_logit(w.drow, w.bf16, v);
-    p = (double)expf((tv - w.Mt) * w.invT) / w.Zt;
-    q = (double)expf((dv - w.Md) * w.invT) / w.Zd;
-    for (int r = 0; r < w.k; ++r) {
-        const double z = w.Zs[r];
-        if (z > 0.0) p = fmax(0.0, p - q) / z;
+__device__ __forceinline__ double walk_p(const WalkRows& w, float t) {
+    return exp2(((double)t - w.Mt) * w.kT - w.lzt);
+}
+__device__ __forceinline__ double walk_q(const WalkRows& w, float d) {
+    return exp2(((double)d - w.Md) * w.kT - w.lzd);
+}
+
+// block-wide sum over the vocabulary of fn(t_v, d_v) in fp64; when only the
+// target row is needed (UseD false) the draft row is not read
+template <bool UseD, class Fn>
+__device__ double walk_pass(const WalkRows& w, int V, double* s_red, Fn fn) {
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    double acc = 0.0;
+    for (int v0 = tid * 4; v0 < V; v0 += VF_NT * 4) {
+        float tx[4], dx[4];
+        ld4(w.trow, w.bf16, w.alt, V, v0, tx);
+        if (UseD) ld4(w.drow, w.bf16, w.ald, V, v0, dx);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc += fn(tx[e], UseD ? dx[e] : 0.f);
     }
+    const double d = wave_sum_f64(acc);
+    __syncthreads();
+    if (lane == 0) s_red[wid] = d;
+    __syncthreads();
+    double tot = 0.0;
+    for (int q = 0; q < VF_NT / 64; ++q) tot += s_red[q];
+    __syncthreads();
+    return tot;
 }
 
 __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
@@ -562,11 +679,10 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
     __shared__ float s_M[MK_NT], s_S[MK_NT];
     __shared__ int s_fp[MK_NT], s_ft[MK_NT];
     __shared__ double s_tile[VF_MAXTILES];
-    __shared__ double s_Zs[DDT_MAX_K + 1];
     __shared__ double s_red[VF_NT / 64];
     __shared__ int s_path[DDT_MAX_DEPTH + 2];
     __shared__ int s_ch[MK_NT];
-    __shared__ int s_nch, s_u, s_len, s_done, s_acc, s_next;
+    __shared__ int s_nch, s_u, s_len, s_acc, s_next;
     __shared__ unsigned long long s_best;
     const int m = min(max(f.m[b], 0), P - 1);
     const int n = m + 1;
@@ -634,9 +750,9 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
     }
 
     // T > 0: sibling walk with residual resampling
-    const float invT = 1.f / T;
+    const double kT = (double)DDT_LOG2E_D / (double)T;
     const float* Ub = a.U + fo * 2;
-    if (tid == 0) { s_u = 0; s_len = 0; s_path[0] = 0; s_done = 0; }
+    if (tid == 0) { s_u = 0; s_len = 0; s_path[0] = 0; }
     __syncthreads();
     while (true) {
         const int u = s_u;
@@ -650,78 +766,60 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
         const int unode = f.node[fo + u];
         const int uslot = (unode >= 0 && unode < t.cap) ? t.eslot[(size_t)b * t.cap + unode] : -1;
         const int udep = (unode >= 0 && unode < t.cap) ? t.depth[(size_t)b * t.cap + unode] : 0;
-        WalkState w;
-        w.bf16 = a.bf16;
-        w.trow = a.bf16 ? (const void*)((const uint16_t*)a.tgt + b * a.ts0 + u * a.ts1)
-                        : (const void*)((const float*)a.tgt + b * a.ts0 + u * a.ts1);
-        w.invT = invT;
-        w.Mt = s_M[u];
-        w.k = 0;
-        w.Zs = s_Zs;
         const bool has_q = nch > 0 && uslot >= 0 && a.drf != nullptr && udep < t.D_max;
+        WalkRows w;
+        w.bf16 = a.bf16 != 0;
+        const size_t es = a.bf16 ? 2 : 4;
+        w.trow = (const char*)a.tgt + (size_t)(b * a.ts0 + u * a.ts1) * es;
+        size_t ri = 0;
         if (has_q) {
             const int64_t doff = (int64_t)udep * a.dl + (int64_t)b * a.ds0 + (int64_t)uslot * a.ds1;
-            w.drow = a.bf16 ? (const void*)((const uint16_t*)a.drf + doff)
-                            : (const void*)((const float*)a.drf + doff);
-            const size_t ri = ((size_t)b * t.D_max + udep) * t.R_max + uslot;
-            w.Md = t.rmax[ri];
+            w.drow = (const char*)a.drf + (size_t)doff * es;
+            ri = ((size_t)b * t.D_max + udep) * t.R_max + uslot;
         } else {
             w.drow = w.trow;
-            w.Md = w.Mt;
         }
-        // normalisers of p and q at this temperature
-        if (T == 1.f) {
-            w.Zt = 1.0 + (double)s_S[u];
-            w.Zd = has_q ? 1.0 + (double)t.rsp[((size_t)b * t.D_max + udep) * t.R_max + uslot] : 1.0;
+        const uintptr_t amask = w.bf16 ? 7u : 15u;     // 4-element vector loads
+        w.alt = (((uintptr_t)w.trow) & amask) == 0;
+        w.ald = (((uintptr_t)w.drow) & amask) == 0;
+        w.kT = kT;
+        w.Mt = s_M[u];
+        w.Md = has_q ? (double)t.rmax[ri] : w.Mt;
+        w.lzt = 0.0;
+        w.lzd = 0.0;
+        // normalisers (p always, q when u has children)
+        if (has_q) {
+            WalkRows wd = w;                           // the draft row alone
+            wd.trow = w.drow;
+            wd.alt = w.ald;
+            const double Zt = walk_pass<false>(w, a.V, s_red, [&](float tv, float) { return walk_p(w, tv); });
+            const double Zd = walk_pass<false>(wd, a.V, s_red, [&](float dv, float) { return walk_q(w, dv); });
+            w.lzt = log2(Zt);
+            w.lzd = log2(Zd);
         } else {
-            double zt = 0.0, zd = 0.0;
-            for (int v = tid; v < a.V; v += VF_NT) {
-                zt += (double)expf((ld_logit(w.trow, w.bf16, v) - w.Mt) * invT);
-                if (has_q) zd += (double)expf((ld_logit(w.drow, w.bf16, v) - w.Md) * invT);
-            }
-            zt = wave_sum_f64(zt); zd = wave_sum_f64(zd);
-            __syncthreads();
-            if (lane == 0) s_red[wid] = zt;
-            __syncthreads();
-            double tz = 0.0;
-            for (int q = 0; q < VF_NT / 64; ++q) tz += s_red[q];
-            __syncthreads();
-            if (lane == 0) s_red[wid] = zd;
-            __syncthreads();
-            double dz = 0.0;
-            for (int q = 0; q < VF_NT / 64; ++q) dz += s_red[q];
-            w.Zt = tz; w.Zd = has_q ? dz : 1.0;
+            w.lzt = log2(walk_pass<false>(w, a.V, s_red, [&](float tv, float) { return walk_p(w, tv); }));
         }
+        double ra = 0.0, rb = 1.0;                      // residual p_k = max(0, p - ra q) / rb
         int accepted = -1;
         if (has_q) {
             for (int ci = 0; ci < nch; ++ci) {
                 const int c = s_ch[ci];
                 if (tid == 0) {
                     const int x = min(max(s_ft[c], 0), a.V - 1);
-                    double p, q;
-                    walk_pq(w, x, p, q);
-                    const double ratio = q > 0.0 ? p / q : INFINITY;
+                    const double px = walk_p(w, ld_logit(w.trow, w.bf16, x));
+                    const double qx = walk_q(w, ld_logit(w.drow, w.bf16, x));
+                    const double pk = fmax(0.0, px - ra * qx) / rb;
+                    const double ratio = qx > 0.0 ? pk / qx : INFINITY;
                     s_acc = ((double)Ub[2 * c] < ratio) ? 1 : 0;
                 }
                 __syncthreads();
                 if (s_acc) { accepted = c; break; }
-                // rejection: Z = sum_v max(0, p_k(v) - q(v))
-                double z = 0.0;
-                for (int v = tid; v < a.V; v += VF_NT) {
-                    double p, q;
-                    walk_pq(w, v, p, q);
-                    z += fmax(0.0, p - q);
-                }
-                z = wave_sum_f64(z);
-                if (lane == 0) s_red[wid] = z;
-                __syncthreads();
-                if (tid == 0) {
-                    double zz = 0.0;
-                    for (int q = 0; q < VF_NT / 64; ++q) zz += s_red[q];
-                    s_Zs[w.k] = zz;
-                }
-                __syncthreads();
-                w.k = min(w.k + 1, DDT_MAX_K);
+                // rejection: b' = F(a + b)
+                const double an = ra + rb;
+                const double F = walk_pass<true>(w, a.V, s_red, [&](float tv, float dv) {
+                    return fmax(0.0, walk_p(w, tv) - an * walk_q(w, dv));
+                });
+                if (F > 0.0) { ra = an; rb = F; }
             }
         }
         if (accepted >= 0) {
@@ -729,16 +827,21 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
             __syncthreads();
             continue;
         }
-        // emission from the current p by inverse CDF with U[u][1]
+        // emission from the current residual by inverse CDF with U[u][1] over
+        // the unnormalised weights r(v) = max(0, p(v) - a q(v)); the threshold
+        // scales with their total.  Tiles of 256 ids: one wave each.
         const int ntiles = (a.V + VF_TILE - 1) / VF_TILE;
         for (int tile = wid; tile < ntiles; tile += VF_NT / 64) {
+            float tx[4], dx[4];
+            const int v0 = tile * VF_TILE + lane * 4;
+            ld4(w.trow, w.bf16, w.alt, a.V, v0, tx);
+            if (has_q) ld4(w.drow, w.bf16, w.ald, a.V, v0, dx);
             double ls = 0.0;
-            for (int e = 0; e < 8; ++e) {
-                const int v = tile * VF_TILE + lane * 8 + e;
-                if (v < a.V) { double p, q; walk_pq(w, v, p, q); ls += p; }
-            }
-            ls = wave_sum_f64(ls);
-            if (lane == 0) s_tile[tile] = ls;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ls += has_q ? fmax(0.0, walk_p(w, tx[e]) - ra * walk_q(w, dx[e])) : walk_p(w, tx[e]);
+            const double ws = wave_sum_f64(ls);
+            if (lane == 0) s_tile[tile] = ws;
         }
         __syncthreads();
         if (tid == 0) {
@@ -751,7 +854,13 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
                 if (acc + s_tile[i] > thr) { ts = i; break; }
                 acc += s_tile[i];
             }
-            if (ts < 0) { ts = ntiles - 1; acc -= s_tile[ts]; }
+            if (ts < 0) {                              // rounding at the top end: last tile with mass
+                acc = 0.0;
+                int last = 0;
+                for (int i = 0; i < ntiles; ++i) if (s_tile[i] > 0.0) last = i;
+                for (int i = 0; i < last; ++i) acc += s_tile[i];
+                ts = last;
+            }
             s_red[0] = acc; s_red[1] = thr;
             s_next = ts;
         }
@@ -759,12 +868,16 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
         if (wid == 0) {
             const int tile = s_next;
             const double base = s_red[0], thr = s_red[1];
-            double pv[8], ls = 0.0;
-            for (int e = 0; e < 8; ++e) {
-                const int v = tile * VF_TILE + lane * 8 + e;
-                double p = 0.0, q;
-                if (v < a.V) walk_pq(w, v, p, q);
-                pv[e] = p; ls += p;
+            float tx[4], dx[4];
+            const int v0 = tile * VF_TILE + lane * 4;
+            ld4(w.trow, w.bf16, w.alt, a.V, v0, tx);
+            if (has_q) ld4(w.drow, w.bf16, w.ald, a.V, v0, dx);
+            double pv[4];
+            double ls = 0.0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                pv[e] = has_q ? fmax(0.0, walk_p(w, tx[e]) - ra * walk_q(w, dx[e])) : walk_p(w, tx[e]);
+                ls += pv[e];
             }
             // exclusive prefix over lanes, in lane order
             double incl = ls;
@@ -772,12 +885,12 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
                 const double o = __shfl_up(incl, d);
                 if (lane >= d) incl += o;
             }
-            const double excl = incl - ls;
-            // first element whose running sum exceeds thr; fall back to the last positive
+            double run = base + (incl - ls);
+            // first id whose running sum exceeds thr; else the last one with mass
             int hit = 0x7FFFFFFF, lastpos = -1;
-            double run = base + excl;
-            for (int e = 0; e < 8; ++e) {
-                const int v = tile * VF_TILE + lane * 8 + e;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int v = v0 + e;
                 run += pv[e];
                 if (v < a.V && pv[e] > 0.0) {
                     if (run > thr && hit == 0x7FFFFFFF) hit = v;
@@ -794,7 +907,7 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
     }
     if (tid == 0) {
         const int len = s_len;
-        for (int s = 0; s <= Dp; ++s) apath[s] = s <= len ? s_path[s] : -1;
+        for (int s2 = 0; s2 <= Dp; ++s2) apath[s2] = s2 <= len ? s_path[s2] : -1;
         a.accept_len[b] = len;
         a.next_token[b] = s_next;
     }

@@ -115,6 +115,7 @@ typedef struct ddt_tree {
     int32_t* cont;       /* [1] CAST: 1 while the batch keeps growing */
     int32_t* widths;     /* [D_max] CAST: width n_i chosen at layer i (0 for layers not built) */
     double* cast_state;  /* [16] CAST per-round state (gain FIFO, utility, context) */
+    uint32_t* ticket;    /* [1] CAST: workgroups of a layer done so far (back to 0 after each layer) */
 } ddt_tree;
 
 /* Bytes of device memory a tree of these sizes needs (256-byte aligned base). */
@@ -122,8 +123,10 @@ size_t ddt_tree_bytes(int B, int cap, int D_max, int R_max);
 
 /*
  * Fill *t with pointers into `base` (device, >= ddt_tree_bytes, 256-byte
- * aligned).  Host-only: touches no device memory.  The tree is (re)initialised
- * by ddt_tree_expand with layer = 1.
+ * aligned).  Host-only: touches no device memory.  The memory must be
+ * zero-filled once before its first use (the CAST layer counter starts at 0
+ * and every call leaves it at 0); the tree itself is (re)initialised by
+ * ddt_tree_expand with layer = 1.
  */
 int ddt_tree_bind(ddt_tree* t /*host*/, void* base, size_t bytes, int B, int cap, int D_max,
                   int R_max);
