@@ -19,7 +19,8 @@ class Tree(C.Structure):
     _fields_ = [("B", i32), ("cap", i32), ("D_max", i32), ("R_max", i32),
                 ("token", P), ("parent", P), ("depth", P), ("eslot", P), ("key", P),
                 ("S", P), ("logc", P), ("rmax", P), ("rsp", P), ("n_nodes", P),
-                ("layer_base", P), ("n_front", P), ("frontier", P), ("active", P),
+                ("layer_base", P), ("n_front", P), ("frontier", P), ("front_S", P), ("front_key", P),
+                ("active", P),
                 ("k_draft", P), ("cont", P), ("widths", P), ("cast_state", P), ("ticket", P)]
 
 

@@ -18,17 +18,10 @@ inline int chunk_elems(int dtype) {
 
 inline int chunks_of(int V, int dtype) { return (V + chunk_elems(dtype) - 1) / chunk_elems(dtype); }
 
-// Chunks per workgroup of the row reduction: one while the grid is small (more
-// workgroups, more bytes in flight), more once there are workgroups to spare.
-inline int tpw_of(long long rows, int V, int dtype) {
-    (void)rows; (void)V; (void)dtype;
-    return 1;
-}
-
-// Partials per row; producer and consumers derive it from the same grid rows.
+// Partials per row (one per chunk); producer and consumers agree on it.
 inline int groups_of(long long rows, int V, int dtype) {
-    const int t = tpw_of(rows, V, dtype);
-    return (chunks_of(V, dtype) + t - 1) / t;
+    (void)rows;
+    return chunks_of(V, dtype);
 }
 
 inline size_t ws_need(long long rows, int V, int dtype, int K) {
@@ -46,6 +39,7 @@ int check_tree(const ddt_tree* t) {
         t->eslot == nullptr || t->key == nullptr || t->S == nullptr || t->logc == nullptr ||
         t->rmax == nullptr || t->rsp == nullptr || t->n_nodes == nullptr ||
         t->layer_base == nullptr || t->n_front == nullptr || t->frontier == nullptr ||
+        t->front_S == nullptr || t->front_key == nullptr ||
         t->active == nullptr || t->k_draft == nullptr || t->cont == nullptr ||
         t->widths == nullptr || t->cast_state == nullptr || t->ticket == nullptr)
         return DDT_EINVAL;
@@ -71,7 +65,7 @@ int check_cast(const ddt_cast* c, int B) {
         return DDT_EINVAL;
     if (c->L < 1 || c->M < 1 || c->N < 1 || c->R < 1 || c->R > 8 || c->ctx_verify < 0)
         return DDT_EINVAL;
-    if (B > 64) return DDT_ECAPACITY;
+    if (B > 64 || c->M > DDT_CAST_MAX_M) return DDT_ECAPACITY;
     return DDT_OK;
 }
 
@@ -92,19 +86,19 @@ int launch_partials(const ddt_logits* x, int n0, int n1, const int32_t* count, i
     rs.base = x->data; rs.s0 = x->s0; rs.s1 = x->s1; rs.n1 = n1;
     rs.count = count; rs.count_add = count_add;
     const long long rows = (long long)n0 * n1;
-    const int tpw = tpw_of(rows, x->V, x->dtype);
     const int groups = groups_of(rows, x->V, x->dtype);
-    const long long blocks = rows * groups;
-    if (blocks <= 0) return DDT_OK;
+    const long long total = rows * groups;
+    if (total <= 0) return DDT_OK;
+    if (total > INT32_MAX) return DDT_ECAPACITY;
+    const bool bf16 = x->dtype == DDT_BF16;
     const bool timed = g_events != nullptr && g_used < g_pairs;
     if (timed && hipEventRecord((hipEvent_t)g_events[2 * g_used], s) != hipSuccess) return DDT_ELAUNCH;
-    const dim3 grid((unsigned)blocks), blk(RR_NT);
+    const dim3 grid((unsigned)total), blk(RR_NT);
     uint32_t* part = (uint32_t*)ws;
-    (void)tpw;
-    if (x->dtype == DDT_BF16)
-        hipLaunchKernelGGL((k_row_partial<true, 1>), grid, blk, 0, s, rs, x->V, groups, K, part);
+    if (bf16)
+        hipLaunchKernelGGL((k_row_partial<true>), grid, blk, 0, s, rs, x->V, groups, K, part);
     else
-        hipLaunchKernelGGL((k_row_partial<false, 1>), grid, blk, 0, s, rs, x->V, groups, K, part);
+        hipLaunchKernelGGL((k_row_partial<false>), grid, blk, 0, s, rs, x->V, groups, K, part);
     const int st = launched();
     if (timed) {
         if (hipEventRecord((hipEvent_t)g_events[2 * g_used + 1], s) != hipSuccess) return DDT_ELAUNCH;
@@ -156,7 +150,8 @@ size_t ddt_tree_bytes(int B, int cap, int D_max, int R_max) {
     n += 2 * align256(bc * 4);                                 // S logc
     n += 2 * align256((size_t)B * D_max * R_max * 4);          // rmax rsp
     n += 5 * align256((size_t)B * 4);                          // n_nodes layer_base n_front active k_draft
-    n += align256((size_t)B * R_max * 4);                      // frontier
+    n += 2 * align256((size_t)B * R_max * 4);                  // frontier front_S
+    n += align256((size_t)B * R_max * 8);                      // front_key
     n += align256(4);                                          // cont
     n += align256((size_t)D_max * 4);                          // widths
     n += align256(16 * 8);                                     // cast_state
@@ -188,6 +183,8 @@ int ddt_tree_bind(ddt_tree* t, void* base, size_t bytes, int B, int cap, int D_m
     t->active = carve<int32_t>(p, B);
     t->k_draft = carve<int32_t>(p, B);
     t->frontier = carve<int32_t>(p, (size_t)B * R_max);
+    t->front_S = carve<float>(p, (size_t)B * R_max);
+    t->front_key = carve<uint64_t>(p, (size_t)B * R_max);
     t->cont = carve<int32_t>(p, 1);
     t->widths = carve<int32_t>(p, D_max);
     t->cast_state = carve<double>(p, 16);

@@ -1,16 +1,17 @@
 // Vocabulary-wide row reduction: max, sigma' and top-K of logit rows.
 //
-// One workgroup reduces TPW consecutive fixed-size chunks ("tiles") of one row,
-// streaming them from HBM once with 16-byte non-temporal loads; the next
-// tile's loads are issued before the current one is processed.  Each thread
-// keeps four independent online-softmax chains (running max, first index of
-// the max, and sigma' = sum of exp(x - max) over the chain with the max element
-// itself left out), so a tile costs one exp per element and no cross-lane
-// traffic.  Top-K candidates are filtered against a threshold: the K-th largest
-// per-lane maximum of the first tile, which cannot exceed the workgroup's K-th
-// largest element; survivors go to an LDS list and the workgroup's top-K is
-// picked from it by rank counting.  The workgroup writes one partial (max,
-// sigma', top-K keys); consumers merge the partials of a row.
+// One workgroup of 256 threads reduces one fixed-size chunk of one row (8192
+// bf16 or 4096 fp32 logits): every thread issues its four 16-byte
+// non-temporal loads up front and keeps them in registers.  Pass 1 takes the
+// thread maximum; a bit-by-bit ballot search gives each wave the K-th largest
+// lane maximum, and the largest of those over the waves is a lower bound for
+// the chunk's K-th largest element (the candidate threshold).  Pass 2 sums
+// exp(x - M) over the elements below the chunk maximum M (only the wave that
+// holds M tests for it).  The few lanes whose maximum reaches the threshold
+// stage their words in LDS, the wave tests those elements one per lane, and
+// the chunk's top K is placed by rank counting over the resulting list.  The
+// workgroup writes one partial (max, sigma', top-K keys); consumers merge the
+// partials of a row (merge_row_wave).
 //
 // The statistics give the log confidence log c = (l - max) - log1p(sigma') of
 // a draft token, the confidence being the draft softmax probability (EAGLE-2
@@ -105,25 +106,38 @@ __device__ __forceinline__ void rr_load(u32x4 (&raw)[NL], const void* row, bool 
     }
 }
 
+// Make one wave's LDS writes visible to its own later LDS reads (no
+// workgroup barrier: the wave only talks to itself).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// max of three floats in one instruction (the operands are plain values
+// decoded from bf16/fp32 bits; no NaN canonicalisation is wanted)
+__device__ __forceinline__ float rr_max3(float a, float b, float c) {
+    float r;
+    asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // element e of 16-byte word vector r
 #define RR_X(r, e) (BF16 ? __uint_as_float(((e) & 1) ? ((r)[(e) >> 1] & 0xFFFF0000u) : ((r)[(e) >> 1] << 16)) \
                          : __uint_as_float((r)[(e)]))
 
-// One workgroup: TPW consecutive chunks of one row, all loads issued up front
-// and held in registers.  Pass 1 takes the thread maximum; one barrier gives
-// the workgroup maximum M and the candidate threshold; pass 2 sums
-// exp(x - M).  The single element that sigma' leaves out (the first occurrence
-// of M) is removed exactly by the thread that holds it, in a branch only such
-// threads take.
-template <bool BF16, int TPW>
+// One workgroup reduces one chunk of one row.
+template <bool BF16>
 __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int groups, int K,
                                                        uint32_t* __restrict__ part) {
     using SH = RRShape<BF16>;
-    constexpr int VEC = SH::VEC, CH = SH::CH, NW = RR_NT / DDT_WAVE, NL = RR_NV * TPW;
-    __shared__ uint32_t s_wmax[NW], s_wtau[NW], s_wtie[NW];
+    constexpr int VEC = SH::VEC, CH = SH::CH, NW = RR_NT / DDT_WAVE, NL = RR_NV;
+    __shared__ uint32_t s_wmax[NW], s_wtau[NW];
     __shared__ float s_wsum[NW];
     __shared__ int s_cnt, s_ties;
     __shared__ uint64_t s_list[RR_CAP];
+    __shared__ u32x4 s_stage[RR_NT * RR_NV];
+    __shared__ int s_stid[RR_NT];
 
     const int g = blockIdx.x % groups;
     const int rowg = blockIdx.x / groups;
@@ -134,8 +148,8 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
     const void* row = (const char*)rs.base + off * (BF16 ? 2 : 4);
     const bool al = (((uintptr_t)row) & 15u) == 0;
     uint32_t* out = part + ((size_t)rowg * groups + g) * rr_ps(K);
-    const int start = g * TPW * CH;
-    // load i covers ids start + (i*NT + tid)*VEC .. +VEC  (tile i / RR_NV)
+    const int start = g * CH;
+    // load i covers ids start + (i*NT + tid)*VEC .. +VEC
 #define RR_ID(i, e) (start + ((i) * RR_NT + tid) * VEC + (e))
 
     u32x4 raw[NL];
@@ -147,7 +161,7 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
 #pragma unroll
-        for (int e = 0; e < VEC; e += 2) tm = fmaxf(tm, fmaxf(RR_X(raw[i], e), RR_X(raw[i], e + 1)));
+        for (int e = 0; e < VEC; e += 2) tm = rr_max3(tm, RR_X(raw[i], e), RR_X(raw[i], e + 1));
     }
     // wave maximum and the candidate threshold: the K-th largest lane maximum
     // (exact, bit by bit; bf16 codes differ only in their top 16 bits) bounds
@@ -175,43 +189,66 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
     const float tauf = bt ? unord_f32(bt) : -INFINITY;
     const float ML = M * DDT_LOG2E;
 
-    // pass 2: sum of exp(x - M) over every element
+    // pass 2: sum of exp(x - M) over the elements below M and the count of
+    // elements equal to M (sigma' leaves out exactly one of them; the others
+    // add exp(0) = 1 each, put back below).  The raw exp2 flushes results
+    // below 2^-126 to zero, far below the sum's precision.
     float s0 = 0.f, s1 = 0.f;
+    int ties = 0;
+    if (__ballot(tm == M)) {
+        // a wave holding the maximum: leave out and count the elements equal to M
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
+        for (int i = 0; i < NL; ++i) {
 #pragma unroll
-        for (int e = 0; e < VEC; e += 2) {
-            s0 += exp2f(fmaf(RR_X(raw[i], e), DDT_LOG2E, -ML));
-            s1 += exp2f(fmaf(RR_X(raw[i], e + 1), DDT_LOG2E, -ML));
+            for (int e = 0; e < VEC; e += 2) {
+                const float x0 = RR_X(raw[i], e), x1 = RR_X(raw[i], e + 1);
+                ties += (x0 == M) + (x1 == M);
+                s0 += x0 == M ? 0.f : __builtin_amdgcn_exp2f(fmaf(x0, DDT_LOG2E, -ML));
+                s1 += x1 == M ? 0.f : __builtin_amdgcn_exp2f(fmaf(x1, DDT_LOG2E, -ML));
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+#pragma unroll
+            for (int e = 0; e < VEC; e += 2) {
+                s0 += __builtin_amdgcn_exp2f(fmaf(RR_X(raw[i], e), DDT_LOG2E, -ML));
+                s1 += __builtin_amdgcn_exp2f(fmaf(RR_X(raw[i], e + 1), DDT_LOG2E, -ML));
+            }
         }
     }
     float s = s0 + s1;
-    if (tm == M) {
-        // this thread holds the maximum: redo its sum without those elements
-        // (summing 1.0 into small terms would cost them precision) and count them
-        s = 0.f;
-        int c = 0;
+    if (ties) atomicAdd(&s_ties, ties);
+    // candidates at or above the threshold go to the LDS list.  The lanes of a
+    // wave whose maximum reaches the threshold (usually a few) stage their
+    // loaded words in LDS; the whole wave then tests those elements, one per
+    // lane, and appends the ones that qualify.  Ids need checking only in a
+    // ragged chunk or when the threshold is -inf (padding is -inf).
+    {
+        const bool chk = !(tauf > -INFINITY) || start + CH > V;
+        const uint64_t pm = __ballot(tm >= tauf);
+        if (pm) {
+            u32x4* st = s_stage + wid * DDT_WAVE * NL;
+            int* stid = s_stid + wid * DDT_WAVE;
+            if (tm >= tauf) {
+                const int idx = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(pm >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)pm, 0u));
 #pragma unroll
-        for (int i = 0; i < NL; ++i) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const float x = RR_X(raw[i], e);
-                c += x == M;
-                s += x == M ? 0.f : exp2f(fmaf(x, DDT_LOG2E, -ML));
+                for (int i = 0; i < NL; ++i) st[idx * NL + i] = raw[i];
+                stid[idx] = tid;
             }
-        }
-        atomicAdd(&s_ties, c);
-    }
-    if (tm >= tauf) {
-        // candidates at or above the threshold go to the LDS list
-#pragma unroll
-        for (int i = 0; i < NL; ++i) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const float x = RR_X(raw[i], e);
-                if (x >= tauf && RR_ID(i, e) < V) {
+            wave_lds_sync();
+            const int np = __popcll(pm);
+            constexpr int EPL = NL * VEC;                  // elements per lane
+            for (int q = lane; q < np * EPL; q += DDT_WAVE) {
+                const int src = q / EPL, e = q - src * EPL;
+                const int i = e / VEC, k = e - i * VEC;
+                const uint32_t w = ((const uint32_t*)&st[src * NL + i])[BF16 ? (k >> 1) : k];
+                const float x = BF16 ? __uint_as_float((k & 1) ? (w & 0xFFFF0000u) : (w << 16)) : __uint_as_float(w);
+                const int id = start + (i * RR_NT + stid[src]) * VEC + k;
+                if (x >= tauf && (!chk || id < V)) {
                     const int slot = atomicAdd(&s_cnt, 1);
-                    if (slot < RR_CAP) s_list[slot] = vkey(x, RR_ID(i, e));
+                    if (slot < RR_CAP) s_list[slot] = vkey(x, id);
                 }
             }
         }
@@ -226,7 +263,8 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
         for (int p = tid; p < cnt; p += RR_NT) {
             const uint64_t k = s_list[p];
             int rank = 0;
-            for (int q = 0; q < cnt; ++q) rank += s_list[q] > k;
+#pragma unroll 8
+            for (int q = 0; q < cnt; ++q) rank += s_list[q] > k ? 1 : 0;
             if (rank < K) okeys[rank] = k;
         }
         for (int k = cnt + tid; k < K; k += RR_NT) okeys[k] = 0ull;
@@ -266,29 +304,36 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
 #undef RR_ID
 }
 
-// Merge the group partials of one row; all 64 lanes of a wave call it.
-// Returns the row max M and sigma' (same value in every lane); lane k < K
-// receives the row's k-th best key (0 if the row has fewer than k+1 elements).
+#define MRG_CAP 128                      // candidate list per wave
+#define MRG_SCR (MRG_CAP + 32)           // u64 LDS entries per wave: candidates + output
+
+
+// Merge the `groups` partials of one row with one wave: row max M, sigma'
+// (partials' sums rescaled to M, the excluded element taken from the first
+// group holding M), and the row's top-K keys, lane k holding the k-th (key 0
+// past the row's length).  scr: MRG_SCR entries of LDS private to the wave.
+//
+// Top-K: with j = ceil(K / groups), the j best keys of every group are
+// groups * j >= K distinct keys, all at least the smallest of the groups'
+// j-th keys; so every key of the row's top K has a value code (high word) at
+// least that group-minimum T.  The keys passing that test (typically K to 2K
+// of the groups * K) are ranked by counting.  When more than MRG_CAP pass
+// (long runs of equal values) the top K is taken in K max-extraction rounds.
 __device__ __forceinline__ uint64_t merge_row_wave(const uint32_t* __restrict__ p, int groups, int K,
-                                                   float& M, float& Sp) {
-    constexpr int MR = 8;                              // keys held in registers per lane
+                                                   float& M, float& Sp, uint64_t* scr) {
+    constexpr int MR = 4;                              // keys held in registers per lane
     const int lane = threadIdx.x & (DDT_WAVE - 1);
     const int PS = rr_ps(K);
+    const int jth = (K + groups - 1) / groups;         // 1 <= jth <= K
+    const int total = groups * K;
+    const bool fits = total <= MR * DDT_WAVE;
     float mc = -INFINITY, sc = 0.f;
+    uint32_t th = 0xFFFFFFFFu;
     if (lane < groups) {
         mc = __uint_as_float(p[lane * PS]);
         sc = __uint_as_float(p[lane * PS + 1]);
+        th = p[lane * PS + 2 + 2 * (jth - 1) + 1];     // high word of the group's jth key
     }
-    M = unord_f32(wave_max_u32(lane < groups ? ord_f32(mc) : 0u));
-    const int cstar = (int)wave_min_u32((lane < groups && mc == M) ? (uint32_t)lane : 0xFFFFFFFFu);
-    float contrib = 0.f;
-    if (lane < groups && mc > -INFINITY) {
-        const float e = exp2f((mc - M) * DDT_LOG2E);
-        contrib = sc * e + (lane != cstar ? e : 0.f);
-    }
-    Sp = wave_sumf(contrib);
-    const int total = groups * K;
-    const bool fits = total <= MR * DDT_WAVE;
     uint64_t kk[MR];
 #pragma unroll
     for (int r = 0; r < MR; ++r) {
@@ -299,6 +344,44 @@ __device__ __forceinline__ uint64_t merge_row_wave(const uint32_t* __restrict__ 
             kk[r] = *(const uint64_t*)(p + c * PS + 2 + 2 * e);
         }
     }
+    M = unord_f32(wave_max_u32(lane < groups ? ord_f32(mc) : 0u));
+    const uint32_t T = wave_min_u32(th);
+    const int cstar = (int)wave_min_u32((lane < groups && mc == M) ? (uint32_t)lane : 0xFFFFFFFFu);
+    float contrib = 0.f;
+    if (lane < groups && mc > -INFINITY) {
+        const float e = exp2f((mc - M) * DDT_LOG2E);
+        contrib = sc * e + (lane != cstar ? e : 0.f);
+    }
+    Sp = wave_sumf(contrib);
+
+    if (fits) {
+        int nc = 0;
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+            const bool f = kk[r] != 0ull && (uint32_t)(kk[r] >> 32) >= T;
+            const uint64_t m = __ballot(f);
+            const int pos = nc + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (f && pos < MRG_CAP) scr[pos] = kk[r];
+            nc += __popcll(m);
+        }
+        if (nc <= MRG_CAP) {
+            if (lane < K) scr[MRG_CAP + lane] = 0ull;
+            wave_lds_sync();
+            for (int i = lane; i < nc; i += DDT_WAVE) {
+                const uint64_t x = scr[i];
+                int r = 0;
+#pragma unroll 4
+                for (int q = 0; q < nc; ++q) r += scr[q] > x ? 1 : 0;
+                if (r < K) scr[MRG_CAP + r] = x;
+            }
+            wave_lds_sync();
+            const uint64_t mine = lane < K ? scr[MRG_CAP + lane] : 0ull;
+            wave_lds_sync();
+            return mine;
+        }
+    }
+    // K max-extraction rounds
     uint64_t prev = ~0ull, mine = 0ull;
     for (int k = 0; k < K; ++k) {
         uint64_t best = 0ull;

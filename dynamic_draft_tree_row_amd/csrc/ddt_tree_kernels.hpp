@@ -38,88 +38,129 @@ __device__ __forceinline__ int cast_sel_row(long long c, int L, int M) {
     return (int)(r < M - 1 ? r : M - 1);
 }
 
-// keep 1, move the anchor to k while the average marginal from it reaches C
-__device__ int anchor_scan_dev(const double* u, const double* c, double C, int kmax) {
+// Anchor scan over cumulative utility u[1..kmax] and cost c[1..kmax] (LDS):
+// keep 1, then for k = 2..kmax move the anchor a to k when the average
+// marginal (u_k - u_a) / (c_k - c_a) reaches C; a non-increasing cost step
+// counts as an infinite marginal when utility grows.  The test is written
+// u_k - u_a >= C (c_k - c_a), which differs from the quotient only at a
+// rounding boundary.  One wave: a run of moves to adjacent items is found
+// with one ballot over (k-1, k) pairs, a search from a fixed anchor with one
+// ballot per 64 items, so a typical scan takes a handful of steps.  Every
+// lane returns the same count.
+__device__ __forceinline__ bool anchor_moves(const double* u, const double* c, double C, int a, int k) {
+    const double du = u[k] - u[a], dc = c[k] - c[a];
+    return dc > 0.0 ? du >= C * dc : du > 0.0;
+}
+
+__device__ int anchor_scan_wave(const double* u, const double* c, double C, int kmax) {
     if (kmax <= 0) return 0;
-    int a = 1;
-    for (int k = 2; k <= kmax; ++k) {
-        const double du = u[k] - u[a], dc = c[k] - c[a];
-        if (dc > 0.0) {
-            if (du / dc >= C) a = k;
-        } else if (du > 0.0) {
-            a = k;
+    const int lane = threadIdx.x & (DDT_WAVE - 1);
+    int a = 1, k0 = 2;                       // items below k0 are settled
+    while (k0 <= kmax) {
+        int hit = -1;
+        if (a == k0 - 1) {
+            // walk: first k >= k0 whose adjacent step does not move
+            for (int base = k0; base <= kmax && hit < 0; base += DDT_WAVE) {
+                const int k = base + lane;
+                const uint64_t m = __ballot(k <= kmax && !anchor_moves(u, c, C, k - 1, k));
+                if (m) hit = base + __ffsll((unsigned long long)m) - 1;
+            }
+            if (hit < 0) return kmax;
+            a = hit - 1;
+            k0 = hit + 1;
+        } else {
+            // fixed anchor: first k >= k0 it moves to
+            for (int base = k0; base <= kmax && hit < 0; base += DDT_WAVE) {
+                const int k = base + lane;
+                const uint64_t m = __ballot(k <= kmax && anchor_moves(u, c, C, a, k));
+                if (m) hit = base + __ffsll((unsigned long long)m) - 1;
+            }
+            if (hit < 0) return a;
+            a = hit;
+            k0 = hit + 1;
         }
     }
     return a;
 }
 
-// Run by one whole workgroup of NT threads once every row's layer is attached.
+// Run by one whole workgroup of NT threads once every row's layer is attached
+// (the rows' frontier values front_S are visible).  One round of global
+// loads: the state, the row counts, the frontier values and the first R_max
+// entries of every cost-table row (M <= DDT_CAST_MAX_M); wave 0 then runs the
+// anchor scan and lane 0 the gain FIFO.
+#define DDT_CAST_MAX_M 64
+
 template <int NT>
 __device__ void cast_layer(const ddt_tree& t, const ddt_cast& cp, int layer, int K_e) {
-    const int tid = threadIdx.x, B = t.B;
+    const int tid = threadIdx.x, B = t.B, R = t.R_max;
     __shared__ double s_v[64 * DDT_MAX_FRONT];
-    __shared__ double s_col[DDT_MAX_FRONT + 1];
-    __shared__ double u[DDT_MAX_FRONT + 1], c[DDT_MAX_FRONT + 1];
+    __shared__ float s_sd[DDT_CAST_MAX_M * DDT_MAX_FRONT], s_st1[DDT_CAST_MAX_M];
+    __shared__ double s_c[DDT_MAX_FRONT + 1], s_u[DDT_MAX_FRONT + 1];
+    __shared__ double s_st[11];
     __shared__ int s_kcap, s_n;
     double* st = t.cast_state;
-    if (tid == 0) {
-        s_kcap = min(K_e, t.R_max);
-        if (layer == 1) {
-            st[0] = 1.0;
-            for (int i = 1; i < 8; ++i) st[i] = 0.0;
-            st[8] = 1.0; st[9] = -1.0; st[10] = 0.0;
-        }
+    if (tid == 0) s_kcap = min(K_e, R);
+    if (tid < 11) {
+        double v;
+        if (layer == 1) v = tid == 0 ? 1.0 : tid == 8 ? 1.0 : tid == 9 ? -1.0 : 0.0;
+        else v = st[tid];
+        s_st[tid] = v;
     }
     if (layer == 1)
         for (int i = tid; i < t.D_max; i += NT) t.widths[i] = 0;
+    for (int q = tid; q < B * R; q += NT) s_v[q] = exp((double)t.front_S[q]);
+    for (int q = tid; q < cp.M * R; q += NT) {
+        const int r = q / R, k = q - r * R;
+        s_sd[q] = k < cp.N ? cp.S_D[(size_t)r * (cp.N + 1) + k + 1] : 0.f;
+    }
+    for (int r = tid; r < cp.M; r += NT) s_st1[r] = cp.S_T[(size_t)r * (cp.N + 1) + 1];
+    int cnt = 0x7FFFFFFF;
+    if (tid < B) cnt = max(0, t.n_nodes[tid] - t.layer_base[tid]);
     __syncthreads();
-    for (int b = tid; b < B; b += NT) atomicMin(&s_kcap, max(0, t.n_nodes[b] - t.layer_base[b]));
+    if (tid < B) atomicMin(&s_kcap, cnt);
     __syncthreads();
     const int kcap = s_kcap;
-    for (int q = tid; q < B * kcap; q += NT) {
-        const int b = q / kcap, k = q - b * kcap;
-        const int node = t.frontier[(size_t)b * t.R_max + k];
-        const int nn = min(max(node, 0), t.cap - 1);
-        s_v[q] = exp((double)t.S[(size_t)b * t.cap + nn]);
-    }
-    __syncthreads();
+    const int ctx = (int)s_st[10];
+    const int row = cast_sel_row(ctx, cp.L, cp.M);
     for (int k = tid; k < kcap; k += NT) {
         double sum = 0.0;
-        for (int b = 0; b < B; ++b) sum += s_v[b * kcap + k];
-        s_col[k] = sum;
+        for (int b = 0; b < B; ++b) sum += s_v[b * R + k];
+        s_u[k + 1] = sum / (double)B;                 // column mean; prefix-summed below
+        s_c[k + 1] = (double)s_sd[row * R + k] / (double)s_st1[row];
     }
     __syncthreads();
-    if (tid == 0) {
-        u[0] = 0.0; c[0] = 0.0;
-        const int ctx = (int)st[10];
-        const int row = cast_sel_row(ctx, cp.L, cp.M);
-        const float* SD = cp.S_D + (size_t)row * (cp.N + 1);
-        const float* ST = cp.S_T + (size_t)row * (cp.N + 1);
-        for (int k = 1; k <= kcap; ++k) {
-            u[k] = u[k - 1] + s_col[k - 1] / (double)B;
-            c[k] = (double)SD[k] / (double)ST[1];
+    if (tid < DDT_WAVE) {
+        if (tid == 0) {
+            s_u[0] = 0.0; s_c[0] = 0.0;
+            for (int k = 1; k <= kcap; ++k) s_u[k] += s_u[k - 1];
         }
-        const int n = anchor_scan_dev(u, c, (double)cp.C1[layer - 1], kcap);
-        int len = (int)st[8];
-        if (st[9] >= 0.0) {                        // push the previous layer's gain ratio
-            const double phi = st[9] > 0.0 ? u[n] / st[9] : 0.0;
-            if (len < 8) st[len++] = phi;
-            if (len > cp.R) {
-                for (int i = 1; i < len; ++i) st[i - 1] = st[i];
-                --len;
+        wave_lds_sync();
+        const int n = anchor_scan_wave(s_u, s_c, (double)cp.C1[layer - 1], kcap);
+        if (tid == 0) {
+            double* fifo = s_st;                       // entries 0..7
+            int len = (int)s_st[8];
+            const double prev = s_st[9];
+            if (prev >= 0.0) {                         // push the previous layer's gain ratio
+                const double phi = prev > 0.0 ? s_u[n] / prev : 0.0;
+                if (len < 8) fifo[len++] = phi;
+                if (len > cp.R) {
+                    for (int i = 1; i < len; ++i) fifo[i - 1] = fifo[i];
+                    --len;
+                }
             }
+            double mean = 0.0;
+            for (int i = 0; i < len; ++i) mean += fifo[i];
+            mean /= (double)len;
+            const double score = n > 0 ? mean * s_u[n] / s_c[n] : 0.0;
+            const bool stop = (layer >= t.D_max) || !(score >= (double)cp.C2);
+            for (int i = 0; i < 8; ++i) st[i] = fifo[i];
+            st[8] = (double)len;
+            st[9] = s_u[n];
+            st[10] = (double)(ctx + n);
+            t.widths[layer - 1] = n;
+            t.cont[0] = stop ? 0 : 1;
+            s_n = stop ? 0 : n;
         }
-        st[8] = (double)len;
-        double mean = 0.0;
-        for (int i = 0; i < len; ++i) mean += st[i];
-        mean /= (double)len;
-        const double score = n > 0 ? mean * u[n] / c[n] : 0.0;
-        const bool stop = (layer >= t.D_max) || !(score >= (double)cp.C2);
-        st[9] = u[n];
-        st[10] = (double)(ctx + n);
-        t.widths[layer - 1] = n;
-        t.cont[0] = stop ? 0 : 1;
-        s_n = stop ? 0 : n;
     }
     __syncthreads();
     for (int b = tid; b < B; b += NT) t.n_front[b] = s_n;
@@ -137,6 +178,11 @@ __device__ void cast_layer(const ddt_tree& t, const ddt_cast& cp, int layer, int
 // Graft review step 1: at a checkpoint depth the row stops unless
 // exp(max S of the layer) > tau.  With CAST, the last workgroup to finish the
 // layer (device-scope counter) runs the batch-wide width and depth rule.
+//
+// Latency layout: every global input of the layer (the partials of all R
+// slots, merged speculatively, one wave per slot; the row counters; the
+// frontier's node, S and key, stored by the previous layer) is requested in
+// one round before the first barrier; ranks are counted branch-free.
 
 struct AttachArgs {
     ddt_tree t;
@@ -154,13 +200,15 @@ struct AttachArgs {
 __global__ __launch_bounds__(AT_NT) void k_attach(AttachArgs a) {
     const ddt_tree& t = a.t;
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int cap = t.cap;
+    const int cap = t.cap, Rm = t.R_max, Kn = a.K_n;
     __shared__ float s_M[DDT_MAX_FRONT], s_S[DDT_MAX_FRONT];
-    __shared__ int s_par[DDT_MAX_FRONT];
+    __shared__ int s_pn[DDT_MAX_FRONT];
+    __shared__ float s_pS[DDT_MAX_FRONT];
+    __shared__ uint64_t s_pk[DDT_MAX_FRONT];
     __shared__ uint64_t s_key[DDT_MAX_FRONT * DDT_MAX_K];
-    __shared__ uint32_t srt_a[AT_SORT];
-    __shared__ uint64_t srt_b[AT_SORT];
-    __shared__ int s_Rd, s_base, s_last, s_best;
+    __shared__ uint64_t s_sk[AT_SORT];
+    __shared__ uint64_t s_scr[AT_NT / 64][MRG_SCR];
+    __shared__ int s_nf, s_nn, s_last;
 
     int32_t* tok = t.token + (size_t)b * cap;
     int32_t* par = t.parent + (size_t)b * cap;
@@ -169,101 +217,109 @@ __global__ __launch_bounds__(AT_NT) void k_attach(AttachArgs a) {
     uint64_t* key = t.key + (size_t)b * cap;
     float* S = t.S + (size_t)b * cap;
     float* lc = t.logc + (size_t)b * cap;
+    int32_t* fr = t.frontier + (size_t)b * Rm;
+    float* frS = t.front_S + (size_t)b * Rm;
+    uint64_t* frK = t.front_key + (size_t)b * Rm;
 
-    // each wave merges its frontier slots' partials straight away (rows past
-    // the row's frontier width were not reduced and are ignored below)
-    {
-        const int rd = a.layer == 1 ? 1 : min(max(t.n_front[b], 0), a.R);
-        for (int j = wid; j < rd; j += AT_NT / 64) {
-            float M, Sp;
-            const uint32_t* p = a.part + ((size_t)(b * a.R + j) * a.chunks) * rr_ps(a.K_n);
-            const uint64_t mine = merge_row_wave(p, a.chunks, a.K_n, M, Sp);
-            if (lane < a.K_n) s_key[j * a.K_n + lane] = mine;
-            if (lane == 0) { s_M[j] = M; s_S[j] = Sp; }
-        }
-    }
-    if (tid == 0) {
-        int Rd, base;
-        if (a.layer == 1) {
+    // round 1: row state and parent records (wave 0 issues these before its merge)
+    if (a.layer == 1) {
+        if (tid == 0) {
             tok[0] = a.root_tok[b]; par[0] = -1; dep[0] = 0; esl[0] = -1; key[0] = 0ull;
             S[0] = 0.f; lc[0] = 0.f;
-            t.frontier[(size_t)b * t.R_max] = 0;
             t.active[b] = 1;
             t.k_draft[b] = a.gate_on ? a.K_max : 0;
-            t.n_nodes[b] = 1;
             if (a.cast_on && b == 0) t.cont[0] = 1;
-            Rd = 1; base = 1;
-        } else {
-            Rd = min(max(t.n_front[b], 0), a.R);
-            base = t.n_nodes[b];
-            if (base < 1 || base + Rd * a.K_n > cap) Rd = 0;      // capacity guard
+            s_nf = 1; s_nn = 1;
+            s_pn[0] = 0; s_pS[0] = 0.f; s_pk[0] = 0ull;
         }
-        s_Rd = Rd; s_base = base;
+    } else {
+        if (tid < a.R) { s_pn[tid] = fr[tid]; s_pS[tid] = frS[tid]; s_pk[tid] = frK[tid]; }
+        if (tid == 0) { s_nf = t.n_front[b]; s_nn = t.n_nodes[b]; }
+    }
+    // merges: wave j takes slot j (slots past the row's frontier width hold no
+    // partials of this layer and are ignored below)
+    for (int j = wid; j < a.R; j += AT_NT / 64) {
+        float M, Sp;
+        const uint32_t* p = a.part + ((size_t)(b * a.R + j) * a.chunks) * rr_ps(Kn);
+        const uint64_t mine = merge_row_wave(p, a.chunks, Kn, M, Sp, s_scr[wid]);
+        if (lane < Kn) s_key[j * Kn + lane] = mine;
+        if (lane == 0) { s_M[j] = M; s_S[j] = Sp; }
     }
     __syncthreads();
-    const int Rd = s_Rd, base = s_base;
-    if (Rd > 0) {
-        for (int j = tid; j < Rd; j += AT_NT) {
-            const int u = a.layer == 1 ? 0 : t.frontier[(size_t)b * t.R_max + j];
-            s_par[j] = (u >= 0 && u < base) ? u : 0;
+    const int base = s_nn;
+    int Rd = min(max(s_nf, 0), a.R);
+    if (base < 1 || base + Rd * Kn > cap) Rd = 0;          // capacity guard
+    const int count = Rd * Kn;
+    const int du = a.layer - 1;                            // depth of every frontier node
+    for (int q = tid; q < count; q += AT_NT) {
+        const int j = q / Kn, r = q - j * Kn;
+        const int u0 = s_pn[j];
+        const int u = (u0 >= 0 && u0 < base) ? u0 : 0;
+        const uint64_t kk = s_key[j * Kn + r];
+        const float logc = (vkey_val(kk) - s_M[j]) - log1pf(s_S[j]);
+        const float Sv = s_pS[j] + logc;
+        const uint64_t pk = s_pk[j];
+        const uint64_t nk = key_child(pk, du, r, 0);
+        const int node = base + q;
+        tok[node] = vkey_id(kk); par[node] = u; dep[node] = du + 1; esl[node] = -1;
+        S[node] = Sv; lc[node] = logc; key[node] = nk;
+        // the layer's canonical-key order is (parent key, sibling rank): the
+        // parent's rank among the slots' keys makes a 64-bit sort key
+        int pr = 0;
+#pragma unroll 8
+        for (int jj = 0; jj < Rd; ++jj) pr += s_pk[jj] < pk ? 1 : 0;
+        s_sk[q] = ((uint64_t)~ord_f32(Sv) << 32) | (uint32_t)(pr * Kn + r);
+        if (r == 0) {
+            esl[u] = j;
+            const size_t ri = ((size_t)b * t.D_max + du) * Rm + j;
+            t.rmax[ri] = s_M[j];
+            t.rsp[ri] = s_S[j];
         }
-        __syncthreads();
-        const int count = Rd * a.K_n;
-        for (int q = tid; q < count; q += AT_NT) {
-            const int j = q / a.K_n, r = q - j * a.K_n;
-            const int u = s_par[j];
-            const uint64_t kk = s_key[j * a.K_n + r];
-            const float l1p = log1pf(s_S[j]);
-            const float logc = (vkey_val(kk) - s_M[j]) - l1p;
-            const float Sv = S[u] + logc;
-            const int du = dep[u];
-            const uint64_t nk = key_child(key[u], du, r, 0);
-            const int node = base + q;
-            tok[node] = vkey_id(kk); par[node] = u; dep[node] = du + 1; esl[node] = -1;
-            S[node] = Sv; lc[node] = logc; key[node] = nk;
-            srt_a[q] = ~ord_f32(Sv); srt_b[q] = nk;
+    }
+    __syncthreads();
+    // frontier: the first R_max of the layer by (S desc, key asc); the best
+    // node's thread closes the row's layer
+    for (int q = tid; q < count; q += AT_NT) {
+        const uint64_t sk = s_sk[q];
+        int r = 0;
+#pragma unroll 8
+        for (int p = 0; p < count; ++p) r += s_sk[p] < sk ? 1 : 0;
+        if (r < Rm) {
+            const float Sv = unord_f32(~(uint32_t)(sk >> 32));
+            const int j = q / Kn;
+            fr[r] = base + q; frS[r] = Sv; frK[r] = key_child(s_pk[j], du, q - j * Kn, 0);
             if (r == 0) {
-                esl[u] = j;
-                const size_t ri = ((size_t)b * t.D_max + (a.layer - 1)) * t.R_max + j;
-                t.rmax[ri] = s_M[j];
-                t.rsp[ri] = s_S[j];
-            }
-        }
-        __syncthreads();
-        // frontier: the first R_max of the layer by (S desc, key asc)
-        for (int q = tid; q < count; q += AT_NT) {
-            const int r = rank_among(srt_a, srt_b, count, srt_a[q], srt_b[q]);
-            if (r < t.R_max) t.frontier[(size_t)b * t.R_max + r] = base + q;
-            if (r == 0) s_best = q;                     // best node of the layer
-        }
-        __syncthreads();
-        if (tid == 0) {
-            t.n_nodes[b] = base + count;
-            t.layer_base[b] = base;
-            int nf = min(a.K_e, count);
-            if (a.layer >= t.D_max) nf = 0;
-            if (a.ck) {
-                const float smax = unord_f32(~srt_a[s_best]);
-                if (!(expf(smax) > a.tau)) {       // g_d = 1[c_d > tau_d]
+                t.n_nodes[b] = base + count;
+                t.layer_base[b] = base;
+                int nf = min(a.K_e, count);
+                if (a.layer >= t.D_max) nf = 0;
+                if (a.ck && !(expf(Sv) > a.tau)) {       // g_d = 1[c_d > tau_d]
                     t.active[b] = 0;
                     t.k_draft[b] = a.kd_ck;
                     nf = 0;
                 }
+                t.n_front[b] = nf;
             }
-            t.n_front[b] = nf;
         }
-    } else if (tid == 0) {
+    }
+    if (count == 0 && tid == 0) {
+        if (a.layer == 1) { t.n_nodes[b] = 1; t.layer_base[b] = 1; }
         t.n_front[b] = 0;
     }
     if (!a.cast_on) return;
-    // the last workgroup of the layer runs CAST for the batch
-    __threadfence();
+    // the last workgroup of the layer runs CAST for the batch: the barrier
+    // orders the workgroup's stores before thread 0's device-scope release
     __syncthreads();
-    if (tid == 0) s_last = atomicAdd(t.ticket, 1u) == gridDim.x - 1;
+    if (tid == 0) {
+        __threadfence();
+        s_last = atomicAdd(t.ticket, 1u) == gridDim.x - 1;
+        if (s_last) {
+            __threadfence();
+            atomicExch(t.ticket, 0u);
+        }
+    }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
-    if (tid == 0) atomicExch(t.ticket, 0u);
     if (t.cont[0]) cast_layer<AT_NT>(t, a.c, a.layer, a.K_e);
     else
         for (int bb = tid; bb < t.B; bb += AT_NT) t.n_front[bb] = 0;
@@ -275,10 +331,15 @@ __global__ __launch_bounds__(AT_NT) void k_attach(AttachArgs a) {
 //
 // EAGLE-2 explainer, reranking section: every candidate node is ranked by
 // value, the top m are verified; a child never outranks its parent and equal
-// values go to the shallower node, so the set is a connected subtree.  Ranks
-// come from counting, not sorting: only positions below m_max are kept.  CAST
+// values go to the shallower node, so the set is a connected subtree.  CAST
 // key design 4: m per row by the anchor scan of the sorted cumulative values
 // against the verify cost.  Graft: m = the row's k_draft.
+//
+// Only the first m_max positions are needed.  A four-pass byte-wise radix
+// select over the value codes finds T, the code of the m_max-th largest value;
+// the nodes above T and the ties at T (up to RK_CAND in all) are ordered by
+// rank counting on (value code, canonical key).  Rows with more ties at T than
+// that fall back to a full bitonic sort of the row.
 
 struct RerankArgs {
     ddt_tree t;
@@ -289,7 +350,9 @@ struct RerankArgs {
 };
 
 #define RK_NT 1024
+#define RK_PER (DDT_MAX_NODES / RK_NT)   // nodes per thread
 #define RK_SORT DDT_MAX_NODES
+#define RK_CAND 1024
 
 // In-LDS bitonic sort of n2 (power of two) 64-bit keys, ascending.
 template <int NT>
@@ -307,27 +370,19 @@ __device__ void bitonic_sort_u64(uint64_t* v, int n2) {
     }
 }
 
-__global__ __launch_bounds__(RK_NT) void k_rerank(RerankArgs a) {
-    const ddt_tree& t = a.t;
-    const int b = blockIdx.x, tid = threadIdx.x;
-    __shared__ uint64_t sv[RK_SORT];
-    __shared__ double s_v[DDT_MAX_VERIFY + 1];
-    __shared__ double u[DDT_MAX_VERIFY + 1], c[DDT_MAX_VERIFY + 1];
-    __shared__ int s_m;
-    const int nn = min(max(t.n_nodes[b], 1), t.cap);
-    const int N = nn - 1;
+// Fallback: full sort of the row's N non-root nodes by (~code, node), runs of
+// equal value re-ordered by canonical key; writes the first kmax nodes to
+// out_node in order.
+template <int NT>
+__device__ void rerank_sort_all(const float* S, const uint64_t* key, int N, int kmax, uint64_t* sv,
+                                int32_t* out_node) {
+    const int tid = threadIdx.x;
     const int n2 = next_pow2(N > 0 ? N : 1);
-    const float* S = t.S + (size_t)b * t.cap;
-    const uint64_t* key = t.key + (size_t)b * t.cap;
-    // sort (value code, node): S descending; equal values tie-broken by node
-    // index first and fixed up to canonical-key order below
-    for (int q = tid; q < n2; q += RK_NT)
+    for (int q = tid; q < n2; q += NT)
         sv[q] = q < N ? ((uint64_t)~ord_f32(S[1 + q]) << 32) | (uint32_t)(1 + q) : ~0ull;
     __syncthreads();
-    bitonic_sort_u64<RK_NT>(sv, n2);
-    // runs of equal value (siblings with equal logits, or exact coincidences)
-    // are re-ordered by canonical key by the thread at each run's start
-    for (int q = tid; q < N; q += RK_NT) {
+    bitonic_sort_u64<NT>(sv, n2);
+    for (int q = tid; q < N; q += NT) {
         const uint32_t hv = (uint32_t)(sv[q] >> 32);
         if ((q > 0 && (uint32_t)(sv[q - 1] >> 32) == hv) || q + 1 >= N ||
             (uint32_t)(sv[q + 1] >> 32) != hv)
@@ -343,28 +398,164 @@ __global__ __launch_bounds__(RK_NT) void k_rerank(RerankArgs a) {
         }
     }
     __syncthreads();
+    for (int k = tid; k < kmax; k += NT) out_node[k] = (int32_t)(uint32_t)sv[k];
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(RK_NT) void k_rerank(RerankArgs a) {
+    const ddt_tree& t = a.t;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    __shared__ int s_hist[256];
+    __shared__ int s_bin, s_need, s_ngt, s_ntie, s_slot, s_m;
+    __shared__ uint32_t s_ca[RK_CAND];
+    __shared__ uint64_t s_ck[RK_CAND];
+    __shared__ int32_t s_cn[RK_CAND];
+    __shared__ int32_t s_node[DDT_MAX_VERIFY];
+    __shared__ double s_u[DDT_MAX_VERIFY + 1], s_c[DDT_MAX_VERIFY + 1];
+    __shared__ uint64_t s_sort[RK_SORT];
+    const int nn = min(max(t.n_nodes[b], 1), t.cap);
+    const int N = nn - 1;
     const int kmax = min(a.m_max, N);
+    const float* S = t.S + (size_t)b * t.cap;
+    const uint64_t* key = t.key + (size_t)b * t.cap;
+
+    // one round of loads: values and keys of this thread's nodes, verify costs
+    uint32_t o[RK_PER];
+    uint64_t kk[RK_PER];
+#pragma unroll
+    for (int i = 0; i < RK_PER; ++i) {
+        const int q = tid + i * RK_NT;
+        o[i] = q < N ? ord_f32(S[1 + q]) : 0u;
+        kk[i] = q < N ? key[1 + q] : 0ull;
+    }
     if (a.cast_on) {
-        for (int k = tid; k < kmax; k += RK_NT) s_v[k] = exp((double)unord_f32(~(uint32_t)(sv[k] >> 32)));
-        __syncthreads();
-        if (tid == 0) {
-            u[0] = 0.0; c[0] = 0.0;
-            const int row = cast_sel_row(a.c.ctx_verify, a.c.L, a.c.M);
-            const float* ST = a.c.S_T + (size_t)row * (a.c.N + 1);
-            for (int k = 1; k <= kmax; ++k) {
-                u[k] = u[k - 1] + s_v[k - 1];
-                c[k] = (double)ST[k] / (double)ST[1];
+        const int row = cast_sel_row(a.c.ctx_verify, a.c.L, a.c.M);
+        const float* ST = a.c.S_T + (size_t)row * (a.c.N + 1);
+        for (int k = tid; k < kmax; k += RK_NT) s_c[k + 1] = (double)ST[k + 1] / (double)ST[1];
+    }
+    if (tid == 0) { s_need = kmax; s_ngt = 0; s_ntie = 0; s_slot = 0; }
+
+    // radix select: T = code of the kmax-th largest value (0 when every node is kept)
+    uint32_t T = 0u;
+    if (kmax > 0 && kmax < N) {
+        uint32_t prefix = 0u, pmask = 0u;
+        for (int pass = 0; pass < 4; ++pass) {
+            const int shift = 24 - 8 * pass;
+            if (tid < 256) s_hist[tid] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < RK_PER; ++i) {
+                const int q = tid + i * RK_NT;
+                if (q < N && (o[i] & pmask) == prefix) atomicAdd(&s_hist[(o[i] >> shift) & 255], 1);
             }
-            s_m = anchor_scan_dev(u, c, (double)a.c.C3[b], kmax);
+            __syncthreads();
+            if (wid == 0) {
+                // lane l holds bins 255-4l .. 252-4l (descending)
+                const int need = s_need;
+                int h[4], loc = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) { h[i] = s_hist[255 - 4 * lane - i]; loc += h[i]; }
+                int incl = loc;
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const int v = __shfl_up(incl, d);
+                    if (lane >= d) incl += v;
+                }
+                int ex = incl - loc;
+                if (ex < need && need <= incl) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if (ex < need && need <= ex + h[i]) { s_bin = 255 - 4 * lane - i; s_need = need - ex; }
+                        ex += h[i];
+                    }
+                }
+            }
+            __syncthreads();
+            prefix |= (uint32_t)s_bin << shift;
+            pmask |= 0xFFu << shift;
+        }
+        T = prefix;
+    }
+    // candidates: every node strictly above T, and the ties at T
+    {
+        int ngt = 0, ntie = 0;
+#pragma unroll
+        for (int i = 0; i < RK_PER; ++i) {
+            const int q = tid + i * RK_NT;
+            ngt += (q < N) & (o[i] > T);
+            ntie += (q < N) & (o[i] == T);
+        }
+        if (ngt) atomicAdd(&s_ngt, ngt);
+        if (ntie) atomicAdd(&s_ntie, ntie);
+    }
+    __syncthreads();
+    const int nc = s_ngt + s_ntie;
+    int32_t* sel = a.sel + (size_t)b * (a.m_max + 1);
+    if (kmax == 0) {
+        // nothing to rank
+    } else if (nc <= RK_CAND) {
+        int mine = 0;
+#pragma unroll
+        for (int i = 0; i < RK_PER; ++i) mine += (tid + i * RK_NT < N) & (o[i] >= T);
+        int slot = mine ? atomicAdd(&s_slot, mine) : 0;
+#pragma unroll
+        for (int i = 0; i < RK_PER; ++i) {
+            const int q = tid + i * RK_NT;
+            if (q < N && o[i] >= T) { s_ca[slot] = ~o[i]; s_ck[slot] = kk[i]; s_cn[slot] = 1 + q; ++slot; }
+        }
+        __syncthreads();
+        for (int c = tid; c < nc; c += RK_NT) {
+            const uint32_t ca = s_ca[c];
+            const uint64_t ck = s_ck[c];
+            int r = 0;
+#pragma unroll 8
+            for (int p = 0; p < nc; ++p) {
+                const uint32_t pa = s_ca[p];
+                r += (int)(pa < ca) | ((int)(pa == ca) & (int)(s_ck[p] < ck));
+            }
+            if (r < kmax) s_node[r] = s_cn[c];
+        }
+        __syncthreads();
+    } else {
+        rerank_sort_all<RK_NT>(S, key, N, kmax, s_sort, s_node);
+    }
+    // verify count
+    if (a.cast_on) {
+        for (int k = tid; k < kmax; k += RK_NT) s_u[k + 1] = exp((double)S[s_node[k]]);
+        __syncthreads();
+        if (wid == 0) {
+            // prefix sums: four consecutive items per lane, then across lanes
+            double loc[4], run = 0.0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int k = 4 * lane + i + 1;
+                run += k <= kmax ? s_u[k] : 0.0;
+                loc[i] = run;
+            }
+            double incl = run;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const double v = __shfl_up(incl, d);
+                if (lane >= d) incl += v;
+            }
+            const double ex = incl - run;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int k = 4 * lane + i + 1;
+                if (k <= kmax) s_u[k] = ex + loc[i];
+            }
+            if (lane == 0) { s_u[0] = 0.0; s_c[0] = 0.0; }
+            wave_lds_sync();
+            const int m = anchor_scan_wave(s_u, s_c, (double)a.c.C3[b], kmax);
+            if (lane == 0) s_m = m;
         }
     } else if (tid == 0) {
         s_m = a.use_k_draft ? min(max(t.k_draft[b], 0), kmax) : kmax;
     }
     __syncthreads();
     const int m = s_m;
-    int32_t* sel = a.sel + (size_t)b * (a.m_max + 1);
     for (int k = tid; k <= a.m_max; k += RK_NT)
-        sel[k] = k == 0 ? 0 : (k <= m ? (int32_t)(uint32_t)sv[k - 1] : -1);
+        sel[k] = k == 0 ? 0 : (k <= m ? s_node[k - 1] : -1);
     if (tid == 0) a.m_out[b] = m;
 }
 
@@ -684,6 +875,7 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
     __shared__ int s_ch[MK_NT];
     __shared__ int s_nch, s_u, s_len, s_acc, s_next;
     __shared__ unsigned long long s_best;
+    __shared__ uint64_t s_mscr[VF_NT / 64][MRG_SCR];
     const int m = min(max(f.m[b], 0), P - 1);
     const int n = m + 1;
     const size_t fo = (size_t)b * P;
@@ -691,7 +883,7 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
     for (int i = wid; i < n; i += VF_NT / 64) {
         float M, Sp;
         const uint32_t* p = a.part + ((size_t)(b * P + i) * a.chunks) * rr_ps(a.Kp);
-        const uint64_t mine = merge_row_wave(p, a.chunks, a.Kp, M, Sp);
+        const uint64_t mine = merge_row_wave(p, a.chunks, a.Kp, M, Sp, s_mscr[wid]);
         const int am = __shfl(vkey_id(mine), 0);
         if (lane == 0) {
             s_am[i] = am; s_M[i] = M; s_S[i] = Sp;
@@ -940,6 +1132,7 @@ __global__ __launch_bounds__(UP_NT) void k_succ_update(UpdateArgs a) {
     const int P = f.P;
     const int b0 = a.shared ? 0 : blockIdx.x, b1 = a.shared ? a.B : blockIdx.x + 1;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    __shared__ uint64_t s_mscr[UP_NT / 64][MRG_SCR];
     for (int b = b0; b < b1; ++b) {
         const int m = min(max(f.m[b], 0), P - 1);
         const size_t fo = (size_t)b * P;
@@ -970,7 +1163,7 @@ __global__ __launch_bounds__(UP_NT) void k_succ_update(UpdateArgs a) {
                 }
                 float M, Sp;
                 const uint32_t* p = a.part + ((size_t)(b * P + i) * a.chunks) * rr_ps(a.Kp);
-                const uint64_t mine = merge_row_wave(p, a.chunks, a.Kp, M, Sp);
+                const uint64_t mine = merge_row_wave(p, a.chunks, a.Kp, M, Sp, s_mscr[wid]);
                 if (last && lane < a.k_succ) Mb[(size_t)tk * a.k_succ + lane] = vkey_id(mine);
             }
         }
@@ -997,7 +1190,8 @@ __global__ __launch_bounds__(256) void k_row_finish(RowFinishArgs a) {
     if (row >= a.rows) return;
     float M, Sp;
     const uint32_t* p = a.part + (size_t)row * a.chunks * rr_ps(a.K);
-    const uint64_t mine = merge_row_wave(p, a.chunks, a.K, M, Sp);
+    __shared__ uint64_t s_mscr[4][MRG_SCR];
+    const uint64_t mine = merge_row_wave(p, a.chunks, a.K, M, Sp, s_mscr[threadIdx.x >> 6]);
     if (lane < a.K) {
         if (a.ids) a.ids[(size_t)row * a.K + lane] = vkey_id(mine);
         if (a.logc)

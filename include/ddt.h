@@ -110,6 +110,8 @@ typedef struct ddt_tree {
     int32_t* layer_base; /* [B] first node of the most recent layer */
     int32_t* n_front;    /* [B] frontier width the next layer expands (0: row stopped) */
     int32_t* frontier;   /* [B][R_max] latest layer's nodes by (S desc, key asc) */
+    float* front_S;      /* [B][R_max] S of those nodes */
+    uint64_t* front_key; /* [B][R_max] canonical key of those nodes */
     int32_t* active;     /* [B] Graft: 1 until the row is pruned */
     int32_t* k_draft;    /* [B] Graft: draft nodes the row keeps (K_max if never pruned) */
     int32_t* cont;       /* [1] CAST: 1 while the batch keeps growing */
@@ -170,12 +172,13 @@ int ddt_flat_bind(ddt_flat* f /*host*/, void* base, size_t bytes, int B, int m_m
  * mean(FIFO) * u_n / c_n >= C2.  Verify count per row: anchor scan over the
  * row's sorted node values with cost S_T[sel(ctx_verify)][k]/S_T[..][1] and
  * threshold C3[b].  "Anchor scan": keep 1; move the anchor a to k whenever
- * (u_k - u_a)/(c_k - c_a) >= C.
+ * (u_k - u_a)/(c_k - c_a) >= C.  Batches of more than 64 rows are refused
+ * (DDT_ECAPACITY).
  */
 typedef struct ddt_cast {
     const float* S_T;    /* [M][N+1] */
     const float* S_D;    /* [M][N+1] */
-    int L, M, N;
+    int L, M, N;         /* grid step; rows 1..64 (DDT_ECAPACITY above); columns */
     const float* C1;     /* [D_max] width threshold per layer (device) */
     float C2;            /* depth threshold */
     const float* C3;     /* [B] verify-count threshold per row (device) */
