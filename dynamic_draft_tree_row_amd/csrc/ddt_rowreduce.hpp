@@ -314,11 +314,12 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
 // past the row's length).  scr: MRG_SCR entries of LDS private to the wave.
 //
 // Top-K: with j = ceil(K / groups), the j best keys of every group are
-// groups * j >= K distinct keys, all at least the smallest of the groups'
-// j-th keys; so every key of the row's top K has a value code (high word) at
-// least that group-minimum T.  The keys passing that test (typically K to 2K
-// of the groups * K) are ranked by counting.  When more than MRG_CAP pass
-// (long runs of equal values) the top K is taken in K max-extraction rounds.
+// groups * j >= K distinct keys of the row; T, the K-th largest value code
+// among them, is at most the value code of the row's K-th best key, so every
+// key of the row's top K has a value code of at least T.  The keys passing
+// that test (typically little more than K of the groups * K) are ranked by
+// counting.  When more than MRG_CAP pass (long runs of equal values) the top K
+// is taken in K max-extraction rounds.
 __device__ __forceinline__ uint64_t merge_row_wave(const uint32_t* __restrict__ p, int groups, int K,
                                                    float& M, float& Sp, uint64_t* scr) {
     constexpr int MR = 4;                              // keys held in registers per lane
@@ -328,11 +329,15 @@ __device__ __forceinline__ uint64_t merge_row_wave(const uint32_t* __restrict__ 
     const int total = groups * K;
     const bool fits = total <= MR * DDT_WAVE;
     float mc = -INFINITY, sc = 0.f;
-    uint32_t th = 0xFFFFFFFFu;
     if (lane < groups) {
         mc = __uint_as_float(p[lane * PS]);
         sc = __uint_as_float(p[lane * PS + 1]);
-        th = p[lane * PS + 2 + 2 * (jth - 1) + 1];     // high word of the group's jth key
+    }
+    // sample: the jth best keys of every group (groups * jth <= 64 lanes)
+    uint32_t hv = 0u;
+    if (lane < groups * jth) {
+        const int c = lane / jth, e = lane - c * jth;
+        hv = p[c * PS + 2 + 2 * e + 1];                // high word (value code)
     }
     uint64_t kk[MR];
 #pragma unroll
@@ -345,14 +350,25 @@ __device__ __forceinline__ uint64_t merge_row_wave(const uint32_t* __restrict__ 
         }
     }
     M = unord_f32(wave_max_u32(lane < groups ? ord_f32(mc) : 0u));
-    const uint32_t T = wave_min_u32(th);
-    const int cstar = (int)wave_min_u32((lane < groups && mc == M) ? (uint32_t)lane : 0xFFFFFFFFu);
+    // T: the K-th largest sampled value code, bit by bit over the top 16 bits
+    // (a lower T only admits a few more candidates); K = 1 needs none
+    uint32_t T = 0u;
+    for (int bit = 31; K > 1 && bit >= 16; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        if (__popcll(__ballot(hv >= cand)) >= (unsigned)K) T = cand;
+    }
+    const uint64_t mm = __ballot(lane < groups && mc == M);
+    const int cstar = mm ? __ffsll((unsigned long long)mm) - 1 : -1;
     float contrib = 0.f;
     if (lane < groups && mc > -INFINITY) {
         const float e = exp2f((mc - M) * DDT_LOG2E);
         contrib = sc * e + (lane != cstar ? e : 0.f);
     }
     Sp = wave_sumf(contrib);
+    if (K == 1) {                                      // the best group head
+        const uint64_t best = wave_max_key(kk[0]);
+        return lane == 0 ? best : 0ull;
+    }
 
     if (fits) {
         int nc = 0;

@@ -108,7 +108,7 @@ __device__ void cast_layer(const ddt_tree& t, const ddt_cast& cp, int layer, int
     }
     if (layer == 1)
         for (int i = tid; i < t.D_max; i += NT) t.widths[i] = 0;
-    for (int q = tid; q < B * R; q += NT) s_v[q] = exp((double)t.front_S[q]);
+    for (int q = tid; q < B * R; q += NT) s_v[q] = (double)expf(t.front_S[q]);
     for (int q = tid; q < cp.M * R; q += NT) {
         const int r = q / R, k = q - r * R;
         s_sd[q] = k < cp.N ? cp.S_D[(size_t)r * (cp.N + 1) + k + 1] : 0.f;
@@ -122,10 +122,11 @@ __device__ void cast_layer(const ddt_tree& t, const ddt_cast& cp, int layer, int
     const int kcap = s_kcap;
     const int ctx = (int)s_st[10];
     const int row = cast_sel_row(ctx, cp.L, cp.M);
+    const double invB = 1.0 / (double)B;
     for (int k = tid; k < kcap; k += NT) {
         double sum = 0.0;
         for (int b = 0; b < B; ++b) sum += s_v[b * R + k];
-        s_u[k + 1] = sum / (double)B;                 // column mean; prefix-summed below
+        s_u[k + 1] = sum * invB;                      // column mean; prefix-summed below
         s_c[k + 1] = (double)s_sd[row * R + k] / (double)s_st1[row];
     }
     __syncthreads();
@@ -521,7 +522,7 @@ __global__ __launch_bounds__(RK_NT) void k_rerank(RerankArgs a) {
     }
     // verify count
     if (a.cast_on) {
-        for (int k = tid; k < kmax; k += RK_NT) s_u[k + 1] = exp((double)S[s_node[k]]);
+        for (int k = tid; k < kmax; k += RK_NT) s_u[k + 1] = (double)expf(S[s_node[k]]);
         __syncthreads();
         if (wid == 0) {
             // prefix sums: four consecutive items per lane, then across lanes
@@ -642,36 +643,45 @@ struct MaskArgs {
 
 #define MK_NT 256
 
+// One workgroup per row, P <= MK_NT.  Two rounds of global loads (the
+// selection, then the selected nodes' key, token, parent and depth); flat
+// indices by rank counting on the keys; a node -> flat index table in LDS
+// gives each node's flat parent; leaves are numbered by a ballot prefix sum.
 __global__ __launch_bounds__(MK_NT) void k_build_mask(MaskArgs a) {
     const ddt_tree& t = a.t;
     const ddt_flat& f = a.f;
-    const int b = blockIdx.x, tid = threadIdx.x;
-    const int P = f.P, W = f.W, Dp = f.Dp;
-    __shared__ uint64_t s_key[MK_NT], s_fkey[MK_NT];
-    __shared__ int32_t s_node[MK_NT], s_fnode[MK_NT];
-    __shared__ int s_fp[MK_NT], s_dep[MK_NT], s_hc[MK_NT], s_lidx[MK_NT];
-    __shared__ int s_nl;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int P = f.P, W = f.W, Dp = f.Dp, cap = t.cap;
+    __shared__ uint64_t s_key[MK_NT];
+    __shared__ int32_t s_node[MK_NT], s_tok[MK_NT], s_par[MK_NT], s_dep[MK_NT];
+    __shared__ int32_t s_fnode[MK_NT], s_ftok[MK_NT], s_fpn[MK_NT], s_fdep[MK_NT];
+    __shared__ int s_fp[MK_NT], s_hc[MK_NT], s_lidx[MK_NT];
+    __shared__ int16_t s_inv[DDT_MAX_NODES];
+    __shared__ int s_woff[MK_NT / 64];
     const int m = min(max(a.m[b], 0), P - 1);
-    const size_t o = (size_t)b * t.cap;
+    const int n = m + 1;
+    const size_t o = (size_t)b * cap;
     const int32_t* sel = a.sel + (size_t)b * P;
-    // valid selected nodes (the selection is a prefix of sel)
     for (int q = tid; q < P; q += MK_NT) {
         int node = q <= m ? sel[q] : -1;
-        if (node < 0 || node >= t.cap) node = -1;
+        if (node < 0 || node >= cap) node = -1;
         s_node[q] = node;
         s_key[q] = node >= 0 ? t.key[o + node] : ~0ull;
+        s_tok[q] = node >= 0 ? t.token[o + node] : -1;
+        s_par[q] = node >= 0 ? t.parent[o + node] : -1;
+        s_dep[q] = node >= 0 ? t.depth[o + node] : 0;
         s_hc[q] = 0;
     }
+    for (int i = tid; i < cap; i += MK_NT) s_inv[i] = -1;
     __syncthreads();
-    const int n = m + 1;
     // flat index = rank of the key among the selected keys (keys are unique)
     for (int q = tid; q < n; q += MK_NT) {
         const uint64_t k = s_key[q];
         int r = 0;
 #pragma unroll 8
-        for (int p = 0; p < n; ++p) r += s_key[p] < k;
-        s_fkey[r] = k;
-        s_fnode[r] = s_node[q];
+        for (int p = 0; p < n; ++p) r += s_key[p] < k ? 1 : 0;
+        s_fnode[r] = s_node[q]; s_ftok[r] = s_tok[q]; s_fpn[r] = s_par[q]; s_fdep[r] = s_dep[q];
+        if (s_node[q] >= 0) s_inv[s_node[q]] = (int16_t)r;
     }
     __syncthreads();
     const size_t fo = (size_t)b * P;
@@ -679,66 +689,63 @@ __global__ __launch_bounds__(MK_NT) void k_build_mask(MaskArgs a) {
         int node = -1, tk = -1, fp = -1, d = 0;
         if (i < n && s_fnode[i] >= 0) {
             node = s_fnode[i];
-            tk = t.token[o + node];
-            const int pn = t.parent[o + node];
-            if (pn >= 0 && pn < t.cap) {
-                // parent's flat index: binary search of its key in the sorted keys
-                const uint64_t pk = t.key[o + pn];
-                int lo = 0, hi = n;
-                while (lo < hi) {
-                    const int mid = (lo + hi) >> 1;
-                    if (s_fkey[mid] < pk) lo = mid + 1;
-                    else hi = mid;
-                }
-                fp = (lo < n && s_fkey[lo] == pk) ? lo : -1;
-            }
-            d = t.depth[o + node];
+            tk = s_ftok[i];
+            const int pn = s_fpn[i];
+            fp = (pn >= 0 && pn < cap) ? (int)s_inv[pn] : -1;
+            d = s_fdep[i];
         }
         f.node[fo + i] = node;
         f.token[fo + i] = tk;
         f.parent[fo + i] = fp;
         f.pos[fo + i] = a.prefix + d;
-        s_fp[i] = fp; s_dep[i] = d;
+        s_fp[i] = fp; s_fdep[i] = d;
+        if (i >= 1 && i < n && fp >= 0) s_hc[fp] = 1;
     }
     __syncthreads();
-    for (int i = tid; i < P; i += MK_NT) {
-        const int cols = a.prefix + P;
-        uint8_t* dr = a.dense != nullptr ? a.dense + ((size_t)b * P + i) * cols : nullptr;
-        if (dr != nullptr)
-            for (int col = 0; col < a.prefix; ++col) dr[col] = 1;
-        for (int k = 0; k < W; ++k) {
-            uint32_t word = 0u;
-            int j = i, guard = 0;
-            while (j >= 0 && guard++ <= DDT_MAX_DEPTH + 1) {
-                if ((j >> 5) == k) word |= 1u << (j & 31);
-                j = (i < n) ? s_fp[j] : -1;
-            }
-            f.mask[(fo + i) * W + k] = word;
-            if (dr != nullptr)
-                for (int e = 0; e < 32 && k * 32 + e < P; ++e)
-                    dr[a.prefix + k * 32 + e] = (uint8_t)((word >> e) & 1u);
+    // leaves (no selected child), numbered in flat order
+    {
+        const bool leaf = tid < n && !s_hc[tid];
+        const uint64_t bal = __ballot(leaf);
+        if (lane == 0) s_woff[wid] = __popcll(bal);
+        __syncthreads();
+        int off = 0, tot = 0;
+#pragma unroll
+        for (int w = 0; w < MK_NT / 64; ++w) { off += w < wid ? s_woff[w] : 0; tot += s_woff[w]; }
+        if (tid < P)
+            s_lidx[tid] = leaf ? off + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u)) : -1;
+        if (tid == 0) { f.n_leaves[b] = tot; f.m[b] = m; }
+        __syncthreads();
+    }
+    // ancestor mask: one thread per (row, word), walking the parent chain
+    const int cols = a.prefix + P;
+    for (int q = tid; q < P * W; q += MK_NT) {
+        const int i = q / W, k = q - i * W;
+        uint32_t word = 0u;
+        int j = i, guard = 0;
+        while (j >= 0 && guard++ <= DDT_MAX_DEPTH + 1) {
+            if ((j >> 5) == k) word |= 1u << (j & 31);
+            j = (i < n) ? s_fp[j] : -1;
         }
-        if (i >= 1 && i < n && s_fp[i] >= 0) s_hc[s_fp[i]] = 1;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        int c = 0;
-        for (int i = 0; i < n; ++i) {
-            if (!s_hc[i]) s_lidx[i] = c++;
-            else s_lidx[i] = -1;
+        f.mask[(fo + i) * W + k] = word;
+        if (a.dense != nullptr) {
+            uint8_t* dr = a.dense + ((size_t)b * P + i) * cols;
+            if (k == 0)
+                for (int col = 0; col < a.prefix; ++col) dr[col] = 1;
+            for (int e = 0; e < 32 && k * 32 + e < P; ++e)
+                dr[a.prefix + k * 32 + e] = (uint8_t)((word >> e) & 1u);
         }
-        s_nl = c;
-        f.n_leaves[b] = c;
-        f.m[b] = m;
     }
-    __syncthreads();
     const int L = f.L;
     int32_t* ret = f.retrieve + (size_t)b * L * (Dp + 1);
+    int nl = 0;
+#pragma unroll
+    for (int w = 0; w < MK_NT / 64; ++w) nl += s_woff[w];
     for (int i = tid; i < n; i += MK_NT) {
         const int li = s_lidx[i];
         if (li < 0 || li >= L) continue;
         int32_t* row = ret + (size_t)li * (Dp + 1);
-        const int d = min(s_dep[i], Dp);
+        const int d = min(s_fdep[i], Dp);
         for (int s2 = d + 1; s2 <= Dp; ++s2) row[s2] = -1;
         int j = i;
         for (int s2 = d; s2 >= 0; --s2) {
@@ -746,7 +753,7 @@ __global__ __launch_bounds__(MK_NT) void k_build_mask(MaskArgs a) {
             j = j >= 0 ? s_fp[j] : -1;
         }
     }
-    for (int q = s_nl * (Dp + 1) + tid; q < L * (Dp + 1); q += MK_NT) ret[q] = -1;
+    for (int q = nl * (Dp + 1) + tid; q < L * (Dp + 1); q += MK_NT) ret[q] = -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -780,6 +787,7 @@ struct VerifyArgs {
 };
 
 #define VF_NT 1024
+#define VF_RET 3072           // candidate-path entries staged in LDS
 #define VF_TILE 256            // one wave x 4 elements
 #define VF_MAXTILES 2048       // V <= 524288
 
@@ -876,9 +884,18 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
     __shared__ int s_nch, s_u, s_len, s_acc, s_next;
     __shared__ unsigned long long s_best;
     __shared__ uint64_t s_mscr[VF_NT / 64][MRG_SCR];
+    __shared__ int32_t s_ret[VF_RET];
     const int m = min(max(f.m[b], 0), P - 1);
     const int n = m + 1;
     const size_t fo = (size_t)b * P;
+    const float T = a.temperature[b];
+    const int Lr = min(max(f.n_leaves[b], 0), f.L);
+    const bool ret_lds = Lr * (Dp + 1) <= VF_RET;
+    // greedy: the candidate paths go to LDS in the same round as the merges
+    if (!(T > 0.f) && ret_lds) {
+        const int32_t* ret = f.retrieve + (size_t)b * f.L * (Dp + 1);
+        for (int q = tid; q < Lr * (Dp + 1); q += VF_NT) s_ret[q] = ret[q];
+    }
 
     for (int i = wid; i < n; i += VF_NT / 64) {
         float M, Sp;
@@ -901,16 +918,15 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
     }
     if (tid == 0) s_best = 0ull;
     __syncthreads();
-    const float T = a.temperature[b];
     int32_t* apath = a.accept_path + (size_t)b * (Dp + 1);
 
     if (!(T > 0.f)) {
         // greedy: longest matching prefix over the candidate paths
-        const int L = min(f.n_leaves[b], f.L);
+        const int L = Lr;
         const int32_t* ret = f.retrieve + (size_t)b * f.L * (Dp + 1);
         unsigned long long best = 0ull;
         for (int l = tid; l < L; l += VF_NT) {
-            const int32_t* path = ret + (size_t)l * (Dp + 1);
+            const int32_t* path = ret_lds ? s_ret + l * (Dp + 1) : ret + (size_t)l * (Dp + 1);
             int len = 0;
             for (int s = 1; s <= Dp; ++s) {
                 const int j = path[s], pj = path[s - 1];
@@ -932,7 +948,7 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
             } else {
                 const int len = (int)(s_best >> 32);
                 const int l = 0x7FFFFFFF - (int)(s_best & 0xFFFFFFFFu);
-                const int32_t* path = ret + (size_t)l * (Dp + 1);
+                const int32_t* path = ret_lds ? s_ret + l * (Dp + 1) : ret + (size_t)l * (Dp + 1);
                 for (int s = 0; s <= Dp; ++s) apath[s] = s <= len ? path[s] : -1;
                 a.accept_len[b] = len;
                 a.next_token[b] = s_am[path[len]];
