@@ -30,7 +30,11 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 SEED = 1002
-PMC_FILE = os.path.join(ROOT, "profiles", "row_reduce_traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def pmc_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"k_row_partial_traffic_{workload}.json")
 KERNEL_SRC = os.path.join(ROOT, "dynamic_draft_tree_row_amd", "csrc", "ddt_rowreduce.hpp")
 
 
@@ -102,12 +106,65 @@ def traffic_per_launch(workload: str):
     """HBM bytes per row-reduction launch from the committed rocprofv3 counter
     summary, if it was taken on the current kernel source for this workload."""
     try:
-        d = json.load(open(PMC_FILE))
+        d = json.load(open(pmc_file(workload)))
     except (OSError, ValueError):
         return None
     if d.get("kernel_sha") != kernel_hash() or d.get("workload") != workload:
         return None
     return d.get("bytes_per_launch")
+
+
+CAL_BYTES = 256 << 20          # the calibration copy: reads and writes this many bytes
+
+
+def ingest_pmc(fetch_csv: str, write_csv: str, workload: str, ring: int) -> None:
+    """Per-launch HBM bytes of the row reduction from two rocprofv3 --pmc passes
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).  Each counter is scaled by
+    what it reads for the calibration copy of CAL_BYTES read + CAL_BYTES written."""
+    import csv
+
+    def per_dispatch(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        return vals
+
+    f = per_dispatch(fetch_csv, "FETCH_SIZE")
+    wr = per_dispatch(write_csv, "WRITE_SIZE")
+
+    # the reduction launches of the pmc run's last two eager passes over the
+    # ring: the same per-round launch mix as the event-timed rounds
+    from gen import configs
+    wl = configs.C2 if workload in ("cast_b8_v128256_bf16", "eagle2_b8_v128256_bf16") \
+        else configs.WORKLOADS[workload]
+    n_last = 2 * ring * (wl.D + 1)
+
+    def split(vals):
+        red = [v for (d, n), v in sorted(vals.items()) if "k_row_partial" in n][-n_last:]
+        cal = [v for (d, n), v in sorted(vals.items()) if "neg" in n.lower()]
+        if not red or not cal:
+            raise SystemExit("counter CSV lacks the reduction or the calibration dispatches")
+        return red, cal[-1]
+
+    fr, fcal = split(f)
+    wr_, wcal = split(wr)
+    ff = (CAL_BYTES / 1024.0) / fcal
+    wf = (CAL_BYTES / 1024.0) / wcal
+    fetch_b = float(np.mean(fr)) * 1024.0 * ff
+    write_b = float(np.mean(wr_)) * 1024.0 * wf
+    out = {"workload": workload, "kernel_sha": kernel_hash(),
+           "bytes_per_launch": round(fetch_b + write_b, 1),
+           "fetch_bytes_per_launch": round(fetch_b, 1), "write_bytes_per_launch": round(write_b, 1),
+           "fetch_scale": round(ff, 4), "write_scale": round(wf, 4),
+           "dispatches": [len(fr), len(wr_)],
+           "calibration": f"torch.neg over {CAL_BYTES >> 20} MiB fp32 (reads and writes {CAL_BYTES} bytes)"}
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(pmc_file(workload), "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
 
 
 def cpu_baseline(w, slot, cast_np, seconds):
@@ -141,10 +198,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--break-even", action="store_true",
                     help="CAST at the break-even thresholds C1=1, C2=0.1, C3=0.5")
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="for rocprofv3 --pmc passes: eager rounds over the ring, then one "
+                         "plain 256 MiB copy (torch.neg, fp32) whose counters scale the bytes")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn the two --pmc passes' counter CSVs into "
+                         "profiles/k_row_partial_traffic_<workload>.json")
     ap.add_argument("--workload", default=None,
                     help="profile another workload instead (e.g. eagle2_mixed_b64_v128256_bf16; "
                          "'fixed' = the CAST shape with fixed EAGLE-2 widths)")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.workload or "cast_b8_v128256_bf16", args.ring)
+        return
     if args.gpus != 1:
         log("bench.py measures one GPU only: this build has no multi-GPU path "
             "(batch rows would shard across GPUs; see the design notes).")
@@ -237,6 +303,19 @@ def main():
                           widths=run.tree.widths.cpu().numpy().tolist(),
                           depth=int(max(d for d, r in enumerate(rows_per_layer, 1) if r > 0))))
 
+    if args.pmc_run:
+        for _ in range(2):
+            for slot in ring:
+                eager(slot)
+        torch.cuda.synchronize()
+        x = torch.ones(CAL_BYTES // 4, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        torch.neg(x, out=y)
+        torch.cuda.synchronize()
+        log(f"pmc run done: {2 * len(ring)} eager rounds, then a {CAL_BYTES >> 20} MiB copy (neg)")
+        return
+
     # ---- capture one graph per ring slot -----------------------------------
     graphs = []
     for slot in ring:
@@ -282,26 +361,20 @@ def main():
     eager_us = (time.perf_counter() - t0) * 1e6 / ne
 
     # ---- dominant kernel: the vocabulary-wide row reduction ----------------
-    # Its launches inside the same replays are bracketed by HIP events recorded
-    # on the launching stream (ddt_set_reduce_events); per round: D expand
-    # launches + 1 verify launch.
+    # Per round: D expand launches + 1 verify launch.  The library launches
+    # them with start/stop events that the runtime stamps at the kernel's own
+    # start and end (ddt_set_reduce_events).  Events inside a captured graph
+    # are not valid timing events on this runtime, so the launches are timed
+    # in eager rounds of the same ring slots, on the same stream.
     per_round = w.D + 1
     n_pairs = per_round * R * 4
     evs = hip.events(2 * n_pairs)
     arr = (C.c_void_p * len(evs))(*[e.value for e in evs])
-    # Events recorded inside a captured graph are not valid timing events on
-    # this runtime, so the launches are timed in eager rounds enqueued behind a
-    # long device operation: the whole queue is in place before the GPU reaches
-    # it and each event pair brackets its kernel with no host gap.
-    busy = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     lib.ddt_set_reduce_events(arr, n_pairs)
-    for _ in range(40):
-        busy.mul_(1.0)
     for slot in ring:
         eager(slot)
     used = lib.ddt_set_reduce_events(None, 0)
-    assert used == per_round * R, f"expected {per_round * R} bracketed launches, got {used}"
-    del busy
+    assert used == per_round * R, f"expected {per_round * R} timed launches, got {used}"
     torch.cuda.synchronize()
     durs, nbytes = [], []
     ebytes = w.V * (2 if w.dtype == "bf16" else 4)
@@ -344,7 +417,7 @@ def main():
                      "kernel": "k_row_partial<bf16> (vocab row reduction: max, sigma', top-k)",
                      "algorithmic_bytes_per_launch": round(float(nbytes.mean()), 1),
                      "avg_launch_us": round(float(durs.mean() * 1e6), 3),
-                     "launches": int(len(durs)), "timing": "HIP events around each launch, eager rounds queued behind a busy op",
+                     "launches": int(len(durs)), "timing": "kernel-stamped HIP start/stop events per launch (hipExtLaunchKernelGGL), eager rounds",
                      "big_launches_gbs": round(float(nbytes[big].sum() / durs[big].sum() / 1e9), 1)},
         "logit_gbs": round(logit_gbs, 1),
         "logit_frac_of_peak": round(logit_gbs / PEAK_HBM_GBS, 4),

@@ -1,6 +1,7 @@
 // C ABI of the draft-tree library: argument checks on the host, then kernel
 // launches on the caller's stream.  No allocation, no synchronisation.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <string.h>
 
 #include "../../include/ddt.h"
@@ -91,19 +92,23 @@ int launch_partials(const ddt_logits* x, int n0, int n1, const int32_t* count, i
     if (total <= 0) return DDT_OK;
     if (total > INT32_MAX) return DDT_ECAPACITY;
     const bool bf16 = x->dtype == DDT_BF16;
-    const bool timed = g_events != nullptr && g_used < g_pairs;
-    if (timed && hipEventRecord((hipEvent_t)g_events[2 * g_used], s) != hipSuccess) return DDT_ELAUNCH;
     const dim3 grid((unsigned)total), blk(RR_NT);
     uint32_t* part = (uint32_t*)ws;
+    if (g_events != nullptr && g_used < g_pairs) {
+        // timed: the runtime stamps the two events at the kernel's own start and end
+        hipEvent_t e0 = (hipEvent_t)g_events[2 * g_used], e1 = (hipEvent_t)g_events[2 * g_used + 1];
+        if (bf16)
+            hipExtLaunchKernelGGL((k_row_partial<true>), grid, blk, 0, s, e0, e1, 0, rs, x->V, groups, K, part);
+        else
+            hipExtLaunchKernelGGL((k_row_partial<false>), grid, blk, 0, s, e0, e1, 0, rs, x->V, groups, K, part);
+        ++g_used;
+        return launched();
+    }
     if (bf16)
         hipLaunchKernelGGL((k_row_partial<true>), grid, blk, 0, s, rs, x->V, groups, K, part);
     else
         hipLaunchKernelGGL((k_row_partial<false>), grid, blk, 0, s, rs, x->V, groups, K, part);
     const int st = launched();
-    if (timed) {
-        if (hipEventRecord((hipEvent_t)g_events[2 * g_used + 1], s) != hipSuccess) return DDT_ELAUNCH;
-        ++g_used;
-    }
     return st;
 }
 

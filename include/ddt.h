@@ -339,9 +339,10 @@ int ddt_row_topk(const ddt_logits* x /*host*/, int n0, int n1, int K, int32_t* i
 /*
  * ddt_set_reduce_events -- timing hook for the vocabulary-wide row reduction.
  * While set, the i-th launch of that kernel (any call, any stream), i <
- * n_pairs, is bracketed by hipEventRecord(events[2i]) before and
- * hipEventRecord(events[2i+1]) after, on the launching stream; later launches
- * are not bracketed.  events are hipEvent_t handles created by the caller.
+ * n_pairs, is launched with events[2i] and events[2i+1] as its start and stop
+ * events (hipExtLaunchKernelGGL: the runtime stamps them when the kernel
+ * itself starts and ends); later launches are not timed.  events are
+ * hipEvent_t handles created by the caller.
  * NULL / 0 clears the hook.  Returns the number of launches bracketed since
  * the previous call.  Process-wide host state; not thread-safe.
  */
