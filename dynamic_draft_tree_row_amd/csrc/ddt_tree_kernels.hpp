@@ -83,88 +83,103 @@ __device__ int anchor_scan_wave(const double* u, const double* c, double C, int 
     return a;
 }
 
-// Run by one whole workgroup of NT threads once every row's layer is attached
-// (the rows' frontier values front_S are visible).  One round of global
-// loads: the state, the row counts, the frontier values and the first R_max
-// entries of every cost-table row (M <= DDT_CAST_MAX_M); wave 0 then runs the
-// anchor scan and lane 0 the gain FIFO.
+// CAST's batch rule runs in the last workgroup of a layer.  Every workgroup
+// stages the rule's inputs that do not depend on the layer's results (state,
+// the first R_max entries of every cost-table row, M <= DDT_CAST_MAX_M) in
+// LDS at its start, so the last one only loads the rows' frontier values and
+// counts after the layer ticket.
 #define DDT_CAST_MAX_M 64
 
+struct CastLds {
+    double v[64 * DDT_MAX_FRONT];
+    float sd[DDT_CAST_MAX_M * DDT_MAX_FRONT], st1[DDT_CAST_MAX_M];
+    double c[DDT_MAX_FRONT + 1], u[DDT_MAX_FRONT + 1];
+    double st[11];
+    int kcap, n;
+};
+
 template <int NT>
-__device__ void cast_layer(const ddt_tree& t, const ddt_cast& cp, int layer, int K_e) {
-    const int tid = threadIdx.x, B = t.B, R = t.R_max;
-    __shared__ double s_v[64 * DDT_MAX_FRONT];
-    __shared__ float s_sd[DDT_CAST_MAX_M * DDT_MAX_FRONT], s_st1[DDT_CAST_MAX_M];
-    __shared__ double s_c[DDT_MAX_FRONT + 1], s_u[DDT_MAX_FRONT + 1];
-    __shared__ double s_st[11];
-    __shared__ int s_kcap, s_n;
-    double* st = t.cast_state;
-    if (tid == 0) s_kcap = min(K_e, R);
+__device__ void cast_stage(CastLds& L, const ddt_tree& t, const ddt_cast& cp, int layer) {
+    const int tid = threadIdx.x, R = t.R_max;
     if (tid < 11) {
         double v;
         if (layer == 1) v = tid == 0 ? 1.0 : tid == 8 ? 1.0 : tid == 9 ? -1.0 : 0.0;
-        else v = st[tid];
-        s_st[tid] = v;
+        else v = t.cast_state[tid];
+        L.st[tid] = v;
     }
-    if (layer == 1)
-        for (int i = tid; i < t.D_max; i += NT) t.widths[i] = 0;
-    for (int q = tid; q < B * R; q += NT) s_v[q] = (double)expf(t.front_S[q]);
     for (int q = tid; q < cp.M * R; q += NT) {
         const int r = q / R, k = q - r * R;
-        s_sd[q] = k < cp.N ? cp.S_D[(size_t)r * (cp.N + 1) + k + 1] : 0.f;
+        L.sd[q] = k < cp.N ? cp.S_D[(size_t)r * (cp.N + 1) + k + 1] : 0.f;
     }
-    for (int r = tid; r < cp.M; r += NT) s_st1[r] = cp.S_T[(size_t)r * (cp.N + 1) + 1];
+    for (int r = tid; r < cp.M; r += NT) L.st1[r] = cp.S_T[(size_t)r * (cp.N + 1) + 1];
+}
+
+// The batch rule (after cast_stage and a barrier): width by the anchor scan on
+// the batch-averaged cumulative utility, then the depth gate with the gain FIFO.
+template <int NT>
+__device__ void cast_layer(CastLds& L, const ddt_tree& t, const ddt_cast& cp, int layer, int K_e) {
+    const int tid = threadIdx.x, lane = tid & 63, B = t.B, R = t.R_max;
+    double* st = t.cast_state;
+    if (tid == 0) L.kcap = min(K_e, R);
+    if (layer == 1)
+        for (int i = tid; i < t.D_max; i += NT) t.widths[i] = 0;
+    for (int q = tid; q < B * R; q += NT) L.v[q] = (double)expf(t.front_S[q]);
     int cnt = 0x7FFFFFFF;
     if (tid < B) cnt = max(0, t.n_nodes[tid] - t.layer_base[tid]);
     __syncthreads();
-    if (tid < B) atomicMin(&s_kcap, cnt);
+    if (tid < B) atomicMin(&L.kcap, cnt);
     __syncthreads();
-    const int kcap = s_kcap;
-    const int ctx = (int)s_st[10];
+    const int kcap = L.kcap;
+    const int ctx = (int)L.st[10];
     const int row = cast_sel_row(ctx, cp.L, cp.M);
-    const double invB = 1.0 / (double)B;
-    for (int k = tid; k < kcap; k += NT) {
-        double sum = 0.0;
-        for (int b = 0; b < B; ++b) sum += s_v[b * R + k];
-        s_u[k + 1] = sum * invB;                      // column mean; prefix-summed below
-        s_c[k + 1] = (double)s_sd[row * R + k] / (double)s_st1[row];
-    }
-    __syncthreads();
     if (tid < DDT_WAVE) {
-        if (tid == 0) {
-            s_u[0] = 0.0; s_c[0] = 0.0;
-            for (int k = 1; k <= kcap; ++k) s_u[k] += s_u[k - 1];
+        // column means of e^S, prefix-summed across lanes (kcap <= 32)
+        double mean = 0.0;
+        if (lane < kcap) {
+            for (int b = 0; b < B; ++b) mean += L.v[b * R + lane];
+            mean *= 1.0 / (double)B;
         }
+        double incl = mean;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const double o = __shfl_up(incl, d);
+            if (lane >= d) incl += o;
+        }
+        if (lane < kcap) {
+            L.u[lane + 1] = incl;
+            L.c[lane + 1] = (double)L.sd[row * R + lane] / (double)L.st1[row];
+        }
+        if (lane == 0) { L.u[0] = 0.0; L.c[0] = 0.0; }
         wave_lds_sync();
-        const int n = anchor_scan_wave(s_u, s_c, (double)cp.C1[layer - 1], kcap);
+        const int n = anchor_scan_wave(L.u, L.c, (double)cp.C1[layer - 1], kcap);
         if (tid == 0) {
-            double* fifo = s_st;                       // entries 0..7
-            int len = (int)s_st[8];
-            const double prev = s_st[9];
+            double* fifo = L.st;                       // entries 0..7
+            int len = (int)L.st[8];
+            const double prev = L.st[9];
             if (prev >= 0.0) {                         // push the previous layer's gain ratio
-                const double phi = prev > 0.0 ? s_u[n] / prev : 0.0;
+                const double phi = prev > 0.0 ? L.u[n] / prev : 0.0;
                 if (len < 8) fifo[len++] = phi;
                 if (len > cp.R) {
                     for (int i = 1; i < len; ++i) fifo[i - 1] = fifo[i];
                     --len;
                 }
             }
-            double mean = 0.0;
-            for (int i = 0; i < len; ++i) mean += fifo[i];
-            mean /= (double)len;
-            const double score = n > 0 ? mean * s_u[n] / s_c[n] : 0.0;
+            double fm = 0.0;
+            for (int i = 0; i < len; ++i) fm += fifo[i];
+            fm /= (double)len;
+            const double score = n > 0 ? fm * L.u[n] / L.c[n] : 0.0;
             const bool stop = (layer >= t.D_max) || !(score >= (double)cp.C2);
             for (int i = 0; i < 8; ++i) st[i] = fifo[i];
             st[8] = (double)len;
-            st[9] = s_u[n];
+            st[9] = L.u[n];
             st[10] = (double)(ctx + n);
             t.widths[layer - 1] = n;
             t.cont[0] = stop ? 0 : 1;
-            s_n = stop ? 0 : n;
+            L.n = stop ? 0 : n;
         }
     }
     __syncthreads();
-    for (int b = tid; b < B; b += NT) t.n_front[b] = s_n;
+    for (int b = tid; b < B; b += NT) t.n_front[b] = L.n;
 }
 
 // ---------------------------------------------------------------------------
@@ -202,7 +217,7 @@ __global__ __launch_bounds__(AT_NT) void k_attach(AttachArgs a) {
     const ddt_tree& t = a.t;
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int cap = t.cap, Rm = t.R_max, Kn = a.K_n;
-    __shared__ float s_M[DDT_MAX_FRONT], s_S[DDT_MAX_FRONT];
+    __shared__ float s_M[DDT_MAX_FRONT], s_S[DDT_MAX_FRONT], s_l1p[DDT_MAX_FRONT];
     __shared__ int s_pn[DDT_MAX_FRONT];
     __shared__ float s_pS[DDT_MAX_FRONT];
     __shared__ uint64_t s_pk[DDT_MAX_FRONT];
@@ -210,6 +225,7 @@ __global__ __launch_bounds__(AT_NT) void k_attach(AttachArgs a) {
     __shared__ uint64_t s_sk[AT_SORT];
     __shared__ uint64_t s_scr[AT_NT / 64][MRG_SCR];
     __shared__ int s_nf, s_nn, s_last;
+    __shared__ CastLds s_cast;
 
     int32_t* tok = t.token + (size_t)b * cap;
     int32_t* par = t.parent + (size_t)b * cap;
@@ -237,6 +253,7 @@ __global__ __launch_bounds__(AT_NT) void k_attach(AttachArgs a) {
         if (tid < a.R) { s_pn[tid] = fr[tid]; s_pS[tid] = frS[tid]; s_pk[tid] = frK[tid]; }
         if (tid == 0) { s_nf = t.n_front[b]; s_nn = t.n_nodes[b]; }
     }
+    if (a.cast_on) cast_stage<AT_NT>(s_cast, t, a.c, a.layer);
     // merges: wave j takes slot j (slots past the row's frontier width hold no
     // partials of this layer and are ignored below)
     for (int j = wid; j < a.R; j += AT_NT / 64) {
@@ -244,7 +261,7 @@ __global__ __launch_bounds__(AT_NT) void k_attach(AttachArgs a) {
         const uint32_t* p = a.part + ((size_t)(b * a.R + j) * a.chunks) * rr_ps(Kn);
         const uint64_t mine = merge_row_wave(p, a.chunks, Kn, M, Sp, s_scr[wid]);
         if (lane < Kn) s_key[j * Kn + lane] = mine;
-        if (lane == 0) { s_M[j] = M; s_S[j] = Sp; }
+        if (lane == 0) { s_M[j] = M; s_S[j] = Sp; s_l1p[j] = log1pf(Sp); }
     }
     __syncthreads();
     const int base = s_nn;
@@ -257,7 +274,7 @@ __global__ __launch_bounds__(AT_NT) void k_attach(AttachArgs a) {
         const int u0 = s_pn[j];
         const int u = (u0 >= 0 && u0 < base) ? u0 : 0;
         const uint64_t kk = s_key[j * Kn + r];
-        const float logc = (vkey_val(kk) - s_M[j]) - log1pf(s_S[j]);
+        const float logc = (vkey_val(kk) - s_M[j]) - s_l1p[j];
         const float Sv = s_pS[j] + logc;
         const uint64_t pk = s_pk[j];
         const uint64_t nk = key_child(pk, du, r, 0);
@@ -321,7 +338,7 @@ __global__ __launch_bounds__(AT_NT) void k_attach(AttachArgs a) {
     }
     __syncthreads();
     if (!s_last) return;
-    if (t.cont[0]) cast_layer<AT_NT>(t, a.c, a.layer, a.K_e);
+    if (t.cont[0]) cast_layer<AT_NT>(s_cast, t, a.c, a.layer, a.K_e);
     else
         for (int bb = tid; bb < t.B; bb += AT_NT) t.n_front[bb] = 0;
 }
@@ -832,18 +849,38 @@ __device__ __forceinline__ float ld_logit(const void* row, bool bf16, int v) {
 // was), so each rejection costs one pass over the two rows and no division.
 // Per-element values are fp64: b_k can be small when target and draft are
 // close, and the error of p - a q is amplified by 1 / b_k.
+// 2^x in fp64 for x <= 0 by Tang's table method: x = k/64 + r with
+// |r| <= 1/128, 2^x = 2^(k>>6) * 2^((k&63)/64) * e^(r ln2).  The 64 table
+// entries come from the library exp2 at kernel start; e^z for |z| < 0.0055 is
+// a degree-5 Taylor polynomial (truncation below 4e-17).  Results below
+// 2^-1100 are 0.
+__device__ __forceinline__ double exp2_tab(double x, const double* tab) {
+    x = fmax(x, -1100.0);
+    const double k = rint(x * 64.0);
+    const int ki = (int)k;
+    const double r = fma(k, -0.015625, x);             // exact
+    const double z = r * 0.6931471805599453094;
+    double pz = fma(z, 1.0 / 120.0, 1.0 / 24.0);
+    pz = fma(z, pz, 1.0 / 6.0);
+    pz = fma(z, pz, 0.5);
+    pz = fma(z, pz, 1.0);
+    pz = fma(z, pz, 1.0);
+    return ldexp(tab[ki & 63] * pz, ki >> 6);
+}
+
 struct WalkRows {
     const void* trow;
     const void* drow;
+    const double* tab;                                 // 2^(j/64), j < 64 (LDS)
     bool bf16, alt, ald;
     double kT, Mt, Md, lzt, lzd;
 };
 
 __device__ __forceinline__ double walk_p(const WalkRows& w, float t) {
-    return exp2(((double)t - w.Mt) * w.kT - w.lzt);
+    return exp2_tab(((double)t - w.Mt) * w.kT - w.lzt, w.tab);
 }
 __device__ __forceinline__ double walk_q(const WalkRows& w, float d) {
-    return exp2(((double)d - w.Md) * w.kT - w.lzd);
+    return exp2_tab(((double)d - w.Md) * w.kT - w.lzd, w.tab);
 }
 
 // block-wide sum over the vocabulary of fn(t_v, d_v) in fp64; when only the
@@ -869,6 +906,150 @@ __device__ double walk_pass(const WalkRows& w, int V, double* s_red, Fn fn) {
     return tot;
 }
 
+// both softmax normalisers of a node in one sweep over its two rows
+__device__ void walk_norms(const WalkRows& w, int V, double* s_red, double& Zt, double& Zd) {
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    double at = 0.0, ad = 0.0;
+    for (int v0 = tid * 4; v0 < V; v0 += VF_NT * 4) {
+        float tx[4], dx[4];
+        ld4(w.trow, w.bf16, w.alt, V, v0, tx);
+        ld4(w.drow, w.bf16, w.ald, V, v0, dx);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { at += walk_p(w, tx[e]); ad += walk_q(w, dx[e]); }
+    }
+    at = wave_sum_f64(at);
+    ad = wave_sum_f64(ad);
+    __syncthreads();
+    if (lane == 0) { s_red[wid] = at; s_red[VF_NT / 64 + wid] = ad; }
+    __syncthreads();
+    Zt = 0.0; Zd = 0.0;
+    for (int q = 0; q < VF_NT / 64; ++q) { Zt += s_red[q]; Zd += s_red[VF_NT / 64 + q]; }
+    __syncthreads();
+}
+
+// Per-tile sums (256 ids, one wave per tile) of the weights max(0, p - aa q)
+// (p alone without q) into s_tile; returns their total.
+__device__ double walk_tiles(const WalkRows& w, int V, bool useq, double aa, double* s_tile,
+                             double* s_red) {
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int ntiles = (V + VF_TILE - 1) / VF_TILE;
+    double mine = 0.0;
+    for (int tile = wid; tile < ntiles; tile += VF_NT / 64) {
+        float tx[4], dx[4];
+        const int v0 = tile * VF_TILE + lane * 4;
+        ld4(w.trow, w.bf16, w.alt, V, v0, tx);
+        if (useq) ld4(w.drow, w.bf16, w.ald, V, v0, dx);
+        double ls = 0.0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            ls += useq ? fmax(0.0, walk_p(w, tx[e]) - aa * walk_q(w, dx[e])) : walk_p(w, tx[e]);
+        const double ws = wave_sum_f64(ls);
+        if (lane == 0) s_tile[tile] = ws;
+        mine += ws;
+    }
+    __syncthreads();
+    if (lane == 0) s_red[wid] = mine;
+    __syncthreads();
+    double tot = 0.0;
+    for (int q = 0; q < VF_NT / 64; ++q) tot += s_red[q];
+    __syncthreads();
+    return tot;
+}
+
+// Inverse CDF over the weights walk_tiles left in s_tile: the smallest id whose
+// running sum (ascending ids) exceeds u * total, else the last id with mass.
+// Wave 0 finds the tile by a lane scan over the tile sums, then the id inside
+// it.  Returns the id in every thread.
+__device__ int walk_pick(const WalkRows& w, int V, bool useq, double aa, double u, double tot,
+                         const double* s_tile, int* s_out) {
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int ntiles = (V + VF_TILE - 1) / VF_TILE;
+    if (wid == 0) {
+        const double thr = u * tot;
+        const int tpl = (ntiles + 63) / 64;            // tiles per lane
+        const int t0 = lane * tpl;
+        double loc = 0.0;
+        int lastpos_t = -1;
+        for (int i = 0; i < tpl; ++i) {
+            const int tt = t0 + i;
+            if (tt < ntiles) {
+                loc += s_tile[tt];
+                if (s_tile[tt] > 0.0) lastpos_t = tt;
+            }
+        }
+        double incl = loc;
+        for (int d = 1; d < 64; d <<= 1) {
+            const double o = __shfl_up(incl, d);
+            if (lane >= d) incl += o;
+        }
+        const double ex = incl - loc;
+        const uint64_t m = __ballot(incl > thr);
+        int ts = -1;
+        double base = 0.0;
+        if (m) {
+            const int L = __ffsll((unsigned long long)m) - 1;
+            if (lane == L) {
+                double acc = ex;
+                for (int i = 0; i < tpl && ts < 0; ++i) {
+                    const int tt = t0 + i;
+                    if (tt >= ntiles) break;
+                    if (acc + s_tile[tt] > thr) { ts = tt; base = acc; }
+                    else acc += s_tile[tt];
+                }
+                if (ts < 0) { ts = lastpos_t >= 0 ? lastpos_t : t0; base = acc; }
+            }
+            ts = __shfl(ts, L);
+            base = __shfl(base, L);
+        } else {
+            // rounding at the top end: the last tile with mass
+            int lt = lastpos_t;
+            for (int d = 32; d >= 1; d >>= 1) lt = max(lt, __shfl_xor(lt, d));
+            if (lt < 0) lt = 0;
+            const int L = lt / tpl;
+            if (lane == L) {
+                double acc = ex;
+                for (int tt = t0; tt < lt; ++tt) acc += s_tile[tt];
+                base = acc;
+            }
+            ts = lt;
+            base = __shfl(base, L);
+        }
+        float tx[4], dx[4];
+        const int v0 = ts * VF_TILE + lane * 4;
+        ld4(w.trow, w.bf16, w.alt, V, v0, tx);
+        if (useq) ld4(w.drow, w.bf16, w.ald, V, v0, dx);
+        double pv[4];
+        double ls = 0.0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            pv[e] = useq ? fmax(0.0, walk_p(w, tx[e]) - aa * walk_q(w, dx[e])) : walk_p(w, tx[e]);
+            ls += pv[e];
+        }
+        double in2 = ls;
+        for (int d = 1; d < 64; d <<= 1) {
+            const double o = __shfl_up(in2, d);
+            if (lane >= d) in2 += o;
+        }
+        double run = base + (in2 - ls);
+        int hit = 0x7FFFFFFF, lastpos = -1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int v = v0 + e;
+            run += pv[e];
+            if (v < V && pv[e] > 0.0) {
+                if (run > thr && hit == 0x7FFFFFFF) hit = v;
+                lastpos = v;
+            }
+        }
+        hit = wave_min_i32(hit);
+        int lp = lastpos;
+        for (int d = 32; d >= 1; d >>= 1) lp = max(lp, __shfl_xor(lp, d));
+        if (lane == 0) *s_out = hit != 0x7FFFFFFF ? hit : (lp >= 0 ? lp : 0);
+    }
+    __syncthreads();
+    return *s_out;
+}
+
 __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
     const ddt_tree& t = a.t;
     const ddt_flat& f = a.f;
@@ -878,7 +1059,8 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
     __shared__ float s_M[MK_NT], s_S[MK_NT];
     __shared__ int s_fp[MK_NT], s_ft[MK_NT];
     __shared__ double s_tile[VF_MAXTILES];
-    __shared__ double s_red[VF_NT / 64];
+    __shared__ double s_red[2 * (VF_NT / 64)];
+    __shared__ double s_e2t[64];
     __shared__ int s_path[DDT_MAX_DEPTH + 2];
     __shared__ int s_ch[MK_NT];
     __shared__ int s_nch, s_u, s_len, s_acc, s_next;
@@ -961,6 +1143,7 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
     const double kT = (double)DDT_LOG2E_D / (double)T;
     const float* Ub = a.U + fo * 2;
     if (tid == 0) { s_u = 0; s_len = 0; s_path[0] = 0; }
+    if (tid < 64) s_e2t[tid] = exp2((double)tid / 64.0);
     __syncthreads();
     while (true) {
         const int u = s_u;
@@ -976,6 +1159,7 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
         const int udep = (unode >= 0 && unode < t.cap) ? t.depth[(size_t)b * t.cap + unode] : 0;
         const bool has_q = nch > 0 && uslot >= 0 && a.drf != nullptr && udep < t.D_max;
         WalkRows w;
+        w.tab = s_e2t;
         w.bf16 = a.bf16 != 0;
         const size_t es = a.bf16 ? 2 : 4;
         w.trow = (const char*)a.tgt + (size_t)(b * a.ts0 + u * a.ts1) * es;
@@ -995,20 +1179,32 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
         w.Md = has_q ? (double)t.rmax[ri] : w.Mt;
         w.lzt = 0.0;
         w.lzd = 0.0;
-        // normalisers (p always, q when u has children)
-        if (has_q) {
-            WalkRows wd = w;                           // the draft row alone
-            wd.trow = w.drow;
-            wd.alt = w.ald;
-            const double Zt = walk_pass<false>(w, a.V, s_red, [&](float tv, float) { return walk_p(w, tv); });
-            const double Zd = walk_pass<false>(wd, a.V, s_red, [&](float dv, float) { return walk_q(w, dv); });
+        // Normalisers.  The accept tests at T = 1 use the rows' own statistics
+        // (the reduction's fp32 sigma', relative error ~1e-6, well inside the
+        // accept-test margin); the fp64 sums are taken only once a rejection
+        // needs a residual.  The emission weights need no normaliser.
+        bool zexact = false;
+        auto exact_norms = [&]() {
+            w.lzt = 0.0;                               // sums of the unnormalised rows
+            w.lzd = 0.0;
+            double Zt, Zd;
+            walk_norms(w, a.V, s_red, Zt, Zd);
             w.lzt = log2(Zt);
             w.lzd = log2(Zd);
-        } else {
-            w.lzt = log2(walk_pass<false>(w, a.V, s_red, [&](float tv, float) { return walk_p(w, tv); }));
+            zexact = true;
+        };
+        if (has_q) {
+            if (T == 1.f) {
+                w.lzt = log2(1.0 + (double)s_S[u]);
+                w.lzd = log2(1.0 + (double)t.rsp[ri]);
+            } else {
+                exact_norms();
+            }
         }
         double ra = 0.0, rb = 1.0;                      // residual p_k = max(0, p - ra q) / rb
         int accepted = -1;
+        bool tiles_ready = false;                       // s_tile holds the current residual's weights
+        double tiles_tot = 0.0;
         if (has_q) {
             for (int ci = 0; ci < nch; ++ci) {
                 const int c = s_ch[ci];
@@ -1022,11 +1218,20 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
                 }
                 __syncthreads();
                 if (s_acc) { accepted = c; break; }
-                // rejection: b' = F(a + b)
+                if (!zexact) exact_norms();
+                // rejection: b' = F(a + b); after the last sibling the same
+                // pass leaves the emission weights per tile
                 const double an = ra + rb;
-                const double F = walk_pass<true>(w, a.V, s_red, [&](float tv, float dv) {
-                    return fmax(0.0, walk_p(w, tv) - an * walk_q(w, dv));
-                });
+                double F;
+                if (ci == nch - 1) {
+                    F = walk_tiles(w, a.V, true, an, s_tile, s_red);
+                    tiles_ready = F > 0.0;
+                    tiles_tot = F;
+                } else {
+                    F = walk_pass<true>(w, a.V, s_red, [&](float tv, float dv) {
+                        return fmax(0.0, walk_p(w, tv) - an * walk_q(w, dv));
+                    });
+                }
                 if (F > 0.0) { ra = an; rb = F; }
             }
         }
@@ -1036,81 +1241,11 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
             continue;
         }
         // emission from the current residual by inverse CDF with U[u][1] over
-        // the unnormalised weights r(v) = max(0, p(v) - a q(v)); the threshold
-        // scales with their total.  Tiles of 256 ids: one wave each.
-        const int ntiles = (a.V + VF_TILE - 1) / VF_TILE;
-        for (int tile = wid; tile < ntiles; tile += VF_NT / 64) {
-            float tx[4], dx[4];
-            const int v0 = tile * VF_TILE + lane * 4;
-            ld4(w.trow, w.bf16, w.alt, a.V, v0, tx);
-            if (has_q) ld4(w.drow, w.bf16, w.ald, a.V, v0, dx);
-            double ls = 0.0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                ls += has_q ? fmax(0.0, walk_p(w, tx[e]) - ra * walk_q(w, dx[e])) : walk_p(w, tx[e]);
-            const double ws = wave_sum_f64(ls);
-            if (lane == 0) s_tile[tile] = ws;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            double tot = 0.0;
-            for (int i = 0; i < ntiles; ++i) tot += s_tile[i];
-            const double thr = (double)Ub[2 * u + 1] * tot;
-            double acc = 0.0;
-            int ts = -1;
-            for (int i = 0; i < ntiles; ++i) {
-                if (acc + s_tile[i] > thr) { ts = i; break; }
-                acc += s_tile[i];
-            }
-            if (ts < 0) {                              // rounding at the top end: last tile with mass
-                acc = 0.0;
-                int last = 0;
-                for (int i = 0; i < ntiles; ++i) if (s_tile[i] > 0.0) last = i;
-                for (int i = 0; i < last; ++i) acc += s_tile[i];
-                ts = last;
-            }
-            s_red[0] = acc; s_red[1] = thr;
-            s_next = ts;
-        }
-        __syncthreads();
-        if (wid == 0) {
-            const int tile = s_next;
-            const double base = s_red[0], thr = s_red[1];
-            float tx[4], dx[4];
-            const int v0 = tile * VF_TILE + lane * 4;
-            ld4(w.trow, w.bf16, w.alt, a.V, v0, tx);
-            if (has_q) ld4(w.drow, w.bf16, w.ald, a.V, v0, dx);
-            double pv[4];
-            double ls = 0.0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                pv[e] = has_q ? fmax(0.0, walk_p(w, tx[e]) - ra * walk_q(w, dx[e])) : walk_p(w, tx[e]);
-                ls += pv[e];
-            }
-            // exclusive prefix over lanes, in lane order
-            double incl = ls;
-            for (int d = 1; d < 64; d <<= 1) {
-                const double o = __shfl_up(incl, d);
-                if (lane >= d) incl += o;
-            }
-            double run = base + (incl - ls);
-            // first id whose running sum exceeds thr; else the last one with mass
-            int hit = 0x7FFFFFFF, lastpos = -1;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int v = v0 + e;
-                run += pv[e];
-                if (v < a.V && pv[e] > 0.0) {
-                    if (run > thr && hit == 0x7FFFFFFF) hit = v;
-                    lastpos = v;
-                }
-            }
-            hit = wave_min_i32(hit);
-            int lp = lastpos;
-            for (int d = 32; d >= 1; d >>= 1) lp = max(lp, __shfl_xor(lp, d));
-            if (lane == 0) s_next = hit != 0x7FFFFFFF ? hit : (lp >= 0 ? lp : 0);
-        }
-        __syncthreads();
+        // the unnormalised weights max(0, p - a q) (p at a leaf); the threshold
+        // scales with their total
+        if (!tiles_ready) tiles_tot = walk_tiles(w, a.V, has_q, ra, s_tile, s_red);
+        const int nx = walk_pick(w, a.V, has_q, ra, (double)Ub[2 * u + 1], tiles_tot, s_tile, &s_next);
+        (void)nx;
         break;
     }
     if (tid == 0) {
