@@ -34,6 +34,7 @@ class RoundShape:
     tpl_depth: int = 8
     tpl_width: int = 8
     k_succ: int = 8
+    shared_M: bool = False       # Graft: one successor matrix [V][k] for every row
 
     @property
     def m_max(self) -> int:
@@ -84,7 +85,7 @@ class RoundRunner:
                         use_k_draft=gate is not None, stream=stream)
         if s.graft:
             api.succ_gather(self.tree, M, s.k_succ, s.tpl_depth, s.tpl_width, s.m_max, s.m_max,
-                            self.sel, self.m_out, stream=stream)
+                            self.sel, self.m_out, shared=s.shared_M, stream=stream)
         api.tree_build_mask(self.tree, self.sel, self.m_out, s.prefix, self.flat, stream=stream)
 
     def verify(self, target: torch.Tensor, draft_arena: Optional[torch.Tensor],
@@ -97,4 +98,4 @@ class RoundRunner:
                         stream=stream)
         if self.shape.graft:
             api.succ_update(M, self.flat, self.shape.k_succ, row_topk=self.row_topk,
-                            k_top=self.k_top, stream=stream)
+                            k_top=self.k_top, shared=self.shape.shared_M, stream=stream)

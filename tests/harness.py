@@ -67,12 +67,25 @@ class Case:
     M_before: Optional[np.ndarray] = None
     M_after: Optional[np.ndarray] = None
     tries: int = 0
+    shared_M: bool = False
+
+
+class SharedRows:
+    """Every request's view of one successor matrix [V][k]: the oracle reads and
+    refreshes the same rows for all requests, in request order."""
+
+    def __init__(self, M1):
+        self.M = M1
+
+    def __getitem__(self, b):
+        return self.M
 
 
 def oracle_case(w: Workload, seed: int, rnd: int, rows=None, cast=None, graft=None,
-                M=None, M0=None, max_tries=60) -> Case:
+                M=None, M0=None, max_tries=60, shared_M=False) -> Case:
     """Run the oracle on batch rows `rows` of (seed, rnd), re-keying rows whose
-    decisions fall inside the margin floor.  M/M0 are full-batch [B][V][k]."""
+    decisions fall inside the margin floor.  M/M0 are full-batch [B][V][k], or
+    one [V][k] matrix shared by every row when shared_M."""
     rows = list(range(w.B)) if rows is None else list(rows)
     nb = len(rows)
     att = np.zeros(nb, np.int64)
@@ -87,10 +100,15 @@ def oracle_case(w: Workload, seed: int, rnd: int, rows=None, cast=None, graft=No
 
         def tfn(dr, flats):
             fk, fd, fs, ft = flat_layout(dr.trees, flats, w.m_max + 1)
-            held["t"] = synth.target_arena(w, seed, rnd, draft, fk, fd, fs, ft, att, M0, rows=rows)
+            held["t"] = synth.target_arena(w, seed, rnd, draft, fk, fd, fs, ft, att, M0r, rows=rows)
             return held["t"]
 
-        Mc = M[rows].copy() if M is not None else None
+        if shared_M:
+            Mc = SharedRows(M.copy())
+            M0r = np.stack([M0] * w.B) if M0 is not None else None
+        else:
+            Mc = M[rows].copy() if M is not None else None
+            M0r = M0
         cst = None
         if cast is not None:
             cst = dict(cast)
@@ -104,11 +122,13 @@ def oracle_case(w: Workload, seed: int, rnd: int, rows=None, cast=None, graft=No
         bad = O.margin_failures(out["margins"])
         if not bad:
             M_after = None
-            if M is not None:
+            if shared_M:
+                M_after = Mc.M
+            elif M is not None:
                 M_after = M.copy()
                 M_after[rows] = Mc
             return Case(w, seed, rnd, rows, att, draft, held["t"], roots, U, T, out, cst, graft,
-                        M, M_after, tries)
+                        M, M_after, tries, shared_M)
         redo = list(range(nb)) if -1 in bad else sorted(bad)
         att[redo] += 1
         synth.draft_arena(w, seed, rnd, att, rows=rows, out=draft, only=redo)
@@ -126,14 +146,15 @@ def to_dev(raw: np.ndarray, dtype: str, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).to(device).view(torch.bfloat16)
 
 
-def runner_for(w: Workload, device="cuda"):
+def runner_for(w: Workload, device="cuda", shared_M=False):
     import torch
     from dynamic_draft_tree_row_amd.round_driver import RoundRunner, RoundShape
     gs = w.graft
     shape = RoundShape(B=w.B, V=w.V, dtype=torch.float32 if w.dtype == "f32" else torch.bfloat16,
                        D=w.D, K_e=w.K_e, K_n=w.K_n, m=w.m_max, prefix=w.prefix,
                        graft=gs is not None, tpl_depth=gs.tpl_depth if gs else 8,
-                       tpl_width=gs.tpl_width if gs else 8, k_succ=gs.k_succ if gs else 8)
+                       tpl_width=gs.tpl_width if gs else 8, k_succ=gs.k_succ if gs else 8,
+                       shared_M=shared_M)
     return RoundRunner(shape, device)
 
 
@@ -156,13 +177,17 @@ def gpu_round(case: Case, device="cuda") -> dict:
     import torch
     w = case.w
     wb = Workload(**{**w.__dict__, "B": len(case.rows)})
-    run = runner_for(wb, device)
+    run = runner_for(wb, device, case.shared_M)
     arena = to_dev(case.draft, w.dtype, device)
     roots = torch.from_numpy(case.roots).to(device)
     cast = dev_cast(case.cast, device) if case.cast else None
     gate = dev_gate(case.graft) if case.graft else None
-    M = torch.from_numpy(np.ascontiguousarray(case.M_before[case.rows])).to(device) \
-        if case.M_before is not None else None
+    if case.M_before is None:
+        M = None
+    elif case.shared_M:
+        M = torch.from_numpy(np.ascontiguousarray(case.M_before)).to(device)
+    else:
+        M = torch.from_numpy(np.ascontiguousarray(case.M_before[case.rows])).to(device)
     run.draft(arena, roots, cast=cast, gate=gate, M=M)
     target = to_dev(case.target, w.dtype, device)
     T = torch.from_numpy(case.T).to(device)
@@ -233,7 +258,8 @@ def compare(case: Case, r: dict) -> None:
         np.testing.assert_array_equal(r["widths"][:len(wd)], wd, err_msg="CAST widths")
     if case.graft is not None:
         np.testing.assert_array_equal(r["k_draft"], o["draft"].k_draft, err_msg="Graft k_draft")
-        np.testing.assert_array_equal(r["M"], case.M_after[case.rows], err_msg="successor matrix")
+        exp_M = case.M_after if case.shared_M else case.M_after[case.rows]
+        np.testing.assert_array_equal(r["M"], exp_M, err_msg="successor matrix")
 
 
 def calibrate_tau(w: Workload, seed: int, rounds: int, q: float = 25.0):

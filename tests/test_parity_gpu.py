@@ -133,6 +133,20 @@ def test_graft_small_multi_round():
         M = case.M_after
 
 
+def test_graft_shared_successor_matrix():
+    # one successor matrix for the whole batch (row stride 0): every request
+    # reads it in the draft phase, refreshes land in request order
+    w = configs.shrink(configs.C4, V=5000, B=4)
+    tau = H.calibrate_tau(w, 91, 4)
+    M = synth.succ_matrix0(w, 91)[0].copy()
+    M0 = M.copy()
+    for rnd in range(2):
+        case = H.oracle_case(w, 91, rnd, graft=H.graft_params(w, tau), M=M, M0=M0, shared_M=True)
+        say(f"graft shared-M round {rnd} k_draft={case.out['draft'].k_draft}")
+        H.compare(case, H.gpu_round(case))
+        M = case.M_after
+
+
 def test_determinism_bitwise():
     w = SMALL["mixed_prefix"]
     case = _case(w, 5, 0)
