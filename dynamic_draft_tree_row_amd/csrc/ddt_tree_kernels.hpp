@@ -114,22 +114,16 @@ __device__ void cast_stage(CastLds& L, const ddt_tree& t, const ddt_cast& cp, in
     for (int r = tid; r < cp.M; r += NT) L.st1[r] = cp.S_T[(size_t)r * (cp.N + 1) + 1];
 }
 
-// The batch rule (after cast_stage and a barrier): width by the anchor scan on
-// the batch-averaged cumulative utility, then the depth gate with the gain FIFO.
+// The batch rule, once L.v[b * R_max + k] = e^S of row b's k-th frontier node
+// (k < kcap) and the staged inputs are in LDS: width by the anchor scan on the
+// batch-averaged cumulative utility, then the depth gate with the gain FIFO;
+// every row's n_front gets the result.
 template <int NT>
-__device__ void cast_layer(CastLds& L, const ddt_tree& t, const ddt_cast& cp, int layer, int K_e) {
+__device__ void cast_decide(CastLds& L, const ddt_tree& t, const ddt_cast& cp, int layer, int kcap) {
     const int tid = threadIdx.x, lane = tid & 63, B = t.B, R = t.R_max;
     double* st = t.cast_state;
-    if (tid == 0) L.kcap = min(K_e, R);
     if (layer == 1)
         for (int i = tid; i < t.D_max; i += NT) t.widths[i] = 0;
-    for (int q = tid; q < B * R; q += NT) L.v[q] = (double)expf(t.front_S[q]);
-    int cnt = 0x7FFFFFFF;
-    if (tid < B) cnt = max(0, t.n_nodes[tid] - t.layer_base[tid]);
-    __syncthreads();
-    if (tid < B) atomicMin(&L.kcap, cnt);
-    __syncthreads();
-    const int kcap = L.kcap;
     const int ctx = (int)L.st[10];
     const int row = cast_sel_row(ctx, cp.L, cp.M);
     if (tid < DDT_WAVE) {
@@ -180,6 +174,21 @@ __device__ void cast_layer(CastLds& L, const ddt_tree& t, const ddt_cast& cp, in
     }
     __syncthreads();
     for (int b = tid; b < B; b += NT) t.n_front[b] = L.n;
+}
+
+// The batch rule in the last workgroup of a multi-workgroup layer: loads the
+// rows' frontier values and counts first.
+template <int NT>
+__device__ void cast_layer(CastLds& L, const ddt_tree& t, const ddt_cast& cp, int layer, int K_e) {
+    const int tid = threadIdx.x, B = t.B, R = t.R_max;
+    if (tid == 0) L.kcap = min(K_e, R);
+    for (int q = tid; q < B * R; q += NT) L.v[q] = (double)expf(t.front_S[q]);
+    int cnt = 0x7FFFFFFF;
+    if (tid < B) cnt = max(0, t.n_nodes[tid] - t.layer_base[tid]);
+    __syncthreads();
+    if (tid < B) atomicMin(&L.kcap, cnt);
+    __syncthreads();
+    cast_decide<NT>(L, t, cp, layer, L.kcap);
 }
 
 // ---------------------------------------------------------------------------

@@ -96,6 +96,7 @@ def _case(w, seed, rnd, rows=None, M=None, tau=None):
 SMALL = {
     "eagle2_f32": configs.shrink(configs.C1, V=5000, B=2),
     "cast": configs.shrink(configs.C2, V=17000),
+    "cast_b12": configs.shrink(configs.C2, V=9000, B=12),       # more workgroups sharing the layer ticket
     "t1": configs.shrink(configs.C3, V=9001, B=4),            # odd V: unaligned bf16 rows
     "mixed_prefix": configs.shrink(configs.C5, V=4100, B=6),
 }
