@@ -21,7 +21,8 @@ class Tree(C.Structure):
                 ("S", P), ("logc", P), ("rmax", P), ("rsp", P), ("n_nodes", P),
                 ("layer_base", P), ("n_front", P), ("frontier", P), ("front_S", P), ("front_key", P),
                 ("active", P),
-                ("k_draft", P), ("cont", P), ("widths", P), ("cast_state", P), ("ticket", P)]
+                ("k_draft", P), ("cont", P), ("widths", P), ("cast_state", P), ("ticket", P),
+                ("walk_buf", P), ("walk_sync", P)]
 
 
 class Flat(C.Structure):

@@ -42,7 +42,8 @@ int check_tree(const ddt_tree* t) {
         t->layer_base == nullptr || t->n_front == nullptr || t->frontier == nullptr ||
         t->front_S == nullptr || t->front_key == nullptr ||
         t->active == nullptr || t->k_draft == nullptr || t->cont == nullptr ||
-        t->widths == nullptr || t->cast_state == nullptr || t->ticket == nullptr)
+        t->widths == nullptr || t->cast_state == nullptr || t->ticket == nullptr ||
+        t->walk_buf == nullptr || t->walk_sync == nullptr)
         return DDT_EINVAL;
     if (t->B < 1 || t->cap < 2 || t->D_max < 1 || t->R_max < 1) return DDT_EINVAL;
     if (t->cap > DDT_MAX_NODES || t->D_max > DDT_MAX_DEPTH || t->R_max > DDT_MAX_FRONT)
@@ -80,6 +81,20 @@ inline T* carve(char*& p, size_t n) {
 // timing hook (ddt_set_reduce_events)
 void* const* g_events = nullptr;
 int g_pairs = 0, g_used = 0;
+
+// Workgroups of the verify kernel the device holds at once (cached per device).
+int resident_verify_blocks() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+    if (cache[dev] == 0) {
+        int cus = 0, per = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_verify, VF_NT, 0) != hipSuccess) per = 0;
+        cache[dev] = cus > 0 && per > 0 ? cus * per : 1;
+    }
+    return cache[dev];
+}
 
 int launch_partials(const ddt_logits* x, int n0, int n1, const int32_t* count, int count_add,
                     int K, void* ws, hipStream_t s) {
@@ -161,6 +176,8 @@ size_t ddt_tree_bytes(int B, int cap, int D_max, int R_max) {
     n += align256((size_t)D_max * 4);                          // widths
     n += align256(16 * 8);                                     // cast_state
     n += align256(4);                                          // ticket
+    n += align256((size_t)B * DDT_WALK_STRIDE * 8);            // walk_buf
+    n += align256((size_t)B * 2 * 4);                          // walk_sync
     return n;
 }
 
@@ -194,6 +211,8 @@ int ddt_tree_bind(ddt_tree* t, void* base, size_t bytes, int B, int cap, int D_m
     t->widths = carve<int32_t>(p, D_max);
     t->cast_state = carve<double>(p, 16);
     t->ticket = carve<uint32_t>(p, 1);
+    t->walk_buf = carve<double>(p, (size_t)B * DDT_WALK_STRIDE);
+    t->walk_sync = carve<uint32_t>(p, (size_t)B * 2);
     return DDT_OK;
 }
 
@@ -349,7 +368,15 @@ int ddt_tree_verify(const ddt_tree* t, const ddt_flat* f, const ddt_logits* targ
     a.temperature = temperature; a.U = uniforms; a.k_top = k_top; a.row_topk = row_topk;
     a.row_argmax = row_argmax; a.accept_len = accept_len; a.accept_path = accept_path;
     a.next_token = next_token;
-    hipLaunchKernelGGL(k_verify, dim3(t->B), dim3(VF_NT), 0, s, a);
+    // T > 0 requests split their vocabulary passes over G workgroups; the grid
+    // stays within what the device holds at once, so the workgroups of a
+    // request are resident together
+    const int ntiles = (target->V + VF_TILE - 1) / VF_TILE;
+    int G = resident_verify_blocks() / t->B;
+    G = G < 1 ? 1 : (G > 32 ? 32 : G);
+    if (G > ntiles) G = ntiles;
+    a.G = G;
+    hipLaunchKernelGGL(k_verify, dim3((unsigned)(t->B * G)), dim3(VF_NT), 0, s, a);
     return launched();
 }
 

@@ -794,6 +794,8 @@ __global__ __launch_bounds__(MK_NT) void k_build_mask(MaskArgs a) {
 
 struct VerifyArgs {
     ddt_tree t;
+    int G;                 // workgroups per request
+
     ddt_flat f;
     const uint32_t* part;
     int chunks, Kp;
@@ -892,13 +894,64 @@ __device__ __forceinline__ double walk_q(const WalkRows& w, float d) {
     return exp2_tab(((double)d - w.Md) * w.kT - w.lzd, w.tab);
 }
 
-// block-wide sum over the vocabulary of fn(t_v, d_v) in fp64; when only the
-// target row is needed (UseD false) the draft row is not read
+// A request's T > 0 walk may run on G workgroups, each over its own slice of
+// the vocabulary (whole tiles).  Every workgroup takes the same decisions from
+// the same totals; a pass's totals are combined through global memory:
+// thread 0 stores the workgroup's sums in the pass's slot (two slots,
+// alternating), releases, counts itself in, and spins (bounded) until all G
+// have arrived.  A workgroup reaches pass k + 2's store only after all G
+// arrived at pass k + 1, i.e. after every workgroup read pass k's slot.
+#define WALK_SPIN_LIMIT (1u << 22)
+
+struct RowSync {
+    double* buf;         // [2][G][2] pass sums
+    double* tiles;       // [VF_MAXTILES] tile sums
+    uint32_t* cnt;       // [0] arrivals (k + 1) * G after pass k, [1] exits
+    int G, g, k;         // workgroups of the request, this one, passes so far
+    int lo, hi;          // vocabulary slice [lo, hi)
+    int t_lo, t_hi;      // the same slice in tiles
+};
+
+// combine two workgroup sums over the request's workgroups (every thread
+// returns the totals); s_bc: 2 doubles of LDS, s_err: set on a timed-out wait
+__device__ void row_combine(RowSync& rs, double& x0, double& x1, double* s_bc, int* s_err) {
+    if (rs.G == 1) return;
+    if (threadIdx.x == 0) {
+        double* slot = rs.buf + (size_t)(rs.k & 1) * rs.G * 2;
+        slot[2 * rs.g] = x0;
+        slot[2 * rs.g + 1] = x1;
+        __threadfence();
+        atomicAdd(rs.cnt, 1u);
+        const uint32_t target = (uint32_t)(rs.k + 1) * (uint32_t)rs.G;
+        unsigned spins = 0;
+        while (!*s_err &&
+               __hip_atomic_load(rs.cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            if (++spins > WALK_SPIN_LIMIT) { *s_err = 1; break; }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        __threadfence();
+        double a0 = 0.0, a1 = 0.0;
+        for (int q = 0; q < rs.G; ++q) {
+            a0 += __hip_atomic_load(slot + 2 * q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            a1 += __hip_atomic_load(slot + 2 * q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        s_bc[0] = a0; s_bc[1] = a1;
+    }
+    __syncthreads();
+    x0 = s_bc[0]; x1 = s_bc[1];
+    __syncthreads();
+    rs.k++;
+}
+
+// block-wide sum over the slice of fn(t_v, d_v) in fp64, combined over the
+// request's workgroups; when only the target row is needed (UseD false) the
+// draft row is not read
 template <bool UseD, class Fn>
-__device__ double walk_pass(const WalkRows& w, int V, double* s_red, Fn fn) {
+__device__ double walk_pass(const WalkRows& w, RowSync& rs, double* s_red, double* s_bc, int* s_err,
+                            int V, Fn fn) {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     double acc = 0.0;
-    for (int v0 = tid * 4; v0 < V; v0 += VF_NT * 4) {
+    for (int v0 = rs.lo + tid * 4; v0 < rs.hi; v0 += VF_NT * 4) {
         float tx[4], dx[4];
         ld4(w.trow, w.bf16, w.alt, V, v0, tx);
         if (UseD) ld4(w.drow, w.bf16, w.ald, V, v0, dx);
@@ -909,17 +962,19 @@ __device__ double walk_pass(const WalkRows& w, int V, double* s_red, Fn fn) {
     __syncthreads();
     if (lane == 0) s_red[wid] = d;
     __syncthreads();
-    double tot = 0.0;
+    double tot = 0.0, zero = 0.0;
     for (int q = 0; q < VF_NT / 64; ++q) tot += s_red[q];
     __syncthreads();
+    row_combine(rs, tot, zero, s_bc, s_err);
     return tot;
 }
 
 // both softmax normalisers of a node in one sweep over its two rows
-__device__ void walk_norms(const WalkRows& w, int V, double* s_red, double& Zt, double& Zd) {
+__device__ void walk_norms(const WalkRows& w, RowSync& rs, double* s_red, double* s_bc, int* s_err,
+                           int V, double& Zt, double& Zd) {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     double at = 0.0, ad = 0.0;
-    for (int v0 = tid * 4; v0 < V; v0 += VF_NT * 4) {
+    for (int v0 = rs.lo + tid * 4; v0 < rs.hi; v0 += VF_NT * 4) {
         float tx[4], dx[4];
         ld4(w.trow, w.bf16, w.alt, V, v0, tx);
         ld4(w.drow, w.bf16, w.ald, V, v0, dx);
@@ -934,16 +989,17 @@ __device__ void walk_norms(const WalkRows& w, int V, double* s_red, double& Zt, 
     Zt = 0.0; Zd = 0.0;
     for (int q = 0; q < VF_NT / 64; ++q) { Zt += s_red[q]; Zd += s_red[VF_NT / 64 + q]; }
     __syncthreads();
+    row_combine(rs, Zt, Zd, s_bc, s_err);
 }
 
 // Per-tile sums (256 ids, one wave per tile) of the weights max(0, p - aa q)
-// (p alone without q) into s_tile; returns their total.
-__device__ double walk_tiles(const WalkRows& w, int V, bool useq, double aa, double* s_tile,
-                             double* s_red) {
+// (p alone without q) over the slice, into s_tile and, with several
+// workgroups, rs.tiles; returns the request's total.
+__device__ double walk_tiles(const WalkRows& w, RowSync& rs, double* s_red, double* s_bc, int* s_err,
+                             int V, bool useq, double aa, double* s_tile) {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int ntiles = (V + VF_TILE - 1) / VF_TILE;
     double mine = 0.0;
-    for (int tile = wid; tile < ntiles; tile += VF_NT / 64) {
+    for (int tile = rs.t_lo + wid; tile < rs.t_hi; tile += VF_NT / 64) {
         float tx[4], dx[4];
         const int v0 = tile * VF_TILE + lane * 4;
         ld4(w.trow, w.bf16, w.alt, V, v0, tx);
@@ -953,22 +1009,26 @@ __device__ double walk_tiles(const WalkRows& w, int V, bool useq, double aa, dou
         for (int e = 0; e < 4; ++e)
             ls += useq ? fmax(0.0, walk_p(w, tx[e]) - aa * walk_q(w, dx[e])) : walk_p(w, tx[e]);
         const double ws = wave_sum_f64(ls);
-        if (lane == 0) s_tile[tile] = ws;
+        if (lane == 0) {
+            s_tile[tile] = ws;
+            if (rs.G > 1) rs.tiles[tile] = ws;
+        }
         mine += ws;
     }
     __syncthreads();
     if (lane == 0) s_red[wid] = mine;
     __syncthreads();
-    double tot = 0.0;
+    double tot = 0.0, zero = 0.0;
     for (int q = 0; q < VF_NT / 64; ++q) tot += s_red[q];
     __syncthreads();
+    row_combine(rs, tot, zero, s_bc, s_err);
     return tot;
 }
 
-// Inverse CDF over the weights walk_tiles left in s_tile: the smallest id whose
-// running sum (ascending ids) exceeds u * total, else the last id with mass.
-// Wave 0 finds the tile by a lane scan over the tile sums, then the id inside
-// it.  Returns the id in every thread.
+// Inverse CDF over the tile sums in s_tile (all tiles of the request): the
+// smallest id whose running sum (ascending ids) exceeds u * total, else the
+// last id with mass.  Wave 0 finds the tile by a lane scan over the tile
+// sums, then the id inside it.  Returns the id in every thread.
 __device__ int walk_pick(const WalkRows& w, int V, bool useq, double aa, double u, double tot,
                          const double* s_tile, int* s_out) {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -1062,7 +1122,9 @@ __device__ int walk_pick(const WalkRows& w, int V, bool useq, double aa, double 
 __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
     const ddt_tree& t = a.t;
     const ddt_flat& f = a.f;
-    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int G = a.G;                                 // workgroups per request (T > 0 walk)
+    const int b = blockIdx.x / G, g = blockIdx.x - (blockIdx.x / G) * G;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int P = f.P, Dp = f.Dp;
     __shared__ int s_am[MK_NT];
     __shared__ float s_M[MK_NT], s_S[MK_NT];
@@ -1076,10 +1138,13 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
     __shared__ unsigned long long s_best;
     __shared__ uint64_t s_mscr[VF_NT / 64][MRG_SCR];
     __shared__ int32_t s_ret[VF_RET];
+    __shared__ double s_bc[2];
+    __shared__ int s_err;
     const int m = min(max(f.m[b], 0), P - 1);
     const int n = m + 1;
     const size_t fo = (size_t)b * P;
     const float T = a.temperature[b];
+    if (!(T > 0.f) && g != 0) return;                  // greedy rows: one workgroup
     const int Lr = min(max(f.n_leaves[b], 0), f.L);
     const bool ret_lds = Lr * (Dp + 1) <= VF_RET;
     // greedy: the candidate paths go to LDS in the same round as the merges
@@ -1095,14 +1160,14 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
         const int am = __shfl(vkey_id(mine), 0);
         if (lane == 0) {
             s_am[i] = am; s_M[i] = M; s_S[i] = Sp;
-            if (a.row_argmax) a.row_argmax[fo + i] = am;
+            if (a.row_argmax && g == 0) a.row_argmax[fo + i] = am;
         }
-        if (a.row_topk && lane < a.k_top) a.row_topk[(fo + i) * a.k_top + lane] = vkey_id(mine);
+        if (a.row_topk && g == 0 && lane < a.k_top) a.row_topk[(fo + i) * a.k_top + lane] = vkey_id(mine);
     }
     for (int i = tid; i < P; i += VF_NT) {
         s_fp[i] = i < n ? f.parent[fo + i] : -1;
         s_ft[i] = i < n ? f.token[fo + i] : -1;
-        if (i >= n) {                                  // padding positions carry -1
+        if (i >= n && g == 0) {                        // padding positions carry -1
             if (a.row_argmax) a.row_argmax[fo + i] = -1;
             for (int k = 0; a.row_topk && k < a.k_top; ++k) a.row_topk[(fo + i) * a.k_top + k] = -1;
         }
@@ -1151,10 +1216,23 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
     // T > 0: sibling walk with residual resampling
     const double kT = (double)DDT_LOG2E_D / (double)T;
     const float* Ub = a.U + fo * 2;
-    if (tid == 0) { s_u = 0; s_len = 0; s_path[0] = 0; }
+    const int ntiles = (a.V + VF_TILE - 1) / VF_TILE;
+    RowSync rs;
+    rs.buf = t.walk_buf + (size_t)b * DDT_WALK_STRIDE;
+    rs.tiles = rs.buf + 4 * 32;
+    rs.cnt = t.walk_sync + 2 * (size_t)b;
+    rs.G = G; rs.g = g; rs.k = 0;
+    {
+        const int tpw = (ntiles + G - 1) / G;
+        rs.t_lo = min(g * tpw, ntiles);
+        rs.t_hi = min(rs.t_lo + tpw, ntiles);
+        rs.lo = rs.t_lo * VF_TILE;
+        rs.hi = min(a.V, rs.t_hi * VF_TILE);
+    }
+    if (tid == 0) { s_u = 0; s_len = 0; s_path[0] = 0; s_err = 0; s_next = 0; }
     if (tid < 64) s_e2t[tid] = exp2((double)tid / 64.0);
     __syncthreads();
-    while (true) {
+    while (!s_err) {
         const int u = s_u;
         if (tid == 0) {
             int c = 0;
@@ -1197,7 +1275,7 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
             w.lzt = 0.0;                               // sums of the unnormalised rows
             w.lzd = 0.0;
             double Zt, Zd;
-            walk_norms(w, a.V, s_red, Zt, Zd);
+            walk_norms(w, rs, s_red, s_bc, &s_err, a.V, Zt, Zd);
             w.lzt = log2(Zt);
             w.lzd = log2(Zd);
             zexact = true;
@@ -1212,10 +1290,10 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
         }
         double ra = 0.0, rb = 1.0;                      // residual p_k = max(0, p - ra q) / rb
         int accepted = -1;
-        bool tiles_ready = false;                       // s_tile holds the current residual's weights
+        bool tiles_ready = false;                       // the tiles hold the current residual's weights
         double tiles_tot = 0.0;
         if (has_q) {
-            for (int ci = 0; ci < nch; ++ci) {
+            for (int ci = 0; ci < nch && !s_err; ++ci) {
                 const int c = s_ch[ci];
                 if (tid == 0) {
                     const int x = min(max(s_ft[c], 0), a.V - 1);
@@ -1233,17 +1311,18 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
                 const double an = ra + rb;
                 double F;
                 if (ci == nch - 1) {
-                    F = walk_tiles(w, a.V, true, an, s_tile, s_red);
+                    F = walk_tiles(w, rs, s_red, s_bc, &s_err, a.V, true, an, s_tile);
                     tiles_ready = F > 0.0;
                     tiles_tot = F;
                 } else {
-                    F = walk_pass<true>(w, a.V, s_red, [&](float tv, float dv) {
+                    F = walk_pass<true>(w, rs, s_red, s_bc, &s_err, a.V, [&](float tv, float dv) {
                         return fmax(0.0, walk_p(w, tv) - an * walk_q(w, dv));
                     });
                 }
                 if (F > 0.0) { ra = an; rb = F; }
             }
         }
+        if (s_err) break;
         if (accepted >= 0) {
             if (tid == 0) { s_u = accepted; s_path[++s_len] = accepted; }
             __syncthreads();
@@ -1252,16 +1331,30 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
         // emission from the current residual by inverse CDF with U[u][1] over
         // the unnormalised weights max(0, p - a q) (p at a leaf); the threshold
         // scales with their total
-        if (!tiles_ready) tiles_tot = walk_tiles(w, a.V, has_q, ra, s_tile, s_red);
-        const int nx = walk_pick(w, a.V, has_q, ra, (double)Ub[2 * u + 1], tiles_tot, s_tile, &s_next);
-        (void)nx;
+        if (!tiles_ready) tiles_tot = walk_tiles(w, rs, s_red, s_bc, &s_err, a.V, has_q, ra, s_tile);
+        if (s_err) break;
+        if (g == 0) {
+            if (G > 1)                                 // the other workgroups' tiles
+                for (int q = tid; q < ntiles; q += VF_NT)
+                    s_tile[q] = __hip_atomic_load(rs.tiles + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            walk_pick(w, a.V, has_q, ra, (double)Ub[2 * u + 1], tiles_tot, s_tile, &s_next);
+        }
         break;
     }
-    if (tid == 0) {
-        const int len = s_len;
+    if (g == 0 && tid == 0) {
+        const int len = s_err ? -1 : s_len;
         for (int s2 = 0; s2 <= Dp; ++s2) apath[s2] = s2 <= len ? s_path[s2] : -1;
         a.accept_len[b] = len;
-        a.next_token[b] = s_next;
+        a.next_token[b] = s_err ? -1 : s_next;
+    }
+    if (G > 1 && tid == 0) {
+        // the last workgroup of the request to leave returns the counters to 0
+        __threadfence();
+        if (atomicAdd(rs.cnt + 1, 1u) == (uint32_t)G - 1) {
+            atomicExch(rs.cnt, 0u);
+            atomicExch(rs.cnt + 1, 0u);
+        }
     }
 }
 

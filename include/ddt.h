@@ -66,6 +66,7 @@ extern "C" {
 #define DDT_MAX_NODES 4096  /* nodes per row (draft + retrieval, root included) */
 #define DDT_MAX_VERIFY 255  /* draft nodes sent to verification per row */
 #define DDT_MAX_CHUNKS 64   /* vocab chunks per row: V <= 64*8192 (bf16), 64*4096 (f32) */
+#define DDT_WALK_STRIDE 2176 /* doubles per request in walk_buf: 2 x 32 x 2 pass sums + 2048 tile sums */
 
 /*
  * Canonical node key (uint64): bits 62..59 depth, bit 58 source (0 draft,
@@ -118,6 +119,8 @@ typedef struct ddt_tree {
     int32_t* widths;     /* [D_max] CAST: width n_i chosen at layer i (0 for layers not built) */
     double* cast_state;  /* [16] CAST per-round state (gain FIFO, utility, context) */
     uint32_t* ticket;    /* [1] CAST: workgroups of a layer done so far (back to 0 after each layer) */
+    double* walk_buf;    /* [B][DDT_WALK_STRIDE] T>0 verify: partial sums shared by a request's workgroups */
+    uint32_t* walk_sync; /* [B][2] T>0 verify: arrival and exit counters (back to 0 after each call) */
 } ddt_tree;
 
 /* Bytes of device memory a tree of these sizes needs (256-byte aligned base). */
@@ -126,9 +129,9 @@ size_t ddt_tree_bytes(int B, int cap, int D_max, int R_max);
 /*
  * Fill *t with pointers into `base` (device, >= ddt_tree_bytes, 256-byte
  * aligned).  Host-only: touches no device memory.  The memory must be
- * zero-filled once before its first use (the CAST layer counter starts at 0
- * and every call leaves it at 0); the tree itself is (re)initialised by
- * ddt_tree_expand with layer = 1.
+ * zero-filled once before its first use (the CAST layer counter and the T>0
+ * walk counters start at 0 and every call leaves them at 0); the tree itself
+ * is (re)initialised by ddt_tree_expand with layer = 1.
  */
 int ddt_tree_bind(ddt_tree* t /*host*/, void* base, size_t bytes, int B, int cap, int D_max,
                   int R_max);
@@ -307,6 +310,11 @@ int ddt_tree_build_mask(const ddt_tree* t /*host*/, const int32_t* sel, const in
  * Both hold -1 at padding positions (past f->m[b]).
  * accept_len [B]; accept_path [B][Dp+1] flat indices root first, -1 padded;
  * next_token [B].  ws >= ddt_workspace_bytes(B*P, V, dtype, max(1,k_top)).
+ * A T > 0 request's vocabulary passes may be split over several workgroups
+ * that exchange partial sums through t->walk_buf / t->walk_sync; they wait
+ * for each other with a bounded spin.  If that wait ever runs out (the
+ * workgroups were not resident together), the request's accept_len and
+ * next_token are set to -1.
  */
 int ddt_tree_verify(const ddt_tree* t /*host*/, const ddt_flat* f /*host*/,
                     const ddt_logits* target /*host*/, const ddt_logits* draft /*host or NULL*/,
