@@ -183,9 +183,17 @@ def cpu_baseline(w, slot, cast_np, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
+    cpu = "unknown cpu"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": n / el, "unit": "rounds/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} rounds of the same workload (ring slot 0, {el:.1f} s, single thread, "
-                      f"float64 numpy; input generation excluded)"}
+            "sample": f"{n} rounds of the same workload (ring slot 0, {el:.1f} s, single thread "
+                      f"of {os.cpu_count()} on {cpu}, float64 numpy; input generation excluded)"}
 
 
 def main():
@@ -390,6 +398,37 @@ def main():
     log(f"row reduction: {len(durs)} launches, mean {durs.mean() * 1e6:.2f} us, "
         f"{nbytes.mean() / 1e6:.2f} MB/launch, {achieved:.0f} GB/s")
 
+    # ---- per-round spread: replays bracketed one by one ----------------------
+    nspread = 100
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nspread)]
+    for i in range(nspread):
+        sev[2 * i].record()
+        graphs[i % R].replay()
+        sev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    per_round_us = np.array([sev[2 * i].elapsed_time(sev[2 * i + 1]) * 1e3 for i in range(nspread)])
+
+    # ---- the same reduction over all of a round's draft rows in one launch ----
+    # (streaming efficiency without the layer-to-layer dependence)
+    arena = ring[0]["draft"]
+    flat_rows = arena.reshape(-1, arena.shape[-2], w.V)          # [D*B][R][V]
+    nrows = flat_rows.shape[0] * flat_rows.shape[1]
+    ws_b = torch.empty(api.workspace_bytes(nrows, w.V, tdt, w.K_n), dtype=torch.uint8, device=dev)
+    nb = 10
+    bev = hip.events(2 * nb)
+    barr = (C.c_void_p * len(bev))(*[e.value for e in bev])
+    api.row_topk(flat_rows, w.K_n, ws_b)
+    torch.cuda.synchronize()
+    lib.ddt_set_reduce_events(barr, nb)
+    for _ in range(nb):
+        api.row_topk(flat_rows, w.K_n, ws_b)
+    lib.ddt_set_reduce_events(None, 0)
+    torch.cuda.synchronize()
+    bd = np.array([hip.elapsed_ms(bev[2 * i], bev[2 * i + 1]) * 1e-3 for i in range(nb)])
+    batched_bytes = nrows * w.V * (2 if w.dtype == "bf16" else 4)
+    batched_gbs = batched_bytes / bd.mean() / 1e9
+    del ws_b
+
     # ---- algorithmic logit bytes per round ----------------------------------
     expand_bytes = np.mean([sum(s["rows_per_layer"]) for s in stats]) * ebytes
     walk_bytes = np.mean([s["walk_rows"] for s in stats]) * ebytes
@@ -423,6 +462,11 @@ def main():
         "logit_frac_of_peak": round(logit_gbs / PEAK_HBM_GBS, 4),
         "detail": {
             "gpu_event_us_per_round": round(gpu_ms * 1e3 / K, 2),
+            "round_us_p10_p50_p90": [round(float(np.percentile(per_round_us, q)), 2) for q in (10, 50, 90)],
+            "rows_batched_reduction": {"rows": int(nrows), "mb": round(batched_bytes / 1e6, 1),
+                                       "us": round(float(bd.mean() * 1e6), 2),
+                                       "gbs": round(float(batched_gbs), 1),
+                                       "frac": round(float(batched_gbs / PEAK_HBM_GBS), 4)},
             "eager_us_per_round": round(eager_us, 2),
             "expand_mb_per_round": round(expand_bytes / 1e6, 3),
             "verify_walk_mb_per_round": round(walk_bytes / 1e6, 3),
