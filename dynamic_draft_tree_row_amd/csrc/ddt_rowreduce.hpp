@@ -320,8 +320,13 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
 // that test (typically little more than K of the groups * K) are ranked by
 // counting.  When more than MRG_CAP pass (long runs of equal values) the top K
 // is taken in K max-extraction rounds.
+//
+// live = false (a slot whose partials are not current): the loads are still
+// issued, so a caller can request them before the value that decides
+// liveness has arrived, and the wave returns M = -inf, sigma' = 0, no keys.
 __device__ __forceinline__ uint64_t merge_row_wave(const uint32_t* __restrict__ p, int groups, int K,
-                                                   float& M, float& Sp, uint64_t* scr) {
+                                                   float& M, float& Sp, uint64_t* scr,
+                                                   bool live = true) {
     constexpr int MR = 4;                              // keys held in registers per lane
     const int lane = threadIdx.x & (DDT_WAVE - 1);
     const int PS = rr_ps(K);
@@ -348,6 +353,15 @@ __device__ __forceinline__ uint64_t merge_row_wave(const uint32_t* __restrict__ 
             const int c = q / K, e = q - c * K;
             kk[r] = *(const uint64_t*)(p + c * PS + 2 + 2 * e);
         }
+    }
+    // the loads stay ahead of the liveness test (no sinking into the branch)
+    asm volatile("" : "+v"(mc), "+v"(sc), "+v"(hv));
+#pragma unroll
+    for (int r = 0; r < MR; ++r) asm volatile("" : "+v"(kk[r]));
+    if (!live) {
+        M = -INFINITY;
+        Sp = 0.f;
+        return 0ull;
     }
     M = unord_f32(wave_max_u32(lane < groups ? ord_f32(mc) : 0u));
     // T: the K-th largest sampled value code, bit by bit over the top 16 bits

@@ -93,9 +93,7 @@ __device__ int anchor_scan_wave(const double* u, const double* c, double C, int 
 struct CastLds {
     double v[64 * DDT_MAX_FRONT];
     float sd[DDT_CAST_MAX_M * DDT_MAX_FRONT], st1[DDT_CAST_MAX_M];
-    double c[DDT_MAX_FRONT + 1], u[DDT_MAX_FRONT + 1];
     double st[11];
-    int kcap, n;
 };
 
 template <int NT>
@@ -114,81 +112,132 @@ __device__ void cast_stage(CastLds& L, const ddt_tree& t, const ddt_cast& cp, in
     for (int r = tid; r < cp.M; r += NT) L.st1[r] = cp.S_T[(size_t)r * (cp.N + 1) + 1];
 }
 
-// The batch rule, once L.v[b * R_max + k] = e^S of row b's k-th frontier node
-// (k < kcap) and the staged inputs are in LDS: width by the anchor scan on the
-// batch-averaged cumulative utility, then the depth gate with the gain FIFO;
-// every row's n_front gets the result.
-template <int NT>
-__device__ void cast_decide(CastLds& L, const ddt_tree& t, const ddt_cast& cp, int layer, int kcap) {
-    const int tid = threadIdx.x, lane = tid & 63, B = t.B, R = t.R_max;
-    double* st = t.cast_state;
-    if (layer == 1)
-        for (int i = tid; i < t.D_max; i += NT) t.widths[i] = 0;
-    const int ctx = (int)L.st[10];
-    const int row = cast_sel_row(ctx, cp.L, cp.M);
-    if (tid < DDT_WAVE) {
-        // column means of e^S, prefix-summed across lanes (kcap <= 32)
-        double mean = 0.0;
-        if (lane < kcap) {
-            for (int b = 0; b < B; ++b) mean += L.v[b * R + lane];
-            mean *= 1.0 / (double)B;
-        }
-        double incl = mean;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const double o = __shfl_up(incl, d);
-            if (lane >= d) incl += o;
-        }
-        if (lane < kcap) {
-            L.u[lane + 1] = incl;
-            L.c[lane + 1] = (double)L.sd[row * R + lane] / (double)L.st1[row];
-        }
-        if (lane == 0) { L.u[0] = 0.0; L.c[0] = 0.0; }
-        wave_lds_sync();
-        const int n = anchor_scan_wave(L.u, L.c, (double)cp.C1[layer - 1], kcap);
-        if (tid == 0) {
-            double* fifo = L.st;                       // entries 0..7
-            int len = (int)L.st[8];
-            const double prev = L.st[9];
-            if (prev >= 0.0) {                         // push the previous layer's gain ratio
-                const double phi = prev > 0.0 ? L.u[n] / prev : 0.0;
-                if (len < 8) fifo[len++] = phi;
-                if (len > cp.R) {
-                    for (int i = 1; i < len; ++i) fifo[i - 1] = fifo[i];
-                    --len;
-                }
-            }
-            double fm = 0.0;
-            for (int i = 0; i < len; ++i) fm += fifo[i];
-            fm /= (double)len;
-            const double score = n > 0 ? fm * L.u[n] / L.c[n] : 0.0;
-            const bool stop = (layer >= t.D_max) || !(score >= (double)cp.C2);
-            for (int i = 0; i < 8; ++i) st[i] = fifo[i];
-            st[8] = (double)len;
-            st[9] = L.u[n];
-            st[10] = (double)(ctx + n);
-            t.widths[layer - 1] = n;
-            t.cont[0] = stop ? 0 : 1;
-            L.n = stop ? 0 : n;
-        }
-    }
-    __syncthreads();
-    for (int b = tid; b < B; b += NT) t.n_front[b] = L.n;
+// Wave-level helpers for the batch rule (wave 0, all 64 lanes active).
+// x from lane l (l wave-uniform), through scalar registers.
+__device__ __forceinline__ double readlane_f64(double x, int l) {
+    const uint64_t b = (uint64_t)__double_as_longlong(x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// DPP move of a double (both halves); lanes without a source, and rows
+// outside RM, read 0.
+template <int CTRL, int RM>
+__device__ __forceinline__ double dpp_f64(double x) {
+    const uint64_t b = (uint64_t)__double_as_longlong(x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, RM, 0xF, true);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, RM, 0xF, true);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// Inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 inside each
+// row of 16, then the totals of earlier rows by broadcast.
+__device__ __forceinline__ double wave_incl_scan_f64(double x) {
+    x += dpp_f64<0x111, 0xF>(x);
+    x += dpp_f64<0x112, 0xF>(x);
+    x += dpp_f64<0x114, 0xF>(x);
+    x += dpp_f64<0x118, 0xF>(x);
+    x += dpp_f64<0x142, 0xA>(x);
+    x += dpp_f64<0x143, 0xC>(x);
+    return x;
 }
 
-// The batch rule in the last workgroup of a multi-workgroup layer: loads the
-// rows' frontier values and counts first.
+// The batch rule, run by wave 0 of the layer's last workgroup once
+// L.v[b * R_max + k] = e^S of row b's k-th frontier node is in LDS (k < kcap
+// <= 32): width by the anchor scan on the batch-averaged cumulative utility,
+// then the depth gate with the gain FIFO; every row's n_front gets the
+// result.  Item k (1-based) lives in lane k - 1: u_k, c_k in registers; the
+// anchor scan works on ballot masks and the FIFO on lanes 0..7.
+__device__ void cast_decide(CastLds& L, const ddt_tree& t, const ddt_cast& cp, int layer, int kcap) {
+    const int lane = threadIdx.x & (DDT_WAVE - 1), B = t.B, R = t.R_max;
+    if (layer == 1 && lane < t.D_max) t.widths[lane] = 0;
+    const int ctx = (int)L.st[10];
+    const int row = cast_sel_row(ctx, cp.L, cp.M);
+    const bool item = lane < kcap;
+    // column means of e^S, prefix-summed across lanes
+    double mean = 0.0;
+    if (item) {
+        for (int b = 0; b < B; ++b) mean += L.v[b * R + lane];
+        mean *= 1.0 / (double)B;
+    }
+    const double u = wave_incl_scan_f64(mean);
+    const double c = item ? (double)L.sd[row * R + lane] / (double)L.st1[row] : 0.0;
+    // anchor scan: keep 1, move the anchor a to k when u_k - u_a >= C (c_k - c_a)
+    // (a non-increasing cost step moves it when utility grows)
+    const double C = (double)cp.C1[layer - 1];
+    const double up = __shfl_up(u, 1), cpv = __shfl_up(c, 1);
+    const bool adj_moves = (c - cpv) > 0.0 ? (u - up) >= C * (c - cpv) : (u - up) > 0.0;
+    // bit k-1 set: items k-1 -> k is a step the anchor does not take
+    const uint64_t stop_adj = __ballot(lane >= 1 && item && !adj_moves);
+    int n = 0;
+    if (kcap > 0) {
+        int a = 1, k0 = 2;
+        while (k0 <= kcap) {
+            if (a == k0 - 1) {
+                const uint64_t m = stop_adj & (~0ull << (k0 - 1));
+                if (!m) { a = kcap; break; }
+                const int hit = __ffsll((unsigned long long)m);      // lane + 1 = item
+                a = hit - 1;
+                k0 = hit + 1;
+            } else {
+                const double ua = readlane_f64(u, a - 1), ca = readlane_f64(c, a - 1);
+                const double du = u - ua, dc = c - ca;
+                const bool mv = dc > 0.0 ? du >= C * dc : du > 0.0;
+                const uint64_t m = __ballot(item && lane + 1 >= k0 && mv);
+                if (!m) break;
+                a = __ffsll((unsigned long long)m);
+                k0 = a + 1;
+            }
+        }
+        n = a;
+    }
+    const double un = n > 0 ? readlane_f64(u, n - 1) : 0.0;
+    const double cn = n > 0 ? readlane_f64(c, n - 1) : 0.0;
+    // gain FIFO (entries 0..7 of the state, one per lane), length, previous u_n
+    double f = lane < 8 ? L.st[lane] : 0.0;
+    int len = (int)L.st[8];
+    const double prev = L.st[9];
+    if (prev >= 0.0) {                                  // push the previous layer's gain ratio
+        const double phi = prev > 0.0 ? un / prev : 0.0;
+        if (len < 8) {
+            if (lane == len) f = phi;
+            ++len;
+        }
+        if (len > cp.R) {
+            const double g = __shfl_down(f, 1);
+            if (lane < len - 1) f = g;
+            --len;
+        }
+    }
+    double fm = 0.0;
+    for (int i = 0; i < len; ++i) fm += readlane_f64(f, i);
+    fm /= (double)len;
+    const double score = n > 0 ? fm * un / cn : 0.0;
+    const bool stop = (layer >= t.D_max) || !(score >= (double)cp.C2);
+    double* st = t.cast_state;
+    if (lane < 8) st[lane] = f;
+    if (lane == 8) st[8] = (double)len;
+    if (lane == 9) st[9] = un;
+    if (lane == 10) st[10] = (double)(ctx + n);
+    if (lane == 0) {
+        t.widths[layer - 1] = n;
+        t.cont[0] = stop ? 0 : 1;
+    }
+    if (lane < B) t.n_front[lane] = stop ? 0 : n;
+}
+
+// The batch rule in the last workgroup of a layer: every thread loads the
+// rows' frontier values, wave 0 the row counts; then wave 0 decides.
 template <int NT>
 __device__ void cast_layer(CastLds& L, const ddt_tree& t, const ddt_cast& cp, int layer, int K_e) {
     const int tid = threadIdx.x, B = t.B, R = t.R_max;
-    if (tid == 0) L.kcap = min(K_e, R);
     for (int q = tid; q < B * R; q += NT) L.v[q] = (double)expf(t.front_S[q]);
     int cnt = 0x7FFFFFFF;
     if (tid < B) cnt = max(0, t.n_nodes[tid] - t.layer_base[tid]);
     __syncthreads();
-    if (tid < B) atomicMin(&L.kcap, cnt);
-    __syncthreads();
-    cast_decide<NT>(L, t, cp, layer, L.kcap);
+    if (tid < DDT_WAVE) {
+        const int kc = (int)wave_min_u32((uint32_t)cnt);
+        cast_decide(L, t, cp, layer, min(min(K_e, R), kc));
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -263,12 +312,14 @@ __global__ __launch_bounds__(AT_NT) void k_attach(AttachArgs a) {
         if (tid == 0) { s_nf = t.n_front[b]; s_nn = t.n_nodes[b]; }
     }
     if (a.cast_on) cast_stage<AT_NT>(s_cast, t, a.c, a.layer);
-    // merges: wave j takes slot j (slots past the row's frontier width hold no
-    // partials of this layer and are ignored below)
+    // merges: wave j takes slot j.  Slots past the row's frontier width hold no
+    // partials of this layer: their loads go out with the others, and the
+    // width, loaded in the same round, stops the merge work there.
+    const int nf_w = a.layer == 1 ? 1 : t.n_front[b];
     for (int j = wid; j < a.R; j += AT_NT / 64) {
         float M, Sp;
         const uint32_t* p = a.part + ((size_t)(b * a.R + j) * a.chunks) * rr_ps(Kn);
-        const uint64_t mine = merge_row_wave(p, a.chunks, Kn, M, Sp, s_scr[wid]);
+        const uint64_t mine = merge_row_wave(p, a.chunks, Kn, M, Sp, s_scr[wid], j < nf_w);
         if (lane < Kn) s_key[j * Kn + lane] = mine;
         if (lane == 0) { s_M[j] = M; s_S[j] = Sp; s_l1p[j] = log1pf(Sp); }
     }
