@@ -98,8 +98,16 @@ def same(a, b) -> bool:
     return all(torch.equal(a[k], b[k]) for k in a)
 
 
+KERNEL_END = "#undef RR_ID\n}\n"   # the end of k_row_partial in its source file
+
+
 def kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the row-reduction kernel's source: its file up to the end of
+    k_row_partial, which holds the kernel and every helper it calls (the
+    consumers' merge code that follows does not change its traffic)."""
+    text = open(KERNEL_SRC, "rb").read().decode()
+    end = text.index(KERNEL_END) + len(KERNEL_END)
+    return hashlib.sha256(text[:end].encode()).hexdigest()[:16]
 
 
 def traffic_per_launch(workload: str):
