@@ -321,48 +321,67 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
 // counting.  When more than MRG_CAP pass (long runs of equal values) the top K
 // is taken in K max-extraction rounds.
 //
-// live = false (a slot whose partials are not current): the loads are still
-// issued, so a caller can request them before the value that decides
-// liveness has arrived, and the wave returns M = -inf, sigma' = 0, no keys.
-__device__ __forceinline__ uint64_t merge_row_wave(const uint32_t* __restrict__ p, int groups, int K,
-                                                   float& M, float& Sp, uint64_t* scr,
-                                                   bool live = true) {
-    constexpr int MR = 4;                              // keys held in registers per lane
+// The merge is split in two so that a kernel can request the partials of its
+// rows together with its other inputs: merge_issue only issues the loads,
+// merge_finish waits for them and merges.  live = false (a slot whose
+// partials are not current): the wave returns M = -inf, sigma' = 0, no keys.
+#define MRG_MR 4                         // keys held in registers per lane
+
+struct MergeIn {
+    float mc, sc;                        // group max and sigma' (lane < groups)
+    uint32_t hv;                         // sampled value code (K > 1)
+    uint64_t kk[MRG_MR];                 // keys lane + 64 r, when they fit
+};
+
+// Every lane loads, from a clamped address inside the row's partials, so that
+// the loads are straight-line code: a load under a branch ends in a register
+// copy that waits for it.  merge_finish masks the lanes past the data.
+__device__ __forceinline__ void merge_issue(const uint32_t* __restrict__ p, int groups, int K,
+                                            MergeIn& in) {
     const int lane = threadIdx.x & (DDT_WAVE - 1);
     const int PS = rr_ps(K);
     const int jth = (K + groups - 1) / groups;         // 1 <= jth <= K
     const int total = groups * K;
-    const bool fits = total <= MR * DDT_WAVE;
-    float mc = -INFINITY, sc = 0.f;
-    if (lane < groups) {
-        mc = __uint_as_float(p[lane * PS]);
-        sc = __uint_as_float(p[lane * PS + 1]);
-    }
+    const int gl = lane < groups ? lane : 0;
+    in.mc = __uint_as_float(p[gl * PS]);
+    in.sc = __uint_as_float(p[gl * PS + 1]);
     // sample: the jth best keys of every group (groups * jth <= 64 lanes)
-    uint32_t hv = 0u;
-    if (lane < groups * jth) {
-        const int c = lane / jth, e = lane - c * jth;
-        hv = p[c * PS + 2 + 2 * e + 1];                // high word (value code)
-    }
-    uint64_t kk[MR];
+    const int hl = lane < groups * jth ? lane : 0;
+    const int hc = hl / jth, he = hl - hc * jth;
+    in.hv = p[hc * PS + 2 + 2 * he + 1];               // high word (value code)
 #pragma unroll
-    for (int r = 0; r < MR; ++r) {
+    for (int r = 0; r < MRG_MR; ++r) {
         const int q = lane + r * DDT_WAVE;
-        kk[r] = 0ull;
-        if (fits && q < total) {
-            const int c = q / K, e = q - c * K;
-            kk[r] = *(const uint64_t*)(p + c * PS + 2 + 2 * e);
-        }
+        const int qc = q < total ? q : 0;
+        const int c = qc / K, e = qc - c * K;
+        in.kk[r] = *(const uint64_t*)(p + c * PS + 2 + 2 * e);
     }
-    // the loads stay ahead of the liveness test (no sinking into the branch)
-    asm volatile("" : "+v"(mc), "+v"(sc), "+v"(hv));
+}
+
+__device__ __forceinline__ uint64_t merge_finish(MergeIn& in, const uint32_t* __restrict__ p,
+                                                 int groups, int K, float& M, float& Sp,
+                                                 uint64_t* scr, bool live) {
+    const int lane = threadIdx.x & (DDT_WAVE - 1);
+    const int PS = rr_ps(K);
+    const int jth = (K + groups - 1) / groups;
+    const int total = groups * K;
+    const bool fits = total <= MRG_MR * DDT_WAVE;
+    // the loads stay ahead of this point (no sinking into the branch below)
+    asm volatile("" : "+v"(in.mc), "+v"(in.sc), "+v"(in.hv));
 #pragma unroll
-    for (int r = 0; r < MR; ++r) asm volatile("" : "+v"(kk[r]));
+    for (int r = 0; r < MRG_MR; ++r) asm volatile("" : "+v"(in.kk[r]));
     if (!live) {
         M = -INFINITY;
         Sp = 0.f;
         return 0ull;
     }
+    const float mc = lane < groups ? in.mc : -INFINITY;
+    const float sc = lane < groups ? in.sc : 0.f;
+    const uint32_t hv = K > 1 && lane < groups * jth ? in.hv : 0u;
+    constexpr int MR = MRG_MR;
+    uint64_t kk[MR];
+#pragma unroll
+    for (int r = 0; r < MR; ++r) kk[r] = fits && lane + r * DDT_WAVE < total ? in.kk[r] : 0ull;
     M = unord_f32(wave_max_u32(lane < groups ? ord_f32(mc) : 0u));
     // T: the K-th largest sampled value code, bit by bit over the top 16 bits
     // (a lower T only admits a few more candidates); K = 1 needs none
@@ -431,4 +450,46 @@ __device__ __forceinline__ uint64_t merge_row_wave(const uint32_t* __restrict__ 
         prev = best;
     }
     return mine;
+}
+
+// K = 1 (argmax rows): the group maxima, sums and head keys only.
+struct MergeIn1 {
+    float mc, sc;
+    uint64_t k0;
+};
+
+// Straight-line loads from clamped addresses, as in merge_issue.
+__device__ __forceinline__ void merge1_issue(const uint32_t* __restrict__ p, int groups, MergeIn1& in) {
+    const int lane = threadIdx.x & (DDT_WAVE - 1);
+    constexpr int PS = 2 + 2 * 1;
+    const int gl = lane < groups ? lane : 0;
+    in.mc = __uint_as_float(p[gl * PS]);
+    in.sc = __uint_as_float(p[gl * PS + 1]);
+    in.k0 = *(const uint64_t*)(p + gl * PS + 2);
+}
+
+// The K = 1 merge_finish: lane 0 returns the row's best key.
+__device__ __forceinline__ uint64_t merge1_finish(const MergeIn1& in, int groups, float& M, float& Sp) {
+    const int lane = threadIdx.x & (DDT_WAVE - 1);
+    const bool on = lane < groups;
+    const float mc = on ? in.mc : -INFINITY;
+    M = unord_f32(wave_max_u32(on ? ord_f32(mc) : 0u));
+    const uint64_t mm = __ballot(on && mc == M);
+    const int cstar = mm ? __ffsll((unsigned long long)mm) - 1 : -1;
+    float contrib = 0.f;
+    if (on && mc > -INFINITY) {
+        const float e = exp2f((mc - M) * DDT_LOG2E);
+        contrib = in.sc * e + (lane != cstar ? e : 0.f);
+    }
+    Sp = wave_sumf(contrib);
+    const uint64_t best = wave_max_key(on ? in.k0 : 0ull);
+    return lane == 0 ? best : 0ull;
+}
+
+__device__ __forceinline__ uint64_t merge_row_wave(const uint32_t* __restrict__ p, int groups, int K,
+                                                   float& M, float& Sp, uint64_t* scr,
+                                                   bool live = true) {
+    MergeIn in;
+    merge_issue(p, groups, K, in);
+    return merge_finish(in, p, groups, K, M, Sp, scr, live);
 }

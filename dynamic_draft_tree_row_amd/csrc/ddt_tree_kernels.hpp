@@ -96,20 +96,39 @@ struct CastLds {
     double st[11];
 };
 
+// The staged inputs in registers between their loads and their LDS stores.
+// Every thread loads from a clamped address (straight-line code: a load under
+// a branch ends in a register copy that waits for it); cast_store keeps what
+// is in range.
+struct CastIn {
+    double st;                           // state entry min(tid, 10)
+    float sd0, sd1, st1;                 // cost entries tid and tid + NT, S_T[tid][1]
+};
+
 template <int NT>
-__device__ void cast_stage(CastLds& L, const ddt_tree& t, const ddt_cast& cp, int layer) {
-    const int tid = threadIdx.x, R = t.R_max;
+__device__ void cast_issue(CastIn& ci, const ddt_tree& t, const ddt_cast& cp, int layer) {
+    static_assert(2 * NT >= DDT_CAST_MAX_M * DDT_MAX_FRONT, "two cost entries per thread");
+    const int tid = threadIdx.x, R = t.R_max, MR = cp.M * R, N = cp.N;
+    ci.st = t.cast_state[tid < 11 ? tid : 10];
+    const int q0 = tid < MR ? tid : 0, q1 = tid + NT < MR ? tid + NT : 0;
+    const int r0 = q0 / R, k0 = min(q0 - r0 * R, N - 1);
+    const int r1 = q1 / R, k1 = min(q1 - r1 * R, N - 1);
+    ci.sd0 = cp.S_D[(size_t)r0 * (N + 1) + k0 + 1];
+    ci.sd1 = cp.S_D[(size_t)r1 * (N + 1) + k1 + 1];
+    ci.st1 = cp.S_T[(size_t)(tid < cp.M ? tid : 0) * (N + 1) + 1];
+}
+
+template <int NT>
+__device__ void cast_store(CastLds& L, const CastIn& ci, const ddt_tree& t, const ddt_cast& cp,
+                           int layer) {
+    const int tid = threadIdx.x, R = t.R_max, MR = cp.M * R;
     if (tid < 11) {
-        double v;
-        if (layer == 1) v = tid == 0 ? 1.0 : tid == 8 ? 1.0 : tid == 9 ? -1.0 : 0.0;
-        else v = t.cast_state[tid];
-        L.st[tid] = v;
+        // layer 1 starts the state: FIFO {1}, length 1, no previous u_n, context 0
+        L.st[tid] = layer > 1 ? ci.st : tid == 0 ? 1.0 : tid == 8 ? 1.0 : tid == 9 ? -1.0 : 0.0;
     }
-    for (int q = tid; q < cp.M * R; q += NT) {
-        const int r = q / R, k = q - r * R;
-        L.sd[q] = k < cp.N ? cp.S_D[(size_t)r * (cp.N + 1) + k + 1] : 0.f;
-    }
-    for (int r = tid; r < cp.M; r += NT) L.st1[r] = cp.S_T[(size_t)r * (cp.N + 1) + 1];
+    if (tid < MR) L.sd[tid] = tid % R < cp.N ? ci.sd0 : 0.f;
+    if (tid + NT < MR) L.sd[tid + NT] = (tid + NT) % R < cp.N ? ci.sd1 : 0.f;
+    if (tid < cp.M) L.st1[tid] = ci.st1;
 }
 
 // Wave-level helpers for the batch rule (wave 0, all 64 lanes active).
@@ -282,7 +301,7 @@ __global__ __launch_bounds__(AT_NT) void k_attach(AttachArgs a) {
     __shared__ uint64_t s_key[DDT_MAX_FRONT * DDT_MAX_K];
     __shared__ uint64_t s_sk[AT_SORT];
     __shared__ uint64_t s_scr[AT_NT / 64][MRG_SCR];
-    __shared__ int s_nf, s_nn, s_last;
+    __shared__ int s_last;
     __shared__ CastLds s_cast;
 
     int32_t* tok = t.token + (size_t)b * cap;
@@ -296,7 +315,22 @@ __global__ __launch_bounds__(AT_NT) void k_attach(AttachArgs a) {
     float* frS = t.front_S + (size_t)b * Rm;
     uint64_t* frK = t.front_key + (size_t)b * Rm;
 
-    // round 1: row state and parent records (wave 0 issues these before its merge)
+    // round 1: every global input of the layer is requested before anything
+    // waits on one: the request's counters (scalar), the frontier records, the
+    // CAST inputs and, for wave j, the partials of slot j
+    const int nf0 = a.layer == 1 ? 1 : t.n_front[b];
+    const int nn0 = a.layer == 1 ? 1 : t.n_nodes[b];
+    // (straight-line loads from clamped addresses: a load under a branch ends
+    // in a register copy that waits for it)
+    const int tf = tid < Rm ? tid : 0;
+    const int r_pn = fr[tf];
+    const float r_pS = frS[tf];
+    const uint64_t r_pk = frK[tf];
+    CastIn ci;
+    if (a.cast_on) cast_issue<AT_NT>(ci, t, a.c, a.layer);
+    MergeIn mi;
+    merge_issue(a.part + ((size_t)(b * a.R + (wid < a.R ? wid : 0)) * a.chunks) * rr_ps(Kn), a.chunks, Kn, mi);
+    // LDS staging from registers
     if (a.layer == 1) {
         if (tid == 0) {
             tok[0] = a.root_tok[b]; par[0] = -1; dep[0] = 0; esl[0] = -1; key[0] = 0ull;
@@ -304,28 +338,26 @@ __global__ __launch_bounds__(AT_NT) void k_attach(AttachArgs a) {
             t.active[b] = 1;
             t.k_draft[b] = a.gate_on ? a.K_max : 0;
             if (a.cast_on && b == 0) t.cont[0] = 1;
-            s_nf = 1; s_nn = 1;
             s_pn[0] = 0; s_pS[0] = 0.f; s_pk[0] = 0ull;
         }
-    } else {
-        if (tid < a.R) { s_pn[tid] = fr[tid]; s_pS[tid] = frS[tid]; s_pk[tid] = frK[tid]; }
-        if (tid == 0) { s_nf = t.n_front[b]; s_nn = t.n_nodes[b]; }
+    } else if (tid < a.R) {
+        s_pn[tid] = r_pn; s_pS[tid] = r_pS; s_pk[tid] = r_pk;
     }
-    if (a.cast_on) cast_stage<AT_NT>(s_cast, t, a.c, a.layer);
+    if (a.cast_on) cast_store<AT_NT>(s_cast, ci, t, a.c, a.layer);
     // merges: wave j takes slot j.  Slots past the row's frontier width hold no
-    // partials of this layer: their loads go out with the others, and the
-    // width, loaded in the same round, stops the merge work there.
-    const int nf_w = a.layer == 1 ? 1 : t.n_front[b];
+    // partials of this layer: their loads went out with the others, and the
+    // width stops the merge work there.
     for (int j = wid; j < a.R; j += AT_NT / 64) {
         float M, Sp;
         const uint32_t* p = a.part + ((size_t)(b * a.R + j) * a.chunks) * rr_ps(Kn);
-        const uint64_t mine = merge_row_wave(p, a.chunks, Kn, M, Sp, s_scr[wid], j < nf_w);
+        const uint64_t mine = j == wid ? merge_finish(mi, p, a.chunks, Kn, M, Sp, s_scr[wid], j < nf0)
+                                       : merge_row_wave(p, a.chunks, Kn, M, Sp, s_scr[wid], j < nf0);
         if (lane < Kn) s_key[j * Kn + lane] = mine;
         if (lane == 0) { s_M[j] = M; s_S[j] = Sp; s_l1p[j] = log1pf(Sp); }
     }
     __syncthreads();
-    const int base = s_nn;
-    int Rd = min(max(s_nf, 0), a.R);
+    const int base = nn0;
+    int Rd = min(max(nf0, 0), a.R);
     if (base < 1 || base + Rd * Kn > cap) Rd = 0;          // capacity guard
     const int count = Rd * Kn;
     const int du = a.layer - 1;                            // depth of every frontier node
@@ -1198,29 +1230,81 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
     if (!(T > 0.f) && g != 0) return;                  // greedy rows: one workgroup
     const int Lr = min(max(f.n_leaves[b], 0), f.L);
     const bool ret_lds = Lr * (Dp + 1) <= VF_RET;
-    // greedy: the candidate paths go to LDS in the same round as the merges
-    if (!(T > 0.f) && ret_lds) {
-        const int32_t* ret = f.retrieve + (size_t)b * f.L * (Dp + 1);
-        for (int q = tid; q < Lr * (Dp + 1); q += VF_NT) s_ret[q] = ret[q];
+    const bool greedy = !(T > 0.f);
+    // round 2: the candidate paths (greedy), the flat parents and tokens and
+    // the first batch of argmax merges are requested before anything waits
+    // (straight-line loads from clamped addresses: a load under a branch ends
+    // in a register copy that waits for it)
+    const int32_t* ret = f.retrieve + (size_t)b * f.L * (Dp + 1);
+    const int nret = greedy && ret_lds ? Lr * (Dp + 1) : 0;
+    int32_t r_ret[VF_RET / VF_NT];
+#pragma unroll
+    for (int k = 0; k < VF_RET / VF_NT; ++k) {
+        const int q = tid + k * VF_NT;
+        r_ret[k] = ret[q < nret ? q : 0];
     }
-
-    for (int i = wid; i < n; i += VF_NT / 64) {
-        float M, Sp;
-        const uint32_t* p = a.part + ((size_t)(b * P + i) * a.chunks) * rr_ps(a.Kp);
-        const uint64_t mine = merge_row_wave(p, a.chunks, a.Kp, M, Sp, s_mscr[wid]);
-        const int am = __shfl(vkey_id(mine), 0);
-        if (lane == 0) {
-            s_am[i] = am; s_M[i] = M; s_S[i] = Sp;
-            if (a.row_argmax && g == 0) a.row_argmax[fo + i] = am;
+    const int tn = tid < n ? tid : 0;                  // P <= MK_NT <= VF_NT
+    const int r_fp = f.parent[fo + tn], r_ft = f.token[fo + tn];
+    const bool k1 = a.Kp == 1;
+    constexpr int VB = 4, NWV = VF_NT / 64;           // rows per wave per batch, waves
+    MergeIn1 in1[VB];
+    if (k1) {
+#pragma unroll
+        for (int r = 0; r < VB; ++r) {
+            const int i = min(wid + r * NWV, n - 1);
+            merge1_issue(a.part + ((size_t)(b * P + i) * a.chunks) * rr_ps(1), a.chunks, in1[r]);
         }
-        if (a.row_topk && g == 0 && lane < a.k_top) a.row_topk[(fo + i) * a.k_top + lane] = vkey_id(mine);
     }
-    for (int i = tid; i < P; i += VF_NT) {
-        s_fp[i] = i < n ? f.parent[fo + i] : -1;
-        s_ft[i] = i < n ? f.token[fo + i] : -1;
-        if (i >= n && g == 0) {                        // padding positions carry -1
-            if (a.row_argmax) a.row_argmax[fo + i] = -1;
-            for (int k = 0; a.row_topk && k < a.k_top; ++k) a.row_topk[(fo + i) * a.k_top + k] = -1;
+    // LDS staging from registers
+#pragma unroll
+    for (int k = 0; k < VF_RET / VF_NT; ++k) {
+        const int q = tid + k * VF_NT;
+        if (q < nret) s_ret[q] = r_ret[k];
+    }
+    if (tid < P) {
+        s_fp[tid] = tid < n ? r_fp : -1;
+        s_ft[tid] = tid < n ? r_ft : -1;
+        if (tid >= n && g == 0) {                      // padding positions carry -1
+            if (a.row_argmax) a.row_argmax[fo + tid] = -1;
+            for (int k = 0; a.row_topk && k < a.k_top; ++k) a.row_topk[(fo + tid) * a.k_top + k] = -1;
+        }
+    }
+    // merges: wave w takes rows w, w + 16, ...; argmax rows in batches of VB
+    // whose loads go out together
+    if (k1) {
+        for (int i0 = wid; i0 < n; i0 += VB * NWV) {
+            if (i0 != wid) {
+#pragma unroll
+                for (int r = 0; r < VB; ++r) {
+                    const int i = min(i0 + r * NWV, n - 1);
+                    merge1_issue(a.part + ((size_t)(b * P + i) * a.chunks) * rr_ps(1), a.chunks, in1[r]);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < VB; ++r) {
+                const int i = i0 + r * NWV;
+                if (i >= n) break;
+                float M, Sp;
+                const uint64_t mine = merge1_finish(in1[r], a.chunks, M, Sp);
+                if (lane == 0) {
+                    const int am = vkey_id(mine);
+                    s_am[i] = am; s_M[i] = M; s_S[i] = Sp;
+                    if (a.row_argmax && g == 0) a.row_argmax[fo + i] = am;
+                    if (a.row_topk && g == 0 && a.k_top > 0) a.row_topk[(fo + i) * a.k_top] = am;
+                }
+            }
+        }
+    } else {
+        for (int i = wid; i < n; i += NWV) {
+            float M, Sp;
+            const uint32_t* p = a.part + ((size_t)(b * P + i) * a.chunks) * rr_ps(a.Kp);
+            const uint64_t mine = merge_row_wave(p, a.chunks, a.Kp, M, Sp, s_mscr[wid]);
+            const int am = __shfl(vkey_id(mine), 0);
+            if (lane == 0) {
+                s_am[i] = am; s_M[i] = M; s_S[i] = Sp;
+                if (a.row_argmax && g == 0) a.row_argmax[fo + i] = am;
+            }
+            if (a.row_topk && g == 0 && lane < a.k_top) a.row_topk[(fo + i) * a.k_top + lane] = vkey_id(mine);
         }
     }
     if (tid == 0) s_best = 0ull;
