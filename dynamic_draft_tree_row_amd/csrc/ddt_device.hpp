@@ -58,6 +58,27 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
     return v;
 }
 
+// Rank counts split over lanes: n items, nt threads; item c is counted by the
+// S aligned lanes c*S .. c*S + S - 1, each over a slice of the items.  S is
+// the largest power of two <= 64 with S * n <= nt (1 when n > nt / 2).
+__device__ __forceinline__ int split_lanes(int n, int nt) {
+    int S = 1;
+    while (S < 64 && 2 * S * n <= nt) S <<= 1;
+    return S;
+}
+// Sum of v over each aligned group of S lanes (S a power of two <= 64).
+// Every lane of the wave must take part.
+__device__ __forceinline__ int group_sum(int v, int S) {
+    for (int d = 1; d < S; d <<= 1) v += __shfl_xor(v, d);
+    return v;
+}
+// v from lane l (l wave-uniform), through scalar registers.
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+
 // exp(d) for d <= 0 via the hardware exp2.
 __device__ __forceinline__ float exp_neg(float d) { return exp2f(d * DDT_LOG2E); }
 

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
     constexpr int VEC = SH::VEC, CH = SH::CH, NW = RR_NT / DDT_WAVE, NL = RR_NV;
     __shared__ uint32_t s_wmax[NW], s_wtau[NW];
     __shared__ float s_wsum[NW];
-    __shared__ int s_cnt, s_ties;
+    __shared__ int s_cnt, s_ties, s_amin;
     __shared__ uint64_t s_list[RR_CAP];
     __shared__ u32x4 s_stage[RR_NT * RR_NV];
     __shared__ int s_stid[RR_NT];
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
 
     u32x4 raw[NL];
     rr_load<BF16, NL>(raw, row, al, start, V, tid);
-    if (tid == 0) { s_cnt = 0; s_ties = 0; }
+    if (tid == 0) { s_cnt = 0; s_ties = 0; s_amin = 0x7FFFFFFF; }
 
     // pass 1: thread maximum (padding is -inf)
     float tm = -INFINITY;
@@ -168,10 +168,13 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
     // the workgroup's K-th largest element from below
     const uint32_t lo = tm > -INFINITY ? ord_f32(tm) : 0u;
     const uint32_t wmax = wave_max_u32(lo);
-    uint32_t tau = 0u;
-    for (int bit = 31; bit >= (BF16 ? 16 : 0); --bit) {
-        const uint32_t cand = tau | (1u << bit);
-        if (__popcll(__ballot(lo >= cand)) >= (unsigned)K) tau = cand;
+    uint32_t tau = wmax;                                       // K = 1: the wave maximum
+    if (K > 1) {
+        tau = 0u;
+        for (int bit = 31; bit >= (BF16 ? 16 : 0); --bit) {
+            const uint32_t cand = tau | (1u << bit);
+            if (__popcll(__ballot(lo >= cand)) >= (unsigned)K) tau = cand;
+        }
     }
     if (lane == 0) { s_wmax[wid] = wmax; s_wtau[wid] = tau; }
     __syncthreads();
@@ -219,12 +222,24 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
     }
     float s = s0 + s1;
     if (ties) atomicAdd(&s_ties, ties);
-    // candidates at or above the threshold go to the LDS list.  The lanes of a
-    // wave whose maximum reaches the threshold (usually a few) stage their
-    // loaded words in LDS; the whole wave then tests those elements, one per
-    // lane, and appends the ones that qualify.  Ids need checking only in a
-    // ragged chunk or when the threshold is -inf (padding is -inf).
-    {
+    if (K == 1) {
+        // argmax: the smallest id holding M (a lane's ids grow with (i, e))
+        if (tm == M) {
+            int idm = 0x7FFFFFFF;
+#pragma unroll
+            for (int i = NL - 1; i >= 0; --i) {
+#pragma unroll
+                for (int e = VEC - 1; e >= 0; --e)
+                    if (RR_X(raw[i], e) == M) idm = RR_ID(i, e);
+            }
+            atomicMin(&s_amin, idm);
+        }
+    } else {
+        // candidates at or above the threshold go to the LDS list.  The lanes
+        // of a wave whose maximum reaches the threshold (usually a few) stage
+        // their loaded words in LDS; the whole wave then tests those elements,
+        // one per lane, and appends the ones that qualify.  Ids need checking
+        // only in a ragged chunk or when the threshold is -inf (padding is -inf).
         const bool chk = !(tauf > -INFINITY) || start + CH > V;
         const uint64_t pm = __ballot(tm >= tauf);
         if (pm) {
@@ -258,7 +273,9 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
     __syncthreads();
     const int cnt = s_cnt;
     uint64_t* okeys = (uint64_t*)(out + 2);
-    if (cnt <= RR_CAP) {
+    if (K == 1) {
+        if (tid == 0) okeys[0] = vkey(M, s_amin);
+    } else if (cnt <= RR_CAP) {
         // rank counting: keys are unique, so rank < K places the key exactly
         for (int p = tid; p < cnt; p += RR_NT) {
             const uint64_t k = s_list[p];
@@ -417,12 +434,20 @@ __device__ __forceinline__ uint64_t merge_finish(MergeIn& in, const uint32_t* __
         if (nc <= MRG_CAP) {
             if (lane < K) scr[MRG_CAP + lane] = 0ull;
             wave_lds_sync();
-            for (int i = lane; i < nc; i += DDT_WAVE) {
-                const uint64_t x = scr[i];
+            if (nc <= DDT_WAVE) {
+                // one candidate per lane, the others read through scalar registers
+                const uint64_t x = lane < nc ? scr[lane] : 0ull;
                 int r = 0;
+                for (int q = 0; q < nc; ++q) r += readlane_u64(x, q) > x ? 1 : 0;
+                if (lane < nc && r < K) scr[MRG_CAP + r] = x;
+            } else {
+                for (int i = lane; i < nc; i += DDT_WAVE) {
+                    const uint64_t x = scr[i];
+                    int r = 0;
 #pragma unroll 4
-                for (int q = 0; q < nc; ++q) r += scr[q] > x ? 1 : 0;
-                if (r < K) scr[MRG_CAP + r] = x;
+                    for (int q = 0; q < nc; ++q) r += scr[q] > x ? 1 : 0;
+                    if (r < K) scr[MRG_CAP + r] = x;
+                }
             }
             wave_lds_sync();
             const uint64_t mine = lane < K ? scr[MRG_CAP + lane] : 0ull;

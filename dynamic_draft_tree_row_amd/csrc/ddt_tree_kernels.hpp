@@ -160,6 +160,40 @@ __device__ __forceinline__ double wave_incl_scan_f64(double x) {
     return x;
 }
 
+// Anchor scan with item k (1-based, k <= kmax <= 64) in lane k - 1: u = u_k,
+// c = c_k.  Keeps 1, moves the anchor a to k when u_k - u_a >= C (c_k - c_a)
+// (a non-increasing cost step moves it when utility grows); same walk as
+// anchor_scan_wave, on ballot masks instead of LDS.  Returns the anchor
+// (0 when kmax = 0); every lane gets it.
+__device__ __forceinline__ int anchor_scan_regs(double u, double c, double C, int kmax) {
+    const int lane = threadIdx.x & (DDT_WAVE - 1);
+    const bool item = lane < kmax;
+    const double up = __shfl_up(u, 1), cpv = __shfl_up(c, 1);
+    const bool adj_moves = (c - cpv) > 0.0 ? (u - up) >= C * (c - cpv) : (u - up) > 0.0;
+    // bit k-1 set: items k-1 -> k is a step the anchor does not take
+    const uint64_t stop_adj = __ballot(lane >= 1 && item && !adj_moves);
+    if (kmax <= 0) return 0;
+    int a = 1, k0 = 2;
+    while (k0 <= kmax) {
+        if (a == k0 - 1) {
+            const uint64_t m = stop_adj & (~0ull << (k0 - 1));
+            if (!m) return kmax;
+            const int hit = __ffsll((unsigned long long)m);          // lane + 1 = item
+            a = hit - 1;
+            k0 = hit + 1;
+        } else {
+            const double ua = readlane_f64(u, a - 1), ca = readlane_f64(c, a - 1);
+            const double du = u - ua, dc = c - ca;
+            const bool mv = dc > 0.0 ? du >= C * dc : du > 0.0;
+            const uint64_t m = __ballot(item && lane + 1 >= k0 && mv);
+            if (!m) return a;
+            a = __ffsll((unsigned long long)m);
+            k0 = a + 1;
+        }
+    }
+    return a;
+}
+
 // The batch rule, run by wave 0 of the layer's last workgroup once
 // L.v[b * R_max + k] = e^S of row b's k-th frontier node is in LDS (k < kcap
 // <= 32): width by the anchor scan on the batch-averaged cumulative utility,
@@ -180,35 +214,7 @@ __device__ void cast_decide(CastLds& L, const ddt_tree& t, const ddt_cast& cp, i
     }
     const double u = wave_incl_scan_f64(mean);
     const double c = item ? (double)L.sd[row * R + lane] / (double)L.st1[row] : 0.0;
-    // anchor scan: keep 1, move the anchor a to k when u_k - u_a >= C (c_k - c_a)
-    // (a non-increasing cost step moves it when utility grows)
-    const double C = (double)cp.C1[layer - 1];
-    const double up = __shfl_up(u, 1), cpv = __shfl_up(c, 1);
-    const bool adj_moves = (c - cpv) > 0.0 ? (u - up) >= C * (c - cpv) : (u - up) > 0.0;
-    // bit k-1 set: items k-1 -> k is a step the anchor does not take
-    const uint64_t stop_adj = __ballot(lane >= 1 && item && !adj_moves);
-    int n = 0;
-    if (kcap > 0) {
-        int a = 1, k0 = 2;
-        while (k0 <= kcap) {
-            if (a == k0 - 1) {
-                const uint64_t m = stop_adj & (~0ull << (k0 - 1));
-                if (!m) { a = kcap; break; }
-                const int hit = __ffsll((unsigned long long)m);      // lane + 1 = item
-                a = hit - 1;
-                k0 = hit + 1;
-            } else {
-                const double ua = readlane_f64(u, a - 1), ca = readlane_f64(c, a - 1);
-                const double du = u - ua, dc = c - ca;
-                const bool mv = dc > 0.0 ? du >= C * dc : du > 0.0;
-                const uint64_t m = __ballot(item && lane + 1 >= k0 && mv);
-                if (!m) break;
-                a = __ffsll((unsigned long long)m);
-                k0 = a + 1;
-            }
-        }
-        n = a;
-    }
+    const int n = anchor_scan_regs(u, c, (double)cp.C1[layer - 1], kcap);
     const double un = n > 0 ? readlane_f64(u, n - 1) : 0.0;
     const double cn = n > 0 ? readlane_f64(c, n - 1) : 0.0;
     // gain FIFO (entries 0..7 of the state, one per lane), length, previous u_n
@@ -387,14 +393,21 @@ __global__ __launch_bounds__(AT_NT) void k_attach(AttachArgs a) {
         }
     }
     __syncthreads();
-    // frontier: the first R_max of the layer by (S desc, key asc); the best
-    // node's thread closes the row's layer
-    for (int q = tid; q < count; q += AT_NT) {
-        const uint64_t sk = s_sk[q];
+    // frontier: the first R_max of the layer by (S desc, key asc), each rank
+    // counted by S lanes; the best node's lane closes the row's layer
+    {
+        const int SL = split_lanes(count, AT_NT);      // count <= R_max * K_n <= AT_NT
+        const int lg = __ffs(SL) - 1;
+        const int q = tid >> lg, part = tid & (SL - 1);
+        uint64_t sk = 0ull;
         int r = 0;
-#pragma unroll 8
-        for (int p = 0; p < count; ++p) r += s_sk[p] < sk ? 1 : 0;
-        if (r < Rm) {
+        if (q < count) {
+            sk = s_sk[q];
+#pragma unroll 4
+            for (int p = part; p < count; p += SL) r += s_sk[p] < sk ? 1 : 0;
+        }
+        r = group_sum(r, SL);
+        if (part == 0 && q < count && r < Rm) {
             const float Sv = unord_f32(~(uint32_t)(sk >> 32));
             const int j = q / Kn;
             fr[r] = base + q; frS[r] = Sv; frK[r] = key_child(s_pk[j], du, q - j * Kn, 0);
@@ -521,6 +534,7 @@ __global__ __launch_bounds__(RK_NT) void k_rerank(RerankArgs a) {
     __shared__ uint64_t s_ck[RK_CAND];
     __shared__ int32_t s_cn[RK_CAND];
     __shared__ int32_t s_node[DDT_MAX_VERIFY];
+    __shared__ float s_sv[DDT_MAX_VERIFY];
     __shared__ double s_u[DDT_MAX_VERIFY + 1], s_c[DDT_MAX_VERIFY + 1];
     __shared__ uint64_t s_sort[RK_SORT];
     const int nn = min(max(t.n_nodes[b], 1), t.cap);
@@ -529,20 +543,33 @@ __global__ __launch_bounds__(RK_NT) void k_rerank(RerankArgs a) {
     const float* S = t.S + (size_t)b * t.cap;
     const uint64_t* key = t.key + (size_t)b * t.cap;
 
-    // one round of loads: values and keys of this thread's nodes, verify costs
+    // one round of loads: values and keys of this thread's nodes, verify costs.
+    // Straight-line loads from clamped addresses (a load under a branch ends in
+    // a register copy that waits for it); the values past the data are masked
+    // after the loads.
     uint32_t o[RK_PER];
     uint64_t kk[RK_PER];
+    float sraw[RK_PER];
 #pragma unroll
     for (int i = 0; i < RK_PER; ++i) {
         const int q = tid + i * RK_NT;
-        o[i] = q < N ? ord_f32(S[1 + q]) : 0u;
-        kk[i] = q < N ? key[1 + q] : 0ull;
+        const int qc = q < N ? q : 0;
+        sraw[i] = S[1 + qc];
+        kk[i] = key[1 + qc];
     }
-    if (a.cast_on) {
-        const int row = cast_sel_row(a.c.ctx_verify, a.c.L, a.c.M);
-        const float* ST = a.c.S_T + (size_t)row * (a.c.N + 1);
-        for (int k = tid; k < kmax; k += RK_NT) s_c[k + 1] = (double)ST[k + 1] / (double)ST[1];
+    // verify costs c_k = S_T[row][k] / S_T[row][1] for k = tid + 1 (without
+    // CAST the loads read the row's own values and are not used)
+    const int kc = tid < kmax ? tid : 0;
+    const float* ST = S;
+    if (a.cast_on) ST = a.c.S_T + (size_t)cast_sel_row(a.c.ctx_verify, a.c.L, a.c.M) * (a.c.N + 1);
+    const float c_num = ST[kc + 1], c_den = ST[1];
+#pragma unroll
+    for (int i = 0; i < RK_PER; ++i) {
+        const int q = tid + i * RK_NT;
+        o[i] = q < N ? ord_f32(sraw[i]) : 0u;
+        kk[i] = q < N ? kk[i] : 0ull;
     }
+    if (a.cast_on && tid < kmax) s_c[tid + 1] = (double)c_num / (double)c_den;
     if (tid == 0) { s_need = kmax; s_ngt = 0; s_ntie = 0; s_slot = 0; }
 
     // radix select: T = code of the kmax-th largest value (0 when every node is kept)
@@ -614,24 +641,46 @@ __global__ __launch_bounds__(RK_NT) void k_rerank(RerankArgs a) {
             if (q < N && o[i] >= T) { s_ca[slot] = ~o[i]; s_ck[slot] = kk[i]; s_cn[slot] = 1 + q; ++slot; }
         }
         __syncthreads();
-        for (int c = tid; c < nc; c += RK_NT) {
-            const uint32_t ca = s_ca[c];
-            const uint64_t ck = s_ck[c];
-            int r = 0;
-#pragma unroll 8
-            for (int p = 0; p < nc; ++p) {
+        // rank of candidate c, counted by S lanes (nc <= RK_CAND = RK_NT)
+        const int SL = split_lanes(nc, RK_NT);
+        const int lg = __ffs(SL) - 1;
+        const int c = tid >> lg, part = tid & (SL - 1);
+        uint32_t ca = 0u;
+        uint64_t ck = 0ull;
+        int r = 0;
+        if (c < nc) {
+            ca = s_ca[c];
+            ck = s_ck[c];
+#pragma unroll 4
+            for (int p = part; p < nc; p += SL) {
                 const uint32_t pa = s_ca[p];
                 r += (int)(pa < ca) | ((int)(pa == ca) & (int)(s_ck[p] < ck));
             }
-            if (r < kmax) s_node[r] = s_cn[c];
+        }
+        r = group_sum(r, SL);
+        if (part == 0 && c < nc && r < kmax) {
+            s_node[r] = s_cn[c];
+            s_sv[r] = unord_f32(~ca);
         }
         __syncthreads();
     } else {
         rerank_sort_all<RK_NT>(S, key, N, kmax, s_sort, s_node);
+        for (int k = tid; k < kmax; k += RK_NT) s_sv[k] = S[s_node[k]];
+        __syncthreads();
     }
     // verify count
-    if (a.cast_on) {
-        for (int k = tid; k < kmax; k += RK_NT) s_u[k + 1] = (double)expf(S[s_node[k]]);
+    if (a.cast_on && kmax <= DDT_WAVE) {
+        // item k in lane k - 1: cumulative values and costs in registers
+        if (wid == 0) {
+            const bool item = lane < kmax;
+            const double v = item ? (double)expf(s_sv[lane]) : 0.0;
+            const double u = wave_incl_scan_f64(v);
+            const double c = item ? s_c[lane + 1] : 0.0;
+            const int m = anchor_scan_regs(u, c, (double)a.c.C3[b], kmax);
+            if (lane == 0) s_m = m;
+        }
+    } else if (a.cast_on) {
+        for (int k = tid; k < kmax; k += RK_NT) s_u[k + 1] = (double)expf(s_sv[k]);
         __syncthreads();
         if (wid == 0) {
             // prefix sums: four consecutive items per lane, then across lanes
@@ -771,14 +820,21 @@ __global__ __launch_bounds__(MK_NT) void k_build_mask(MaskArgs a) {
     const int n = m + 1;
     const size_t o = (size_t)b * cap;
     const int32_t* sel = a.sel + (size_t)b * P;
+    // the selection (issued with the count), then the selected nodes' records:
+    // straight-line loads from clamped addresses, masked afterwards (a load
+    // under a branch ends in a register copy that waits for it)
     for (int q = tid; q < P; q += MK_NT) {
-        int node = q <= m ? sel[q] : -1;
+        const int raw = sel[q];
+        int node = q <= m ? raw : -1;
         if (node < 0 || node >= cap) node = -1;
+        const int nc = node >= 0 ? node : 0;
+        const uint64_t kv = t.key[o + nc];
+        const int32_t tv = t.token[o + nc], pv = t.parent[o + nc], dv = t.depth[o + nc];
         s_node[q] = node;
-        s_key[q] = node >= 0 ? t.key[o + node] : ~0ull;
-        s_tok[q] = node >= 0 ? t.token[o + node] : -1;
-        s_par[q] = node >= 0 ? t.parent[o + node] : -1;
-        s_dep[q] = node >= 0 ? t.depth[o + node] : 0;
+        s_key[q] = node >= 0 ? kv : ~0ull;
+        s_tok[q] = node >= 0 ? tv : -1;
+        s_par[q] = node >= 0 ? pv : -1;
+        s_dep[q] = node >= 0 ? dv : 0;
         s_hc[q] = 0;
     }
     for (int i = tid; i < cap; i += MK_NT) s_inv[i] = -1;
