@@ -60,16 +60,20 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 
 // Rank counts split over lanes: n items, nt threads; item c is counted by the
 // S aligned lanes c*S .. c*S + S - 1, each over a slice of the items.  S is
-// the largest power of two <= 64 with S * n <= nt (1 when n > nt / 2).
+// the largest power of two <= 16 with S * n <= nt (1 when n > nt / 2).
 __device__ __forceinline__ int split_lanes(int n, int nt) {
     int S = 1;
-    while (S < 64 && 2 * S * n <= nt) S <<= 1;
+    while (S < 16 && 2 * S * n <= nt) S <<= 1;
     return S;
 }
-// Sum of v over each aligned group of S lanes (S a power of two <= 64).
-// Every lane of the wave must take part.
+// Sum of v over each aligned group of S lanes (S = 1, 2, 4, 8 or 16), by DPP
+// inside rows of 16: swap neighbours, swap pairs, mirror halves, mirror the
+// row.  Every lane of the wave must take part.
 __device__ __forceinline__ int group_sum(int v, int S) {
-    for (int d = 1; d < S; d <<= 1) v += __shfl_xor(v, d);
+    if (S >= 2) v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
+    if (S >= 4) v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
+    if (S >= 8) v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+    if (S >= 16) v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);
     return v;
 }
 // v from lane l (l wave-uniform), through scalar registers.

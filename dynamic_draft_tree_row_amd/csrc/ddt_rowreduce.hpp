@@ -76,6 +76,18 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
     return ((uint64_t)hi << 32) | lo;
 }
 
+// Inclusive prefix sum of v over the 64 lanes (DPP: shifts by 1, 2, 4, 8
+// inside each row of 16, then the totals of earlier rows by broadcast).
+__device__ __forceinline__ int wave_incl_scan_i32(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, true);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, true);
+    return v;
+}
+
 template <bool BF16, int NL>
 __device__ __forceinline__ void rr_load(u32x4 (&raw)[NL], const void* row, bool al, int start,
                                         int V, int tid) {
@@ -253,17 +265,34 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
                 stid[idx] = tid;
             }
             wave_lds_sync();
-            const int np = __popcll(pm);
-            constexpr int EPL = NL * VEC;                  // elements per lane
-            for (int q = lane; q < np * EPL; q += DDT_WAVE) {
-                const int src = q / EPL, e = q - src * EPL;
-                const int i = e / VEC, k = e - i * VEC;
-                const uint32_t w = ((const uint32_t*)&st[src * NL + i])[BF16 ? (k >> 1) : k];
-                const float x = BF16 ? __uint_as_float((k & 1) ? (w & 0xFFFF0000u) : (w << 16)) : __uint_as_float(w);
-                const int id = start + (i * RR_NT + stid[src]) * VEC + k;
-                if (x >= tauf && (!chk || id < V)) {
-                    const int slot = atomicAdd(&s_cnt, 1);
-                    if (slot < RR_CAP) s_list[slot] = vkey(x, id);
+            // one staged 16-byte word (VEC elements) per lane per step; a
+            // wave prefix of the hit counts places the hits in the list
+            const int nq = __popcll(pm) * NL;              // words staged: src * NL + i
+            for (int q0 = 0; q0 < nq; q0 += DDT_WAVE) {
+                const int q = q0 + lane;
+                uint32_t hit = 0u;
+                u32x4 w = u32x4{0u, 0u, 0u, 0u};
+                int id0 = 0;
+                if (q < nq) {
+                    w = st[q];
+                    const int src = q / NL, i = q - src * NL;
+                    id0 = start + (i * RR_NT + stid[src]) * VEC;
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        hit |= (uint32_t)((RR_X(w, e) >= tauf) & (!chk | (id0 + e < V))) << e;
+                }
+                const int nh = __popc(hit);
+                const int incl = wave_incl_scan_i32(nh);
+                const int tot = __builtin_amdgcn_readlane(incl, DDT_WAVE - 1);
+                int base = 0;
+                if (lane == 0) base = atomicAdd(&s_cnt, tot);
+                base = __builtin_amdgcn_readfirstlane(base);
+                int slot = base + incl - nh;
+                while (hit) {
+                    const int e = __ffs(hit) - 1;
+                    hit &= hit - 1;
+                    if (slot < RR_CAP) s_list[slot] = vkey(RR_X(w, e), id0 + e);
+                    ++slot;
                 }
             }
         }
@@ -276,13 +305,21 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
     if (K == 1) {
         if (tid == 0) okeys[0] = vkey(M, s_amin);
     } else if (cnt <= RR_CAP) {
-        // rank counting: keys are unique, so rank < K places the key exactly
-        for (int p = tid; p < cnt; p += RR_NT) {
-            const uint64_t k = s_list[p];
+        // rank counting, each rank counted by S lanes: keys are unique, so
+        // rank < K places the key exactly
+        const int SL = split_lanes(cnt, RR_NT);
+        const int lg = __ffs(SL) - 1;
+        for (int cb = 0; cb < cnt; cb += RR_NT >> lg) {
+            const int c = cb + (tid >> lg), part = tid & (SL - 1);
+            uint64_t k = 0ull;
             int rank = 0;
-#pragma unroll 8
-            for (int q = 0; q < cnt; ++q) rank += s_list[q] > k ? 1 : 0;
-            if (rank < K) okeys[rank] = k;
+            if (c < cnt) {
+                k = s_list[c];
+#pragma unroll 4
+                for (int q = part; q < cnt; q += SL) rank += s_list[q] > k ? 1 : 0;
+            }
+            rank = group_sum(rank, SL);
+            if (part == 0 && c < cnt && rank < K) okeys[rank] = k;
         }
         for (int k = cnt + tid; k < K; k += RR_NT) okeys[k] = 0ull;
     } else {
