@@ -97,10 +97,10 @@ int resident_verify_blocks() {
 }
 
 int launch_partials(const ddt_logits* x, int n0, int n1, const int32_t* count, int count_add,
-                    int K, void* ws, hipStream_t s) {
+                    int K, void* ws, hipStream_t s, const float* sum_if = nullptr) {
     RowSrc rs;
     rs.base = x->data; rs.s0 = x->s0; rs.s1 = x->s1; rs.n1 = n1;
-    rs.count = count; rs.count_add = count_add;
+    rs.count = count; rs.count_add = count_add; rs.sum_if = sum_if;
     const long long rows = (long long)n0 * n1;
     const int groups = groups_of(rows, x->V, x->dtype);
     const long long total = rows * groups;
@@ -356,7 +356,8 @@ int ddt_tree_verify(const ddt_tree* t, const ddt_flat* f, const ddt_logits* targ
     if (ws_bytes < ws_need((long long)t->B * f->P, target->V, target->dtype, Kp))
         return DDT_EWORKSPACE;
     hipStream_t s = (hipStream_t)stream;
-    st = launch_partials(target, t->B, f->P, f->m, 1, Kp, ws, s);
+    // greedy requests (temperature 0) use only the rows' argmax and top k
+    st = launch_partials(target, t->B, f->P, f->m, 1, Kp, ws, s, temperature);
     if (st) return st;
     VerifyArgs a;
     a.t = *t; a.f = *f; a.part = (const uint32_t*)ws;

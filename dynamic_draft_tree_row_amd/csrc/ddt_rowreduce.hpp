@@ -32,13 +32,16 @@ template <bool BF16> struct RRShape {
 
 // Rows (i0, i1) with i0 < n0 (grid-derived) and i1 < n1; row base at
 // base + i0*s0 + i1*s1 elements.  Rows with i1 >= count[i0] + count_add are
-// skipped when count is given.
+// skipped when count is given.  When sum_if is given, rows with
+// !(sum_if[i0] > 0) need only the max and the top K: sigma' is not summed and
+// reads 0 (greedy verify rows, whose temperature is 0, use only the argmax).
 struct RowSrc {
     const void* base;
     int64_t s0, s1;
     int n1;
     const int32_t* count;
     int count_add;
+    const float* sum_if;
 };
 
 // Partial layout per (row, group): PS = 2 + 2K words: [0] max, [1] sigma',
@@ -155,6 +158,7 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
     const int rowg = blockIdx.x / groups;
     const int i0 = rowg / rs.n1, i1 = rowg - i0 * rs.n1;
     if (rs.count != nullptr && i1 >= rs.count[i0] + rs.count_add) return;   // block-uniform
+    const bool sums = rs.sum_if == nullptr || rs.sum_if[i0] > 0.f;        // block-uniform
     const int tid = threadIdx.x, lane = tid & (DDT_WAVE - 1), wid = tid / DDT_WAVE;
     const int64_t off = (int64_t)i0 * rs.s0 + (int64_t)i1 * rs.s1;
     const void* row = (const char*)rs.base + off * (BF16 ? 2 : 4);
@@ -210,7 +214,9 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
     // below 2^-126 to zero, far below the sum's precision.
     float s0 = 0.f, s1 = 0.f;
     int ties = 0;
-    if (__ballot(tm == M)) {
+    if (!sums) {
+        // max and top K only
+    } else if (__ballot(tm == M)) {
         // a wave holding the maximum: leave out and count the elements equal to M
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
@@ -353,7 +359,7 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
 #pragma unroll
         for (int w = 0; w < NW; ++w) st += s_wsum[w];
         out[0] = __float_as_uint(M);
-        out[1] = __float_as_uint(st + (float)(s_ties - 1));
+        out[1] = __float_as_uint(sums ? st + (float)(s_ties - 1) : 0.f);
     }
 #undef RR_ID
 }
