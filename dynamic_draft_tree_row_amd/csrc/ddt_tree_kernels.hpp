@@ -1273,6 +1273,12 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
     __shared__ double s_e2t[64];
     __shared__ int s_path[DDT_MAX_DEPTH + 2];
     __shared__ int s_ch[MK_NT];
+    // T > 0 walk, per flat position i: draft slot and depth of its node, the
+    // reduction statistics of the draft row it expanded, and the target and
+    // draft logits of its token under its parent's rows
+    __shared__ int s_wslot[MK_NT], s_wdep[MK_NT];
+    __shared__ float s_wrm[MK_NT], s_wrs[MK_NT], s_wtl[MK_NT], s_wdl[MK_NT];
+    __shared__ int s_wcnt[MK_NT / 64];
     __shared__ int s_nch, s_u, s_len, s_acc, s_next;
     __shared__ unsigned long long s_best;
     __shared__ uint64_t s_mscr[VF_NT / 64][MRG_SCR];
@@ -1422,39 +1428,76 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
     }
     if (tid == 0) { s_u = 0; s_len = 0; s_path[0] = 0; s_err = 0; s_next = 0; }
     if (tid < 64) s_e2t[tid] = exp2((double)tid / 64.0);
+    // every position's draft slot, depth and row statistics (a chain of three
+    // loads, once), then its logits under its parent's rows (one more round):
+    // the walk's steps read LDS only
+    const size_t es = a.bf16 ? 2 : 4;
+    auto drow_of = [&](int slot, int dep) -> const char* {
+        const int64_t doff = (int64_t)dep * a.dl + (int64_t)b * a.ds0 + (int64_t)slot * a.ds1;
+        return (const char*)a.drf + (size_t)doff * es;
+    };
+    if (tid < n) {
+        const int node = f.node[fo + tid];
+        const bool ok = node >= 0 && node < t.cap;
+        const int nc = ok ? node : 0;
+        int slot = t.eslot[(size_t)b * t.cap + nc];
+        const int dep = t.depth[(size_t)b * t.cap + nc];
+        if (!ok || a.drf == nullptr || dep < 0 || dep >= t.D_max || slot >= t.R_max) slot = -1;
+        const size_t ri = ((size_t)b * t.D_max + (slot >= 0 ? dep : 0)) * t.R_max + (slot >= 0 ? slot : 0);
+        const float rm = t.rmax[ri], rsv = t.rsp[ri];
+        s_wslot[tid] = slot;
+        s_wdep[tid] = ok ? dep : 0;
+        s_wrm[tid] = rm;
+        s_wrs[tid] = rsv;
+    }
+    __syncthreads();
+    if (tid < n) {
+        const int pa = min(max(s_fp[tid], 0), n - 1);
+        const int x = min(max(s_ft[tid], 0), a.V - 1);
+        const char* trow = (const char*)a.tgt + (size_t)(b * a.ts0 + pa * a.ts1) * es;
+        const int ps = s_wslot[pa];
+        const char* drow = ps >= 0 ? drow_of(ps, s_wdep[pa]) : trow;
+        s_wtl[tid] = ld_logit(trow, a.bf16 != 0, x);
+        s_wdl[tid] = ld_logit(drow, a.bf16 != 0, x);
+    }
     __syncthreads();
     while (!s_err) {
         const int u = s_u;
-        if (tid == 0) {
-            int c = 0;
-            for (int i = u + 1; i < n; ++i) if (s_fp[i] == u) s_ch[c++] = i;
-            s_nch = c;
+        // children of u in flat order: ballots over the positions, then each
+        // wave's offset from the counts of the waves before it
+        {
+            const bool is_ch = tid < n && tid > u && s_fp[tid] == u;
+            const uint64_t bm = __ballot(is_ch);
+            if (lane == 0 && wid < MK_NT / 64) s_wcnt[wid] = __popcll(bm);
+            __syncthreads();
+            if (is_ch) {
+                int off = 0;
+                for (int w2 = 0; w2 < wid; ++w2) off += s_wcnt[w2];
+                s_ch[off + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u))] = tid;
+            }
+            if (tid == 0) {
+                int c = 0;
+                for (int w2 = 0; w2 < MK_NT / 64; ++w2) c += s_wcnt[w2];
+                s_nch = c;
+            }
         }
         __syncthreads();
         const int nch = s_nch;
-        const int unode = f.node[fo + u];
-        const int uslot = (unode >= 0 && unode < t.cap) ? t.eslot[(size_t)b * t.cap + unode] : -1;
-        const int udep = (unode >= 0 && unode < t.cap) ? t.depth[(size_t)b * t.cap + unode] : 0;
-        const bool has_q = nch > 0 && uslot >= 0 && a.drf != nullptr && udep < t.D_max;
+        const int uslot = s_wslot[u];
+        const int udep = s_wdep[u];
+        const bool has_q = nch > 0 && uslot >= 0;
         WalkRows w;
         w.tab = s_e2t;
         w.bf16 = a.bf16 != 0;
-        const size_t es = a.bf16 ? 2 : 4;
         w.trow = (const char*)a.tgt + (size_t)(b * a.ts0 + u * a.ts1) * es;
-        size_t ri = 0;
-        if (has_q) {
-            const int64_t doff = (int64_t)udep * a.dl + (int64_t)b * a.ds0 + (int64_t)uslot * a.ds1;
-            w.drow = (const char*)a.drf + (size_t)doff * es;
-            ri = ((size_t)b * t.D_max + udep) * t.R_max + uslot;
-        } else {
-            w.drow = w.trow;
-        }
+        w.drow = has_q ? drow_of(uslot, udep) : w.trow;
         const uintptr_t amask = w.bf16 ? 7u : 15u;     // 4-element vector loads
         w.alt = (((uintptr_t)w.trow) & amask) == 0;
         w.ald = (((uintptr_t)w.drow) & amask) == 0;
         w.kT = kT;
         w.Mt = s_M[u];
-        w.Md = has_q ? (double)t.rmax[ri] : w.Mt;
+        w.Md = has_q ? (double)s_wrm[u] : w.Mt;
         w.lzt = 0.0;
         w.lzd = 0.0;
         // Normalisers.  The accept tests at T = 1 use the rows' own statistics
@@ -1474,7 +1517,7 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
         if (has_q) {
             if (T == 1.f) {
                 w.lzt = log2(1.0 + (double)s_S[u]);
-                w.lzd = log2(1.0 + (double)t.rsp[ri]);
+                w.lzd = log2(1.0 + (double)s_wrs[u]);
             } else {
                 exact_norms();
             }
@@ -1487,9 +1530,8 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
             for (int ci = 0; ci < nch && !s_err; ++ci) {
                 const int c = s_ch[ci];
                 if (tid == 0) {
-                    const int x = min(max(s_ft[c], 0), a.V - 1);
-                    const double px = walk_p(w, ld_logit(w.trow, w.bf16, x));
-                    const double qx = walk_q(w, ld_logit(w.drow, w.bf16, x));
+                    const double px = walk_p(w, s_wtl[c]);
+                    const double qx = walk_q(w, s_wdl[c]);
                     const double pk = fmax(0.0, px - ra * qx) / rb;
                     const double ratio = qx > 0.0 ? pk / qx : INFINITY;
                     s_acc = ((double)Ub[2 * c] < ratio) ? 1 : 0;
