@@ -13,16 +13,25 @@ namespace {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-inline int chunk_elems(int dtype) {
-    return dtype == DDT_BF16 ? RRShape<true>::CH : RRShape<false>::CH;
+// Launches of RR_WIDE_ROWS rows or more reduce wide chunks.
+inline bool wide_rows(long long rows) { return rows >= RR_WIDE_ROWS; }
+
+inline int chunk_elems(int dtype, bool wide) {
+    if (dtype == DDT_BF16) return wide ? RRShape<true, RR_NV_WIDE>::CH : RRShape<true, RR_NV>::CH;
+    return wide ? RRShape<false, RR_NV_WIDE>::CH : RRShape<false, RR_NV>::CH;
 }
 
-inline int chunks_of(int V, int dtype) { return (V + chunk_elems(dtype) - 1) / chunk_elems(dtype); }
+// Chunks per row of the small-launch shape: the most a launch can use (sizes
+// workspaces and the capacity check).
+inline int chunks_of(int V, int dtype) {
+    return (V + chunk_elems(dtype, false) - 1) / chunk_elems(dtype, false);
+}
 
-// Partials per row (one per chunk); producer and consumers agree on it.
+// Partials per row (one per chunk) of a launch over `rows` rows; the producer
+// and its consumers call this with the same rows, so they agree.
 inline int groups_of(long long rows, int V, int dtype) {
-    (void)rows;
-    return chunks_of(V, dtype);
+    const int ch = chunk_elems(dtype, wide_rows(rows));
+    return (V + ch - 1) / ch;
 }
 
 inline size_t ws_need(long long rows, int V, int dtype, int K) {
@@ -98,7 +107,7 @@ int resident_verify_blocks() {
 
 int launch_partials(const ddt_logits* x, int n0, int n1, const int32_t* count, int count_add,
                     int K, void* ws, hipStream_t s, const float* sum_if = nullptr) {
-    RowSrc rs;
+    RowSrc rs{};
     rs.base = x->data; rs.s0 = x->s0; rs.s1 = x->s1; rs.n1 = n1;
     rs.count = count; rs.count_add = count_add; rs.sum_if = sum_if;
     const long long rows = (long long)n0 * n1;
@@ -106,23 +115,19 @@ int launch_partials(const ddt_logits* x, int n0, int n1, const int32_t* count, i
     const long long total = rows * groups;
     if (total <= 0) return DDT_OK;
     if (total > INT32_MAX) return DDT_ECAPACITY;
-    const bool bf16 = x->dtype == DDT_BF16;
+    const bool bf16 = x->dtype == DDT_BF16, wide = wide_rows(rows);
     const dim3 grid((unsigned)total), blk(RR_NT);
     uint32_t* part = (uint32_t*)ws;
+    auto kern = bf16 ? (wide ? &k_row_partial<true, RR_NV_WIDE> : &k_row_partial<true, RR_NV>)
+                     : (wide ? &k_row_partial<false, RR_NV_WIDE> : &k_row_partial<false, RR_NV>);
     if (g_events != nullptr && g_used < g_pairs) {
         // timed: the runtime stamps the two events at the kernel's own start and end
         hipEvent_t e0 = (hipEvent_t)g_events[2 * g_used], e1 = (hipEvent_t)g_events[2 * g_used + 1];
-        if (bf16)
-            hipExtLaunchKernelGGL((k_row_partial<true>), grid, blk, 0, s, e0, e1, 0, rs, x->V, groups, K, part);
-        else
-            hipExtLaunchKernelGGL((k_row_partial<false>), grid, blk, 0, s, e0, e1, 0, rs, x->V, groups, K, part);
+        hipExtLaunchKernelGGL(kern, grid, blk, 0, s, e0, e1, 0, rs, x->V, groups, K, part);
         ++g_used;
         return launched();
     }
-    if (bf16)
-        hipLaunchKernelGGL((k_row_partial<true>), grid, blk, 0, s, rs, x->V, groups, K, part);
-    else
-        hipLaunchKernelGGL((k_row_partial<false>), grid, blk, 0, s, rs, x->V, groups, K, part);
+    hipLaunchKernelGGL(kern, grid, blk, 0, s, rs, x->V, groups, K, part);
     const int st = launched();
     return st;
 }
@@ -153,7 +158,7 @@ int ddt_set_reduce_events(void* const* events, int n_pairs) {
 
 int ddt_chunk_elems(int dtype) {
     if (dtype != DDT_F32 && dtype != DDT_BF16) return -1;
-    return chunk_elems(dtype);
+    return chunk_elems(dtype, false);
 }
 
 size_t ddt_workspace_bytes(int rows, int V, int dtype, int K) {

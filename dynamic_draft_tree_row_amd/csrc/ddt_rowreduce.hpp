@@ -21,13 +21,20 @@
 #include "ddt_device.hpp"
 
 #define RR_NT 256           // threads per workgroup
-#define RR_NV 4             // 16-byte loads per thread per tile
+#define RR_NV 4             // 16-byte loads per thread per chunk (small launches)
+#define RR_NV_WIDE 8        // the same for launches of RR_WIDE_ROWS rows or more
+#define RR_WIDE_ROWS 256
 #define RR_CAP 1024         // LDS candidate list
+#define RR_SCAP 16          // lanes per wave staged at a time
 
-template <bool BF16> struct RRShape {
+// Chunk shape for NL 16-byte loads per thread.  Wide chunks (8 loads, 64 bf16
+// per thread) halve the per-wave fixed work per element, which is what bounds
+// a launch that fills the chip; small launches keep 4 loads, so that each
+// workgroup's latency stays short.
+template <bool BF16, int NL = RR_NV> struct RRShape {
     static constexpr int VEC = BF16 ? 8 : 4;          // elements per 16-byte load
-    static constexpr int EPT = VEC * RR_NV;           // elements per thread per tile
-    static constexpr int CH = RR_NT * EPT;            // elements per tile (chunk)
+    static constexpr int EPT = VEC * NL;              // elements per thread per chunk
+    static constexpr int CH = RR_NT * EPT;            // elements per chunk
 };
 
 // Rows (i0, i1) with i0 < n0 (grid-derived) and i1 < n1; row base at
@@ -94,7 +101,7 @@ __device__ __forceinline__ int wave_incl_scan_i32(int v) {
 template <bool BF16, int NL>
 __device__ __forceinline__ void rr_load(u32x4 (&raw)[NL], const void* row, bool al, int start,
                                         int V, int tid) {
-    using SH = RRShape<BF16>;
+    using SH = RRShape<BF16, NL>;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
         const int e0 = start + (i * RR_NT + tid) * SH::VEC;
@@ -142,17 +149,17 @@ __device__ __forceinline__ float rr_max3(float a, float b, float c) {
                          : __uint_as_float((r)[(e)]))
 
 // One workgroup reduces one chunk of one row.
-template <bool BF16>
+template <bool BF16, int NL>
 __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int groups, int K,
                                                        uint32_t* __restrict__ part) {
-    using SH = RRShape<BF16>;
-    constexpr int VEC = SH::VEC, CH = SH::CH, NW = RR_NT / DDT_WAVE, NL = RR_NV;
+    using SH = RRShape<BF16, NL>;
+    constexpr int VEC = SH::VEC, CH = SH::CH, NW = RR_NT / DDT_WAVE;
     __shared__ uint32_t s_wmax[NW], s_wtau[NW];
     __shared__ float s_wsum[NW];
     __shared__ int s_cnt, s_ties, s_amin;
     __shared__ uint64_t s_list[RR_CAP];
-    __shared__ u32x4 s_stage[RR_NT * RR_NV];
-    __shared__ int s_stid[RR_NT];
+    __shared__ u32x4 s_stage[NW * RR_SCAP * NL];
+    __shared__ int s_stid[NW * RR_SCAP];
 
     const int g = blockIdx.x % groups;
     const int rowg = blockIdx.x / groups;
@@ -207,6 +214,10 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
     const float M = unord_f32(bmax);
     const float tauf = bt ? unord_f32(bt) : -INFINITY;
     const float ML = M * DDT_LOG2E;
+    // pass 2 unpacks the raw words again: no unpacked copies live across the
+    // passes (registers, not instructions, would bound the wide chunks)
+#pragma unroll
+    for (int i = 0; i < NL; ++i) asm volatile("" : "+v"(raw[i]));
 
     // pass 2: sum of exp(x - M) over the elements below M and the count of
     // elements equal to M (sigma' leaves out exactly one of them; the others
@@ -261,45 +272,50 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
         const bool chk = !(tauf > -INFINITY) || start + CH > V;
         const uint64_t pm = __ballot(tm >= tauf);
         if (pm) {
-            u32x4* st = s_stage + wid * DDT_WAVE * NL;
-            int* stid = s_stid + wid * DDT_WAVE;
-            if (tm >= tauf) {
-                const int idx = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(pm >> 32),
-                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)pm, 0u));
+            u32x4* st = s_stage + wid * RR_SCAP * NL;
+            int* stid = s_stid + wid * RR_SCAP;
+            const int np = __popcll(pm);
+            const int rk = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(pm >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)pm, 0u));
+            // RR_SCAP lanes at a time
+            for (int b0 = 0; b0 < np; b0 += RR_SCAP) {
+                if (tm >= tauf && rk >= b0 && rk < b0 + RR_SCAP) {
 #pragma unroll
-                for (int i = 0; i < NL; ++i) st[idx * NL + i] = raw[i];
-                stid[idx] = tid;
-            }
-            wave_lds_sync();
-            // one staged 16-byte word (VEC elements) per lane per step; a
-            // wave prefix of the hit counts places the hits in the list
-            const int nq = __popcll(pm) * NL;              // words staged: src * NL + i
-            for (int q0 = 0; q0 < nq; q0 += DDT_WAVE) {
-                const int q = q0 + lane;
-                uint32_t hit = 0u;
-                u32x4 w = u32x4{0u, 0u, 0u, 0u};
-                int id0 = 0;
-                if (q < nq) {
-                    w = st[q];
-                    const int src = q / NL, i = q - src * NL;
-                    id0 = start + (i * RR_NT + stid[src]) * VEC;
+                    for (int i = 0; i < NL; ++i) st[(rk - b0) * NL + i] = raw[i];
+                    stid[rk - b0] = tid;
+                }
+                wave_lds_sync();
+                // one staged 16-byte word (VEC elements) per lane per step; a
+                // wave prefix of the hit counts places the hits in the list
+                const int nq = min(RR_SCAP, np - b0) * NL;     // words: src * NL + i
+                for (int q0 = 0; q0 < nq; q0 += DDT_WAVE) {
+                    const int q = q0 + lane;
+                    uint32_t hit = 0u;
+                    u32x4 w = u32x4{0u, 0u, 0u, 0u};
+                    int id0 = 0;
+                    if (q < nq) {
+                        w = st[q];
+                        const int src = q / NL, i = q - src * NL;
+                        id0 = start + (i * RR_NT + stid[src]) * VEC;
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e)
-                        hit |= (uint32_t)((RR_X(w, e) >= tauf) & (!chk | (id0 + e < V))) << e;
+                        for (int e = 0; e < VEC; ++e)
+                            hit |= (uint32_t)((RR_X(w, e) >= tauf) & (!chk | (id0 + e < V))) << e;
+                    }
+                    const int nh = __popc(hit);
+                    const int incl = wave_incl_scan_i32(nh);
+                    const int tot = __builtin_amdgcn_readlane(incl, DDT_WAVE - 1);
+                    int base = 0;
+                    if (lane == 0) base = atomicAdd(&s_cnt, tot);
+                    base = __builtin_amdgcn_readfirstlane(base);
+                    int slot = base + incl - nh;
+                    while (hit) {
+                        const int e = __ffs(hit) - 1;
+                        hit &= hit - 1;
+                        if (slot < RR_CAP) s_list[slot] = vkey(RR_X(w, e), id0 + e);
+                        ++slot;
+                    }
                 }
-                const int nh = __popc(hit);
-                const int incl = wave_incl_scan_i32(nh);
-                const int tot = __builtin_amdgcn_readlane(incl, DDT_WAVE - 1);
-                int base = 0;
-                if (lane == 0) base = atomicAdd(&s_cnt, tot);
-                base = __builtin_amdgcn_readfirstlane(base);
-                int slot = base + incl - nh;
-                while (hit) {
-                    const int e = __ffs(hit) - 1;
-                    hit &= hit - 1;
-                    if (slot < RR_CAP) s_list[slot] = vkey(RR_X(w, e), id0 + e);
-                    ++slot;
-                }
+                wave_lds_sync();                         // before the next batch is staged
             }
         }
     }
@@ -329,16 +345,20 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
         }
         for (int k = cnt + tid; k < K; k += RR_NT) okeys[k] = 0ull;
     } else {
-        // list overflow (massive ties): exact K rounds over the registers
+        // list overflow (massive ties): exact K rounds, each reading the
+        // chunk again one 16-byte word at a time (keeping every element's key
+        // in registers would set the register budget of the whole kernel)
         uint64_t prev = ~0ull;
         for (int k = 0; k < K; ++k) {
             uint64_t best = 0ull;
-#pragma unroll
+#pragma unroll 1
             for (int i = 0; i < NL; ++i) {
+                u32x4 rw[1];
+                rr_load<BF16, 1>(rw, row, al, start + i * RR_NT * VEC, V, tid);
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
                     if (RR_ID(i, e) < V) {
-                        const uint64_t v = vkey(RR_X(raw[i], e), RR_ID(i, e));
+                        const uint64_t v = vkey(RR_X(rw[0], e), RR_ID(i, e));
                         if (v < prev && v > best) best = v;
                     }
                 }

@@ -359,7 +359,9 @@ int ddt_set_reduce_events(void* const* events, int n_pairs);
 /* Text for a status code. */
 const char* ddt_strerror(int status);
 
-/* Chunk length (elements) of the row reduction for a dtype. */
+/* Chunk length (elements) of the row reduction for a dtype, for launches of
+ * fewer than 256 rows (8192 bf16, 4096 fp32).  Launches of 256 rows or more
+ * use chunks twice as long.  Returns -1 for an unknown dtype. */
 int ddt_chunk_elems(int dtype);
 
 #ifdef __cplusplus

@@ -82,6 +82,41 @@ def test_row_topk_parity(dtype, V):
             np.testing.assert_allclose(float(sp[i]), s, rtol=1e-5, atol=1e-30)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [8193, 33001])
+def test_row_topk_parity_wide_launch(dtype, V):
+    # 260 rows: launches of 256 rows or more reduce chunks of twice the length
+    from dynamic_draft_tree_row_amd import api
+    n = 260
+    base = _rows_with_ties(V, dtype, V + 1)
+    g = np.random.default_rng(V)
+    extra = np.stack([synth.cast_row((g.standard_normal(V) * g.uniform(0.3, 3)).astype(np.float32), dtype)
+                      for _ in range(n - base.shape[0])])
+    raw = np.concatenate([base, extra])
+    pad = 5
+    host = np.zeros((1, n, V + pad), raw.dtype)
+    host[0, :, :V] = raw
+    x = H.to_dev(host, dtype)[:, :, :V]
+    for K in (1, 10, 32):
+        say(f"row_topk wide dtype={dtype} V={V} K={K}")
+        ws = torch.empty(api.workspace_bytes(n, V, x.dtype, K), dtype=torch.uint8, device="cuda")
+        ids = torch.empty((n, K), dtype=torch.int32, device="cuda")
+        lc = torch.empty((n, K), dtype=torch.float32, device="cuda")
+        mx = torch.empty(n, dtype=torch.float32, device="cuda")
+        sp = torch.empty(n, dtype=torch.float32, device="cuda")
+        api.row_topk(x, K, ws, ids, lc, mx, sp)
+        torch.cuda.synchronize()
+        ids_h, lc_h, mx_h, sp_h = ids.cpu().numpy(), lc.cpu().numpy(), mx.cpu().numpy(), sp.cpu().numpy()
+        for i in range(n):
+            l = O.decode(raw[i], dtype)
+            m, _, s_ = O.row_stats(l)
+            want = O.topk_ids(l, K)
+            assert ids_h[i].tolist() == want.tolist(), f"row {i} K={K}"
+            np.testing.assert_allclose(lc_h[i], O.log_conf(l, want, m, s_), rtol=1e-5, atol=1e-30)
+            assert mx_h[i] == np.float32(m)
+            np.testing.assert_allclose(sp_h[i], s_, rtol=1e-5, atol=1e-30)
+
+
 # ---------------------------------------------------------------------------
 # whole rounds, small vocabularies
 # ---------------------------------------------------------------------------
