@@ -25,7 +25,7 @@
 #define RR_NV_WIDE 8        // the same for launches of RR_WIDE_ROWS rows or more
 #define RR_WIDE_ROWS 256
 #define RR_CAP 1024         // LDS candidate list
-#define RR_SCAP 16          // lanes per wave staged at a time
+#define RR_SW 64            // words per wave staged at a time
 
 // Chunk shape for NL 16-byte loads per thread.  Wide chunks (8 loads, 64 bf16
 // per thread) halve the per-wave fixed work per element, which is what bounds
@@ -158,8 +158,8 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
     __shared__ float s_wsum[NW];
     __shared__ int s_cnt, s_ties, s_amin;
     __shared__ uint64_t s_list[RR_CAP];
-    __shared__ u32x4 s_stage[NW * RR_SCAP * NL];
-    __shared__ int s_stid[NW * RR_SCAP];
+    __shared__ u32x4 s_stage[NW * RR_SW];
+    __shared__ int s_sid[NW * RR_SW];
 
     const int g = blockIdx.x % groups;
     const int rowg = blockIdx.x / groups;
@@ -179,13 +179,19 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
     rr_load<BF16, NL>(raw, row, al, start, V, tid);
     if (tid == 0) { s_cnt = 0; s_ties = 0; s_amin = 0x7FFFFFFF; }
 
-    // pass 1: thread maximum (padding is -inf)
-    float tm = -INFINITY;
+    // pass 1: the maximum of every 16-byte word, then of the thread (padding
+    // is -inf); the word maxima let only words holding a candidate be staged
+    float wm[NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
+        float a = rr_max3(RR_X(raw[i], 0), RR_X(raw[i], 1), RR_X(raw[i], 2));
 #pragma unroll
-        for (int e = 0; e < VEC; e += 2) tm = rr_max3(tm, RR_X(raw[i], e), RR_X(raw[i], e + 1));
+        for (int e = 3; e < VEC; e += 2) a = rr_max3(a, RR_X(raw[i], e), RR_X(raw[i], e + 1 < VEC ? e + 1 : e));
+        wm[i] = a;
     }
+    float tm = wm[0];
+#pragma unroll
+    for (int i = 1; i < NL; i += 2) tm = rr_max3(tm, wm[i], wm[i + 1 < NL ? i + 1 : i]);
     // wave maximum and the candidate threshold: the K-th largest lane maximum
     // (exact, bit by bit; bf16 codes differ only in their top 16 bits) bounds
     // the workgroup's K-th largest element from below
@@ -272,22 +278,30 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
         const bool chk = !(tauf > -INFINITY) || start + CH > V;
         const uint64_t pm = __ballot(tm >= tauf);
         if (pm) {
-            u32x4* st = s_stage + wid * RR_SCAP * NL;
-            int* stid = s_stid + wid * RR_SCAP;
-            const int np = __popcll(pm);
-            const int rk = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(pm >> 32),
-                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)pm, 0u));
-            // RR_SCAP lanes at a time
-            for (int b0 = 0; b0 < np; b0 += RR_SCAP) {
-                if (tm >= tauf && rk >= b0 && rk < b0 + RR_SCAP) {
+            u32x4* st = s_stage + wid * RR_SW;
+            int* sid = s_sid + wid * RR_SW;
+            // the words whose maximum reaches the threshold, in (word, lane)
+            // order, RR_SW at a time
+            int nw = 0;                                  // words holding a candidate
+            for (int b0 = 0; b0 == 0 || b0 < nw; b0 += RR_SW) {
+                int c = 0;
 #pragma unroll
-                    for (int i = 0; i < NL; ++i) st[(rk - b0) * NL + i] = raw[i];
-                    stid[rk - b0] = tid;
+                for (int i = 0; i < NL; ++i) {
+                    const bool h = wm[i] >= tauf;
+                    const uint64_t m = __ballot(h);
+                    const int pos = c - b0 + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                    if (h && pos >= 0 && pos < RR_SW) {
+                        st[pos] = raw[i];
+                        sid[pos] = start + (i * RR_NT + tid) * VEC;
+                    }
+                    c += __popcll(m);
                 }
+                nw = c;
                 wave_lds_sync();
-                // one staged 16-byte word (VEC elements) per lane per step; a
-                // wave prefix of the hit counts places the hits in the list
-                const int nq = min(RR_SCAP, np - b0) * NL;     // words: src * NL + i
+                // one staged word (VEC elements) per lane; a wave prefix of the
+                // hit counts places the hits in the list
+                const int nq = min(RR_SW, nw - b0);
                 for (int q0 = 0; q0 < nq; q0 += DDT_WAVE) {
                     const int q = q0 + lane;
                     uint32_t hit = 0u;
@@ -295,8 +309,7 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
                     int id0 = 0;
                     if (q < nq) {
                         w = st[q];
-                        const int src = q / NL, i = q - src * NL;
-                        id0 = start + (i * RR_NT + stid[src]) * VEC;
+                        id0 = sid[q];
 #pragma unroll
                         for (int e = 0; e < VEC; ++e)
                             hit |= (uint32_t)((RR_X(w, e) >= tauf) & (!chk | (id0 + e < V))) << e;
