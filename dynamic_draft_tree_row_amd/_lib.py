@@ -46,6 +46,14 @@ class Gate(C.Structure):
 
 
 # exported name -> (restype, argtypes)
+class Attn(C.Structure):
+    """ddt_attn (include/ddt.h)."""
+    _fields_ = [("q", C.c_void_p), ("k_pre", C.c_void_p), ("v_pre", C.c_void_p),
+                ("k_tree", C.c_void_p), ("v_tree", C.c_void_p),
+                ("B", C.c_int32), ("P", C.c_int32), ("Hq", C.c_int32), ("Hkv", C.c_int32),
+                ("D", C.c_int32), ("L", C.c_int32), ("scale", C.c_float)]
+
+
 SIGNATURES = {
     "ddt_strerror": (C.c_char_p, [C.c_int]),
     "ddt_chunk_elems": (C.c_int, [C.c_int]),
@@ -64,6 +72,7 @@ SIGNATURES = {
                                   C.POINTER(Logits), i64, P, P, C.c_int, P, P, P, P, P, P, sz, P]),
     "ddt_succ_update": (C.c_int, [P, i64, C.c_int, C.c_int, C.POINTER(Flat), P, C.c_int,
                                   C.POINTER(Logits), P, sz, P]),
+    "ddt_tree_attention": (C.c_int, [C.POINTER(Flat), C.POINTER(Attn), P, P]),
     "ddt_row_topk": (C.c_int, [C.POINTER(Logits), C.c_int, C.c_int, C.c_int, P, P, P, P, P, sz, P]),
     "ddt_set_reduce_events": (C.c_int, [C.POINTER(P), C.c_int]),
 }

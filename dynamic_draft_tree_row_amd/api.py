@@ -221,6 +221,26 @@ def succ_update(M: torch.Tensor, flat: DeviceFlat, k_succ: int, row_topk: Option
         _stream(stream, M.device)))
 
 
+def tree_attention(flat: DeviceFlat, q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor,
+                   out: torch.Tensor, k_pre: Optional[torch.Tensor] = None,
+                   v_pre: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                   stream=None) -> None:
+    """ddt_tree_attention: q [B][P][Hq][D], k/v_tree [B][P][Hkv][D], k/v_pre [B][L][Hkv][D]
+    (bf16, contiguous); out fp32 [B][P][Hq][D]."""
+    B, P, Hq, D = q.shape
+    Hkv = k_tree.shape[2]
+    Lp = 0 if k_pre is None else k_pre.shape[1]
+    for t in (q, k_tree, v_tree) + ((k_pre, v_pre) if Lp else ()):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("tree_attention takes contiguous bf16 tensors")
+    if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != (B, P, Hq, D):
+        raise ValueError("out must be contiguous fp32 [B][P][Hq][D]")
+    a = L.Attn(_ptr(q), _ptr(k_pre) if Lp else None, _ptr(v_pre) if Lp else None, _ptr(k_tree),
+               _ptr(v_tree), B, P, Hq, Hkv, D, Lp, float(scale if scale is not None else D ** -0.5))
+    L.check("ddt_tree_attention", L.load().ddt_tree_attention(C.byref(flat.c), C.byref(a), _ptr(out),
+                                                                _stream(stream, q.device)))
+
+
 def row_topk(x: torch.Tensor, K: int, ws: torch.Tensor, ids: Optional[torch.Tensor] = None,
              logc: Optional[torch.Tensor] = None, rmax: Optional[torch.Tensor] = None,
              rsp: Optional[torch.Tensor] = None, stream=None) -> None:

@@ -8,6 +8,7 @@
 #include "ddt_device.hpp"
 #include "ddt_rowreduce.hpp"
 #include "ddt_tree_kernels.hpp"
+#include "ddt_attention.hpp"
 
 namespace {
 
@@ -383,6 +384,32 @@ int ddt_tree_verify(const ddt_tree* t, const ddt_flat* f, const ddt_logits* targ
     if (G > ntiles) G = ntiles;
     a.G = G;
     hipLaunchKernelGGL(k_verify, dim3((unsigned)(t->B * G)), dim3(VF_NT), 0, s, a);
+    return launched();
+}
+
+int ddt_tree_attention(const ddt_flat* f, const ddt_attn* a, float* out, void* stream) {
+    if (f == nullptr || a == nullptr || out == nullptr) return DDT_EINVAL;
+    int st = check_flat(f, a->B);
+    if (st) return st;
+    if (a->P != f->P || a->B < 1 || a->Hq < 1 || a->Hkv < 1 || a->L < 0) return DDT_EINVAL;
+    if (a->q == nullptr || a->k_tree == nullptr || a->v_tree == nullptr) return DDT_EINVAL;
+    if (a->L > 0 && (a->k_pre == nullptr || a->v_pre == nullptr)) return DDT_EINVAL;
+    if (a->Hq % a->Hkv != 0) return DDT_EINVAL;
+    if (a->D != TA_D || a->Hq / a->Hkv > 16 || f->W > TA_MW) return DDT_ECAPACITY;
+    const long long qn = (long long)a->B * a->P * a->Hq * TA_D;
+    const long long pn = (long long)a->B * a->L * a->Hkv * TA_D;
+    const long long tn = (long long)a->B * a->P * a->Hkv * TA_D;
+    if (qn > INT32_MAX || pn > INT32_MAX || tn > INT32_MAX) return DDT_ECAPACITY;
+    AttnArgs x;
+    x.q = (const uint16_t*)a->q; x.kp = (const uint16_t*)a->k_pre; x.vp = (const uint16_t*)a->v_pre;
+    x.kt = (const uint16_t*)a->k_tree; x.vt = (const uint16_t*)a->v_tree;
+    x.mask = f->mask; x.m = f->m; x.out = out;
+    x.P = a->P; x.W = f->W; x.Hq = a->Hq; x.Hkv = a->Hkv; x.G = a->Hq / a->Hkv; x.L = a->L;
+    x.tiles = (a->P * x.G + TA_ROWS - 1) / TA_ROWS;
+    x.sl2 = a->scale * DDT_LOG2E;
+    const long long grid = (long long)a->B * a->Hkv * x.tiles;
+    if (grid > INT32_MAX) return DDT_ECAPACITY;
+    hipLaunchKernelGGL(k_tree_attention, dim3((unsigned)grid), dim3(TA_NT), 0, (hipStream_t)stream, x);
     return launched();
 }
 

@@ -335,6 +335,43 @@ int ddt_succ_update(int32_t* M, int64_t M_bstride, int V, int k_succ, const ddt_
                     const int32_t* row_topk, int k_top, const ddt_logits* target /*host or NULL*/,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Tree attention: the verify forward's attention over prefix and tree        */
+/* ------------------------------------------------------------------------ */
+/*
+ * ddt_tree_attention -- scaled dot-product attention of every verified flat
+ * position over the context prefix and its own ancestors, itself included;
+ * siblings are never visible ([E2] reranking section and engineering
+ * difficulty one; [GR] step (3): the hybrid tree is flattened with the same
+ * mask before the one verify forward).  The tree positions visible to flat
+ * position i are the set bits of f->mask row i (as ddt_tree_build_mask
+ * writes it); every prefix position is visible.  Query head h reads
+ * key/value head h / (Hq / Hkv).
+ *
+ * Tensors are bf16 and contiguous (element strides follow from the sizes):
+ *   q               [B][P][Hq][D]    queries of the flat positions, P = f->P
+ *   k_pre, v_pre    [B][L][Hkv][D]   the context's keys and values (may be NULL if L = 0)
+ *   k_tree, v_tree  [B][P][Hkv][D]   keys and values of the flat positions
+ * out: fp32 [B][P][Hq][D], device; positions past f->m[b] are written as 0.
+ * The softmax uses scale * q.k; P (the attention weights) enters the value
+ * product rounded to bf16, everything else accumulates in fp32.
+ * Limits: D = 128; Hq a multiple of Hkv with Hq / Hkv <= 16.
+ * Errors: DDT_EINVAL for null or inconsistent arguments (B or P differing from
+ * f), DDT_ECAPACITY for other D, larger groups, or tensors past 2^31 elements.
+ */
+typedef struct ddt_attn {
+    const void* q;
+    const void* k_pre;
+    const void* v_pre;
+    const void* k_tree;
+    const void* v_tree;
+    int32_t B, P, Hq, Hkv, D, L;
+    float scale;
+} ddt_attn;
+
+int ddt_tree_attention(const ddt_flat* f /*host*/, const ddt_attn* a /*host*/, float* out,
+                       void* stream);
+
 /*
  * ddt_row_topk -- the vocabulary-wide row reduction on its own: for rows
  * (i0, i1) in [n0) x [n1), max, sigma' and the top-K ids with their log
