@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libddt.so")
 SOURCES = ["ddt_api.hip"]
-DEPS = ["ddt_api.hip", "ddt_device.hpp", "ddt_rowreduce.hpp", "ddt_tree_kernels.hpp"]
+DEPS = ["ddt_api.hip", "ddt_device.hpp", "ddt_rowreduce.hpp", "ddt_tree_kernels.hpp", "ddt_attention.hpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

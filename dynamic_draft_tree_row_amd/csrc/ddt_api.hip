@@ -394,7 +394,7 @@ int ddt_tree_attention(const ddt_flat* f, const ddt_attn* a, float* out, void* s
     if (a->P != f->P || a->B < 1 || a->Hq < 1 || a->Hkv < 1 || a->L < 0) return DDT_EINVAL;
     if (a->q == nullptr || a->k_tree == nullptr || a->v_tree == nullptr) return DDT_EINVAL;
     if (a->L > 0 && (a->k_pre == nullptr || a->v_pre == nullptr)) return DDT_EINVAL;
-    if (a->Hq % a->Hkv != 0) return DDT_EINVAL;
+    if (a->Hq % a->Hkv != 0 || !(a->scale > 0.f) || !(a->scale < INFINITY)) return DDT_EINVAL;
     if (a->D != TA_D || a->Hq / a->Hkv > 16 || f->W > TA_MW) return DDT_ECAPACITY;
     const long long qn = (long long)a->B * a->P * a->Hq * TA_D;
     const long long pn = (long long)a->B * a->L * a->Hkv * TA_D;
@@ -406,6 +406,7 @@ int ddt_tree_attention(const ddt_flat* f, const ddt_attn* a, float* out, void* s
     x.mask = f->mask; x.m = f->m; x.out = out;
     x.P = a->P; x.W = f->W; x.Hq = a->Hq; x.Hkv = a->Hkv; x.G = a->Hq / a->Hkv; x.L = a->L;
     x.tiles = (a->P * x.G + TA_ROWS - 1) / TA_ROWS;
+    x.groups = a->B * a->Hkv;
     x.sl2 = a->scale * DDT_LOG2E;
     const long long grid = (long long)a->B * a->Hkv * x.tiles;
     if (grid > INT32_MAX) return DDT_ECAPACITY;

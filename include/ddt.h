@@ -357,7 +357,8 @@ int ddt_succ_update(int32_t* M, int64_t M_bstride, int V, int k_succ, const ddt_
  * product rounded to bf16, everything else accumulates in fp32.
  * Limits: D = 128; Hq a multiple of Hkv with Hq / Hkv <= 16.
  * Errors: DDT_EINVAL for null or inconsistent arguments (B or P differing from
- * f), DDT_ECAPACITY for other D, larger groups, or tensors past 2^31 elements.
+ * f, scale not positive and finite), DDT_ECAPACITY for other D, larger groups,
+ * or tensors past 2^31 elements.
  */
 typedef struct ddt_attn {
     const void* q;
