@@ -4,15 +4,22 @@ from __future__ import annotations
 import os
 import shutil
 import subprocess
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libddt.so")
-SOURCES = ["ddt_api.hip"]
-DEPS = ["ddt_api.hip", "ddt_device.hpp", "ddt_rowreduce.hpp", "ddt_tree_kernels.hpp", "ddt_attention.hpp"]
+# (source, extra flags): the attention kernel assumes no NaNs and runs with
+# the IEEE mode off, so that its float maxima need no operand canonicalisation
+SOURCES = [
+    ("ddt_api.hip", []),
+    ("ddt_attention.hip", ["-fno-honor-nans", "-mno-amdgpu-ieee"]),
+]
+DEPS = ["ddt_api.hip", "ddt_attention.hip", "ddt_device.hpp", "ddt_rowreduce.hpp",
+        "ddt_tree_kernels.hpp", "ddt_attention.hpp"]
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
@@ -25,15 +32,24 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; the draft-tree library needs ROCm's hipcc to build")
 
 
+def _run(cmd, verbose):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + r.stdout + r.stderr)
+    if verbose and r.stderr.strip():
+        print(r.stderr)
+
+
 def build(verbose: bool = False) -> str:
     """Always recompiles; writes libddt.so next to this file and returns its path."""
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + r.stdout + r.stderr)
-    if verbose and r.stderr.strip():
-        print(r.stderr)
+    with tempfile.TemporaryDirectory() as d:
+        objs = []
+        for src, extra in SOURCES:
+            obj = os.path.join(d, src + ".o")
+            _run([hipcc(), *HIPCC_FLAGS, *extra, "-c", "-o", obj, os.path.join(CSRC, src)], verbose)
+            objs.append(obj)
+        _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -410,7 +410,7 @@ int ddt_tree_attention(const ddt_flat* f, const ddt_attn* a, float* out, void* s
     x.sl2 = a->scale * DDT_LOG2E;
     const long long grid = (long long)a->B * a->Hkv * x.tiles;
     if (grid > INT32_MAX) return DDT_ECAPACITY;
-    hipLaunchKernelGGL(k_tree_attention, dim3((unsigned)grid), dim3(TA_NT), 0, (hipStream_t)stream, x);
+    ddt_attention_launch(x, (unsigned)grid, (hipStream_t)stream);
     return launched();
 }
 
