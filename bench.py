@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 SEED = 1002
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -175,6 +176,62 @@ def ingest_pmc(fetch_csv: str, write_csv: str, workload: str, ring: int) -> None
     print(json.dumps(out))
 
 
+def tree_attention_detail(api, dev, seed: int = 7, launches: int = 10) -> dict:
+    """The verify forward's tree attention at the B=64 mixed shape: 129 flat
+    positions per request over a 4096-token prefix, 32 query and 8 key/value
+    heads of 128 (an 8B-class target).  Trees are random (every parent within
+    the 16 positions before its child); q, k and v are seeded normal bf16.
+    Timed with events on the launch stream; algorithmic flops count the
+    visible (query, key) pairs only: 4 * D per pair and query head."""
+    import torch
+    B, P, L, Hq, Hkv, D = 64, 129, 4096, 32, 8, 128
+    rng = np.random.default_rng(seed)
+    flat = api.DeviceFlat(B, P - 1, 10, dev)
+    W = flat.W
+    rows = np.arange(B)
+    masks = np.zeros((B, P, W), np.uint32)
+    vis = np.zeros((B, P), np.int64)                 # visible tree positions per query
+    for i in range(P):
+        if i > 0:
+            par = rng.integers(max(0, i - 16), i, size=B)
+            masks[:, i] = masks[rows, par]
+            vis[:, i] = vis[rows, par]
+        masks[:, i, i // 32] |= np.uint32(1 << (i % 32))
+        vis[:, i] += 1
+    flat.mask.copy_(torch.from_numpy(masks.view(np.int32)).to(dev))
+    flat.m.fill_(P - 1)
+    g = torch.Generator(device=dev).manual_seed(seed)
+    mk = lambda *shape: torch.randn(*shape, device=dev, generator=g).to(torch.bfloat16)
+    q, kt, vt = mk(B, P, Hq, D), mk(B, P, Hkv, D), mk(B, P, Hkv, D)
+    kp, vp = mk(B, L, Hkv, D), mk(B, L, Hkv, D)
+    out = torch.empty(B, P, Hq, D, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        api.tree_attention(flat, q, kt, vt, out, k_pre=kp, v_pre=vp)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * launches)]
+    for i in range(launches):
+        ev[2 * i].record()
+        api.tree_attention(flat, q, kt, vt, out, k_pre=kp, v_pre=vp)
+        ev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    us = np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(launches)])
+    pairs = float(B * P * L + vis.sum())
+    flops = 4.0 * D * Hq * pairs
+    tflops = flops / us.mean() / 1e6
+    kv_bytes = (kp.numel() + vp.numel() + kt.numel() + vt.numel()) * 2
+    log(f"tree attention: {us.mean():.1f} us, {tflops:.1f} TFLOP/s ({tflops / PEAK_BF16_TFLOPS:.3f} of peak)")
+    res = {"kernel": "k_tree_attention (bf16 MFMA 32x32x16, fp32 accumulate)",
+           "shape": {"B": B, "P": P, "prefix": L, "Hq": Hq, "Hkv": Hkv, "D": D},
+           "avg_launch_us": round(float(us.mean()), 2), "launches": launches,
+           "flops_per_launch": flops, "tflops": round(float(tflops), 1),
+           "roofline": {"bound": "mfma", "achieved": round(float(tflops), 1), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(float(tflops / PEAK_BF16_TFLOPS), 4)},
+           "kv_gbs": round(float(kv_bytes / us.mean() / 1e3), 1)}
+    del q, kt, vt, kp, vp, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, slot, cast_np, seconds):
     """The oracle as it stands, on one core, on ring slot 0's inputs."""
     from oracle import ddt_oracle as O
@@ -212,6 +269,10 @@ def main():
     ap.add_argument("--ring", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-attention", action="store_true",
+                    help="only a few tree-attention launches and the calibration copy, for rocprofv3 --pmc")
+    ap.add_argument("--no-attention", action="store_true",
+                    help="skip the tree-attention measurement (the verify forward's MFMA kernel)")
     ap.add_argument("--break-even", action="store_true",
                     help="CAST at the break-even thresholds C1=1, C2=0.1, C3=0.5")
     ap.add_argument("--pmc-run", action="store_true",
@@ -236,6 +297,19 @@ def main():
     from gen import configs, synth
     from dynamic_draft_tree_row_amd import _lib, api
     from dynamic_draft_tree_row_amd.round_driver import RoundRunner, RoundShape
+
+    if args.pmc_attention:
+        dev = torch.device("cuda", 0)
+        torch.cuda.set_device(dev)
+        _lib.load()
+        tree_attention_detail(api, dev, launches=2)
+        x = torch.ones(CAL_BYTES // 4, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        torch.neg(x, out=y)
+        torch.cuda.synchronize()
+        log(f"pmc attention run done: 5 launches, then a {CAL_BYTES >> 20} MiB copy (neg)")
+        return
 
     w = configs.C2
     if args.workload == "fixed":
@@ -486,6 +560,8 @@ def main():
             "mean_tau": round(float(np.mean([np.mean(s["accept"]) + 1 for s in stats])), 3),
         },
     }
+    if not args.no_attention:
+        out["detail"]["tree_attention"] = tree_attention_detail(api, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, ring[0], cast_np, args.cpu_seconds)
     else:
