@@ -373,6 +373,93 @@ typedef struct ddt_attn {
 int ddt_tree_attention(const ddt_flat* f /*host*/, const ddt_attn* a /*host*/, float* out,
                        void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Paged KV cache: committing the accepted path, sharing, release            */
+/* ------------------------------------------------------------------------ */
+/*
+ * Candidate KV is kept apart from the committed context; after the verify
+ * the accepted tokens' KV is committed and the rejected candidates' KV is
+ * dropped; with block-paged storage, block allocation, reference counts,
+ * reclamation and copy-on-write are part of that step ([E2] engineering
+ * difficulty two, and the decode-step flow: commit accepted tokens and their
+ * KV, discard rejected candidate KV).
+ *
+ * Reading: the candidates' KV is the round's contiguous tree buffer
+ * (k_tree, v_tree [B][P][Hkv][D], written by the verify forward and read by
+ * ddt_tree_attention), so dropping a rejected candidate costs nothing.  The
+ * committed context is a pool of fixed-size blocks:
+ *   k, v        bf16 [n_blocks][block][Hkv][D]   token t of request b sits at
+ *               slot t % block of block table[b][t / block]
+ *   table       [B][max_blocks]  block ids of each request, -1 past its end
+ *   len         [B]              tokens committed per request
+ *   ref         [n_blocks]       number of tables holding each block
+ *   free_ids    [n_blocks]       stack of free block ids: free_ids[0 .. *n_free)
+ *   n_free      [1]
+ *   plan        [B][4] int32     scratch written by ddt_kv_commit
+ * All arrays are device memory owned by the caller; the library only reads
+ * and writes them.  A consistent state has ref[x] = the number of table rows
+ * holding x, and free_ids[0 .. n_free) = the blocks with ref 0, each once.
+ * Calls on one cache must be ordered on one stream (they are not atomic with
+ * respect to each other).
+ */
+typedef struct ddt_kv_cache {
+    void* k;
+    void* v;
+    int32_t* table;
+    int32_t* len;
+    int32_t* ref;
+    int32_t* free_ids;
+    int32_t* n_free;
+    int32_t* plan;
+    int32_t B, max_blocks, n_blocks, block, Hkv, D;
+} ddt_kv_cache;
+
+/*
+ * ddt_kv_commit -- append each request's accepted path to its context.
+ * For request b with accept_len[b] = a >= 0, the n = a + 1 flat positions
+ * accept_path[b][0 .. a] (root first, as ddt_tree_verify writes them) are
+ * appended in path order: k_tree[b][accept_path[b][j]] becomes context token
+ * len[b] + j, likewise for v.  Only the block holding token len[b] can be
+ * partly filled; if it is and it is shared (ref > 1 when the call starts),
+ * it is copied first (copy-on-write): a new block takes its committed slots
+ * and replaces it in this table, and the old block loses one holder.  Every
+ * other token goes to a new block.  need[b] = new blocks (+1 for a copy).
+ * Requests are admitted in index order while the free stack lasts: b is
+ * admitted iff need[0] + .. + need[b] (over requests that got this far) <=
+ * *n_free, so a request that does not fit, and every later one, is left
+ * unchanged.  Admitted requests take their blocks from the top of the stack
+ * in index order, the copy first, then the new blocks in table order.  Old
+ * blocks left with no holder are then pushed, ordered by the lowest index of
+ * the requests that copied them.  The outcome is deterministic.
+ * status[b]: n (tokens committed); 0 if accept_len[b] < 0 (nothing done);
+ * -1 if the context would pass max_blocks * block tokens; -2 if the free
+ * stack ran out; -3 if a path entry is outside [0, P).
+ * k_tree, v_tree: bf16 [B][P][Hkv][D] (device), Dp = the path row length - 1.
+ * Errors: DDT_EINVAL for null or inconsistent arguments ((Hkv*D) % 8 != 0
+ * included); DDT_ECAPACITY for B > 1024 or max_blocks > 4096.
+ */
+int ddt_kv_commit(const ddt_kv_cache* c /*host struct*/, const int32_t* accept_len /*[B]*/,
+                  const int32_t* accept_path /*[B][Dp+1]*/, int Dp, const void* k_tree,
+                  const void* v_tree, int P, int32_t* status /*[B]*/, void* stream);
+
+/*
+ * ddt_kv_fork -- request dst[i] takes the context of src[i] (for i < n):
+ * it shares src's blocks (each gains a holder) and its length.  dst[i] must
+ * hold no blocks (len 0, table row all -1) and differ from every src; pairs
+ * that break this are skipped with status[i] = -1, otherwise status[i] = 0.
+ * src, dst, status: device [n].  Pairs are applied in order.
+ */
+int ddt_kv_fork(const ddt_kv_cache* c /*host struct*/, const int32_t* src, const int32_t* dst, int n,
+                int32_t* status, void* stream);
+
+/*
+ * ddt_kv_release -- drop the context of requests req[0 .. n) (device), in
+ * order: every block of the request loses one holder, the blocks left with
+ * none are pushed on the free stack in table order, and the request's table
+ * row and length are cleared.  A request listed twice is released once.
+ */
+int ddt_kv_release(const ddt_kv_cache* c /*host struct*/, const int32_t* req, int n, void* stream);
+
 /*
  * ddt_row_topk -- the vocabulary-wide row reduction on its own: for rows
  * (i0, i1) in [n0) x [n1), max, sigma' and the top-K ids with their log
