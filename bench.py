@@ -232,6 +232,90 @@ def tree_attention_detail(api, dev, seed: int = 7, launches: int = 10) -> dict:
     return res
 
 
+def kv_commit_detail(api, dev, seed: int = 11, commits: int = 20) -> dict:
+    """Committing the accepted path into a block-paged KV context at the B=64
+    mixed shape: 16-token blocks, 8 key/value heads of 128, contexts of
+    4096 + b % 16 tokens (so that tails are partly filled), accepted paths of
+    0..10 draft tokens plus the root drawn at random from 129 flat positions.
+    Commits (bookkeeping + copy kernels) are timed with events on the launch
+    stream, eagerly one by one (host issue included) and as replays of a HIP
+    graph that holds `commits` of them; bytes count each committed row read
+    once and written once."""
+    import torch
+    B, P, Dp, Hkv, D, block = 64, 129, 10, 8, 128, 16
+    per = 300                                        # blocks set aside per request
+    kv = api.PagedKV(B, 320, B * per, block, Hkv, D, dev)
+    base = 4096
+    lens = torch.tensor([base + b % 16 for b in range(B)], dtype=torch.int32)
+    used = (lens + block - 1) // block
+    table = torch.full((B, 320), -1, dtype=torch.int32)
+    ref = torch.zeros(B * per, dtype=torch.int32)
+    taken = []
+    for b in range(B):
+        ids = torch.arange(b * per, b * per + int(used[b]), dtype=torch.int32)
+        table[b, :len(ids)] = ids
+        ref[ids.long()] = 1
+        taken.append(ids)
+    free = torch.tensor(sorted(set(range(B * per)) - set(torch.cat(taken).tolist()), reverse=True),
+                        dtype=torch.int32)
+    kv.table.copy_(table.to(dev)); kv.len.copy_(lens.to(dev)); kv.ref.copy_(ref.to(dev))
+    kv.free_ids[:len(free)].copy_(free.to(dev)); kv.n_free.fill_(len(free))
+    rng = np.random.default_rng(seed)
+    g = torch.Generator(device=dev).manual_seed(seed)
+    kt = torch.randn(B, P, Hkv, D, device=dev, generator=g).to(torch.bfloat16)
+    vt = torch.randn(B, P, Hkv, D, device=dev, generator=g).to(torch.bfloat16)
+    acc_all, path_all = [], []
+    for _ in range(2 * commits + 3):
+        acc = rng.integers(0, Dp + 1, size=B).astype(np.int32)
+        path = np.full((B, Dp + 1), -1, np.int32)
+        for b in range(B):
+            path[b, :acc[b] + 1] = np.concatenate([[0], 1 + rng.permutation(P - 1)[:acc[b]]])
+        acc_all.append(torch.from_numpy(acc).to(dev))
+        path_all.append(torch.from_numpy(path).to(dev))
+    status = torch.empty(B, dtype=torch.int32, device=dev)
+    for i in range(3):
+        kv.commit(acc_all[i], path_all[i], kt, vt, status)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * commits)]
+    for i in range(commits):
+        ev[2 * i].record()
+        kv.commit(acc_all[3 + i], path_all[3 + i], kt, vt, status)
+        ev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    if not bool((status > 0).all()):
+        raise RuntimeError("kv commit refused a request in the bench setup")
+    us = np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(commits)])
+    # the next `commits` commits captured once and replayed once
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(commits):
+            kv.commit(acc_all[3 + commits + i], path_all[3 + commits + i], kt, vt, status)
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record()
+    graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    if not bool((status > 0).all()):
+        raise RuntimeError("kv commit refused a request in the bench setup")
+    graph_us = g0.elapsed_time(g1) * 1e3 / commits
+    tokens = float(np.mean([(a.cpu().numpy() + 1).sum() for a in acc_all[3:]]))
+    nbytes = tokens * Hkv * D * 2 * 2 * 2            # k and v, read and written
+    log(f"kv commit: {us.mean():.2f} us eager, {graph_us:.2f} us per commit in a graph, "
+        f"{tokens:.0f} tokens")
+    res = {"calls": "ddt_kv_commit (k_kv_plan + k_kv_copy)",
+           "shape": {"B": B, "block": block, "Hkv": Hkv, "D": D, "context": "4096 + b % 16", "Dp": Dp},
+           "eager_us": round(float(us.mean()), 2), "graph_us": round(float(graph_us), 2),
+           "commits": commits, "tokens_per_commit": round(tokens, 1),
+           "gbs_graph": round(float(nbytes / graph_us / 1e3), 2),
+           "bound": "latency (two dependent launches; about 1.5 MB moved)"}
+    del kv, kt, vt
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, slot, cast_np, seconds):
     """The oracle as it stands, on one core, on ring slot 0's inputs."""
     from oracle import ddt_oracle as O
@@ -562,6 +646,7 @@ def main():
     }
     if not args.no_attention:
         out["detail"]["tree_attention"] = tree_attention_detail(api, dev)
+        out["detail"]["kv_commit"] = kv_commit_detail(api, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, ring[0], cast_np, args.cpu_seconds)
     else:

@@ -54,6 +54,14 @@ class Attn(C.Structure):
                 ("D", C.c_int32), ("L", C.c_int32), ("scale", C.c_float)]
 
 
+class KVCache(C.Structure):
+    """ddt_kv_cache (include/ddt.h)."""
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("table", C.c_void_p), ("len", C.c_void_p),
+                ("ref", C.c_void_p), ("free_ids", C.c_void_p), ("n_free", C.c_void_p),
+                ("plan", C.c_void_p), ("B", C.c_int32), ("max_blocks", C.c_int32),
+                ("n_blocks", C.c_int32), ("block", C.c_int32), ("Hkv", C.c_int32), ("D", C.c_int32)]
+
+
 SIGNATURES = {
     "ddt_strerror": (C.c_char_p, [C.c_int]),
     "ddt_chunk_elems": (C.c_int, [C.c_int]),
@@ -73,6 +81,9 @@ SIGNATURES = {
     "ddt_succ_update": (C.c_int, [P, i64, C.c_int, C.c_int, C.POINTER(Flat), P, C.c_int,
                                   C.POINTER(Logits), P, sz, P]),
     "ddt_tree_attention": (C.c_int, [C.POINTER(Flat), C.POINTER(Attn), P, P]),
+    "ddt_kv_commit": (C.c_int, [C.POINTER(KVCache), P, P, C.c_int, P, P, C.c_int, P, P]),
+    "ddt_kv_fork": (C.c_int, [C.POINTER(KVCache), P, P, C.c_int, P, P]),
+    "ddt_kv_release": (C.c_int, [C.POINTER(KVCache), P, C.c_int, P]),
     "ddt_row_topk": (C.c_int, [C.POINTER(Logits), C.c_int, C.c_int, C.c_int, P, P, P, P, P, sz, P]),
     "ddt_set_reduce_events": (C.c_int, [C.POINTER(P), C.c_int]),
 }

@@ -248,3 +248,54 @@ def row_topk(x: torch.Tensor, K: int, ws: torch.Tensor, ids: Optional[torch.Tens
     L.check("ddt_row_topk", L.load().ddt_row_topk(
         C.byref(d), x.shape[0], x.shape[1], K, _ptr(ids), _ptr(logc), _ptr(rmax), _ptr(rsp),
         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream, x.device)))
+
+
+class PagedKV:
+    """The caller-owned arrays of a block-paged KV context (ddt_kv_cache) on
+    one device: k, v bf16 [n_blocks][block][Hkv][D], table [B][max_blocks],
+    len [B], ref [n_blocks], a free stack with block 0 on top, and the commit's
+    plan scratch.  The methods bind the three calls; all state stays on the
+    device."""
+
+    def __init__(self, B: int, max_blocks: int, n_blocks: int, block: int, Hkv: int, D: int,
+                 device="cuda"):
+        i32 = dict(dtype=torch.int32, device=device)
+        self.k = torch.zeros(n_blocks, block, Hkv, D, dtype=torch.bfloat16, device=device)
+        self.v = torch.zeros_like(self.k)
+        self.table = torch.full((B, max_blocks), -1, **i32)
+        self.len = torch.zeros(B, **i32)
+        self.ref = torch.zeros(n_blocks, **i32)
+        self.free_ids = torch.arange(n_blocks - 1, -1, -1, **i32)
+        self.n_free = torch.tensor([n_blocks], **i32)
+        self.plan = torch.zeros(B, 4, **i32)
+        self.B, self.max_blocks, self.n_blocks, self.block, self.Hkv, self.D = \
+            B, max_blocks, n_blocks, block, Hkv, D
+        self.c = L.KVCache(_ptr(self.k), _ptr(self.v), _ptr(self.table), _ptr(self.len), _ptr(self.ref),
+                           _ptr(self.free_ids), _ptr(self.n_free), _ptr(self.plan),
+                           B, max_blocks, n_blocks, block, Hkv, D)
+
+    def commit(self, accept_len: torch.Tensor, accept_path: torch.Tensor, k_tree: torch.Tensor,
+               v_tree: torch.Tensor, status: torch.Tensor, stream=None) -> None:
+        """ddt_kv_commit: accept_path [B][Dp+1] int32; k/v_tree bf16 [B][P][Hkv][D]."""
+        B, P = k_tree.shape[0], k_tree.shape[1]
+        if B != self.B or tuple(k_tree.shape[2:]) != (self.Hkv, self.D) or v_tree.shape != k_tree.shape:
+            raise ValueError("k_tree / v_tree must be [B][P][Hkv][D] of this cache")
+        for t in (k_tree, v_tree):
+            if t.dtype != torch.bfloat16 or not t.is_contiguous():
+                raise ValueError("k_tree / v_tree must be contiguous bf16")
+        for t in (accept_len, accept_path, status):
+            if t.dtype != torch.int32 or not t.is_contiguous():
+                raise ValueError("accept_len, accept_path and status must be contiguous int32")
+        L.check("ddt_kv_commit", L.load().ddt_kv_commit(
+            C.byref(self.c), _ptr(accept_len), _ptr(accept_path), accept_path.shape[1] - 1,
+            _ptr(k_tree), _ptr(v_tree), P, _ptr(status), _stream(stream, k_tree.device)))
+
+    def fork(self, src: torch.Tensor, dst: torch.Tensor, status: torch.Tensor, stream=None) -> None:
+        """ddt_kv_fork over int32 [n] device vectors."""
+        L.check("ddt_kv_fork", L.load().ddt_kv_fork(C.byref(self.c), _ptr(src), _ptr(dst), src.numel(),
+                                                    _ptr(status), _stream(stream, src.device)))
+
+    def release(self, req: torch.Tensor, stream=None) -> None:
+        """ddt_kv_release over an int32 [n] device vector."""
+        L.check("ddt_kv_release", L.load().ddt_kv_release(C.byref(self.c), _ptr(req), req.numel(),
+                                                          _stream(stream, req.device)))

@@ -9,6 +9,7 @@
 #include "ddt_rowreduce.hpp"
 #include "ddt_tree_kernels.hpp"
 #include "ddt_attention.hpp"
+#include "ddt_kvcache.hpp"
 
 namespace {
 
@@ -411,6 +412,68 @@ int ddt_tree_attention(const ddt_flat* f, const ddt_attn* a, float* out, void* s
     const long long grid = (long long)a->B * a->Hkv * x.tiles;
     if (grid > INT32_MAX) return DDT_ECAPACITY;
     ddt_attention_launch(x, (unsigned)grid, (hipStream_t)stream);
+    return launched();
+}
+
+static int kv_check(const ddt_kv_cache* c, KvCache* out) {
+    if (c == nullptr || c->k == nullptr || c->v == nullptr || c->table == nullptr || c->len == nullptr ||
+        c->ref == nullptr || c->free_ids == nullptr || c->n_free == nullptr || c->plan == nullptr)
+        return DDT_EINVAL;
+    if (c->B < 1 || c->max_blocks < 1 || c->n_blocks < 1 || c->block < 1 || c->Hkv < 1 || c->D < 1)
+        return DDT_EINVAL;
+    if ((long long)c->Hkv * c->D > (1 << 20) || ((long long)c->Hkv * c->D) % 8 != 0) return DDT_EINVAL;
+    if ((((uintptr_t)c->k) | ((uintptr_t)c->v) | ((uintptr_t)c->plan)) & 15) return DDT_EINVAL;
+    if (c->B > KV_MAXB || c->max_blocks > KV_MAXBLK) return DDT_ECAPACITY;
+    if ((long long)c->max_blocks * c->block > INT32_MAX) return DDT_ECAPACITY;
+    out->k = (uint16_t*)c->k; out->v = (uint16_t*)c->v; out->table = c->table; out->len = c->len;
+    out->ref = c->ref; out->free_ids = c->free_ids; out->n_free = c->n_free; out->plan = c->plan;
+    out->B = c->B; out->max_blocks = c->max_blocks; out->n_blocks = c->n_blocks; out->block = c->block;
+    out->Hkv = c->Hkv; out->D = c->D;
+    return DDT_OK;
+}
+
+int ddt_kv_commit(const ddt_kv_cache* c, const int32_t* accept_len, const int32_t* accept_path, int Dp,
+                  const void* k_tree, const void* v_tree, int P, int32_t* status, void* stream) {
+    KvCommitArgs a;
+    int st = kv_check(c, &a.c);
+    if (st) return st;
+    if (accept_len == nullptr || accept_path == nullptr || k_tree == nullptr || v_tree == nullptr ||
+        status == nullptr || P < 1 || Dp < 0)
+        return DDT_EINVAL;
+    if (Dp > DDT_MAX_DEPTH) return DDT_ECAPACITY;
+    if ((((uintptr_t)k_tree) | ((uintptr_t)v_tree)) & 15) return DDT_EINVAL;
+    a.accept_len = accept_len; a.accept_path = accept_path; a.Dp = Dp;
+    a.kt = (const uint16_t*)k_tree; a.vt = (const uint16_t*)v_tree; a.P = P; a.status = status;
+    hipStream_t s = (hipStream_t)stream;
+    hipLaunchKernelGGL(k_kv_plan, dim3(1), dim3(KV_NT), 0, s, a);
+    st = launched();
+    if (st) return st;
+    hipLaunchKernelGGL(k_kv_copy, dim3(c->B, KV_SPLIT), dim3(KV_CT), 0, s, a);
+    return launched();
+}
+
+int ddt_kv_fork(const ddt_kv_cache* c, const int32_t* src, const int32_t* dst, int n, int32_t* status,
+                void* stream) {
+    KvForkArgs a;
+    int st = kv_check(c, &a.c);
+    if (st) return st;
+    if (n < 0) return DDT_EINVAL;
+    if (n == 0) return DDT_OK;
+    if (src == nullptr || dst == nullptr || status == nullptr) return DDT_EINVAL;
+    a.src = src; a.dst = dst; a.n = n; a.status = status;
+    hipLaunchKernelGGL(k_kv_fork, dim3(1), dim3(KV_NT), 0, (hipStream_t)stream, a);
+    return launched();
+}
+
+int ddt_kv_release(const ddt_kv_cache* c, const int32_t* req, int n, void* stream) {
+    KvReleaseArgs a;
+    int st = kv_check(c, &a.c);
+    if (st) return st;
+    if (n < 0) return DDT_EINVAL;
+    if (n == 0) return DDT_OK;
+    if (req == nullptr) return DDT_EINVAL;
+    a.req = req; a.n = n;
+    hipLaunchKernelGGL(k_kv_release, dim3(1), dim3(KV_NT), 0, (hipStream_t)stream, a);
     return launched();
 }
 

@@ -436,7 +436,8 @@ typedef struct ddt_kv_cache {
  * stack ran out; -3 if a path entry is outside [0, P).
  * k_tree, v_tree: bf16 [B][P][Hkv][D] (device), Dp = the path row length - 1.
  * Errors: DDT_EINVAL for null or inconsistent arguments ((Hkv*D) % 8 != 0
- * included); DDT_ECAPACITY for B > 1024 or max_blocks > 4096.
+ * included); DDT_ECAPACITY for B > 1024, max_blocks > 4096 or Dp >
+ * DDT_MAX_DEPTH.
  */
 int ddt_kv_commit(const ddt_kv_cache* c /*host struct*/, const int32_t* accept_len /*[B]*/,
                   const int32_t* accept_path /*[B][Dp+1]*/, int Dp, const void* k_tree,

@@ -45,7 +45,7 @@ def test_struct_layouts_match_the_header():
     """Compile a probe with the host C compiler and compare sizeof/offsetof."""
     fields = {
         "ddt_tree": L.Tree, "ddt_flat": L.Flat, "ddt_logits": L.Logits,
-        "ddt_cast": L.Cast, "ddt_graft_gate": L.Gate,
+        "ddt_cast": L.Cast, "ddt_graft_gate": L.Gate, "ddt_attn": L.Attn, "ddt_kv_cache": L.KVCache,
     }
     lines = ["#include <stdio.h>", "#include <stddef.h>", f'#include "{HEADER}"', "int main(void){"]
     for cname, cls in fields.items():
@@ -140,3 +140,22 @@ def test_calls_reject_bad_arguments_before_launch(lib):
     assert lib.ddt_row_topk(C.byref(huge), 1, 1, 4, None, None, None, None, ws, 1 << 30,
                             None) == L.DDT_ECAPACITY
     assert lib.ddt_strerror(L.DDT_EWORKSPACE).decode() == "workspace too small"
+    # paged KV cache
+    kv = L.KVCache(dummy, dummy, dummy, dummy, dummy, dummy, dummy, dummy, 4, 8, 64, 16, 8, 128)
+    c = lib.ddt_kv_commit
+    assert c(None, dummy, dummy, 8, dummy, dummy, 61, dummy, None) == L.DDT_EINVAL
+    assert c(C.byref(kv), None, dummy, 8, dummy, dummy, 61, dummy, None) == L.DDT_EINVAL
+    assert c(C.byref(kv), dummy, dummy, -1, dummy, dummy, 61, dummy, None) == L.DDT_EINVAL
+    assert c(C.byref(kv), dummy, dummy, 8, dummy, C.c_void_p(base + 8), 61, dummy, None) == L.DDT_EINVAL
+    odd = L.KVCache(dummy, dummy, dummy, dummy, dummy, dummy, dummy, dummy, 4, 8, 64, 16, 3, 5)
+    assert c(C.byref(odd), dummy, dummy, 8, dummy, dummy, 61, dummy, None) == L.DDT_EINVAL
+    big = L.KVCache(dummy, dummy, dummy, dummy, dummy, dummy, dummy, dummy, 2000, 8, 64, 16, 8, 128)
+    assert c(C.byref(big), dummy, dummy, 8, dummy, dummy, 61, dummy, None) == L.DDT_ECAPACITY
+    wide = L.KVCache(dummy, dummy, dummy, dummy, dummy, dummy, dummy, dummy, 4, 5000, 64, 16, 8, 128)
+    assert lib.ddt_kv_release(C.byref(wide), dummy, 1, None) == L.DDT_ECAPACITY
+    assert lib.ddt_kv_fork(C.byref(kv), None, dummy, 1, dummy, None) == L.DDT_EINVAL
+    assert lib.ddt_kv_fork(C.byref(kv), dummy, dummy, -1, dummy, None) == L.DDT_EINVAL
+    assert lib.ddt_kv_release(C.byref(kv), None, 2, None) == L.DDT_EINVAL
+    # nothing to do: no launch, no device touched
+    assert lib.ddt_kv_fork(C.byref(kv), None, None, 0, None, None) == L.DDT_OK
+    assert lib.ddt_kv_release(C.byref(kv), None, 0, None) == L.DDT_OK
