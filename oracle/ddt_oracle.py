@@ -557,7 +557,7 @@ def sample_inverse_cdf(p: np.ndarray, u: float, margins=None) -> int:
 
 
 def verify_stochastic(f: Flat, target_row, draft_row_of, T: float, U: np.ndarray,
-                      margins=None) -> tuple:
+                      margins=None, retrieval=None) -> tuple:
     """Speculative sampling over the flattened tree.
 
     Chain rule (EAGLE-2 explainer, ledger section): accept a drafted token x
@@ -571,6 +571,14 @@ def verify_stochastic(f: Flat, target_row, draft_row_of, T: float, U: np.ndarray
     accepted, or u has no selected child, the next token is drawn from the
     current p by inverse CDF with U[u,1].  p = softmax(target/T), q =
     softmax(draft/T).
+
+    Retrieval children (retrieval[c] true: Graft grafted nodes, which no draft
+    row proposed) are tested with a point-mass proposal q = delta_x (reading
+    of the Graft review's step (3), "the acceptance rule is the standard one"):
+    accepted with probability p(x); a rejection removes x from p and
+    renormalises.  This is an exact speculative-sampling step for any
+    deterministic x, so those nodes keep the output distribution p.  Draft
+    children come first in flat order, then retrieval children.
     """
     n = len([x for x in f.node if x >= 0])
     children = [[] for _ in range(n)]
@@ -583,10 +591,27 @@ def verify_stochastic(f: Flat, target_row, draft_row_of, T: float, U: np.ndarray
         if not children[u]:
             nxt = sample_inverse_cdf(p, float(U[u, 1]), margins)
             break
-        q = softmax_T(draft_row_of(u), T)
+        q = None
         acc = None
         for c in children[u]:
             x = f.token[c]
+            if retrieval is not None and retrieval[c]:
+                ratio = float(p[x])
+                if margins is not None:
+                    margins.append(("accept", abs(float(U[c, 0]) - ratio)))
+                if float(U[c, 0]) < ratio:
+                    acc = c
+                    break
+                r = p.copy()
+                r[x] = 0.0
+                Z = float(np.sum(r))
+                if margins is not None:
+                    margins.append(("residual", Z))
+                if Z > 0.0:
+                    p = r / Z
+                continue
+            if q is None:
+                q = softmax_T(draft_row_of(u), T)
             ratio = p[x] / q[x] if q[x] > 0 else math.inf
             if margins is not None and math.isfinite(ratio):
                 margins.append(("accept", abs(float(U[c, 0]) - ratio) / max(1.0, ratio)))
@@ -701,8 +726,9 @@ def run_round(*, B, V, dtype, D, K_e, K_n, m_max, root_tok, draft_raw, target_ra
                 v = f.node[i]
                 return drow(t.depth[v] + 1, b, t.eslot[v])
 
+            ret = [t.src[v] == 1 if v >= 0 else False for v in f.node]
             mb = []
-            L_, path, tok = verify_stochastic(f, trow, qrow, float(temperature[b]), U[b], mb)
+            L_, path, tok = verify_stochastic(f, trow, qrow, float(temperature[b]), U[b], mb, ret)
             margins.extend((k, v, b) for k, v in mb)
         acc_len[b] = L_
         acc_path[b, :len(path)] = path

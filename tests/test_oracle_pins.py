@@ -523,6 +523,83 @@ def test_residual_after_rejection():
     assert L == 1 and path == [0, 1]
 
 
+def test_point_mass_children_thresholds():
+    """Retrieval children (point-mass proposals): the k-th is accepted iff
+    U < p(x_k) / (1 - p(x_1) - .. - p(x_{k-1})), i.e. from p with the rejected
+    tokens removed and renormalised; the emission then excludes them."""
+    p = np.array([0.1, 0.2, 0.3, 0.15, 0.25])
+    lp = np.log(p)
+    f = _mk_flat([0, 2, 4, 1], [-1, 0, 0, 0])      # root, then children with tokens 2, 4, 1
+    ret = [False, True, True, True]
+    no_q = lambda i: (_ for _ in ()).throw(AssertionError("no draft row is needed"))
+    eps = 1e-9
+    # first child: threshold p(2) = 0.3
+    for u, want in ((0.3 - eps, 1), (0.3 + eps, None)):
+        U = np.array([[0.0, 0.0], [u, 0.0], [0.999, 0.0], [0.999, 0.0]])
+        L, path, _ = O.verify_stochastic(f, lambda i: lp, no_q, 1.0, U, retrieval=ret)
+        assert (path[1] if L else None) == want
+    # second child after rejecting token 2: threshold 0.25 / 0.7
+    t2 = 0.25 / 0.7
+    for u, want in ((t2 - eps, 2), (t2 + eps, None)):
+        U = np.array([[0.0, 0.0], [0.999, 0.0], [u, 0.0], [0.999, 0.0]])
+        L, path, _ = O.verify_stochastic(f, lambda i: lp, no_q, 1.0, U, retrieval=ret)
+        assert (path[1] if L else None) == want
+    # third child after rejecting 2 and 4: threshold 0.2 / 0.45
+    t3 = 0.2 / 0.45
+    for u, want in ((t3 - eps, 3), (t3 + eps, None)):
+        U = np.array([[0.0, 0.0], [0.999, 0.0], [0.999, 0.0], [u, 0.0]])
+        L, path, _ = O.verify_stochastic(f, lambda i: lp, no_q, 1.0, U, retrieval=ret)
+        assert (path[1] if L else None) == want
+    # all rejected: the emission draws from {0: 0.1, 3: 0.15} renormalised
+    for u1, want in ((0.0, 0), (0.4 - eps, 0), (0.4 + eps, 3), (0.999, 3)):
+        U = np.array([[0.0, u1], [0.999, 0.0], [0.999, 0.0], [0.999, 0.0]])
+        L, path, nxt = O.verify_stochastic(f, lambda i: lp, no_q, 1.0, U, retrieval=ret)
+        assert L == 0 and nxt == want
+
+
+def _mixed_trial_counts(N, V, seed=5):
+    """Joint counts of the first two emitted tokens over N verify calls on a
+    tree that mixes sampled draft children and deterministic retrieval nodes:
+    2 draft children of the root drawn from q, then 2 fixed retrieval children,
+    each retrieval child with one fixed retrieval child below it."""
+    g = np.random.default_rng(seed)
+    p = lambda ctx: _cond(seed, ctx, V, 0.03)
+    q = lambda ctx: _cond(seed + 1000, ctx, V, 0.01)
+    counts = np.zeros((V, V))
+    for _ in range(N):
+        tokens, parents, ctxs, ret = [0], [-1], [()], [False]
+        for x in g.choice(V, size=2, p=q(())):
+            tokens.append(int(x)); parents.append(0); ctxs.append((int(x),)); ret.append(False)
+        lvl1 = []
+        for x in (1, 3):                            # fixed retrieval tokens
+            tokens.append(x); parents.append(0); ctxs.append((x,)); ret.append(True)
+            lvl1.append(len(tokens) - 1)
+        for u in lvl1:
+            x = (tokens[u] + 2) % V
+            tokens.append(x); parents.append(u); ctxs.append(ctxs[u] + (x,)); ret.append(True)
+        f = _mk_flat(tokens, parents)
+        U = g.random((len(tokens), 2))
+        L, path, nxt = O.verify_stochastic(f, lambda i: np.log(p(ctxs[i])),
+                                           lambda i: np.log(q(ctxs[i])), 1.0, U, retrieval=ret)
+        emitted = [tokens[i] for i in path[1:]] + [nxt]
+        if len(emitted) < 2:
+            emitted.append(int(g.choice(V, p=p((emitted[0],)))))
+        counts[emitted[0], emitted[1]] += 1
+    expect = np.array([[p(())[a] * p((a,))[c] for c in range(V)] for a in range(V)])
+    return counts, expect
+
+
+@pytest.mark.slow
+def test_point_mass_retrieval_nodes_keep_the_tree_lossless():
+    """Sampled draft children plus deterministic retrieval nodes (point-mass
+    proposals) under the rule: the first two emitted tokens still follow the
+    target's joint distribution."""
+    N, V = 40000, 5
+    counts, expect = _mixed_trial_counts(N, V)
+    assert stats.chisquare(counts.ravel(), expect.ravel() * N).pvalue > 1e-3
+    assert stats.chisquare(counts.sum(1), expect.sum(1) * N).pvalue > 1e-3
+
+
 # ---------------------------------------------------------------------------
 # O9 CAST: P-j Theorem 4.1, P-k anchor scan, P-l select()
 # ---------------------------------------------------------------------------
