@@ -81,6 +81,8 @@ SIGNATURES = {
     "ddt_succ_update": (C.c_int, [P, i64, C.c_int, C.c_int, C.POINTER(Flat), P, C.c_int,
                                   C.POINTER(Logits), P, sz, P]),
     "ddt_tree_attention": (C.c_int, [C.POINTER(Flat), C.POINTER(Attn), P, P]),
+    "ddt_succ_gather_at": (C.c_int, [C.POINTER(Tree), P, C.c_int64, C.c_int, C.c_int, C.c_int, C.c_int,
+                                     C.c_int, C.c_int, C.c_int, P, P, P]),
     "ddt_kv_commit": (C.c_int, [C.POINTER(KVCache), P, P, C.c_int, P, P, C.c_int, P, P]),
     "ddt_kv_fork": (C.c_int, [C.POINTER(KVCache), P, P, C.c_int, P, P]),
     "ddt_kv_release": (C.c_int, [C.POINTER(KVCache), P, C.c_int, P]),

@@ -174,12 +174,19 @@ def tree_rerank(tree: DeviceTree, m_max: int, sel: torch.Tensor, m_out: torch.Te
 
 def succ_gather(tree: DeviceTree, M: torch.Tensor, k_succ: int, tpl_depth: int, tpl_width: int,
                 K_max: int, m_max: int, sel: torch.Tensor, m_out: torch.Tensor, shared: bool = False,
-                stream=None) -> None:
+                anchor: int = 0, stream=None) -> None:
+    """ddt_succ_gather (anchor 0, the root) or ddt_succ_gather_at (anchor 1:
+    the tail of the selected draft tree)."""
     V = M.shape[-2]
     bstride = 0 if shared else V * k_succ
-    L.check("ddt_succ_gather", L.load().ddt_succ_gather(
-        C.byref(tree.c), _ptr(M), bstride, V, k_succ, tpl_depth, tpl_width, K_max, m_max,
-        _ptr(sel), _ptr(m_out), _stream(stream, M.device)))
+    if anchor == 0:
+        L.check("ddt_succ_gather", L.load().ddt_succ_gather(
+            C.byref(tree.c), _ptr(M), bstride, V, k_succ, tpl_depth, tpl_width, K_max, m_max,
+            _ptr(sel), _ptr(m_out), _stream(stream, M.device)))
+    else:
+        L.check("ddt_succ_gather_at", L.load().ddt_succ_gather_at(
+            C.byref(tree.c), _ptr(M), bstride, V, k_succ, tpl_depth, tpl_width, K_max, m_max,
+            anchor, _ptr(sel), _ptr(m_out), _stream(stream, M.device)))
 
 
 def tree_build_mask(tree: DeviceTree, sel: torch.Tensor, m: torch.Tensor, prefix_len: int,

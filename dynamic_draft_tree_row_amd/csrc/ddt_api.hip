@@ -312,6 +312,14 @@ int ddt_tree_rerank(const ddt_tree* t, int m_max, const ddt_cast* cast, int use_
 int ddt_succ_gather(const ddt_tree* t, const int32_t* M, int64_t M_bstride, int V, int k_succ,
                     int tpl_depth, int tpl_width, int K_max, int m_max, int32_t* sel,
                     int32_t* m_out, void* stream) {
+    return ddt_succ_gather_at(t, M, M_bstride, V, k_succ, tpl_depth, tpl_width, K_max, m_max,
+                              DDT_GRAFT_ROOT, sel, m_out, stream);
+}
+
+int ddt_succ_gather_at(const ddt_tree* t, const int32_t* M, int64_t M_bstride, int V, int k_succ,
+                       int tpl_depth, int tpl_width, int K_max, int m_max, int anchor, int32_t* sel,
+                       int32_t* m_out, void* stream) {
+    if (anchor != DDT_GRAFT_ROOT && anchor != DDT_GRAFT_TAIL) return DDT_EINVAL;
     int st = check_tree(t);
     if (st) return st;
     if (M == nullptr || sel == nullptr || m_out == nullptr || V < 1 || M_bstride < 0) return DDT_EINVAL;
@@ -322,6 +330,7 @@ int ddt_succ_gather(const ddt_tree* t, const int32_t* M, int64_t M_bstride, int 
     GatherArgs a;
     a.t = *t; a.M = M; a.M_bstride = M_bstride; a.V = V; a.k_succ = k_succ; a.depth = tpl_depth;
     a.width = tpl_width; a.K_max = K_max; a.m_cap = m_max; a.sel = sel; a.m_out = m_out;
+    a.anchor = anchor;
     hipLaunchKernelGGL(k_succ_gather, dim3(t->B), dim3(64), 0, (hipStream_t)stream, a);
     return launched();
 }

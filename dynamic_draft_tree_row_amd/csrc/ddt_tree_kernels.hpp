@@ -723,15 +723,17 @@ __global__ __launch_bounds__(RK_NT) void k_rerank(RerankArgs a) {
 // ---------------------------------------------------------------------------
 //
 // Graft review step 2: root-centred retrieval, x_u = M[x_parent(u), r_u].
-// Template (reading of "depth x width"): `width` chains under the root; chain
-// c starts with successor c of the root token and continues with successor 0
-// of its own last token; level-major order, the first K_ret = K_max - m kept.
+// Template (reading of "depth x width"): `width` chains under the anchor (the
+// root; or, for the tail-only graft of the Fig. 2 comparison, the tail of the
+// selected draft tree); chain c starts with successor c of the anchor's token
+// and continues with successor 0 of its own last token; level-major order,
+// the first K_ret = K_max - m kept; no level past the canonical key's depth.
 
 struct GatherArgs {
     ddt_tree t;
     const int32_t* M;
     int64_t M_bstride;
-    int V, k_succ, depth, width, K_max, m_cap;
+    int V, k_succ, depth, width, K_max, m_cap, anchor;
     int32_t* sel;
     int32_t* m_out;
 };
@@ -739,34 +741,62 @@ struct GatherArgs {
 __global__ __launch_bounds__(64) void k_succ_gather(GatherArgs a) {
     const ddt_tree& t = a.t;
     const int b = blockIdx.x, c = threadIdx.x;
-    __shared__ int s_kret, s_base, s_m;
+    __shared__ int s_kret, s_base, s_m, s_anc, s_lv;
+    const size_t o = (size_t)b * t.cap;
+    int32_t* sel = a.sel + (size_t)b * (a.m_cap + 1);
+    const int m = min(max(a.m_out[b], 0), a.K_max);
+    // the anchor: the root, or the deepest selected node (ties: higher S,
+    // then smaller key), each lane over its share of sel[1 .. m], then the wave
+    int anc = 0;
+    if (a.anchor == 1) {
+        int bd = -1;
+        float bS = -INFINITY;
+        uint64_t bk = ~0ull;
+        for (int q = 1 + c; q <= m; q += 64) {
+            const int nd = sel[q];
+            if (nd < 1 || nd >= t.cap) continue;
+            const int d = t.depth[o + nd];
+            const float S = t.S[o + nd];
+            const uint64_t k = t.key[o + nd];
+            if (d > bd || (d == bd && (S > bS || (S == bS && k < bk)))) { bd = d; bS = S; bk = k; anc = nd; }
+        }
+#pragma unroll
+        for (int w = 32; w >= 1; w >>= 1) {
+            const int od = __shfl_xor(bd, w);
+            const float oS = __shfl_xor(bS, w);
+            const uint64_t ok = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(bk >> 32), w) << 32) |
+                                (uint32_t)__shfl_xor((int)(uint32_t)bk, w);
+            const int oa = __shfl_xor(anc, w);
+            if (od > bd || (od == bd && (oS > bS || (oS == bS && ok < bk)))) { bd = od; bS = oS; bk = ok; anc = oa; }
+        }
+    }
     if (c == 0) {
-        const int m = min(max(a.m_out[b], 0), a.K_max);
         int kret = a.K_max - m;
         const int base = min(max(t.n_nodes[b], 1), t.cap);
-        kret = min(kret, min(t.cap - base, a.depth * a.width));
-        s_kret = max(kret, 0); s_base = base; s_m = m;
+        const int ad = min(max(t.depth[o + anc], 0), DDT_MAX_DEPTH);
+        const int lv = min(a.depth, DDT_MAX_DEPTH - ad);
+        kret = min(kret, min(t.cap - base, lv * a.width));
+        s_kret = max(kret, 0); s_base = base; s_m = m; s_anc = anc; s_lv = lv;
     }
     __syncthreads();
-    const int kret = s_kret, base = s_base, m = s_m;
-    const size_t o = (size_t)b * t.cap;
+    const int kret = s_kret, base = s_base, lv = s_lv;
     const int32_t* Mb = a.M + (size_t)b * a.M_bstride;
-    int32_t* sel = a.sel + (size_t)b * (a.m_cap + 1);
     if (c < a.width) {
-        int prev = 0;                              // parent node (root for level 1)
-        int ptok = t.token[o];
-        for (int lvl = 1; lvl <= a.depth; ++lvl) {
+        int prev = s_anc;                          // parent node (the anchor for level 1)
+        int ptok = t.token[o + prev];
+        for (int lvl = 1; lvl <= lv; ++lvl) {
             const int idx = (lvl - 1) * a.width + c;
             if (idx >= kret) break;
             const int r = lvl == 1 ? c : 0;
             const int pt = min(max(ptok, 0), a.V - 1);
             const int tk = Mb[(size_t)pt * a.k_succ + r];
             const int node = base + idx;
+            const int pd = t.depth[o + prev];
             t.token[o + node] = tk;
             t.parent[o + node] = prev;
-            t.depth[o + node] = lvl;
+            t.depth[o + node] = pd + 1;
             t.eslot[o + node] = -1;
-            t.key[o + node] = key_child(lvl == 1 ? 0ull : t.key[o + prev], lvl - 1, r, 1);
+            t.key[o + node] = key_child(t.key[o + prev], pd, r, 1);
             t.S[o + node] = -INFINITY;
             t.logc[o + node] = -INFINITY;
             if (1 + m + idx <= a.m_cap) sel[1 + m + idx] = node;
@@ -1166,10 +1196,11 @@ __device__ double walk_tiles(const WalkRows& w, RowSync& rs, double* s_red, doub
 
 // Inverse CDF over the tile sums in s_tile (all tiles of the request): the
 // smallest id whose running sum (ascending ids) exceeds u * total, else the
-// last id with mass.  Wave 0 finds the tile by a lane scan over the tile
+// last id with mass.  The nz ids in zx carry no weight (the caller has taken
+// them out of their tiles' sums).  Wave 0 finds the tile by a lane scan over the tile
 // sums, then the id inside it.  Returns the id in every thread.
 __device__ int walk_pick(const WalkRows& w, int V, bool useq, double aa, double u, double tot,
-                         const double* s_tile, int* s_out) {
+                         const double* s_tile, int* s_out, const int* zx, int nz) {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int ntiles = (V + VF_TILE - 1) / VF_TILE;
     if (wid == 0) {
@@ -1231,6 +1262,8 @@ __device__ int walk_pick(const WalkRows& w, int V, bool useq, double aa, double 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             pv[e] = useq ? fmax(0.0, walk_p(w, tx[e]) - aa * walk_q(w, dx[e])) : walk_p(w, tx[e]);
+            for (int z = 0; z < nz; ++z)
+                if (v0 + e == zx[z]) pv[e] = 0.0;
             ls += pv[e];
         }
         double in2 = ls;
@@ -1278,6 +1311,10 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
     // draft logits of its token under its parent's rows
     __shared__ int s_wslot[MK_NT], s_wdep[MK_NT];
     __shared__ float s_wrm[MK_NT], s_wrs[MK_NT], s_wtl[MK_NT], s_wdl[MK_NT];
+    // retrieval positions (point-mass proposals), and the positions of the
+    // current node's rejected retrieval children (their tokens leave p)
+    __shared__ int s_wret[MK_NT], s_zc[MK_NT];
+    __shared__ int s_nz;
     __shared__ int s_wcnt[MK_NT / 64];
     __shared__ int s_nch, s_u, s_len, s_acc, s_next;
     __shared__ unsigned long long s_best;
@@ -1445,6 +1482,8 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
         if (!ok || a.drf == nullptr || dep < 0 || dep >= t.D_max || slot >= t.R_max) slot = -1;
         const size_t ri = ((size_t)b * t.D_max + (slot >= 0 ? dep : 0)) * t.R_max + (slot >= 0 ? slot : 0);
         const float rm = t.rmax[ri], rsv = t.rsp[ri];
+        const uint64_t key = t.key[(size_t)b * t.cap + nc];
+        s_wret[tid] = ok && ((key >> KEY_SRC_SHIFT) & 1ull) ? 1 : 0;
         s_wslot[tid] = slot;
         s_wdep[tid] = ok ? dep : 0;
         s_wrm[tid] = rm;
@@ -1486,6 +1525,11 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
         const int nch = s_nch;
         const int uslot = s_wslot[u];
         const int udep = s_wdep[u];
+        // u's draft row proposes its draft children; its retrieval children
+        // (and any child of a node without a draft row) get point-mass
+        // proposals q = delta_x: accepted with probability p_k(x), and a
+        // rejection removes x from the residual.  Draft children come first
+        // in flat order, so the excluded tokens never meet a draft pass.
         const bool has_q = nch > 0 && uslot >= 0;
         WalkRows w;
         w.tab = s_e2t;
@@ -1514,46 +1558,69 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
             w.lzd = log2(Zd);
             zexact = true;
         };
-        if (has_q) {
+        if (nch > 0) {
             if (T == 1.f) {
                 w.lzt = log2(1.0 + (double)s_S[u]);
-                w.lzd = log2(1.0 + (double)s_wrs[u]);
+                w.lzd = has_q ? log2(1.0 + (double)s_wrs[u]) : 0.0;
             } else {
                 exact_norms();
             }
         }
-        double ra = 0.0, rb = 1.0;                      // residual p_k = max(0, p - ra q) / rb
+        double ra = 0.0, rb = 1.0;                      // residual p_k = max(0, p - ra q) / rb, minus excluded tokens
         int accepted = -1;
         bool tiles_ready = false;                       // the tiles hold the current residual's weights
         double tiles_tot = 0.0;
-        if (has_q) {
-            for (int ci = 0; ci < nch && !s_err; ++ci) {
-                const int c = s_ch[ci];
-                if (tid == 0) {
-                    const double px = walk_p(w, s_wtl[c]);
-                    const double qx = walk_q(w, s_wdl[c]);
-                    const double pk = fmax(0.0, px - ra * qx) / rb;
-                    const double ratio = qx > 0.0 ? pk / qx : INFINITY;
-                    s_acc = ((double)Ub[2 * c] < ratio) ? 1 : 0;
-                }
+        if (tid == 0) s_nz = 0;
+        __syncthreads();
+        // the unnormalised residual weight of child c's token
+        auto wres = [&](int c) {
+            const double px = walk_p(w, s_wtl[c]);
+            const double qx = has_q ? walk_q(w, s_wdl[c]) : 0.0;
+            double wx = fmax(0.0, px - ra * qx);
+            for (int z = 0; z < s_nz; ++z)
+                if (s_ft[s_zc[z]] == s_ft[c]) wx = 0.0;
+            return wx;
+        };
+        for (int ci = 0; ci < nch && !s_err; ++ci) {
+            const int c = s_ch[ci];
+            if (s_wret[c] || !has_q) {
+                if (tid == 0) s_acc = ((double)Ub[2 * c] < wres(c) / rb) ? 1 : 0;
                 __syncthreads();
                 if (s_acc) { accepted = c; break; }
                 if (!zexact) exact_norms();
-                // rejection: b' = F(a + b); after the last sibling the same
-                // pass leaves the emission weights per tile
-                const double an = ra + rb;
-                double F;
-                if (ci == nch - 1) {
-                    F = walk_tiles(w, rs, s_red, s_bc, &s_err, a.V, true, an, s_tile);
-                    tiles_ready = F > 0.0;
-                    tiles_tot = F;
-                } else {
-                    F = walk_pass<true>(w, rs, s_red, s_bc, &s_err, a.V, [&](float tv, float dv) {
-                        return fmax(0.0, walk_p(w, tv) - an * walk_q(w, dv));
-                    });
+                const double wx = wres(c);              // every thread, exact normalisers
+                __syncthreads();                        // s_nz read by all before it grows
+                if (rb - wx > 0.0) {                    // an all-zero residual keeps p as it was
+                    rb -= wx;
+                    if (tid == 0) s_zc[s_nz++] = c;
                 }
-                if (F > 0.0) { ra = an; rb = F; }
+                __syncthreads();
+                continue;
             }
+            if (tid == 0) {
+                const double px = walk_p(w, s_wtl[c]);
+                const double qx = walk_q(w, s_wdl[c]);
+                const double pk = fmax(0.0, px - ra * qx) / rb;
+                const double ratio = qx > 0.0 ? pk / qx : INFINITY;
+                s_acc = ((double)Ub[2 * c] < ratio) ? 1 : 0;
+            }
+            __syncthreads();
+            if (s_acc) { accepted = c; break; }
+            if (!zexact) exact_norms();
+            // rejection: b' = F(a + b); after the last sibling the same
+            // pass leaves the emission weights per tile
+            const double an = ra + rb;
+            double F;
+            if (ci == nch - 1) {
+                F = walk_tiles(w, rs, s_red, s_bc, &s_err, a.V, true, an, s_tile);
+                tiles_ready = F > 0.0;
+                tiles_tot = F;
+            } else {
+                F = walk_pass<true>(w, rs, s_red, s_bc, &s_err, a.V, [&](float tv, float dv) {
+                    return fmax(0.0, walk_p(w, tv) - an * walk_q(w, dv));
+                });
+            }
+            if (F > 0.0) { ra = an; rb = F; }
         }
         if (s_err) break;
         if (accepted >= 0) {
@@ -1571,7 +1638,25 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
                 for (int q = tid; q < ntiles; q += VF_NT)
                     s_tile[q] = __hip_atomic_load(rs.tiles + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __syncthreads();
-            walk_pick(w, a.V, has_q, ra, (double)Ub[2 * u + 1], tiles_tot, s_tile, &s_next);
+            // rejected retrieval tokens carry no weight: out of their tiles'
+            // sums and the total here, out of the element scan in walk_pick
+            const int nz = s_nz;
+            if (tid == 0) {
+                for (int z = 0; z < nz; ++z) {
+                    const int c = s_zc[z];
+                    const double wx = fmax(0.0, walk_p(w, s_wtl[c]) - ra * (has_q ? walk_q(w, s_wdl[c]) : 0.0));
+                    const int tt = min(max(s_ft[c], 0), a.V - 1) / VF_TILE;
+                    s_tile[tt] = fmax(0.0, s_tile[tt] - wx);
+                    s_zc[z] = s_ft[c];                 // from here on: the excluded tokens
+                }
+            }
+            __syncthreads();
+            if (nz > 0) {
+                double tot = 0.0;
+                for (int q = 0; q < ntiles; ++q) tot += s_tile[q];
+                tiles_tot = tot;
+            }
+            walk_pick(w, a.V, has_q, ra, (double)Ub[2 * u + 1], tiles_tot, s_tile, &s_next, s_zc, nz);
         }
         break;
     }

@@ -35,6 +35,7 @@ class RoundShape:
     tpl_width: int = 8
     k_succ: int = 8
     shared_M: bool = False       # Graft: one successor matrix [V][k] for every row
+    graft_anchor: int = 0        # Graft template under the root (0) or the draft tree's tail (1)
 
     @property
     def m_max(self) -> int:
@@ -42,7 +43,11 @@ class RoundShape:
 
     @property
     def Dp(self) -> int:
-        return max(self.D, self.tpl_depth) if self.graft else self.D
+        if not self.graft:
+            return self.D
+        if self.graft_anchor == 1:
+            return min(self.D + self.tpl_depth, 11)        # the canonical key's depth limit
+        return max(self.D, self.tpl_depth)
 
     @property
     def cap(self) -> int:
@@ -85,7 +90,8 @@ class RoundRunner:
                         use_k_draft=gate is not None, stream=stream)
         if s.graft:
             api.succ_gather(self.tree, M, s.k_succ, s.tpl_depth, s.tpl_width, s.m_max, s.m_max,
-                            self.sel, self.m_out, shared=s.shared_M, stream=stream)
+                            self.sel, self.m_out, shared=s.shared_M, anchor=s.graft_anchor,
+                            stream=stream)
         api.tree_build_mask(self.tree, self.sel, self.m_out, s.prefix, self.flat, stream=stream)
 
     def verify(self, target: torch.Tensor, draft_arena: Optional[torch.Tensor],

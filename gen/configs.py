@@ -55,6 +55,12 @@ class GraftSpec:
     k_succ: int = 8                           # successors per row of M
     zipf_s: float = 1.1
     plant_prob: float = 0.5                   # target rows that follow M0's top successor
+    # "prune_then_graft" (the method), or the two grafts it is compared with
+    # (Graft review, Fig. 2): "root_only" and "tail_only" keep a fixed draft
+    # budget with no checkpoints and hang the template off the root or off
+    # the tail of the draft tree
+    mode: str = "prune_then_graft"
+    fixed_k_draft: int = 24
 
 
 @dataclass(frozen=True)

@@ -273,6 +273,25 @@ int ddt_succ_gather(const ddt_tree* t /*host*/, const int32_t* M, int64_t M_bstr
                     int32_t* m_out, void* stream);
 
 /*
+ * ddt_succ_gather_at -- the same graft with the template hung off another
+ * node, for the two grafts Graft's prune-then-graft is compared with ([GR]
+ * technical-novelty point (2), Fig. 2): anchor DDT_GRAFT_ROOT is
+ * ddt_succ_gather; DDT_GRAFT_TAIL hangs it off the tail of the row's selected
+ * draft tree: the deepest node of sel[1 .. m_out[b]], ties to the higher S,
+ * then the smaller canonical key (the root if nothing is selected).  Chain c
+ * then starts at M[anchor token][c]; template node depths continue from the
+ * anchor's, and levels that would pass DDT_MAX_DEPTH are not built (the flat
+ * layout's Dp must cover the deepest node).  A fixed draft budget without
+ * checkpoints (root-only and tail-only grafting) is a ddt_graft_gate with
+ * n_ck = 0 and K_max = that budget, then this call with the full K_max.
+ */
+#define DDT_GRAFT_ROOT 0
+#define DDT_GRAFT_TAIL 1
+int ddt_succ_gather_at(const ddt_tree* t /*host*/, const int32_t* M, int64_t M_bstride, int V,
+                       int k_succ, int tpl_depth, int tpl_width, int K_max, int m_max, int anchor,
+                       int32_t* sel, int32_t* m_out, void* stream);
+
+/*
  * ddt_tree_build_mask -- flatten {root} + selection in ascending canonical key
  * order; tokens, flat parents, position ids prefix_len + depth, ancestor-only
  * bitmask (self and ancestors visible, never siblings; prefix columns are
@@ -304,7 +323,13 @@ int ddt_tree_build_mask(const ddt_tree* t /*host*/, const int32_t* sel, const in
  * frontier slot j of batch row b (i.e. layer d's slice) starts at
  * draft->data + (d-1)*draft_layer_stride + b*draft->s0 + j*draft->s1
  * elements.  Needed only when some temperature > 0 (may be NULL otherwise).
- * Nodes without a draft row (retrieval nodes) end the walk at T > 0.
+ * Retrieval children (key source bit 1, and any child of a node without a
+ * draft row) are tried with a point-mass proposal q = delta_x after the draft
+ * children: accepted iff uniforms[b][c][0] < p_k(x), and a rejection removes
+ * x from the residual (kept as it was if nothing would be left); the
+ * emission's inverse CDF then skips the removed tokens.  This is an exact
+ * speculative-sampling step for any deterministically chosen x ([GR] step
+ * (3): the acceptance rule is the standard one, and the method is lossless).
  * row_argmax: [B][P] or NULL.  k_top > 0 with row_topk [B][P][k_top]: top-k
  * ids of every verified row from the same pass (feeds ddt_succ_update).
  * Both hold -1 at padding positions (past f->m[b]).

@@ -296,13 +296,15 @@ def draft_phase(draft_rows, B: int, root_tok: Sequence[int], D: int, K_e: int, K
     section and the decode-step flow); layer-D nodes are never expanded.
 
     cast: dict(S_T, S_D, L, M, C1[D], C2, R) switches width and depth to CAST.
-    graft: dict(ck_depth, tau, k_draft, K_max) turns on the Graft gate.
+    graft: dict(ck_depth, tau, k_draft, K_max) turns on the Graft gate; an
+    optional draft_cap (default K_max) is the draft budget of rows never pruned
+    (root-only and tail-only grafting keep a fixed budget and no checkpoints).
     """
     assert not (cast and graft)
     trees = [new_tree(root_tok[b]) for b in range(B)]
     fronts = [[[0]] for _ in range(B)]        # "layer 0" frontier: the root
     active = [True] * B
-    k_draft = [graft["K_max"] if graft else 0] * B
+    k_draft = [graft.get("draft_cap", graft["K_max"]) if graft else 0] * B
     margins: list = []
     widths: List[int] = []
     fifo = [1.0]                              # CAST gain buffer, initial {1}
@@ -404,18 +406,23 @@ def rerank(t: RowTree, m: int, margins=None) -> List[int]:
 # O10: Graft retrieval graft and successor-matrix refresh
 # ---------------------------------------------------------------------------
 
-def graft_template(t: RowTree, M_b: np.ndarray, k_ret: int, depth: int, width: int) -> List[int]:
-    """Append the first k_ret nodes of the root-centred retrieval template.
+def graft_template(t: RowTree, M_b: np.ndarray, k_ret: int, depth: int, width: int,
+                   anchor: int = 0) -> List[int]:
+    """Append the first k_ret nodes of the retrieval template hung off `anchor`
+    (the root for Graft's prune-then-graft).
 
     Each retrieved node's token is a successor-matrix lookup of its parent's
     token, x_u = M[x_parent(u), r_u] (Graft step 2).  Reading of the template
-    (depth x width): `width` chains hang off the root; chain c starts with
-    successor c of the root token and continues with successor 0 of its own
-    last token.  Template order is level-major, then chain; truncating a prefix
-    keeps it parent-closed.  Retrieved nodes have no draft value (S = -inf).
+    (depth x width): `width` chains hang off the anchor; chain c starts with
+    successor c of the anchor's token and continues with successor 0 of its
+    own last token.  Template order is level-major, then chain; truncating a
+    prefix keeps it parent-closed.  Retrieved nodes have no draft value
+    (S = -inf).  Levels that would pass MAX_DEPTH (the canonical key's limit)
+    are not built.
     """
     added = []
-    prev = [0] * width
+    prev = [anchor] * width
+    depth = min(depth, MAX_DEPTH - t.depth[anchor])
     for lvl in range(1, depth + 1):
         for c in range(width):
             idx = (lvl - 1) * width + c
@@ -424,10 +431,22 @@ def graft_template(t: RowTree, M_b: np.ndarray, k_ret: int, depth: int, width: i
             p = prev[c]
             tok = int(M_b[t.token[p], c if lvl == 1 else 0])
             key = key_child(t.key[p], t.depth[p], c if lvl == 1 else 0, src=1)
-            n = t.add(tok, p, lvl, -math.inf, -math.inf, key, src=1)
+            n = t.add(tok, p, t.depth[p] + 1, -math.inf, -math.inf, key, src=1)
             prev[c] = n
             added.append(n)
     return added
+
+
+def graft_tail_anchor(t: RowTree, sel: Sequence[int]) -> int:
+    """The tail of the selected draft tree, for tail-only grafting (Graft
+    review, the Fig. 2 comparison; reading): the deepest selected node, ties
+    to the higher value, then the smaller canonical key; the root if nothing
+    is selected."""
+    best = 0
+    for i in sel:
+        if best == 0 or (t.depth[i], t.S[i], -t.key[i]) > (t.depth[best], t.S[best], -t.key[best]):
+            best = i
+    return best
 
 
 def succ_update(M_b: np.ndarray, flat_token: Sequence[int], n_flat: int, target_rows, k: int):
@@ -679,7 +698,8 @@ def run_round(*, B, V, dtype, D, K_e, K_n, m_max, root_tok, draft_raw, target_ra
     dr = draft_phase(drow, B, root_tok, D, K_e, K_n, cast=cast, graft=graft)
     margins = dr.margins
     P = m_max + 1
-    Dp = max(D, tpl[0]) if graft else D
+    tail = graft is not None and graft.get("anchor") == "tail"
+    Dp = (min(D + tpl[0], MAX_DEPTH) if tail else max(D, tpl[0])) if graft else D
     sels, m_rows, flats = [], [], []
     for b in range(B):
         t = dr.trees[b]
@@ -695,7 +715,8 @@ def run_round(*, B, V, dtype, D, K_e, K_n, m_max, root_tok, draft_raw, target_ra
         margins.extend((k, v, b) for k, v in mb)
         if graft is not None:
             k_ret = graft["K_max"] - len(sel)
-            sel = sel + graft_template(t, M[b], k_ret, tpl[0], tpl[1])
+            anchor = graft_tail_anchor(t, sel) if tail else 0
+            sel = sel + graft_template(t, M[b], k_ret, tpl[0], tpl[1], anchor)
         sels.append(sel)
         m_rows.append(len(sel))
         flats.append(flatten(t, sel, P, prefix, Dp))

@@ -27,8 +27,11 @@ def cast_params(w: Workload, seed: int = 0) -> dict:
 
 def graft_params(w: Workload, tau) -> dict:
     gs = w.graft
-    return dict(ck_depth=tuple(gs.ck_depth), tau=list(tau), k_draft=tuple(gs.k_draft),
-                K_max=gs.K_max)
+    if gs.mode == "prune_then_graft":
+        return dict(ck_depth=tuple(gs.ck_depth), tau=list(tau), k_draft=tuple(gs.k_draft),
+                    K_max=gs.K_max)
+    return dict(ck_depth=(), tau=[], k_draft=(), K_max=gs.K_max, draft_cap=gs.fixed_k_draft,
+                anchor="tail" if gs.mode == "tail_only" else "root")
 
 
 def flat_layout(trees, flats, P):
@@ -154,7 +157,8 @@ def runner_for(w: Workload, device="cuda", shared_M=False):
                        D=w.D, K_e=w.K_e, K_n=w.K_n, m=w.m_max, prefix=w.prefix,
                        graft=gs is not None, tpl_depth=gs.tpl_depth if gs else 8,
                        tpl_width=gs.tpl_width if gs else 8, k_succ=gs.k_succ if gs else 8,
-                       shared_M=shared_M)
+                       shared_M=shared_M,
+                       graft_anchor=1 if gs is not None and gs.mode == "tail_only" else 0)
     return RoundRunner(shape, device)
 
 
@@ -169,7 +173,7 @@ def dev_cast(cast: dict, device="cuda"):
 def dev_gate(graft: dict):
     from dynamic_draft_tree_row_amd.api import GraftGate
     return GraftGate(ck_depth=list(graft["ck_depth"]), tau=[float(x) for x in graft["tau"]],
-                     k_draft=list(graft["k_draft"]), K_max=graft["K_max"])
+                     k_draft=list(graft["k_draft"]), K_max=graft.get("draft_cap", graft["K_max"]))
 
 
 def gpu_round(case: Case, device="cuda") -> dict:

@@ -523,6 +523,52 @@ def test_residual_after_rejection():
     assert L == 1 and path == [0, 1]
 
 
+def test_graft_tail_anchor_rule():
+    """Tail-only grafting hangs the template off the deepest selected node,
+    ties to the higher value, then the smaller key."""
+    t = O.new_tree(5)
+    a = t.add(1, 0, 1, -0.1, -0.1, O.key_child(0, 0, 0))
+    b = t.add(2, 0, 1, -0.5, -0.5, O.key_child(0, 0, 1))
+    c = t.add(3, a, 2, -0.3, -0.2, O.key_child(t.key[a], 1, 0))
+    d = t.add(4, a, 2, -0.2, -0.1, O.key_child(t.key[a], 1, 1))
+    e = t.add(6, b, 2, -0.2, -0.1, O.key_child(t.key[b], 1, 0))
+    assert O.graft_tail_anchor(t, [a, b, c, d, e]) == d      # d and e tie on S; d's key is smaller
+    assert O.graft_tail_anchor(t, [a, b, c]) == c
+    assert O.graft_tail_anchor(t, [a, b]) == a
+    assert O.graft_tail_anchor(t, []) == 0
+
+
+def test_graft_template_under_an_anchor():
+    """Template under a depth-2 anchor: chain c starts at M[x_anchor][c] and
+    continues with successor 0; depths continue from the anchor; keys carry
+    the retrieval bit and sort after draft keys of the same depth; levels
+    past the key's depth limit are not built."""
+    V = 20
+    M = (np.arange(V)[:, None] * 3 + np.arange(4)[None, :] + 1) % V
+    t = O.new_tree(5)
+    a = t.add(1, 0, 1, -0.1, -0.1, O.key_child(0, 0, 0))
+    d = t.add(4, a, 2, -0.2, -0.1, O.key_child(t.key[a], 1, 1))
+    added = O.graft_template(t, M, 5, 3, 2, anchor=d)
+    assert len(added) == 5
+    n1, n2, n3, n4, n5 = added
+    assert [t.token[n] for n in added] == [M[4, 0], M[4, 1], M[M[4, 0], 0], M[M[4, 1], 0],
+                                           M[M[M[4, 0], 0], 0]]
+    assert [t.parent[n] for n in added] == [d, d, n1, n2, n3]
+    assert [t.depth[n] for n in added] == [3, 3, 4, 4, 5]
+    for n in added:
+        assert (t.key[n] >> 58) & 1 == 1 and O.key_depth(t.key[n]) == t.depth[n]
+        assert t.src[n] == 1 and t.S[n] == -math.inf
+    draft3 = O.key_child(t.key[d], 2, 7)                     # a draft node at depth 3
+    assert draft3 < t.key[n1] and draft3 < t.key[n2]
+    # an anchor at depth 10: only one level (depth 11) fits under the key
+    t2 = O.new_tree(5)
+    p = 0
+    for lvl in range(1, 11):
+        p = t2.add(1, p, lvl, -0.1 * lvl, -0.1, O.key_child(t2.key[p], lvl - 1, 0))
+    added = O.graft_template(t2, M, 8, 3, 2, anchor=p)
+    assert len(added) == 2 and all(t2.depth[n] == 11 for n in added)
+
+
 def test_point_mass_children_thresholds():
     """Retrieval children (point-mass proposals): the k-th is accepted iff
     U < p(x_k) / (1 - p(x_1) - .. - p(x_{k-1})), i.e. from p with the rejected

@@ -7,6 +7,7 @@ vocab chunks and a ragged tail; full-size cases run the five workloads in the
 launch configuration the bench times (the B=64 workload is compared on sampled
 rows, every row checked for the method's invariants).
 """
+import dataclasses
 import json
 import os
 import sys
@@ -165,6 +166,45 @@ def test_graft_small_multi_round():
     for rnd in range(3):
         case = H.oracle_case(w, 77, rnd, cast=None, graft=H.graft_params(w, tau), M=M, M0=M0)
         say(f"graft round {rnd} k_draft={case.out['draft'].k_draft}")
+        H.compare(case, H.gpu_round(case))
+        M = case.M_after
+
+
+def test_graft_stochastic_verify_point_mass():
+    # Graft with T > 0: retrieval nodes are verified with point-mass
+    # proposals (accepted with probability p(x), rejected tokens leave the
+    # residual), so a T = 1 request's walk can run through grafted chains
+    # (seed 83: the T = 1 walks accept 8 retrieval nodes over the 3 rounds,
+    # a chain of 3 among them, and reject others)
+    base = configs.shrink(configs.C4, V=6000, B=6)
+    w = configs.Workload(**{**base.__dict__, "verify": "t1", "name": base.name + "_t1"})
+    tau = H.calibrate_tau(w, 83, 4)
+    M = synth.succ_matrix0(w, 83)
+    M0 = M.copy()
+    for rnd in range(3):
+        case = H.oracle_case(w, 83, rnd, cast=None, graft=H.graft_params(w, tau), M=M, M0=M0)
+        say(f"graft T>0 round {rnd} k_draft={case.out['draft'].k_draft} "
+            f"accept={case.out['accept_len'].tolist()}")
+        H.compare(case, H.gpu_round(case))
+        M = case.M_after
+
+
+@pytest.mark.parametrize("verify", ["greedy", "t1"])
+@pytest.mark.parametrize("mode", ["root_only", "tail_only"])
+def test_graft_variants(mode, verify):
+    # the two grafts prune-then-graft is compared with (Graft review, Fig. 2):
+    # a fixed draft budget with no checkpoints, the template under the root or
+    # under the tail of the selected draft tree
+    base = configs.shrink(configs.C4, V=6000, B=5)
+    gs = dataclasses.replace(base.graft, mode=mode)
+    w = configs.Workload(**{**base.__dict__, "graft": gs, "verify": verify,
+                            "name": f"{base.name}_{mode}_{verify}"})
+    M = synth.succ_matrix0(w, 61)
+    M0 = M.copy()
+    for rnd in range(2):
+        case = H.oracle_case(w, 61, rnd, graft=H.graft_params(w, None), M=M, M0=M0)
+        say(f"graft {mode} {verify} round {rnd} m={case.out['m_rows'].tolist()} "
+            f"accept={case.out['accept_len'].tolist()}")
         H.compare(case, H.gpu_round(case))
         M = case.M_after
 
