@@ -316,6 +316,78 @@ def kv_commit_detail(api, dev, seed: int = 11, commits: int = 20) -> dict:
     return res
 
 
+def cast_calibration_detail(w, run, ring, to_dev, dev, slots: int = 2, replays: int = 60) -> dict:
+    """CAST cost tables measured on this GPU at the workload's batch and grid
+    (proxy forwards of an 8B-class target and a one-layer draft head), then
+    rounds of the same ring drafted and verified on those tables, replayed
+    from HIP graphs like the headline rounds."""
+    import torch
+    from gen import configs, synth
+    from dynamic_draft_tree_row_amd import api
+    from dynamic_draft_tree_row_amd import cast_calibrate as CC
+    cs = w.cast
+    t0 = time.perf_counter()
+    S_T, S_D = CC.measure_tables(w.B, cs.L, cs.M, cs.N, reps=3)
+    cal_s = time.perf_counter() - t0
+    log(f"cost tables measured in {cal_s:.1f} s: S_T[0][1] {S_T[0, 1]:.0f} us, S_D[0][1] {S_D[0, 1]:.0f} us")
+    f = lambda a: torch.tensor(np.asarray(a, np.float32), device=dev)
+    cast = api.CastParams(S_T=f(S_T), S_D=f(S_D), L=cs.L, C1=f([cs.C1] * w.D), C2=cs.C2,
+                          C3=f([cs.C3] * w.B), R=cs.R, ctx_verify=w.prefix)
+    ms, stats = [], []
+    for r, slot in enumerate(ring[:slots]):
+        run.draft(slot["draft"], slot["roots"], cast=cast)
+        torch.cuda.synchronize()
+        fk, fd, fs, ft = flat_layout(run, w.B)
+        t_np = synth.target_arena(w, SEED, r, synth.draft_arena(w, SEED, r), fk, fd, fs, ft)
+        m = dict(slot, target=to_dev(t_np))
+        run.verify(m["target"], m["draft"], m["T"], m["U"])
+        torch.cuda.synchronize()
+        acc = run.accept_len.cpu().numpy()
+        n_nodes, dep = run.tree.n_nodes.cpu().numpy(), run.tree.depth.cpu().numpy()
+        depth = max(int(dep[b, :int(n_nodes[b])].max()) for b in range(w.B))
+        stats.append(dict(widths=run.tree.widths.cpu().numpy().tolist(), m=run.m_out.cpu().numpy(),
+                          accept=acc, depth=depth))
+        ms.append(m)
+
+    def one(m):
+        run.draft(m["draft"], m["roots"], cast=cast)
+        run.verify(m["target"], m["draft"], m["T"], m["U"])
+
+    graphs = []
+    for m in ms:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            one(m)
+        graphs.append(g)
+    for i in range(10):
+        graphs[i % len(graphs)].replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(replays):
+        graphs[i % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / replays
+    cols = [n for n in (1, 2, 4, 8, 16, 32, 64, 128) if n <= cs.N]
+    RT = synth.roofline_table(configs.PROXY_TARGET, w.B, cs.L, cs.M, cs.N)
+    free = int(np.max(np.flatnonzero(S_T[0, 1:] <= 1.02 * S_T[0, 1]))) + 1
+    return {
+        "grid": {"B": w.B, "L": cs.L, "M": cs.M, "N": cs.N}, "calibration_s": round(cal_s, 1),
+        "proxy": "target 32 x (d 4096, 32/8 heads of 128, FFN 14336) + LM head 128256; draft 1 layer of the same",
+        "columns_n": cols,
+        "S_T_us_ctx0": [round(float(S_T[0, n]), 1) for n in cols],
+        "S_T_us_ctx_max": [round(float(S_T[-1, n]), 1) for n in cols],
+        "S_D_us_ctx0": [round(float(S_D[0, n]), 1) for n in cols],
+        "S_T_over_roofline_ctx0": [round(float(S_T[0, n] / RT[0, n]), 2) for n in cols],
+        "target_tokens_within_2pct_of_one": free,
+        "rounds_on_measured_tables": {
+            "us_per_round_graph": round(us, 2),
+            "widths": stats[0]["widths"][:stats[0]["depth"]], "depth": [s["depth"] for s in stats],
+            "mean_m": round(float(np.mean([s["m"].mean() for s in stats])), 2),
+            "mean_tau": round(float(np.mean([s["accept"].mean() + 1 for s in stats])), 3)},
+    }
+
+
 def cpu_baseline(w, slot, cast_np, seconds):
     """The oracle as it stands, on one core, on ring slot 0's inputs."""
     from oracle import ddt_oracle as O
@@ -357,6 +429,8 @@ def main():
                     help="only a few tree-attention launches and the calibration copy, for rocprofv3 --pmc")
     ap.add_argument("--no-attention", action="store_true",
                     help="skip the tree-attention measurement (the verify forward's MFMA kernel)")
+    ap.add_argument("--no-calibrate", action="store_true",
+                    help="skip measuring the CAST cost tables on this GPU")
     ap.add_argument("--break-even", action="store_true",
                     help="CAST at the break-even thresholds C1=1, C2=0.1, C3=0.5")
     ap.add_argument("--pmc-run", action="store_true",
@@ -647,6 +721,8 @@ def main():
     if not args.no_attention:
         out["detail"]["tree_attention"] = tree_attention_detail(api, dev)
         out["detail"]["kv_commit"] = kv_commit_detail(api, dev)
+    if w.cast is not None and not args.no_calibrate:
+        out["detail"]["cast_calibration"] = cast_calibration_detail(w, run, ring, to_dev, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, ring[0], cast_np, args.cpu_seconds)
     else:

@@ -38,10 +38,29 @@ class CastSpec:
     N: int = 128             # token-count columns (n = 1..N)
     lam: float = 0.02        # closed-form cost slope
     delta: float = 1.0       # closed-form cost intercept
-    table: str = "linear"    # "linear" (c_k = lam*k + delta) or "seeded"
+    table: str = "linear"    # "linear" (c_k = lam*k + delta), "seeded" or "roofline"
+    table_B: int = 0         # batch of the "roofline" table (0: the workload's B)
 
 
 BREAK_EVEN = dict(C1=1.0, C2=0.1, C3=0.5)
+
+
+@dataclass(frozen=True)
+class ProxyShape:
+    """Decoder shape behind the "roofline" cost tables: an 8B-class target
+    (32 layers, 32 query / 8 key-value heads of 128, FFN 14336, vocabulary
+    128256) and a one-layer draft head of the same width."""
+    d_model: int
+    n_layers: int
+    Hq: int
+    Hkv: int
+    D: int
+    ffn: int
+    V: int
+
+
+PROXY_TARGET = ProxyShape(4096, 32, 32, 8, 128, 14336, 128256)
+PROXY_DRAFT = ProxyShape(4096, 1, 32, 8, 128, 14336, 128256)
 
 
 @dataclass(frozen=True)

@@ -29,7 +29,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-from .configs import Workload
+from .configs import PROXY_DRAFT, PROXY_TARGET, ProxyShape, Workload
 
 # stream tags
 S_DRAFT, S_TNOISE, S_FRESH, S_UNIF, S_TEMP, S_ROOT, S_SUCC, S_COST, S_PLANT = range(1, 10)
@@ -283,9 +283,16 @@ def cost_tables(w: Workload, seed: int = 0):
     normalised width cost S_D[.][k] / S_T[.][1] is lam*k + delta and the verify
     cost S_T[.][k] / S_T[.][1] is lam*k + (1 - lam): both have slope lam.
     "seeded": per-row random positive increments (increasing in n and in r).
+    "roofline": roofline_table of the proxy target and draft shapes at batch
+    table_B (default: the workload's B): flat while a forward is HBM-bound,
+    rising once it is MFMA-bound, so that equal neighbouring costs occur.
     """
     cs = w.cast
     M, N = cs.M, cs.N
+    if cs.table == "roofline":
+        Bt = cs.table_B or w.B
+        return (roofline_table(PROXY_TARGET, Bt, cs.L, M, N),
+                roofline_table(PROXY_DRAFT, Bt, cs.L, M, N))
     S_T = np.zeros((M, N + 1), np.float32)
     S_D = np.zeros((M, N + 1), np.float32)
     n = np.arange(1, N + 1, dtype=np.float64)
@@ -302,3 +309,30 @@ def cost_tables(w: Workload, seed: int = 0):
             inc_d = g.uniform(0.01, 0.05, size=N)
             S_D[r, 1:] = 0.8 + 0.02 * r + np.cumsum(inc_d)
     return S_T, S_D
+
+
+HBM_BYTES_PER_S = 8.0e12        # MI355X HBM3E
+MFMA_BF16_FLOP_PER_S = 2.5e15   # MI355X dense bf16 matrix peak
+
+
+def roofline_table(shape: ProxyShape, B: int, L: int, M: int, N: int) -> np.ndarray:
+    """[M][N+1] float32 microseconds: for context c = k*L (row k) and n new
+    tokens (column n), the larger of HBM time and MFMA time of a bf16 forward of
+    `shape` at batch B (column 0 is 0).  Bytes per layer: the projection weights
+    once plus the context keys and values; flops: 2 per weight per token plus
+    causal attention, 4*Hq*D per (query, key) pair with query i of the n new
+    tokens seeing c + i + 1 keys.  The LM head adds its weights and 2*d*V flops
+    per token."""
+    d, D = shape.d_model, shape.D
+    w_layer = d * (shape.Hq + 2 * shape.Hkv) * D + shape.Hq * D * d + 3 * d * shape.ffn
+    n = np.arange(1, N + 1, dtype=np.float64)
+    head = np.maximum(2.0 * d * shape.V / HBM_BYTES_PER_S,
+                      2.0 * B * n * d * shape.V / MFMA_BF16_FLOP_PER_S)
+    t = np.zeros((M, N + 1), np.float64)
+    for k in range(M):
+        c = k * L
+        by = 2.0 * w_layer + 2.0 * 2 * B * c * shape.Hkv * D
+        fl = 2.0 * B * n * w_layer + 4.0 * B * shape.Hq * D * (n * c + n * (n + 1) / 2)
+        layer = np.maximum(by / HBM_BYTES_PER_S, fl / MFMA_BF16_FLOP_PER_S)
+        t[k, 1:] = (shape.n_layers * layer + head) * 1e6
+    return t.astype(np.float32)

@@ -77,3 +77,28 @@ def test_succ_matrix0_shape_and_zipf_head():
     assert M.shape == (2, 5000, 8) and M.dtype == np.int32
     assert all(len(set(r)) == 8 for r in M[0].tolist()[:500])
     np.testing.assert_array_equal(M, synth.succ_matrix0(w, 7))
+
+
+def test_roofline_cost_table_closed_form():
+    # one layer of the 8B-class proxy: 4096*(48*128) + 4096*4096 + 3*4096*14336
+    # = 218103808 weights, 436207616 bytes, 54.5259520 us at 8 TB/s; the LM head
+    # 2*4096*128256 = 1050673152 bytes, 131.334144 us.  At batch 8 a forward of
+    # one token with no context is HBM-bound: 32 * 54.525952 + 131.334144 us
+    T = synth.roofline_table(configs.PROXY_TARGET, 8, 256, 16, 128)
+    Dh = synth.roofline_table(configs.PROXY_DRAFT, 8, 256, 16, 128)
+    assert T.shape == (16, 129) and (T[:, 0] == 0).all()
+    np.testing.assert_allclose(T[0, 1], 32 * 54.525952 + 131.334144, rtol=1e-6)
+    np.testing.assert_allclose(Dh[0, 1], 54.525952 + 131.334144, rtol=1e-6)
+    # HBM-bound up to 312.5 token rows of a layer (2 flops per weight per row
+    # against 2 bytes per weight: 2.5e15 / 8e12), so 39 tokens at batch 8 cost
+    # the same as one, and the 40th costs more
+    assert (T[0, 1:40] == T[0, 1]).all() and T[0, 40] > T[0, 39]
+    # the context adds 2 * 2 * B * c * Hkv * D bytes of keys and values a layer
+    np.testing.assert_allclose(T[1, 1] - T[0, 1], 32 * 2 * 2 * 8 * 256 * 8 * 128 / 8e12 * 1e6, rtol=1e-5)
+    assert (np.diff(T[:, 1:], axis=1) >= 0).all() and (np.diff(T[:, 1:], axis=0) >= 0).all()
+    w = configs.Workload(**{**configs.C2.__dict__,
+                            "cast": configs.CastSpec(table="roofline", table_B=64)})
+    S_T, S_D = synth.cost_tables(w)
+    np.testing.assert_array_equal(S_T, synth.roofline_table(configs.PROXY_TARGET, 64, 256, 16, 128))
+    np.testing.assert_array_equal(S_D, synth.roofline_table(configs.PROXY_DRAFT, 64, 256, 16, 128))
+    assert (S_T[0, 1:5] == S_T[0, 1]).all() and S_T[0, 5] > S_T[0, 4]

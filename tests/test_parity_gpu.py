@@ -158,6 +158,20 @@ def test_cast_seeded_cost_table():
         H.compare(case, H.gpu_round(case))
 
 
+@pytest.mark.parametrize("table_B,C1,C2,C3", [(64, 10.0, 0.5, 0.5), (16, 2.0, 1.0, 0.3)])
+def test_cast_roofline_cost_table(table_B, C1, C2, C3):
+    # MI355X-shaped costs: flat while a forward is HBM-bound (equal neighbouring
+    # costs, the zero-cost-step branch of the width and verify scans), rising
+    # once it is MFMA-bound
+    cs = configs.CastSpec(table="roofline", table_B=table_B, C1=C1, C2=C2, C3=C3)
+    w = configs.Workload(**{**SMALL["cast"].__dict__, "cast": cs, "name": f"cast_roofline_{table_B}"})
+    cast = H.cast_params(w)
+    for seed in (3, 4):
+        case = H.oracle_case(w, seed, 0, cast=cast)
+        say(f"cast roofline table B={table_B} seed={seed} m={case.out['m_rows'].tolist()}")
+        H.compare(case, H.gpu_round(case))
+
+
 def test_graft_small_multi_round():
     w = configs.shrink(configs.C4, V=6000, B=5)
     tau = H.calibrate_tau(w, 77, 4)
