@@ -176,15 +176,19 @@ def ingest_pmc(fetch_csv: str, write_csv: str, workload: str, ring: int) -> None
     print(json.dumps(out))
 
 
-def tree_attention_detail(api, dev, seed: int = 7, launches: int = 10) -> dict:
-    """The verify forward's tree attention at the B=64 mixed shape: 129 flat
-    positions per request over a 4096-token prefix, 32 query and 8 key/value
-    heads of 128 (an 8B-class target).  Trees are random (every parent within
-    the 16 positions before its child); q, k and v are seeded normal bf16.
-    Timed with events on the launch stream; algorithmic flops count the
-    visible (query, key) pairs only: 4 * D per pair and query head."""
+def tree_attention_detail(api, dev, seed: int = 7, launches: int = 10, B: int = 64, P: int = 129,
+                          L: int = 4096, split_options=(None,)) -> dict:
+    """The verify forward's tree attention, by default at the B=64 mixed
+    shape: 129 flat positions per request over a 4096-token prefix, 32 query
+    and 8 key/value heads of 128 (an 8B-class target).  Trees are random
+    (every parent within the 16 positions before its child); q, k and v are
+    seeded normal bf16.  Timed with events on the launch stream; algorithmic
+    flops count the visible (query, key) pairs only: 4 * D per pair and query
+    head.  split_options: None times ddt_tree_attention, an integer
+    ddt_tree_attention_split with that many key splits (0: the library's
+    choice); the first option gives the top-level figures."""
     import torch
-    B, P, L, Hq, Hkv, D = 64, 129, 4096, 32, 8, 128
+    Hq, Hkv, D = 32, 8, 128
     rng = np.random.default_rng(seed)
     flat = api.DeviceFlat(B, P - 1, 10, dev)
     W = flat.W
@@ -205,28 +209,38 @@ def tree_attention_detail(api, dev, seed: int = 7, launches: int = 10) -> dict:
     q, kt, vt = mk(B, P, Hq, D), mk(B, P, Hkv, D), mk(B, P, Hkv, D)
     kp, vp = mk(B, L, Hkv, D), mk(B, L, Hkv, D)
     out = torch.empty(B, P, Hq, D, dtype=torch.float32, device=dev)
-    for _ in range(3):
-        api.tree_attention(flat, q, kt, vt, out, k_pre=kp, v_pre=vp)
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * launches)]
-    for i in range(launches):
-        ev[2 * i].record()
-        api.tree_attention(flat, q, kt, vt, out, k_pre=kp, v_pre=vp)
-        ev[2 * i + 1].record()
-    torch.cuda.synchronize()
-    us = np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(launches)])
     pairs = float(B * P * L + vis.sum())
     flops = 4.0 * D * Hq * pairs
-    tflops = flops / us.mean() / 1e6
     kv_bytes = (kp.numel() + vp.numel() + kt.numel() + vt.numel()) * 2
-    log(f"tree attention: {us.mean():.1f} us, {tflops:.1f} TFLOP/s ({tflops / PEAK_BF16_TFLOPS:.3f} of peak)")
     res = {"kernel": "k_tree_attention (bf16 MFMA 32x32x16, fp32 accumulate)",
            "shape": {"B": B, "P": P, "prefix": L, "Hq": Hq, "Hkv": Hkv, "D": D},
-           "avg_launch_us": round(float(us.mean()), 2), "launches": launches,
-           "flops_per_launch": flops, "tflops": round(float(tflops), 1),
-           "roofline": {"bound": "mfma", "achieved": round(float(tflops), 1), "peak": PEAK_BF16_TFLOPS,
-                        "unit": "TFLOP/s", "frac": round(float(tflops / PEAK_BF16_TFLOPS), 4)},
-           "kv_gbs": round(float(kv_bytes / us.mean() / 1e3), 1)}
+           "flops_per_launch": flops, "launches": launches}
+    for k, splits in enumerate(split_options):
+        used, need = api.attention_splits(B, P, Hq, Hkv, L, splits or 0) if splits is not None else (1, 0)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        call = lambda: api.tree_attention(flat, q, kt, vt, out, k_pre=kp, v_pre=vp, splits=splits, ws=ws)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * launches)]
+        for i in range(launches):
+            ev[2 * i].record()
+            call()
+            ev[2 * i + 1].record()
+        torch.cuda.synchronize()
+        us = np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(launches)])
+        tflops = flops / us.mean() / 1e6
+        log(f"tree attention B={B} P={P} L={L} splits={splits} ({used}): {us.mean():.1f} us, "
+            f"{tflops:.1f} TFLOP/s ({tflops / PEAK_BF16_TFLOPS:.3f} of peak)")
+        one = {"splits": used, "avg_launch_us": round(float(us.mean()), 2), "tflops": round(float(tflops), 1),
+               "roofline": {"bound": "mfma", "achieved": round(float(tflops), 1), "peak": PEAK_BF16_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(float(tflops / PEAK_BF16_TFLOPS), 4)},
+               "kv_gbs": round(float(kv_bytes / us.mean() / 1e3), 1)}
+        if k == 0:
+            res.update(one)
+        else:
+            res.setdefault("variants", []).append(one)
+        del ws
     del q, kt, vt, kp, vp, out
     torch.cuda.empty_cache()
     return res
@@ -720,6 +734,10 @@ def main():
     }
     if not args.no_attention:
         out["detail"]["tree_attention"] = tree_attention_detail(api, dev)
+        # the CAST workload's verify shape (8 requests, 61 flat positions) over
+        # a 4096-token context: too few tiles to fill the device on their own
+        out["detail"]["tree_attention_b8"] = tree_attention_detail(api, dev, B=8, P=61, L=4096,
+                                                                   split_options=(0, None))
         out["detail"]["kv_commit"] = kv_commit_detail(api, dev)
     if w.cast is not None and not args.no_calibrate:
         out["detail"]["cast_calibration"] = cast_calibration_detail(w, run, ring, to_dev, dev)

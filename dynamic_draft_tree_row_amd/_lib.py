@@ -81,6 +81,9 @@ SIGNATURES = {
     "ddt_succ_update": (C.c_int, [P, i64, C.c_int, C.c_int, C.POINTER(Flat), P, C.c_int,
                                   C.POINTER(Logits), P, sz, P]),
     "ddt_tree_attention": (C.c_int, [C.POINTER(Flat), C.POINTER(Attn), P, P]),
+    "ddt_tree_attention_split": (C.c_int, [C.POINTER(Flat), C.POINTER(Attn), P, C.c_int, P, sz, P]),
+    "ddt_tree_attention_splits": (C.c_int, [C.c_int] * 6),
+    "ddt_tree_attention_ws_bytes": (sz, [C.c_int] * 6),
     "ddt_succ_gather_at": (C.c_int, [C.POINTER(Tree), P, C.c_int64, C.c_int, C.c_int, C.c_int, C.c_int,
                                      C.c_int, C.c_int, C.c_int, P, P, P]),
     "ddt_kv_commit": (C.c_int, [C.POINTER(KVCache), P, P, C.c_int, P, P, C.c_int, P, P]),

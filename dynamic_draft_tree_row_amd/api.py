@@ -8,7 +8,7 @@ from __future__ import annotations
 
 import ctypes as C
 from dataclasses import dataclass
-from typing import Optional, Sequence
+from typing import Optional, Sequence, Tuple
 
 import torch
 
@@ -228,12 +228,23 @@ def succ_update(M: torch.Tensor, flat: DeviceFlat, k_succ: int, row_topk: Option
         _stream(stream, M.device)))
 
 
+def attention_splits(B: int, P: int, Hq: int, Hkv: int, ctx: int, splits: int = 0) -> Tuple[int, int]:
+    """(split count, workspace bytes) of ddt_tree_attention_split for these
+    sizes (ctx: context positions)."""
+    lib = L.load()
+    return (int(lib.ddt_tree_attention_splits(B, P, Hq, Hkv, ctx, splits)),
+            int(lib.ddt_tree_attention_ws_bytes(B, P, Hq, Hkv, ctx, splits)))
+
+
 def tree_attention(flat: DeviceFlat, q: torch.Tensor, k_tree: torch.Tensor, v_tree: torch.Tensor,
                    out: torch.Tensor, k_pre: Optional[torch.Tensor] = None,
                    v_pre: Optional[torch.Tensor] = None, scale: Optional[float] = None,
-                   stream=None) -> None:
+                   stream=None, splits: Optional[int] = None,
+                   ws: Optional[torch.Tensor] = None) -> None:
     """ddt_tree_attention: q [B][P][Hq][D], k/v_tree [B][P][Hkv][D], k/v_pre [B][L][Hkv][D]
-    (bf16, contiguous); out fp32 [B][P][Hq][D]."""
+    (bf16, contiguous); out fp32 [B][P][Hq][D].  splits (0 = the library's
+    choice) calls ddt_tree_attention_split instead, with ws (uint8, device) or
+    a workspace allocated here."""
     B, P, Hq, D = q.shape
     Hkv = k_tree.shape[2]
     Lp = 0 if k_pre is None else k_pre.shape[1]
@@ -244,8 +255,16 @@ def tree_attention(flat: DeviceFlat, q: torch.Tensor, k_tree: torch.Tensor, v_tr
         raise ValueError("out must be contiguous fp32 [B][P][Hq][D]")
     a = L.Attn(_ptr(q), _ptr(k_pre) if Lp else None, _ptr(v_pre) if Lp else None, _ptr(k_tree),
                _ptr(v_tree), B, P, Hq, Hkv, D, Lp, float(scale if scale is not None else D ** -0.5))
-    L.check("ddt_tree_attention", L.load().ddt_tree_attention(C.byref(flat.c), C.byref(a), _ptr(out),
-                                                                _stream(stream, q.device)))
+    if splits is None:
+        L.check("ddt_tree_attention", L.load().ddt_tree_attention(C.byref(flat.c), C.byref(a), _ptr(out),
+                                                                    _stream(stream, q.device)))
+        return
+    _, need = attention_splits(B, P, Hq, Hkv, Lp, splits)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    L.check("ddt_tree_attention_split", L.load().ddt_tree_attention_split(
+        C.byref(flat.c), C.byref(a), _ptr(out), splits, _ptr(ws), nbytes, _stream(stream, q.device)))
 
 
 def row_topk(x: torch.Tensor, K: int, ws: torch.Tensor, ids: Optional[torch.Tensor] = None,

@@ -12,7 +12,8 @@ It times proxy forwards of named model shapes with random bf16 weights: one
 decoder layer, timed and multiplied by the layer count, plus the LM head.  A
 layer is the QKV projection, attention of the n new positions over the c
 context positions and over their own causal prefix (this library's tree
-attention with a chain-shaped tree), the output projection and a gated FFN
+attention with a chain-shaped tree, key-split when the batch is small), the
+output projection and a gated FFN
 with residual adds; the projections are library GEMMs with weights stored
 [out][in] as checkpoints hold them (torch.nn.functional.linear, hipBLASLt on
 this device).  Each timed unit is captured once in a HIP graph and
@@ -137,7 +138,7 @@ class _Proxy:
         k = qkv[:, hq:hq + hk].reshape(B, n, pm.Hkv, pm.D).contiguous()
         v = qkv[:, hq + hk:].reshape(B, n, pm.Hkv, pm.D).contiguous()
         out = torch.empty(B, n, pm.Hq, pm.D, dtype=torch.float32, device=self.device)
-        self.api.tree_attention(self.flat(n), q, k, v, out, k_pre=ly.kp, v_pre=ly.vp)
+        self.api.tree_attention(self.flat(n), q, k, v, out, k_pre=ly.kp, v_pre=ly.vp, splits=0)
         h = x + lin(out.reshape(B * n, hq).to(torch.bfloat16), ly.Wo)
         gu = lin(h, ly.Wgu)
         f = torch.nn.functional.silu(gu[:, :pm.ffn]) * gu[:, pm.ffn:]

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 #include <string.h>
+#include <algorithm>
 
 #include "../../include/ddt.h"
 #include "ddt_device.hpp"
@@ -397,7 +398,47 @@ int ddt_tree_verify(const ddt_tree* t, const ddt_flat* f, const ddt_logits* targ
     return launched();
 }
 
-int ddt_tree_attention(const ddt_flat* f, const ddt_attn* a, float* out, void* stream) {
+// Key splits of the attention: when the tiles alone leave the device
+// underused, as many splits as fit one resident round of 512 workgroups (two
+// per compute unit of a 256-unit device: more rounds lose more to the
+// partials than they gain), at least two 64-key blocks per split, at most 32
+// splits.  Returns the split count (0 on invalid sizes) and the blocks per
+// split.
+static int attn_split_plan(int B, int P, int Hq, int Hkv, int L, int req, int* spb) {
+    if (B < 1 || P < 1 || Hq < 1 || Hkv < 1 || L < 0 || Hq % Hkv != 0) return 0;
+    const long long tiles = ((long long)P * (Hq / Hkv) + TA_ROWS - 1) / TA_ROWS;
+    const int nblk = (L + TA_KB - 1) / TA_KB + (P + TA_KB - 1) / TA_KB;
+    long long s;
+    if (req > 0) {
+        s = req;
+    } else {
+        const long long base = (long long)B * Hkv * tiles;
+        s = base >= 512 ? 1 : 512 / base;
+        s = std::min<long long>(s, std::max(1, nblk / 2));
+    }
+    s = std::max<long long>(1, std::min<long long>({s, 32, nblk}));
+    const int per = (int)((nblk + s - 1) / s);
+    if (spb) *spb = per;
+    return (nblk + per - 1) / per;
+}
+
+static size_t attn_ws_need(int B, int P, int Hq, int splits) {
+    if (splits <= 1) return 0;
+    const size_t rows = (size_t)splits * B * P * Hq;
+    return align256(rows * TA_D * 4) + align256(rows * 8);
+}
+
+int ddt_tree_attention_splits(int B, int P, int Hq, int Hkv, int L, int splits) {
+    return attn_split_plan(B, P, Hq, Hkv, L, splits, nullptr);
+}
+
+size_t ddt_tree_attention_ws_bytes(int B, int P, int Hq, int Hkv, int L, int splits) {
+    const int s = attn_split_plan(B, P, Hq, Hkv, L, splits, nullptr);
+    return s == 0 ? 0 : attn_ws_need(B, P, Hq, s);
+}
+
+static int tree_attention_run(const ddt_flat* f, const ddt_attn* a, float* out, int req, void* ws,
+                              size_t ws_bytes, void* stream) {
     if (f == nullptr || a == nullptr || out == nullptr) return DDT_EINVAL;
     int st = check_flat(f, a->B);
     if (st) return st;
@@ -418,10 +459,28 @@ int ddt_tree_attention(const ddt_flat* f, const ddt_attn* a, float* out, void* s
     x.tiles = (a->P * x.G + TA_ROWS - 1) / TA_ROWS;
     x.groups = a->B * a->Hkv;
     x.sl2 = a->scale * DDT_LOG2E;
-    const long long grid = (long long)a->B * a->Hkv * x.tiles;
+    x.splits = attn_split_plan(a->B, a->P, a->Hq, a->Hkv, a->L, req, &x.spb);
+    x.po = x.pml = nullptr;
+    if (x.splits > 1) {
+        const size_t need = attn_ws_need(a->B, a->P, a->Hq, x.splits);
+        if (ws == nullptr || ws_bytes < need || ((uintptr_t)ws & 255u) != 0) return DDT_EWORKSPACE;
+        x.po = (float*)ws;
+        x.pml = (float*)((char*)ws + align256((size_t)x.splits * a->B * a->P * a->Hq * TA_D * 4));
+    }
+    const long long grid = (long long)a->B * a->Hkv * x.tiles * x.splits;
     if (grid > INT32_MAX) return DDT_ECAPACITY;
     ddt_attention_launch(x, (unsigned)grid, (hipStream_t)stream);
     return launched();
+}
+
+int ddt_tree_attention(const ddt_flat* f, const ddt_attn* a, float* out, void* stream) {
+    return tree_attention_run(f, a, out, 1, nullptr, 0, stream);
+}
+
+int ddt_tree_attention_split(const ddt_flat* f, const ddt_attn* a, float* out, int splits, void* ws,
+                             size_t ws_bytes, void* stream) {
+    if (splits < 0) return DDT_EINVAL;
+    return tree_attention_run(f, a, out, splits, ws, ws_bytes, stream);
 }
 
 static int kv_check(const ddt_kv_cache* c, KvCache* out) {

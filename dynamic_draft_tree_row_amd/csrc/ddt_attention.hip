@@ -8,13 +8,14 @@ __global__ __launch_bounds__(TA_NT, 2) void k_tree_attention(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t s_vt[2 * TA_VBUF];
 
     // workgroups are dealt to the 8 XCDs in turn; renumber so that each XCD
-    // takes a contiguous run of (head, tile) and the tiles of one key/value
-    // head read its keys through the same L2
-    const int total = a.groups * a.tiles;
+    // takes a contiguous run of (head, split, tile) and the tiles of one
+    // key/value head and split read their keys through the same L2
+    const int total = a.groups * a.tiles * a.splits;
     const int xq = total >> 3, xr = total & 7;
     const int xc = blockIdx.x & 7, xs = blockIdx.x >> 3;
     const int lid = xc < xr ? xc * (xq + 1) + xs : xr * (xq + 1) + (xc - xr) * xq + xs;
-    const int tile = lid % a.tiles, bg = lid / a.tiles;
+    const int tile = lid % a.tiles, rest = lid / a.tiles;
+    const int sp = rest % a.splits, bg = rest / a.splits;
     const int b = bg / a.Hkv, g = bg - (bg / a.Hkv) * a.Hkv;
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -26,7 +27,9 @@ __global__ __launch_bounds__(TA_NT, 2) void k_tree_attention(AttnArgs a) {
     const int r0 = tile * TA_ROWS;
 
     if (r0 >= R) {
-        // only padding rows: zeros
+        // only padding rows: zeros (split partials cover live rows only; the
+        // combination writes the padding rows)
+        if (a.splits > 1) return;
         for (int e = tid; e < TA_ROWS * (TA_D / 4); e += TA_NT) {
             const int r = r0 + e / (TA_D / 4), d4 = e - (e / (TA_D / 4)) * (TA_D / 4);
             if (r < RT) {
@@ -241,21 +244,26 @@ __global__ __launch_bounds__(TA_NT, 2) void k_tree_attention(AttnArgs a) {
         }
     };
 
-    fetch(0);
-    stage(0, 0);
+    // this workgroup's key blocks: split sp of the blocks (all of them with
+    // one split); an empty range leaves the partial at no weight
+    const int x0 = sp * a.spb, x1 = min(nblk, x0 + a.spb);
+    if (x0 < x1) {
+        fetch(x0);
+        stage(x0, 0);
+    }
     __syncthreads();
     // compute(x) also loads block x + 1 (past the last block every key is
     // invalid and reads a valid row, so the final extra loads stay in bounds)
-    for (int x = 0; x < nblk; x += 2) {
+    for (int x = x0; x < x1; x += 2) {
         // two blocks per trip so that the buffer offsets are constants
         if (wave_live) compute(x, 0);
         else fetch(x + 1);
-        if (x + 1 < nblk) stage(x + 1, 1);
+        if (x + 1 < x1) stage(x + 1, 1);
         __syncthreads();
-        if (x + 1 >= nblk) break;
+        if (x + 1 >= x1) break;
         if (wave_live) compute(x + 1, 1);
         else fetch(x + 2);
-        if (x + 2 < nblk) stage(x + 2, 0);
+        if (x + 2 < x1) stage(x + 2, 0);
         __syncthreads();
     }
 
@@ -265,9 +273,24 @@ __global__ __launch_bounds__(TA_NT, 2) void k_tree_attention(AttnArgs a) {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
         lsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     }
+    const int i = row / G, hq = g * G + (row - (row / G) * G);
+    if (a.splits > 1) {
+        // this split's share: outputs against the running maximum, unscaled
+        if (live) {
+            const size_t prow = (((size_t)sp * (a.groups / Hkv) + b) * P + i) * Hq + hq;
+            float* dst = a.po + prow * TA_D + 4 * hh;
+#pragma unroll
+            for (int t = 0; t < TA_D / 32; ++t)
+#pragma unroll
+                for (int jq = 0; jq < 4; ++jq)
+                    *(float4*)(dst + 32 * t + 8 * jq) =
+                        make_float4(o[t][4 * jq], o[t][4 * jq + 1], o[t][4 * jq + 2], o[t][4 * jq + 3]);
+            if (hh == 0) *(float2*)(a.pml + 2 * prow) = make_float2(mrun, lsum);
+        }
+        return;
+    }
     if (row < RT) {
         const float inv = live && lsum > 0.f ? 1.f / lsum : 0.f;
-        const int i = row / G, hq = g * G + (row - (row / G) * G);
         float* dst = a.out + (((size_t)b * P + i) * Hq + hq) * TA_D + 4 * hh;
 #pragma unroll
         for (int t = 0; t < TA_D / 32; ++t)
@@ -278,6 +301,47 @@ __global__ __launch_bounds__(TA_NT, 2) void k_tree_attention(AttnArgs a) {
     }
 }
 
+// Combination of the splits: one wave per output row (request, flat
+// position, query head), two dims per lane.  With m_s and l_s the running
+// maximum and weight total of split s and o_s its unnormalised output, all
+// against 2^(sl2 * (score - m_s)), the row is
+//   sum_s 2^(sl2 (m_s - M)) o_s / sum_s 2^(sl2 (m_s - M)) l_s,  M = max_s m_s.
+// Positions past the request's m are written as 0.
+#define TA_CNT 256
+__global__ __launch_bounds__(TA_CNT) void k_attn_combine(AttnArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int B = a.groups / a.Hkv, P = a.P, Hq = a.Hq;
+    const long long rows = (long long)B * P * Hq;
+    const long long r = (long long)blockIdx.x * (TA_CNT / 64) + (threadIdx.x >> 6);
+    if (r >= rows) return;
+    const int b = (int)(r / ((long long)P * Hq));
+    const int i = (int)((r / Hq) % P);
+    const int n = min(max(a.m[b], 0), P - 1) + 1;
+    float2 res = make_float2(0.f, 0.f);
+    if (i < n) {
+        const size_t split_rows = (size_t)rows;
+        float M = TA_MFLOOR;
+        for (int s = 0; s < a.splits; ++s) M = fmaxf(M, a.pml[2 * (s * split_rows + r)]);
+        float den = 0.f, n0 = 0.f, n1 = 0.f;
+        for (int s = 0; s < a.splits; ++s) {
+            const float2 ml = *(const float2*)(a.pml + 2 * (s * split_rows + r));
+            const float w = __builtin_amdgcn_exp2f((ml.x - M) * a.sl2);
+            const float2 os = *(const float2*)(a.po + (s * split_rows + r) * TA_D + 2 * lane);
+            den = fmaf(w, ml.y, den);
+            n0 = fmaf(w, os.x, n0);
+            n1 = fmaf(w, os.y, n1);
+        }
+        const float inv = den > 0.f ? 1.f / den : 0.f;
+        res = make_float2(n0 * inv, n1 * inv);
+    }
+    *(float2*)(a.out + (size_t)r * TA_D + 2 * lane) = res;
+}
+
 void ddt_attention_launch(const AttnArgs& a, unsigned grid, hipStream_t stream) {
     hipLaunchKernelGGL(k_tree_attention, dim3(grid), dim3(TA_NT), 0, stream, a);
+    if (a.splits > 1) {
+        const long long rows = (long long)(a.groups / a.Hkv) * a.P * a.Hq;
+        const unsigned cg = (unsigned)((rows + TA_CNT / 64 - 1) / (TA_CNT / 64));
+        hipLaunchKernelGGL(k_attn_combine, dim3(cg), dim3(TA_CNT), 0, stream, a);
+    }
 }

@@ -64,6 +64,12 @@ struct AttnArgs {
     float* out;                 // fp32 [B][P][Hq][D]
     int P, W, Hq, Hkv, G, L, tiles, groups;     // groups = B * Hkv
     float sl2;                  // scale * log2(e), > 0
+    // key splits: split s takes key blocks [s * spb, (s + 1) * spb); with
+    // splits > 1 the rows' unnormalised outputs go to po [splits][B][P][Hq][D]
+    // and their (running maximum, weight total) to pml [splits][B][P][Hq][2]
+    int splits, spb;
+    float* po;
+    float* pml;
 };
 
 __device__ __forceinline__ ta_bf16x8 ta_as_bf16x8(u32x4 v) { return __builtin_bit_cast(ta_bf16x8, v); }
@@ -72,5 +78,6 @@ __device__ __forceinline__ ta_bf16x8 ta_as_bf16x8(u32x4 v) { return __builtin_bi
 // k + 4, k + 8, k + 12 within 16) land on different chunks
 __device__ __forceinline__ int ta_kswz(int k) { return (k & 3) | ((k >> 1) & 4) | ((k << 1) & 8); }
 
-// Launches k_tree_attention on grid workgroups of TA_NT threads.
+// Launches k_tree_attention on grid workgroups of TA_NT threads, then, with
+// more than one split, the combination of the splits' partials into out.
 void ddt_attention_launch(const AttnArgs& a, unsigned grid, hipStream_t stream);

@@ -251,14 +251,21 @@ __device__ void cast_decide(CastLds& L, const ddt_tree& t, const ddt_cast& cp, i
 }
 
 // The batch rule in the last workgroup of a layer: every thread loads the
-// rows' frontier values, wave 0 the row counts; then wave 0 decides.
+// rows' frontier values, wave 0 the row counts, all together with the
+// batch's continue flag (one round trip); then wave 0 decides, or, when an
+// earlier layer stopped the batch, every row's frontier is cleared.
 template <int NT>
 __device__ void cast_layer(CastLds& L, const ddt_tree& t, const ddt_cast& cp, int layer, int K_e) {
     const int tid = threadIdx.x, B = t.B, R = t.R_max;
+    const int cont = t.cont[0];
     for (int q = tid; q < B * R; q += NT) L.v[q] = (double)expf(t.front_S[q]);
     int cnt = 0x7FFFFFFF;
     if (tid < B) cnt = max(0, t.n_nodes[tid] - t.layer_base[tid]);
     __syncthreads();
+    if (!cont) {
+        for (int bb = tid; bb < B; bb += NT) t.n_front[bb] = 0;
+        return;
+    }
     if (tid < DDT_WAVE) {
         const int kc = (int)wave_min_u32((uint32_t)cnt);
         cast_decide(L, t, cp, layer, min(min(K_e, R), kc));
@@ -443,9 +450,7 @@ __global__ __launch_bounds__(AT_NT) void k_attach(AttachArgs a) {
     }
     __syncthreads();
     if (!s_last) return;
-    if (t.cont[0]) cast_layer<AT_NT>(s_cast, t, a.c, a.layer, a.K_e);
-    else
-        for (int bb = tid; bb < t.B; bb += AT_NT) t.n_front[bb] = 0;
+    cast_layer<AT_NT>(s_cast, t, a.c, a.layer, a.K_e);
 }
 
 // ---------------------------------------------------------------------------

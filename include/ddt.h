@@ -398,6 +398,38 @@ typedef struct ddt_attn {
 int ddt_tree_attention(const ddt_flat* f /*host*/, const ddt_attn* a /*host*/, float* out,
                        void* stream);
 
+/*
+ * ddt_tree_attention_split -- the same attention with each (request,
+ * key/value head, tile of 128 query rows) split over `splits` contiguous
+ * ranges of its 64-key blocks (prefix blocks first, then tree blocks), for
+ * shapes whose tiles alone do not fill the GPU: few requests, few flat
+ * positions, a long context.  Each split writes its rows' unnormalised
+ * outputs and softmax statistics (running maximum, weight total) to ws; a
+ * second kernel combines them, so out holds the same softmax up to fp32
+ * rounding of the combination.  Same tensors, limits and errors as
+ * ddt_tree_attention.
+ *   splits  requested splits; 0 lets the library choose for the shape (one
+ *           split once the tiles fill the device, otherwise as many as fit
+ *           one resident round of 512 workgroups, with at least two key
+ *           blocks each).  The count
+ *           is capped at 32 and at the number of key blocks (ceil(L / 64) +
+ *           ceil(P / 64)), and lowered so that every split but the last has
+ *           the same number of blocks; ddt_tree_attention_splits returns the
+ *           count used.  One split runs ddt_tree_attention.
+ *   ws      device workspace of at least ddt_tree_attention_ws_bytes(...)
+ *           bytes (256-byte aligned), owned by the caller, overwritten.
+ * Errors additionally: DDT_EWORKSPACE if ws is NULL or too small while more
+ * than one split is used.
+ */
+int ddt_tree_attention_split(const ddt_flat* f /*host*/, const ddt_attn* a /*host*/, float* out,
+                             int splits, void* ws, size_t ws_bytes, void* stream);
+
+/* The split count ddt_tree_attention_split uses for these sizes and request
+ * (0 = the library's choice), and the workspace bytes it needs then (0 when
+ * one split is used); both return 0 on invalid sizes. */
+int ddt_tree_attention_splits(int B, int P, int Hq, int Hkv, int L, int splits);
+size_t ddt_tree_attention_ws_bytes(int B, int P, int Hq, int Hkv, int L, int splits);
+
 /* ------------------------------------------------------------------------ */
 /* Paged KV cache: committing the accepted path, sharing, release            */
 /* ------------------------------------------------------------------------ */

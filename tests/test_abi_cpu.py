@@ -140,6 +140,33 @@ def test_calls_reject_bad_arguments_before_launch(lib):
     assert lib.ddt_row_topk(C.byref(huge), 1, 1, 4, None, None, None, None, ws, 1 << 30,
                             None) == L.DDT_ECAPACITY
     assert lib.ddt_strerror(L.DDT_EWORKSPACE).decode() == "workspace too small"
+    # tree attention with key splits: sizes are host arithmetic; a split
+    # count above 1 needs an aligned workspace of the stated size
+    sp, wsb = lib.ddt_tree_attention_splits, lib.ddt_tree_attention_ws_bytes
+    assert sp(64, 129, 32, 8, 4096, 0) == 1 and wsb(64, 129, 32, 8, 4096, 0) == 0
+    # 8 requests x 8 heads x 2 tiles = 128 workgroups: 4 splits (512 in all)
+    # of 17 of the 65 key blocks; partials of 4 x 8 x 61 x 32 rows, 128
+    # outputs + 2 statistics each
+    assert sp(8, 61, 32, 8, 4096, 0) == 4
+    assert wsb(8, 61, 32, 8, 4096, 0) == 4 * 8 * 61 * 32 * (128 * 4 + 8)
+    assert sp(8, 1, 32, 8, 4096, 0) == 8 and sp(16, 61, 32, 8, 4096, 0) == 2
+    assert sp(2, 20, 2, 1, 300, 5) == 3                     # 6 blocks, 2 per split
+    assert sp(2, 20, 2, 1, 300, 99) == 6 and sp(2, 20, 2, 1, 0, 4) == 1
+    assert sp(2, 20, 3, 2, 300, 0) == 0 and wsb(0, 20, 2, 1, 300, 0) == 0
+    nf = lib.ddt_flat_bytes(2, 19, 4)
+    fbuf = (C.c_uint8 * (nf + 256))()
+    fbase = (C.addressof(fbuf) + 255) & ~255
+    fl = L.Flat()
+    assert lib.ddt_flat_bind(C.byref(fl), C.c_void_p(fbase), nf, 2, 19, 4) == L.DDT_OK
+    at = L.Attn(dummy, dummy, dummy, dummy, dummy, 2, 20, 2, 1, 128, 300, 0.1)
+    asp = lib.ddt_tree_attention_split
+    need = wsb(2, 20, 2, 1, 300, 5)
+    assert asp(C.byref(fl), C.byref(at), dummy, -1, ws, need, None) == L.DDT_EINVAL
+    assert asp(C.byref(fl), C.byref(at), dummy, 5, None, need, None) == L.DDT_EWORKSPACE
+    assert asp(C.byref(fl), C.byref(at), dummy, 5, ws, need - 1, None) == L.DDT_EWORKSPACE
+    assert asp(C.byref(fl), C.byref(at), dummy, 5, C.c_void_p(base + 8), need, None) == L.DDT_EWORKSPACE
+    bad_at = L.Attn(dummy, dummy, dummy, dummy, dummy, 2, 20, 2, 1, 128, 300, 0.0)
+    assert asp(C.byref(fl), C.byref(bad_at), dummy, 5, ws, need, None) == L.DDT_EINVAL
     # paged KV cache
     kv = L.KVCache(dummy, dummy, dummy, dummy, dummy, dummy, dummy, dummy, 4, 8, 64, 16, 8, 128)
     c = lib.ddt_kv_commit

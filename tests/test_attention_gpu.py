@@ -78,6 +78,20 @@ def _check(out, q, kp, vp, kt, vt, parents, ns, scale):
 @pytest.mark.parametrize("Lp", [0, 50, 300])
 @pytest.mark.parametrize("P,Hq,Hkv", [(61, 8, 2), (129, 4, 4), (20, 2, 1)])
 def test_tree_attention_random_trees(Lp, P, Hq, Hkv):
+    _random_case(Lp, P, Hq, Hkv)
+
+
+# key splits (ddt_tree_attention_split): the library's choice (0) and forced
+# counts, ragged last splits, a tree-only case (one block: one split), one
+# flat position (a decode step over a long context), the CAST verify shape
+@pytest.mark.parametrize("Lp,P,Hq,Hkv,splits", [
+    (300, 61, 8, 2, 0), (300, 61, 8, 2, 3), (50, 20, 2, 1, 2), (1000, 129, 4, 4, 5),
+    (0, 61, 8, 2, 2), (700, 1, 32, 8, 0), (2000, 61, 32, 8, 0), (130, 70, 2, 2, 32)])
+def test_tree_attention_key_splits(Lp, P, Hq, Hkv, splits):
+    _random_case(Lp, P, Hq, Hkv, splits)
+
+
+def _random_case(Lp, P, Hq, Hkv, splits=None):
     from dynamic_draft_tree_row_amd import api
     rng = np.random.default_rng(1000 * P + Lp + Hq)
     B, D = 3, 128
@@ -98,11 +112,12 @@ def test_tree_attention_random_trees(Lp, P, Hq, Hkv):
     kp = _bf16(rng.standard_normal((B, Lp, Hkv, D)))
     vp = _bf16(rng.standard_normal((B, Lp, Hkv, D)))
     out = torch.full((B, P, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
-    print(f"tree_attention P={P} Hq={Hq} Hkv={Hkv} L={Lp}", flush=True)
+    used = None if splits is None else api.attention_splits(B, P, Hq, Hkv, Lp, splits)[0]
+    print(f"tree_attention P={P} Hq={Hq} Hkv={Hkv} L={Lp} splits={splits} -> {used}", flush=True)
     scale = D ** -0.5
     api.tree_attention(flat, _to_dev(q), _to_dev(kt), _to_dev(vt), out,
                        k_pre=_to_dev(kp) if Lp else None, v_pre=_to_dev(vp) if Lp else None,
-                       scale=scale)
+                       scale=scale, splits=splits)
     torch.cuda.synchronize()
     _check(out.cpu().numpy(), q, kp, vp, kt, vt, parents, ns, scale)
 
