@@ -64,6 +64,11 @@ __global__ __launch_bounds__(TA_NT, 2) void k_tree_attention(AttnArgs a) {
     // written transposed, 4 keys to an 8-byte store
     const int HD = Hkv * TA_D;
     const int sr = tid >> 4, sc = tid & 15;
+    // V keys and dims of this thread: keys 4*vsr .. +3, dims 8*vsc .. +7.
+    // The 16 lanes of one 8-byte LDS store phase then hold both key halves of
+    // one 8-key group and 8 dims 16 apart, whose 16-byte dim slots fall on 8
+    // different bank groups: the transposed stores are conflict-free
+    const int vsr = 2 * (tid >> 5) + (tid & 1), vsc = 2 * ((tid >> 1) & 7) + ((tid >> 4) & 1);
     const uint16_t* kpb = a.kp + ((size_t)b * L * Hkv + g) * TA_D;
     const uint16_t* vpb = a.vp + ((size_t)b * L * Hkv + g) * TA_D;
     const uint16_t* ktb = a.kt + ((size_t)b * P * Hkv + g) * TA_D;
@@ -75,7 +80,7 @@ __global__ __launch_bounds__(TA_NT, 2) void k_tree_attention(AttnArgs a) {
     auto blk_lim = [&](int x) { return x < npb ? L : n; };
 
     u32x4 pk[4], pv[4];
-    uint32_t vval = 0u;                                 // bit u: V key 4*sr + u valid
+    uint32_t vval = 0u;                                 // bit u: V key 4*vsr + u valid
     // every load reads a valid row (invalid keys read the block source's
     // first row) and is issued straight-line, so the next block's loads stay
     // in flight across the current block's compute
@@ -93,10 +98,10 @@ __global__ __launch_bounds__(TA_NT, 2) void k_tree_attention(AttnArgs a) {
         vval = 0u;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            int jv = base + 4 * sr + u;
+            int jv = base + 4 * vsr + u;
             vval |= jv < lim ? (1u << u) : 0u;
             jv = jv < lim ? jv : 0;
-            pv[u] = *(const u32x4*)(vs + (size_t)jv * HD + 8 * sc);
+            pv[u] = *(const u32x4*)(vs + (size_t)jv * HD + 8 * vsc);
         }
     };
     auto stage = [&](int x, int buf) {
@@ -111,10 +116,10 @@ __global__ __launch_bounds__(TA_NT, 2) void k_tree_attention(AttnArgs a) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) pv[u] = (vval >> u) & 1u ? pv[u] : z;
         }
-        // word w of key u holds dims 8*sc + 2w (low half) and + 2w + 1 (high
-        // half); keys 4*sr .. +3 are half sr % 2 of group sr / 2, and dim
-        // 8*sc + e sits at 8*(8*sc + sc/2 + e) in the group
-        const int vofs = (sr >> 1) * TA_VG + 4 * (sr & 1) + 8 * (8 * sc + (sc >> 1));
+        // word w of key u holds dims 8*vsc + 2w (low half) and + 2w + 1 (high
+        // half); keys 4*vsr .. +3 are half vsr % 2 of group vsr / 2, and dim
+        // 8*vsc + e sits at 8*(8*vsc + vsc/2 + e) in the group
+        const int vofs = (vsr >> 1) * TA_VG + 4 * (vsr & 1) + 8 * (8 * vsc + (vsc >> 1));
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             const uint32_t e01 = __builtin_amdgcn_perm(pv[1][w], pv[0][w], 0x05040100u);
@@ -321,8 +326,10 @@ __global__ __launch_bounds__(TA_CNT) void k_attn_combine(AttnArgs a) {
     if (i < n) {
         const size_t split_rows = (size_t)rows;
         float M = TA_MFLOOR;
+#pragma unroll 4
         for (int s = 0; s < a.splits; ++s) M = fmaxf(M, a.pml[2 * (s * split_rows + r)]);
         float den = 0.f, n0 = 0.f, n1 = 0.f;
+#pragma unroll 4
         for (int s = 0; s < a.splits; ++s) {
             const float2 ml = *(const float2*)(a.pml + 2 * (s * split_rows + r));
             const float w = __builtin_amdgcn_exp2f((ml.x - M) * a.sl2);
