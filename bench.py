@@ -402,6 +402,221 @@ def cast_calibration_detail(w, run, ring, to_dev, dev, slots: int = 2, replays: 
     }
 
 
+def graft_main(args, w) -> None:
+    """The Graft workload: prune-then-graft rounds with the successor matrix.
+
+    Checkpoint thresholds come from warm-up rounds drafted on the device
+    without the gate (at each checkpoint depth, the 25th percentile of
+    c_d = exp(max S at that depth) over the rows still active: the Graft
+    review's warm-up calibration).  Every timed round starts from the initial
+    successor matrix (reset outside the timed span, so that a replayed graph
+    repeats its round and its target rows match its tree); rounds are
+    graph-replayed and timed one by one with events, and `value` is
+    1 / mean round time."""
+    import torch
+    from gen import configs, synth
+    from dynamic_draft_tree_row_amd import _lib, api
+    from dynamic_draft_tree_row_amd.round_driver import RoundRunner, RoundShape
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    lib = _lib.load()
+    hip = Hip()
+    gs = w.graft
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def to_dev(raw):
+        if w.dtype == "f32":
+            return torch.from_numpy(np.ascontiguousarray(raw)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    # ---- checkpoint thresholds from device warm-up rounds -------------------
+    dck = max(gs.ck_depth)
+    wck = configs.Workload(**{**w.__dict__, "D": dck, "graft": None})
+    plain = RoundRunner(RoundShape(B=w.B, V=w.V, dtype=tdt, D=dck, K_e=w.K_e, K_n=w.K_n, m=w.m_max), dev)
+    cds = []
+    for r in range(args.tau_rounds):
+        plain.draft(to_dev(synth.draft_arena(wck, SEED, 10_000 + r)),
+                    torch.from_numpy(synth.root_tokens(w, SEED, 10_000 + r)).to(dev))
+        torch.cuda.synchronize()
+        S, dep, nn = plain.tree.S.cpu().numpy(), plain.tree.depth.cpu().numpy(), plain.tree.n_nodes.cpu().numpy()
+        for b in range(w.B):
+            n = int(nn[b])
+            cds.append([float(np.exp(S[b, :n][dep[b, :n] == d].max())) for d in gs.ck_depth])
+    del plain
+    cds = np.array(cds)
+    alive = np.ones(len(cds), bool)
+    tau = []
+    for k in range(len(gs.ck_depth)):
+        tk = float(np.percentile(cds[alive, k], 25.0))
+        tau.append(tk)
+        alive &= cds[:, k] > tk
+    gate = api.GraftGate(ck_depth=list(gs.ck_depth), tau=tau, k_draft=list(gs.k_draft), K_max=gs.K_max)
+    log(f"checkpoint thresholds from {args.tau_rounds} warm-up rounds: {[round(x, 4) for x in tau]}")
+
+    shape = RoundShape(B=w.B, V=w.V, dtype=tdt, D=w.D, K_e=w.K_e, K_n=w.K_n, m=w.m_max, prefix=w.prefix,
+                       graft=True, tpl_depth=gs.tpl_depth, tpl_width=gs.tpl_width, k_succ=gs.k_succ)
+    run = RoundRunner(shape, dev)
+    M0_np = synth.succ_matrix0(w, SEED)
+    M0 = torch.from_numpy(M0_np).to(dev)
+    M = M0.clone()
+
+    # ---- ring of rounds, inputs resident in HBM ------------------------------
+    ring = []
+    t0 = time.perf_counter()
+    for r in range(args.ring):
+        d_np = synth.draft_arena(w, SEED, r)
+        slot = dict(draft=to_dev(d_np), roots=torch.from_numpy(synth.root_tokens(w, SEED, r)).to(dev),
+                    T=torch.from_numpy(synth.temperatures(w, SEED, r)).to(dev),
+                    U=torch.from_numpy(synth.uniforms(w, SEED, r)).to(dev))
+        M.copy_(M0)
+        run.draft(slot["draft"], slot["roots"], gate=gate, M=M)
+        torch.cuda.synchronize()
+        fk, fd, fs, ft = flat_layout(run, w.B)
+        t_np = synth.target_arena(w, SEED, r, d_np, fk, fd, fs, ft, None, M0_np)
+        slot["target"] = to_dev(t_np)
+        if r == 0:
+            slot.update(draft_np=d_np, target_np=t_np, roots_np=synth.root_tokens(w, SEED, r),
+                        T_np=synth.temperatures(w, SEED, r), U_np=synth.uniforms(w, SEED, r))
+        ring.append(slot)
+    log(f"ring of {args.ring} Graft rounds generated in {time.perf_counter() - t0:.1f} s")
+
+    def eager(slot):
+        run.draft(slot["draft"], slot["roots"], gate=gate, M=M)
+        run.verify(slot["target"], slot["draft"], slot["T"], slot["U"], M=M)
+
+    ref, stats = [], []
+    for slot in ring:
+        M.copy_(M0)
+        eager(slot)
+        torch.cuda.synchronize()
+        snap = snapshot(run)
+        snap["M"] = M.clone()
+        ref.append(snap)
+        m = run.m_out.cpu().numpy()
+        tree_esl, tree_dep = run.tree.eslot.cpu().numpy(), run.tree.depth.cpu().numpy()
+        n_nodes = run.tree.n_nodes.cpu().numpy()
+        rows_per_layer = [int(sum(((tree_esl[b, :int(n_nodes[b])] >= 0) &
+                                   (tree_dep[b, :int(n_nodes[b])] == d - 1)).sum() for b in range(w.B)))
+                          for d in range(1, w.D + 1)]
+        stats.append(dict(rows_per_layer=rows_per_layer, verify_rows=int((m + 1).sum()),
+                          k_draft=run.tree.k_draft.cpu().numpy().tolist(),
+                          accept=run.accept_len.cpu().numpy().tolist()))
+    graphs = []
+    for slot in ring:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            eager(slot)
+        graphs.append(g)
+    for rep in range(3):
+        for i, g in enumerate(graphs):
+            M.copy_(M0)
+            g.replay()
+            torch.cuda.synchronize()
+            snap = snapshot(run)
+            snap["M"] = M.clone()
+            if not same(snap, ref[i]):
+                raise RuntimeError(f"graph replay {rep} of slot {i} differs from the eager round")
+            M.copy_(M0)
+            eager(ring[(i + 1) % len(ring)])
+            torch.cuda.synchronize()
+    log("graph replays match the eager rounds (successor matrix included)")
+
+    K, W, R = args.steps, args.warmup, len(graphs)
+    for i in range(W):
+        M.copy_(M0)
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        M.copy_(M0)
+        ev[2 * i].record()
+        graphs[i % R].replay()
+        ev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    us = np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(K)])
+    round_s = float(us.mean()) * 1e-6
+    log(f"{K} Graft rounds: {us.mean():.1f} us/round (events per round; {wall_s * 1e6 / K:.1f} us wall "
+        f"with the successor-matrix resets)")
+
+    # ---- dominant kernel: the row reduction, kernel-stamped events -----------
+    per_round = w.D + 1
+    n_pairs = per_round * R * 4
+    evs = hip.events(2 * n_pairs)
+    arr = (C.c_void_p * len(evs))(*[e.value for e in evs])
+    lib.ddt_set_reduce_events(arr, n_pairs)
+    for slot in ring:
+        M.copy_(M0)
+        eager(slot)
+    used = lib.ddt_set_reduce_events(None, 0)
+    assert used == per_round * R, f"expected {per_round * R} timed launches, got {used}"
+    torch.cuda.synchronize()
+    ebytes = w.V * (2 if w.dtype == "bf16" else 4)
+    durs, nbytes = [], []
+    for k_s, st in enumerate(stats):
+        rows = st["rows_per_layer"] + [st["verify_rows"]]
+        for k in range(per_round):
+            i = k_s * per_round + k
+            durs.append(hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) * 1e-3)
+            nbytes.append(rows[k] * ebytes)
+    durs, nbytes = np.array(durs), np.array(nbytes, dtype=np.float64)
+    achieved = nbytes.sum() / durs.sum() / 1e9
+    log(f"row reduction: {len(durs)} launches, mean {durs.mean() * 1e6:.2f} us, {achieved:.0f} GB/s")
+    expand_bytes = np.mean([sum(st["rows_per_layer"]) for st in stats]) * ebytes
+    verify_bytes = np.mean([st["verify_rows"] for st in stats]) * ebytes
+    out = {
+        "metric": "draft-tree rounds/sec and logit HBM GB/s (% of roofline), Graft workload",
+        "value": round(1.0 / round_s, 2), "unit": "rounds/s",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(round_s * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "V": w.V, "depth": w.D, "expand_topk": w.K_e,
+                   "node_topk": w.K_n, "K_max": gs.K_max, "checkpoints": list(gs.ck_depth),
+                   "k_draft": list(gs.k_draft), "tau": [round(x, 6) for x in tau],
+                   "template": [gs.tpl_depth, gs.tpl_width], "k_succ": gs.k_succ,
+                   "ring_rounds": R, "hip_graph": True,
+                   "timing": "events around each replay; the successor matrix is reset before each"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "k_row_partial<bf16> (vocab row reduction)",
+                     "algorithmic_bytes_per_launch": round(float(nbytes.mean()), 1),
+                     "avg_launch_us": round(float(durs.mean() * 1e6), 3), "launches": int(len(durs))},
+        "logit_gbs": round((expand_bytes + verify_bytes) / round_s / 1e9, 1),
+        "detail": {"round_us_p10_p50_p90": [round(float(np.percentile(us, q)), 2) for q in (10, 50, 90)],
+                   "k_draft": stats[0]["k_draft"], "accept_len": stats[0]["accept"],
+                   "mean_tau": round(float(np.mean([np.mean(st["accept"]) + 1 for st in stats])), 3)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = graft_cpu_baseline(w, ring[0], gate, M0_np, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def graft_cpu_baseline(w, slot, gate, M0_np, seconds):
+    """The oracle on one core, on ring slot 0's inputs, each round from the
+    initial successor matrix."""
+    from oracle import ddt_oracle as O
+    gs = w.graft
+    d_np = slot["draft_np"]
+    graft = dict(ck_depth=tuple(gs.ck_depth), tau=list(gate.tau), k_draft=tuple(gs.k_draft), K_max=gs.K_max)
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        O.run_round(B=w.B, V=w.V, dtype=w.dtype, D=w.D, K_e=w.K_e, K_n=w.K_n, m_max=w.m_max,
+                    root_tok=slot["roots_np"], draft_raw=d_np, target_raw_fn=lambda dr, flats: slot["target_np"],
+                    temperature=slot["T_np"], U=slot["U_np"], prefix=w.prefix, graft=graft,
+                    M=M0_np.copy(), k_succ=gs.k_succ, tpl=(gs.tpl_depth, gs.tpl_width))
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": n / el, "unit": "rounds/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} rounds of the Graft workload (ring slot 0, {el:.1f} s, single thread, float64 numpy; "
+                      f"input generation excluded)"}
+
+
 def cpu_baseline(w, slot, cast_np, seconds):
     """The oracle as it stands, on one core, on ring slot 0's inputs."""
     from oracle import ddt_oracle as O
@@ -443,6 +658,8 @@ def main():
                     help="only a few tree-attention launches and the calibration copy, for rocprofv3 --pmc")
     ap.add_argument("--no-attention", action="store_true",
                     help="skip the tree-attention measurement (the verify forward's MFMA kernel)")
+    ap.add_argument("--tau-rounds", type=int, default=4,
+                    help="Graft workload: warm-up rounds for the checkpoint thresholds")
     ap.add_argument("--no-calibrate", action="store_true",
                     help="skip measuring the CAST cost tables on this GPU")
     ap.add_argument("--break-even", action="store_true",
@@ -454,8 +671,8 @@ def main():
                     help="no GPU: turn the two --pmc passes' counter CSVs into "
                          "profiles/k_row_partial_traffic_<workload>.json")
     ap.add_argument("--workload", default=None,
-                    help="profile another workload instead (e.g. eagle2_mixed_b64_v128256_bf16; "
-                         "'fixed' = the CAST shape with fixed EAGLE-2 widths)")
+                    help="profile another workload instead (e.g. eagle2_mixed_b64_v128256_bf16, "
+                         "graft_b16_v152064_bf16; 'fixed' = the CAST shape with fixed EAGLE-2 widths)")
     args = ap.parse_args()
     if args.ingest_pmc:
         ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.workload or "cast_b8_v128256_bf16", args.ring)
@@ -489,7 +706,7 @@ def main():
     elif args.workload:
         w = configs.WORKLOADS[args.workload]
         if w.graft is not None:
-            raise SystemExit("the Graft workload is exercised by the tests, not by this bench")
+            return graft_main(args, w)
     if args.break_even:
         w = configs.Workload(**{**w.__dict__, "cast": configs.CastSpec(**configs.BREAK_EVEN)})
     dev = torch.device("cuda", 0)
