@@ -388,10 +388,12 @@ int ddt_tree_verify(const ddt_tree* t, const ddt_flat* f, const ddt_logits* targ
     a.next_token = next_token;
     // T > 0 requests split their vocabulary passes over G workgroups; the grid
     // stays within what the device holds at once, so the workgroups of a
-    // request are resident together
+    // request are resident together.  At most 12: every residual pass ends in
+    // a barrier of the request's workgroups, and beyond about 12 the wider
+    // barrier costs more than the shorter slices save
     const int ntiles = (target->V + VF_TILE - 1) / VF_TILE;
     int G = resident_verify_blocks() / t->B;
-    G = G < 1 ? 1 : (G > 32 ? 32 : G);
+    G = G < 1 ? 1 : (G > 12 ? 12 : G);
     if (G > ntiles) G = ntiles;
     a.G = G;
     hipLaunchKernelGGL(k_verify, dim3((unsigned)(t->B * G)), dim3(VF_NT), 0, s, a);
