@@ -306,49 +306,53 @@ __global__ __launch_bounds__(TA_NT, 2) void k_tree_attention(AttnArgs a) {
     }
 }
 
-// Combination of the splits: one wave per output row (request, flat
-// position, query head), two dims per lane.  With m_s and l_s the running
+// Combination of the splits: 32 lanes per output row (request, flat
+// position, query head), four dims per lane.  With m_s and l_s the running
 // maximum and weight total of split s and o_s its unnormalised output, all
 // against 2^(sl2 * (score - m_s)), the row is
 //   sum_s 2^(sl2 (m_s - M)) o_s / sum_s 2^(sl2 (m_s - M)) l_s,  M = max_s m_s.
 // Positions past the request's m are written as 0.
 #define TA_CNT 256
+#define TA_CROWS (TA_CNT / 32)          // rows per workgroup
 __global__ __launch_bounds__(TA_CNT) void k_attn_combine(AttnArgs a) {
-    const int lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 31;
     const int B = a.groups / a.Hkv, P = a.P, Hq = a.Hq;
     const long long rows = (long long)B * P * Hq;
-    const long long r = (long long)blockIdx.x * (TA_CNT / 64) + (threadIdx.x >> 6);
+    const long long r = (long long)blockIdx.x * TA_CROWS + (threadIdx.x >> 5);
     if (r >= rows) return;
     const int b = (int)(r / ((long long)P * Hq));
     const int i = (int)((r / Hq) % P);
     const int n = min(max(a.m[b], 0), P - 1) + 1;
-    float2 res = make_float2(0.f, 0.f);
+    float4 res = make_float4(0.f, 0.f, 0.f, 0.f);
     if (i < n) {
         const size_t split_rows = (size_t)rows;
         float M = TA_MFLOOR;
 #pragma unroll 4
         for (int s = 0; s < a.splits; ++s) M = fmaxf(M, a.pml[2 * (s * split_rows + r)]);
-        float den = 0.f, n0 = 0.f, n1 = 0.f;
+        float den = 0.f;
+        float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll 4
         for (int s = 0; s < a.splits; ++s) {
             const float2 ml = *(const float2*)(a.pml + 2 * (s * split_rows + r));
             const float w = __builtin_amdgcn_exp2f((ml.x - M) * a.sl2);
-            const float2 os = *(const float2*)(a.po + (s * split_rows + r) * TA_D + 2 * lane);
+            const float4 os = *(const float4*)(a.po + (s * split_rows + r) * TA_D + 4 * lane);
             den = fmaf(w, ml.y, den);
-            n0 = fmaf(w, os.x, n0);
-            n1 = fmaf(w, os.y, n1);
+            num.x = fmaf(w, os.x, num.x);
+            num.y = fmaf(w, os.y, num.y);
+            num.z = fmaf(w, os.z, num.z);
+            num.w = fmaf(w, os.w, num.w);
         }
         const float inv = den > 0.f ? 1.f / den : 0.f;
-        res = make_float2(n0 * inv, n1 * inv);
+        res = make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
     }
-    *(float2*)(a.out + (size_t)r * TA_D + 2 * lane) = res;
+    *(float4*)(a.out + (size_t)r * TA_D + 4 * lane) = res;
 }
 
 void ddt_attention_launch(const AttnArgs& a, unsigned grid, hipStream_t stream) {
     hipLaunchKernelGGL(k_tree_attention, dim3(grid), dim3(TA_NT), 0, stream, a);
     if (a.splits > 1) {
         const long long rows = (long long)(a.groups / a.Hkv) * a.P * a.Hq;
-        const unsigned cg = (unsigned)((rows + TA_CNT / 64 - 1) / (TA_CNT / 64));
+        const unsigned cg = (unsigned)((rows + TA_CROWS - 1) / TA_CROWS);
         hipLaunchKernelGGL(k_attn_combine, dim3(cg), dim3(TA_CNT), 0, stream, a);
     }
 }
