@@ -328,7 +328,7 @@ __global__ __launch_bounds__(AT_NT) void k_attach(AttachArgs a) {
     float* frS = t.front_S + (size_t)b * Rm;
     uint64_t* frK = t.front_key + (size_t)b * Rm;
 
-    // round 1: every global input of the layer is requested before anything
+    // first load trip: every global input of the layer is requested before anything
     // waits on one: the request's counters (scalar), the frontier records, the
     // CAST inputs and, for wave j, the partials of slot j
     const int nf0 = a.layer == 1 ? 1 : t.n_front[b];
@@ -1335,7 +1335,7 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
     const int Lr = min(max(f.n_leaves[b], 0), f.L);
     const bool ret_lds = Lr * (Dp + 1) <= VF_RET;
     const bool greedy = !(T > 0.f);
-    // round 2: the candidate paths (greedy), the flat parents and tokens and
+    // second load trip: the candidate paths (greedy), the flat parents and tokens and
     // the first batch of argmax merges are requested before anything waits
     // (straight-line loads from clamped addresses: a load under a branch ends
     // in a register copy that waits for it)
