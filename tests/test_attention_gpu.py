@@ -161,9 +161,10 @@ def test_tree_attention_deterministic():
     flat.m.fill_(P - 1)
     t = [_to_dev(_bf16(rng.standard_normal(s))) for s in
          [(B, P, Hq, D), (B, P, Hkv, D), (B, P, Hkv, D), (B, Lp, Hkv, D), (B, Lp, Hkv, D)]]
-    outs = []
-    for _ in range(2):
-        o = torch.empty((B, P, Hq, D), dtype=torch.float32, device="cuda")
-        api.tree_attention(flat, t[0], t[1], t[2], o, k_pre=t[3], v_pre=t[4])
-        outs.append(o.cpu())
-    assert torch.equal(outs[0], outs[1])
+    for splits in (None, 3):
+        outs = []
+        for _ in range(2):
+            o = torch.empty((B, P, Hq, D), dtype=torch.float32, device="cuda")
+            api.tree_attention(flat, t[0], t[1], t[2], o, k_pre=t[3], v_pre=t[4], splits=splits)
+            outs.append(o.cpu())
+        assert torch.equal(outs[0], outs[1]), f"splits={splits}"
