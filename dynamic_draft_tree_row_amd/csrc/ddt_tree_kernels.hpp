@@ -1086,35 +1086,49 @@ struct RowSync {
     int t_lo, t_hi;      // the same slice in tiles
 };
 
-// combine two workgroup sums over the request's workgroups (every thread
-// returns the totals); s_bc: 2 doubles of LDS, s_err: set on a timed-out wait
-__device__ void row_combine(RowSync& rs, double& x0, double& x1, double* s_bc, int* s_err) {
-    if (rs.G == 1) return;
+// The end of a pass: thread 0 adds the waves' sums (s_red: nw values, then
+// nw more when two sums are taken), combines the two totals over the
+// request's workgroups and broadcasts them through s_bc; every thread
+// returns them.  Two barriers: one before thread 0 reads s_red (all waves
+// have written it), one before the others read s_bc.  A later pass writes
+// s_red only after the second barrier (thread 0 has read it) and s_bc only
+// after its own first barrier (every thread has read it), so no further
+// barrier is needed.  s_err is set on a timed-out wait.
+__device__ void pass_end(RowSync& rs, const double* s_red, int nw, bool two, double& x0, double& x1,
+                         double* s_bc, int* s_err) {
+    __syncthreads();
     if (threadIdx.x == 0) {
-        double* slot = rs.buf + (size_t)(rs.k & 1) * rs.G * 2;
-        slot[2 * rs.g] = x0;
-        slot[2 * rs.g + 1] = x1;
-        __threadfence();
-        atomicAdd(rs.cnt, 1u);
-        const uint32_t target = (uint32_t)(rs.k + 1) * (uint32_t)rs.G;
-        unsigned spins = 0;
-        while (!*s_err &&
-               __hip_atomic_load(rs.cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            if (++spins > WALK_SPIN_LIMIT) { *s_err = 1; break; }
-            __builtin_amdgcn_s_sleep(2);
-        }
-        __threadfence();
         double a0 = 0.0, a1 = 0.0;
-        for (int q = 0; q < rs.G; ++q) {
-            a0 += __hip_atomic_load(slot + 2 * q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            a1 += __hip_atomic_load(slot + 2 * q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int q = 0; q < nw; ++q) a0 += s_red[q];
+        if (two)
+            for (int q = 0; q < nw; ++q) a1 += s_red[nw + q];
+        if (rs.G > 1) {
+            // this workgroup's totals go to the pass's slot; release, count in,
+            // and wait (bounded) for all G before reading every slot
+            double* slot = rs.buf + (size_t)(rs.k & 1) * rs.G * 2;
+            slot[2 * rs.g] = a0;
+            slot[2 * rs.g + 1] = a1;
+            __threadfence();
+            atomicAdd(rs.cnt, 1u);
+            const uint32_t target = (uint32_t)(rs.k + 1) * (uint32_t)rs.G;
+            unsigned spins = 0;
+            while (!*s_err &&
+                   __hip_atomic_load(rs.cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+                if (++spins > WALK_SPIN_LIMIT) { *s_err = 1; break; }
+                __builtin_amdgcn_s_sleep(2);
+            }
+            __threadfence();
+            a0 = 0.0; a1 = 0.0;
+            for (int q = 0; q < rs.G; ++q) {
+                a0 += __hip_atomic_load(slot + 2 * q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                a1 += __hip_atomic_load(slot + 2 * q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
         s_bc[0] = a0; s_bc[1] = a1;
     }
     __syncthreads();
     x0 = s_bc[0]; x1 = s_bc[1];
-    __syncthreads();
-    rs.k++;
+    if (rs.G > 1) rs.k++;
 }
 
 // block-wide sum over the slice of fn(t_v, d_v) in fp64, combined over the
@@ -1133,13 +1147,9 @@ __device__ double walk_pass(const WalkRows& w, RowSync& rs, double* s_red, doubl
         for (int e = 0; e < 4; ++e) acc += fn(tx[e], UseD ? dx[e] : 0.f);
     }
     const double d = wave_sum_f64(acc);
-    __syncthreads();
     if (lane == 0) s_red[wid] = d;
-    __syncthreads();
-    double tot = 0.0, zero = 0.0;
-    for (int q = 0; q < VF_NT / 64; ++q) tot += s_red[q];
-    __syncthreads();
-    row_combine(rs, tot, zero, s_bc, s_err);
+    double tot, zero;
+    pass_end(rs, s_red, VF_NT / 64, false, tot, zero, s_bc, s_err);
     return tot;
 }
 
@@ -1157,13 +1167,8 @@ __device__ void walk_norms(const WalkRows& w, RowSync& rs, double* s_red, double
     }
     at = wave_sum_f64(at);
     ad = wave_sum_f64(ad);
-    __syncthreads();
     if (lane == 0) { s_red[wid] = at; s_red[VF_NT / 64 + wid] = ad; }
-    __syncthreads();
-    Zt = 0.0; Zd = 0.0;
-    for (int q = 0; q < VF_NT / 64; ++q) { Zt += s_red[q]; Zd += s_red[VF_NT / 64 + q]; }
-    __syncthreads();
-    row_combine(rs, Zt, Zd, s_bc, s_err);
+    pass_end(rs, s_red, VF_NT / 64, true, Zt, Zd, s_bc, s_err);
 }
 
 // Per-tile sums (256 ids, one wave per tile) of the weights max(0, p - aa q)
@@ -1189,13 +1194,9 @@ __device__ double walk_tiles(const WalkRows& w, RowSync& rs, double* s_red, doub
         }
         mine += ws;
     }
-    __syncthreads();
     if (lane == 0) s_red[wid] = mine;
-    __syncthreads();
-    double tot = 0.0, zero = 0.0;
-    for (int q = 0; q < VF_NT / 64; ++q) tot += s_red[q];
-    __syncthreads();
-    row_combine(rs, tot, zero, s_bc, s_err);
+    double tot, zero;
+    pass_end(rs, s_red, VF_NT / 64, false, tot, zero, s_bc, s_err);
     return tot;
 }
 
