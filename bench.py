@@ -678,8 +678,8 @@ def main():
         ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.workload or "cast_b8_v128256_bf16", args.ring)
         return
     if args.gpus != 1:
-        log("bench.py measures one GPU only: this build has no multi-GPU path "
-            "(batch rows would shard across GPUs; see the design notes).")
+        log("bench.py measures one GPU only: there is no multi-GPU path (batch rows "
+            "would shard across GPUs, one process each; not built).")
         sys.exit(2)
 
     import torch
