@@ -22,7 +22,7 @@ describe, written in float64, following the pages' steps in their order:
     online top-k refresh (execution-flow paragraph, steps 1-3).
 
 Where the pages are silent or garbled this module takes one reading and says
-so at the point of use; every such reading is also listed in the design notes.
+so at the point of use.
 
 Every function that a parity test relies on is pinned by the oracle self-tests
 (closed forms, invariants, brute force, special-case reductions).  None is left
