@@ -11,7 +11,7 @@ than twice the 256 MB last-level cache).  Each ring slot's round is captured
 once as a HIP graph (the kernels take every size from device memory, so no host
 synchronisation is needed between layers) and the timed region replays them.
 
-Prints one JSON line.  --gpus above 1 is refused: this build measures one GPU.
+Prints one JSON line.  --gpus above 1 is refused: the bench measures one GPU.
 """
 from __future__ import annotations
 
@@ -22,6 +22,7 @@ import json
 import os
 import sys
 import time
+from typing import Optional
 
 import numpy as np
 
@@ -330,7 +331,8 @@ def kv_commit_detail(api, dev, seed: int = 11, commits: int = 20) -> dict:
     return res
 
 
-def cast_calibration_detail(w, run, ring, to_dev, dev, slots: int = 2, replays: int = 60) -> dict:
+def cast_calibration_detail(w, run, ring, to_dev, dev, slots: int = 2, replays: int = 60,
+                            save: Optional[str] = None) -> dict:
     """CAST cost tables measured on this GPU at the workload's batch and grid
     (proxy forwards of an 8B-class target and a one-layer draft head), then
     rounds of the same ring drafted and verified on those tables, replayed
@@ -344,6 +346,8 @@ def cast_calibration_detail(w, run, ring, to_dev, dev, slots: int = 2, replays: 
     S_T, S_D = CC.measure_tables(w.B, cs.L, cs.M, cs.N, reps=3)
     cal_s = time.perf_counter() - t0
     log(f"cost tables measured in {cal_s:.1f} s: S_T[0][1] {S_T[0, 1]:.0f} us, S_D[0][1] {S_D[0, 1]:.0f} us")
+    if save:
+        CC.save_tables(save, S_T, S_D, B=w.B, L=cs.L, device=torch.cuda.get_device_name(dev))
     f = lambda a: torch.tensor(np.asarray(a, np.float32), device=dev)
     cast = api.CastParams(S_T=f(S_T), S_D=f(S_D), L=cs.L, C1=f([cs.C1] * w.D), C2=cs.C2,
                           C3=f([cs.C3] * w.B), R=cs.R, ctx_verify=w.prefix)
@@ -660,6 +664,8 @@ def main():
                     help="skip the tree-attention measurement (the verify forward's MFMA kernel)")
     ap.add_argument("--tau-rounds", type=int, default=4,
                     help="Graft workload: warm-up rounds for the checkpoint thresholds")
+    ap.add_argument("--save-tables", default=None, metavar="PATH",
+                    help="write the measured CAST cost tables to PATH (.npz, cast_calibrate.load_tables)")
     ap.add_argument("--no-calibrate", action="store_true",
                     help="skip measuring the CAST cost tables on this GPU")
     ap.add_argument("--break-even", action="store_true",
@@ -957,7 +963,8 @@ def main():
                                                                    split_options=(0, None))
         out["detail"]["kv_commit"] = kv_commit_detail(api, dev)
     if w.cast is not None and not args.no_calibrate:
-        out["detail"]["cast_calibration"] = cast_calibration_detail(w, run, ring, to_dev, dev)
+        out["detail"]["cast_calibration"] = cast_calibration_detail(w, run, ring, to_dev, dev,
+                                                                    save=args.save_tables)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, ring[0], cast_np, args.cpu_seconds)
     else:

@@ -30,7 +30,7 @@ ratios of table entries, so the unit (microseconds here) cancels.
 """
 from __future__ import annotations
 
-from dataclasses import dataclass
+from dataclasses import astuple, dataclass
 from typing import Callable, Dict, List, Optional, Tuple
 
 import numpy as np
@@ -220,3 +220,25 @@ def measure_tables(B: int, L: int, M: int, N: int, target: ProxyModel = TARGET_8
         torch.cuda.empty_cache()
     del keeper
     return tabs[0], tabs[1]
+
+
+def save_tables(path: str, S_T: np.ndarray, S_D: np.ndarray, B: int, L: int,
+                target: ProxyModel = TARGET_8B, draft: ProxyModel = DRAFT_HEAD,
+                device: str = "") -> None:
+    """Store measured tables with what they were measured for (batch B, grid
+    step L, the proxy shapes, the device name): the tables are computed
+    offline once per GPU and batch size and read back at serving time."""
+    S_T, S_D = np.asarray(S_T, np.float32), np.asarray(S_D, np.float32)
+    if S_T.shape != S_D.shape or S_T.ndim != 2 or S_T.shape[1] < 2:
+        raise ValueError("S_T and S_D must be [M][N+1] tables of the same shape")
+    np.savez(path, S_T=S_T, S_D=S_D, B=np.int64(B), L=np.int64(L),
+             target=np.array(astuple(target), np.int64), draft=np.array(astuple(draft), np.int64),
+             device=np.array(device))
+
+
+def load_tables(path: str) -> dict:
+    """Tables stored by save_tables: dict(S_T, S_D, B, L, target, draft, device)."""
+    with np.load(path, allow_pickle=False) as z:
+        return {"S_T": z["S_T"], "S_D": z["S_D"], "B": int(z["B"]), "L": int(z["L"]),
+                "target": ProxyModel(*[int(x) for x in z["target"]]),
+                "draft": ProxyModel(*[int(x) for x in z["draft"]]), "device": str(z["device"])}

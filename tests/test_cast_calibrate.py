@@ -32,6 +32,20 @@ def test_proxy_shapes_match_the_generator():
     assert CC.TARGET_8B.head_weight_bytes() == 2 * 4096 * 128256
 
 
+def test_tables_round_trip(tmp_path):
+    S_T = CC.assemble(np.array([[10.0, 11.0], [12.0, 12.5]]), np.array([5.0, 6.0]), 32)
+    S_D = CC.assemble(np.array([[1.0, 1.5], [1.2, 1.6]]), np.array([5.0, 6.0]), 1)
+    p = str(tmp_path / "tables.npz")
+    CC.save_tables(p, S_T, S_D, B=8, L=256, device="test device")
+    got = CC.load_tables(p)
+    np.testing.assert_array_equal(got["S_T"], S_T)
+    np.testing.assert_array_equal(got["S_D"], S_D)
+    assert (got["B"], got["L"], got["device"]) == (8, 256, "test device")
+    assert got["target"] == CC.TARGET_8B and got["draft"] == CC.DRAFT_HEAD
+    with pytest.raises(ValueError):
+        CC.save_tables(p, S_T, S_D[:, :2], B=8, L=256)
+
+
 def test_measure_rejects_bad_grids():
     with pytest.raises(ValueError):
         CC.measure_tables(B=1, L=16, M=1, N=300)
