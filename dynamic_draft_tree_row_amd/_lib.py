@@ -9,6 +9,7 @@ LIB_PATH = os.path.join(HERE, "libddt.so")
 
 DDT_OK, DDT_EINVAL, DDT_EDTYPE, DDT_ECAPACITY, DDT_EWORKSPACE, DDT_ELAUNCH = range(6)
 DDT_F32, DDT_BF16 = 0, 1
+DDT_PROPOSAL_DRAFT, DDT_PROPOSAL_POINT = 0, 1
 MAX_K, MAX_DEPTH, MAX_FRONT, MAX_NODES, MAX_VERIFY, MAX_CHUNKS = 32, 11, 32, 4096, 255, 64
 
 P = C.c_void_p
@@ -77,7 +78,8 @@ SIGNATURES = {
                                   C.c_int, C.c_int, P, P, P]),
     "ddt_tree_build_mask": (C.c_int, [C.POINTER(Tree), P, P, C.c_int, C.POINTER(Flat), P, P]),
     "ddt_tree_verify": (C.c_int, [C.POINTER(Tree), C.POINTER(Flat), C.POINTER(Logits),
-                                  C.POINTER(Logits), i64, P, P, C.c_int, P, P, P, P, P, P, sz, P]),
+                                  C.POINTER(Logits), i64, P, P, C.c_int, C.c_int, P, P, P, P, P,
+                                  P, sz, P]),
     "ddt_succ_update": (C.c_int, [P, i64, C.c_int, C.c_int, C.POINTER(Flat), P, C.c_int,
                                   C.POINTER(Logits), P, sz, P]),
     "ddt_tree_attention": (C.c_int, [C.POINTER(Flat), C.POINTER(Attn), P, P]),
@@ -91,6 +93,7 @@ SIGNATURES = {
     "ddt_kv_release": (C.c_int, [C.POINTER(KVCache), P, C.c_int, P]),
     "ddt_row_topk": (C.c_int, [C.POINTER(Logits), C.c_int, C.c_int, C.c_int, P, P, P, P, P, sz, P]),
     "ddt_set_reduce_events": (C.c_int, [C.POINTER(P), C.c_int]),
+    "ddt_set_walk_spin_limit": (C.c_uint, [C.c_uint]),
 }
 
 _lib = None

@@ -91,6 +91,7 @@ class DeviceTree(_Carved):
         self.k_draft = v(c.k_draft, torch.int32, (B,))
         self.cont = v(c.cont, torch.int32, (1,))
         self.widths = v(c.widths, torch.int32, (D_max,))
+        self.walk_sync = v(c.walk_sync, torch.int32, (B, 2))
 
 
 class DeviceFlat(_Carved):
@@ -196,13 +197,18 @@ def tree_build_mask(tree: DeviceTree, sel: torch.Tensor, m: torch.Tensor, prefix
         _stream(stream, sel.device)))
 
 
+PROPOSALS = {"draft": L.DDT_PROPOSAL_DRAFT, "point": L.DDT_PROPOSAL_POINT}
+
+
 def tree_verify(tree: DeviceTree, flat: DeviceFlat, target: torch.Tensor,
                 draft_arena: Optional[torch.Tensor], temperature: torch.Tensor,
                 uniforms: torch.Tensor, accept_len: torch.Tensor, accept_path: torch.Tensor,
                 next_token: torch.Tensor, ws: torch.Tensor, k_top: int = 0,
                 row_topk: Optional[torch.Tensor] = None, row_argmax: Optional[torch.Tensor] = None,
-                stream=None) -> None:
-    """target: [B][P][V]; draft_arena: [D][B][R][V] (layer-major) or None."""
+                proposal: str = "point", stream=None) -> None:
+    """target: [B][P][V]; draft_arena: [D][B][R][V] (layer-major) or None;
+    proposal: "point" (children verified as point-mass proposals; the draft
+    arena is not read) or "draft" (q = the draft row's softmax)."""
     td = logits_desc(target)
     if draft_arena is not None:
         dd = logits_desc(draft_arena[0])
@@ -211,9 +217,15 @@ def tree_verify(tree: DeviceTree, flat: DeviceFlat, target: torch.Tensor,
         dref, dls = None, 0
     L.check("ddt_tree_verify", L.load().ddt_tree_verify(
         C.byref(tree.c), C.byref(flat.c), C.byref(td), dref, dls, _ptr(temperature),
-        _ptr(uniforms), k_top, _ptr(row_topk), _ptr(row_argmax), _ptr(accept_len),
+        _ptr(uniforms), PROPOSALS[proposal], k_top, _ptr(row_topk), _ptr(row_argmax), _ptr(accept_len),
         _ptr(accept_path), _ptr(next_token), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream, target.device)))
+
+
+def set_walk_spin_limit(polls: int) -> int:
+    """ddt_set_walk_spin_limit: polls before a T > 0 walk's cross-workgroup
+    wait gives up (0 restores the default); returns the previous value."""
+    return int(L.load().ddt_set_walk_spin_limit(int(polls)))
 
 
 def succ_update(M: torch.Tensor, flat: DeviceFlat, k_succ: int, row_topk: Optional[torch.Tensor] = None,

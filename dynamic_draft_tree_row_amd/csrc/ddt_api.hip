@@ -94,6 +94,9 @@ inline T* carve(char*& p, size_t n) {
 void* const* g_events = nullptr;
 int g_pairs = 0, g_used = 0;
 
+// polls before a T > 0 walk's cross-workgroup wait gives up (ddt_set_walk_spin_limit)
+unsigned g_walk_spin_limit = WALK_SPIN_LIMIT;
+
 // Workgroups of the verify kernel the device holds at once (cached per device).
 int resident_verify_blocks() {
     static int cache[64];
@@ -157,6 +160,12 @@ int ddt_set_reduce_events(void* const* events, int n_pairs) {
     g_pairs = g_events ? n_pairs : 0;
     g_used = 0;
     return used;
+}
+
+unsigned ddt_set_walk_spin_limit(unsigned polls) {
+    const unsigned prev = g_walk_spin_limit;
+    g_walk_spin_limit = polls == 0 ? WALK_SPIN_LIMIT : polls;
+    return prev;
 }
 
 int ddt_chunk_elems(int dtype) {
@@ -351,7 +360,8 @@ int ddt_tree_build_mask(const ddt_tree* t, const int32_t* sel, const int32_t* m,
 
 int ddt_tree_verify(const ddt_tree* t, const ddt_flat* f, const ddt_logits* target,
                     const ddt_logits* draft, int64_t draft_layer_stride, const float* temperature,
-                    const float* uniforms, int k_top, int32_t* row_topk, int32_t* row_argmax,
+                    const float* uniforms, int proposal, int k_top, int32_t* row_topk,
+                    int32_t* row_argmax,
                     int32_t* accept_len, int32_t* accept_path, int32_t* next_token, void* ws,
                     size_t ws_bytes, void* stream) {
     int st = check_tree(t);
@@ -361,6 +371,7 @@ int ddt_tree_verify(const ddt_tree* t, const ddt_flat* f, const ddt_logits* targ
         accept_len == nullptr || accept_path == nullptr || next_token == nullptr)
         return DDT_EINVAL;
     if (target->dtype != DDT_F32 && target->dtype != DDT_BF16) return DDT_EDTYPE;
+    if (proposal != DDT_PROPOSAL_DRAFT && proposal != DDT_PROPOSAL_POINT) return DDT_EINVAL;
     if (draft != nullptr && (!logits_ok(draft) || draft->dtype != target->dtype ||
                              draft->V != target->V || draft_layer_stride < 0))
         return DDT_EINVAL;
@@ -381,6 +392,8 @@ int ddt_tree_verify(const ddt_tree* t, const ddt_flat* f, const ddt_logits* targ
     a.chunks = groups_of((long long)t->B * f->P, target->V, target->dtype); a.Kp = Kp;
     a.tgt = target->data; a.bf16 = target->dtype == DDT_BF16; a.V = target->V;
     a.ts0 = target->s0; a.ts1 = target->s1;
+    a.point = proposal == DDT_PROPOSAL_POINT;
+    a.spin_limit = g_walk_spin_limit;
     a.drf = draft ? draft->data : nullptr; a.dl = draft_layer_stride;
     a.ds0 = draft ? draft->s0 : 0; a.ds1 = draft ? draft->s1 : 0;
     a.temperature = temperature; a.U = uniforms; a.k_top = k_top; a.row_topk = row_topk;

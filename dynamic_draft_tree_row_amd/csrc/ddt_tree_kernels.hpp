@@ -963,12 +963,18 @@ __global__ __launch_bounds__(MK_NT) void k_build_mask(MaskArgs a) {
 // EAGLE-2 explainer: at T = 0 acceptance is an argmax match along candidate
 // paths (losslessness section); at T > 0 a drafted token x is accepted with
 // probability min(1, p(x)/q(x)) and a rejection resamples from
-// norm(max(0, p - q)) (ledger section).  Tree reading: siblings are tried in
-// flat order with the residual carried between them.
+// norm(max(0, p - q)) (ledger section), q being the distribution x was
+// proposed from.  Tree reading: siblings are tried in flat order with the
+// residual carried between them.  Point-mass proposals (every child in the
+// point mode, Graft retrieval children always) take q = delta_x: accept with
+// probability p_k(x), a rejection removes x from the residual; the draft
+// rows are then not read.
 
 struct VerifyArgs {
     ddt_tree t;
     int G;                 // workgroups per request
+    int point;             // 1: every child is a point-mass proposal
+    unsigned spin_limit;   // bound of the cross-workgroup wait (polls)
 
     ddt_flat f;
     const uint32_t* part;
@@ -1075,13 +1081,18 @@ __device__ __forceinline__ double walk_q(const WalkRows& w, float d) {
 // alternating), releases, counts itself in, and spins (bounded) until all G
 // have arrived.  A workgroup reaches pass k + 2's store only after all G
 // arrived at pass k + 1, i.e. after every workgroup read pass k's slot.
+// The wait is bounded (spin_limit polls).  A workgroup whose wait runs out
+// leaves the walk; workgroup 0 then redoes that pass, and every later one,
+// alone over the whole vocabulary, so the request still completes with the
+// same decisions.
 #define WALK_SPIN_LIMIT (1u << 22)
 
 struct RowSync {
     double* buf;         // [2][G][2] pass sums
     double* tiles;       // [VF_MAXTILES] tile sums
     uint32_t* cnt;       // [0] arrivals (k + 1) * G after pass k, [1] exits
-    int G, g, k;         // workgroups of the request, this one, passes so far
+    unsigned limit;      // polls before the wait gives up
+    int G, g, k;         // workgroups taking part (1 once alone), this one, passes so far
     int lo, hi;          // vocabulary slice [lo, hi)
     int t_lo, t_hi;      // the same slice in tiles
 };
@@ -1114,7 +1125,7 @@ __device__ void pass_end(RowSync& rs, const double* s_red, int nw, bool two, dou
             unsigned spins = 0;
             while (!*s_err &&
                    __hip_atomic_load(rs.cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-                if (++spins > WALK_SPIN_LIMIT) { *s_err = 1; break; }
+                if (++spins > rs.limit) { *s_err = 1; break; }
                 __builtin_amdgcn_s_sleep(2);
             }
             __threadfence();
@@ -1194,6 +1205,9 @@ __device__ double walk_tiles(const WalkRows& w, RowSync& rs, double* s_red, doub
         }
         mine += ws;
     }
+    // the tile sums this wave stored for the other workgroups are complete
+    // (device scope) before the barrier that precedes the arrival count
+    if (rs.G > 1) __threadfence();
     if (lane == 0) s_red[wid] = mine;
     double tot, zero;
     pass_end(rs, s_red, VF_NT / 64, false, tot, zero, s_bc, s_err);
@@ -1461,6 +1475,7 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
     rs.buf = t.walk_buf + (size_t)b * DDT_WALK_STRIDE;
     rs.tiles = rs.buf + 4 * 32;
     rs.cnt = t.walk_sync + 2 * (size_t)b;
+    rs.limit = a.spin_limit;
     rs.G = G; rs.g = g; rs.k = 0;
     {
         const int tpw = (ntiles + G - 1) / G;
@@ -1469,12 +1484,25 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
         rs.lo = rs.t_lo * VF_TILE;
         rs.hi = min(a.V, rs.t_hi * VF_TILE);
     }
+    // After a pass whose wait ran out (s_err set): workgroup 0 leaves the
+    // exchange, takes the whole vocabulary and asks for the pass again
+    // (true); any other workgroup leaves the walk (false, s_err stays set and
+    // it never counts itself in again).  Alone, no wait can run out.
+    auto alone_again = [&]() -> bool {
+        if (!s_err || g != 0) return false;
+        rs.G = 1; rs.t_lo = 0; rs.t_hi = ntiles; rs.lo = 0; rs.hi = a.V;
+        __syncthreads();                               // every thread has read s_err
+        if (tid == 0) s_err = 0;
+        __syncthreads();
+        return true;
+    };
     if (tid == 0) { s_u = 0; s_len = 0; s_path[0] = 0; s_err = 0; s_next = 0; }
     if (tid < 64) s_e2t[tid] = exp2((double)tid / 64.0);
     // every position's draft slot, depth and row statistics (a chain of three
     // loads, once), then its logits under its parent's rows (one more round):
     // the walk's steps read LDS only
     const size_t es = a.bf16 ? 2 : 4;
+    const bool use_draft = a.drf != nullptr && !a.point;
     auto drow_of = [&](int slot, int dep) -> const char* {
         const int64_t doff = (int64_t)dep * a.dl + (int64_t)b * a.ds0 + (int64_t)slot * a.ds1;
         return (const char*)a.drf + (size_t)doff * es;
@@ -1485,7 +1513,7 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
         const int nc = ok ? node : 0;
         int slot = t.eslot[(size_t)b * t.cap + nc];
         const int dep = t.depth[(size_t)b * t.cap + nc];
-        if (!ok || a.drf == nullptr || dep < 0 || dep >= t.D_max || slot >= t.R_max) slot = -1;
+        if (!ok || !use_draft || dep < 0 || dep >= t.D_max || slot >= t.R_max) slot = -1;
         const size_t ri = ((size_t)b * t.D_max + (slot >= 0 ? dep : 0)) * t.R_max + (slot >= 0 ? slot : 0);
         const float rm = t.rmax[ri], rsv = t.rsp[ri];
         const uint64_t key = t.key[(size_t)b * t.cap + nc];
@@ -1532,10 +1560,11 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
         const int uslot = s_wslot[u];
         const int udep = s_wdep[u];
         // u's draft row proposes its draft children; its retrieval children
-        // (and any child of a node without a draft row) get point-mass
-        // proposals q = delta_x: accepted with probability p_k(x), and a
-        // rejection removes x from the residual.  Draft children come first
-        // in flat order, so the excluded tokens never meet a draft pass.
+        // (and every child in the point mode, or of a node without a draft
+        // row) get point-mass proposals q = delta_x: accepted with
+        // probability p_k(x), and a rejection removes x from the residual.
+        // Draft children come first in flat order, so the excluded tokens
+        // never meet a draft pass.
         const bool has_q = nch > 0 && uslot >= 0;
         WalkRows w;
         w.tab = s_e2t;
@@ -1550,18 +1579,34 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
         w.Md = has_q ? (double)s_wrm[u] : w.Mt;
         w.lzt = 0.0;
         w.lzd = 0.0;
+        bool tiles_ready = false;                       // s_tile holds the emission weights
+        bool tiles_unnorm = false;                      // ... as unnormalised p (lzt = 0)
+        double tiles_tot = 0.0;
         // Normalisers.  The accept tests at T = 1 use the rows' own statistics
         // (the reduction's fp32 sigma', relative error ~1e-6, well inside the
         // accept-test margin); the fp64 sums are taken only once a rejection
-        // needs a residual.  The emission weights need no normaliser.
+        // needs a residual.  With point-mass children only, that one pass over
+        // the target row also leaves the emission weights per tile.
         bool zexact = false;
         auto exact_norms = [&]() {
-            w.lzt = 0.0;                               // sums of the unnormalised rows
-            w.lzd = 0.0;
-            double Zt, Zd;
-            walk_norms(w, rs, s_red, s_bc, &s_err, a.V, Zt, Zd);
-            w.lzt = log2(Zt);
-            w.lzd = log2(Zd);
+            if (has_q) {
+                w.lzt = 0.0;                           // sums of the unnormalised rows
+                w.lzd = 0.0;
+                double Zt, Zd;
+                do walk_norms(w, rs, s_red, s_bc, &s_err, a.V, Zt, Zd); while (alone_again());
+                w.lzt = log2(Zt);
+                w.lzd = log2(Zd);
+            } else {
+                WalkRows w0 = w;
+                w0.lzt = 0.0;
+                double Z;
+                do Z = walk_tiles(w0, rs, s_red, s_bc, &s_err, a.V, false, 0.0, s_tile);
+                while (alone_again());
+                w.lzt = log2(Z);                       // Z >= 1: the maximum weighs 1
+                tiles_ready = true;
+                tiles_unnorm = true;
+                tiles_tot = Z;
+            }
             zexact = true;
         };
         if (nch > 0) {
@@ -1574,8 +1619,6 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
         }
         double ra = 0.0, rb = 1.0;                      // residual p_k = max(0, p - ra q) / rb, minus excluded tokens
         int accepted = -1;
-        bool tiles_ready = false;                       // the tiles hold the current residual's weights
-        double tiles_tot = 0.0;
         if (tid == 0) s_nz = 0;
         __syncthreads();
         // the unnormalised residual weight of child c's token
@@ -1593,10 +1636,15 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
                 if (tid == 0) s_acc = ((double)Ub[2 * c] < wres(c) / rb) ? 1 : 0;
                 __syncthreads();
                 if (s_acc) { accepted = c; break; }
-                if (!zexact) exact_norms();
+                if (!zexact) {
+                    exact_norms();
+                    if (s_err) break;
+                }
                 const double wx = wres(c);              // every thread, exact normalisers
                 __syncthreads();                        // s_nz read by all before it grows
-                if (rb - wx > 0.0) {                    // an all-zero residual keeps p as it was
+                // a token already removed (a duplicate sibling) weighs 0 and is
+                // not listed again; an all-zero residual keeps p as it was
+                if (wx > 0.0 && rb - wx > 0.0) {
                     rb -= wx;
                     if (tid == 0) s_zc[s_nz++] = c;
                 }
@@ -1612,20 +1660,27 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
             }
             __syncthreads();
             if (s_acc) { accepted = c; break; }
-            if (!zexact) exact_norms();
+            if (!zexact) {
+                exact_norms();
+                if (s_err) break;
+            }
             // rejection: b' = F(a + b); after the last sibling the same
             // pass leaves the emission weights per tile
             const double an = ra + rb;
             double F;
             if (ci == nch - 1) {
-                F = walk_tiles(w, rs, s_red, s_bc, &s_err, a.V, true, an, s_tile);
+                do F = walk_tiles(w, rs, s_red, s_bc, &s_err, a.V, true, an, s_tile);
+                while (alone_again());
                 tiles_ready = F > 0.0;
+                tiles_unnorm = false;
                 tiles_tot = F;
             } else {
-                F = walk_pass<true>(w, rs, s_red, s_bc, &s_err, a.V, [&](float tv, float dv) {
+                do F = walk_pass<true>(w, rs, s_red, s_bc, &s_err, a.V, [&](float tv, float dv) {
                     return fmax(0.0, walk_p(w, tv) - an * walk_q(w, dv));
                 });
+                while (alone_again());
             }
+            if (s_err) break;
             if (F > 0.0) { ra = an; rb = F; }
         }
         if (s_err) break;
@@ -1637,20 +1692,26 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
         // emission from the current residual by inverse CDF with U[u][1] over
         // the unnormalised weights max(0, p - a q) (p at a leaf); the threshold
         // scales with their total
-        if (!tiles_ready) tiles_tot = walk_tiles(w, rs, s_red, s_bc, &s_err, a.V, has_q, ra, s_tile);
+        if (!tiles_ready) {
+            do tiles_tot = walk_tiles(w, rs, s_red, s_bc, &s_err, a.V, has_q, ra, s_tile);
+            while (alone_again());
+            tiles_unnorm = false;
+        }
         if (s_err) break;
         if (g == 0) {
-            if (G > 1)                                 // the other workgroups' tiles
+            WalkRows we = w;                           // the units the tiles were summed in
+            if (tiles_unnorm) we.lzt = 0.0;
+            if (rs.G > 1)                              // the other workgroups' tiles
                 for (int q = tid; q < ntiles; q += VF_NT)
                     s_tile[q] = __hip_atomic_load(rs.tiles + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __syncthreads();
-            // rejected retrieval tokens carry no weight: out of their tiles'
+            // rejected point-mass tokens carry no weight: out of their tiles'
             // sums and the total here, out of the element scan in walk_pick
             const int nz = s_nz;
             if (tid == 0) {
                 for (int z = 0; z < nz; ++z) {
                     const int c = s_zc[z];
-                    const double wx = fmax(0.0, walk_p(w, s_wtl[c]) - ra * (has_q ? walk_q(w, s_wdl[c]) : 0.0));
+                    const double wx = fmax(0.0, walk_p(we, s_wtl[c]) - ra * (has_q ? walk_q(we, s_wdl[c]) : 0.0));
                     const int tt = min(max(s_ft[c], 0), a.V - 1) / VF_TILE;
                     s_tile[tt] = fmax(0.0, s_tile[tt] - wx);
                     s_zc[z] = s_ft[c];                 // from here on: the excluded tokens
@@ -1662,15 +1723,17 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
                 for (int q = 0; q < ntiles; ++q) tot += s_tile[q];
                 tiles_tot = tot;
             }
-            walk_pick(w, a.V, has_q, ra, (double)Ub[2 * u + 1], tiles_tot, s_tile, &s_next, s_zc, nz);
+            walk_pick(we, a.V, has_q, ra, (double)Ub[2 * u + 1], tiles_tot, s_tile, &s_next, s_zc, nz);
         }
         break;
     }
+    // workgroup 0 never ends with s_err set (a wait that ran out sent it on
+    // alone), so every request gets its outcome
     if (g == 0 && tid == 0) {
-        const int len = s_err ? -1 : s_len;
+        const int len = s_len;
         for (int s2 = 0; s2 <= Dp; ++s2) apath[s2] = s2 <= len ? s_path[s2] : -1;
         a.accept_len[b] = len;
-        a.next_token[b] = s_err ? -1 : s_next;
+        a.next_token[b] = s_next;
     }
     if (G > 1 && tid == 0) {
         // the last workgroup of the request to leave returns the counters to 0

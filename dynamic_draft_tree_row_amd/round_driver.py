@@ -96,12 +96,14 @@ class RoundRunner:
 
     def verify(self, target: torch.Tensor, draft_arena: Optional[torch.Tensor],
                temperature: torch.Tensor, uniforms: torch.Tensor,
-               M: Optional[torch.Tensor] = None, stream=None) -> None:
-        """target: [B][m_max+1][V] in flat order."""
+               M: Optional[torch.Tensor] = None, stream=None, proposal: str = "point") -> None:
+        """target: [B][m_max+1][V] in flat order.  proposal: how T > 0 rows
+        verify draft children ("point": as the deterministic top-k choices
+        they are; "draft": as samples of the draft row)."""
         api.tree_verify(self.tree, self.flat, target, draft_arena, temperature, uniforms,
                         self.accept_len, self.accept_path, self.next_token, self.ws,
                         k_top=self.k_top, row_topk=self.row_topk, row_argmax=self.row_argmax,
-                        stream=stream)
+                        proposal=proposal, stream=stream)
         if self.shape.graft:
             api.succ_update(M, self.flat, self.shape.k_succ, row_topk=self.row_topk,
                             k_top=self.k_top, shared=self.shape.shared_M, stream=stream)

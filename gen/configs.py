@@ -92,11 +92,15 @@ class Workload:
     K_e: int                 # expand budget (frontier size)
     K_n: int                 # children per expanded node (vocab top-k)
     m: int                   # verify budget (draft nodes, root excluded)
-    verify: str              # "greedy", "t1" or "mixed"
+    verify: str              # "greedy", "t1", "mixed" (greedy or T = 1 per row) or "tmix" (T in {0, 0.7, 1, 1.6})
     sigma: float             # target = draft + N(0, sigma) noise (sigma = std dev)
     prefix: int = 0          # context prefix length in front of the tree
     cast: Optional[CastSpec] = None
     graft: Optional[GraftSpec] = None
+    # T > 0 verify of draft children: "point" (point-mass proposals, for the
+    # deterministic top-k children the tree builder attaches) or "draft"
+    # (q = the draft row's softmax, the proposal of sampled children)
+    proposal: str = "point"
 
     @property
     def elem_bytes(self) -> int:

@@ -227,6 +227,8 @@ def temperatures(w: Workload, seed: int, rnd: int, rows=None) -> np.ndarray:
     if w.verify == "t1":
         return np.ones(len(rows), np.float32)
     g = keyed(S_TEMP, seed, rnd)
+    if w.verify == "tmix":            # greedy rows and three sampling temperatures
+        return np.array([0.0, 0.7, 1.0, 1.6], np.float32)[g.integers(0, 4, w.B)][rows]
     return (g.random(w.B) < 0.5).astype(np.float32)[rows]
 
 

@@ -59,6 +59,10 @@ extern "C" {
 #define DDT_F32 0
 #define DDT_BF16 1
 
+/* T > 0 proposal of draft children in ddt_tree_verify */
+#define DDT_PROPOSAL_DRAFT 0  /* q = softmax(draft/T): children drawn i.i.d. from the draft */
+#define DDT_PROPOSAL_POINT 1  /* q = delta_x: children chosen deterministically (top-k trees) */
+
 /* documented limits */
 #define DDT_MAX_K 32        /* children per node, vocab top-k, refresh k */
 #define DDT_MAX_DEPTH 11    /* draft layers (canonical key holds 11 rank fields) */
@@ -313,38 +317,46 @@ int ddt_tree_build_mask(const ddt_tree* t /*host*/, const int32_t* sel, const in
  * temperature[b] == 0: greedy -- the accept length is the longest prefix of a
  * root-to-leaf path whose every token equals the target argmax at its parent
  * (first path on ties); next_token = argmax at the last accepted position.
- * temperature[b] > 0: p = softmax(target/T), q = softmax(draft/T) of the row
- * that expanded the node; children tried in flat order, child c accepted iff
- * uniforms[b][c][0] < p(x_c)/q(x_c); a rejection replaces p by
- * norm(max(0, p - q)) (unchanged if all zero); when no child is accepted, or
- * at a leaf, next_token is the smallest v with prefix sum of p > u * sum(p),
- * u = uniforms[b][pos][1].
+ * temperature[b] > 0: p = softmax(target/T); children are tried in flat
+ * order, each accepted with probability min(1, p_k(x)/q(x)) under the
+ * residual p_k left by the rejected siblings before it, with q the proposal
+ * of that child (uniforms[b][c][0] < p_k(x_c)/q(x_c) accepts child c):
+ *   proposal = DDT_PROPOSAL_POINT: q = delta_x for every child, the proposal
+ *     of a deterministically chosen token such as the top-k children that
+ *     ddt_tree_expand attaches.  Accepted iff uniforms < p_k(x); a rejection
+ *     leaves norm(max(0, p_k - delta_x)) = p_k with x removed and
+ *     renormalised.  Exactly lossless for any tree ([E2] losslessness
+ *     section: the draft distribution only shapes which candidates are
+ *     proposed).  The draft rows are not read (draft may be NULL).
+ *   proposal = DDT_PROPOSAL_DRAFT: q = softmax(draft/T) of the row that
+ *     expanded the node, and a rejection leaves norm(max(0, p_k - q)) (kept
+ *     as it was if all zero).  The proposal of children drawn i.i.d. from the
+ *     draft; on top-k children it is not exactly lossless.  Retrieval
+ *     children (key source bit 1, and any child of a node without a draft
+ *     row) still take point-mass proposals, after the draft children.
+ * When no child is accepted, or at a leaf, next_token is the smallest v with
+ * prefix sum of p_k > u * sum(p_k), u = uniforms[b][pos][1], tokens removed by
+ * point-mass rejections excluded.
  * draft: the draft arena; the row that expanded a node of depth d - 1 from
  * frontier slot j of batch row b (i.e. layer d's slice) starts at
  * draft->data + (d-1)*draft_layer_stride + b*draft->s0 + j*draft->s1
- * elements.  Needed only when some temperature > 0 (may be NULL otherwise).
- * Retrieval children (key source bit 1, and any child of a node without a
- * draft row) are tried with a point-mass proposal q = delta_x after the draft
- * children: accepted iff uniforms[b][c][0] < p_k(x), and a rejection removes
- * x from the residual (kept as it was if nothing would be left); the
- * emission's inverse CDF then skips the removed tokens.  This is an exact
- * speculative-sampling step for any deterministically chosen x ([GR] step
- * (3): the acceptance rule is the standard one, and the method is lossless).
+ * elements.  Read only with DDT_PROPOSAL_DRAFT when some temperature > 0.
  * row_argmax: [B][P] or NULL.  k_top > 0 with row_topk [B][P][k_top]: top-k
  * ids of every verified row from the same pass (feeds ddt_succ_update).
  * Both hold -1 at padding positions (past f->m[b]).
  * accept_len [B]; accept_path [B][Dp+1] flat indices root first, -1 padded;
  * next_token [B].  ws >= ddt_workspace_bytes(B*P, V, dtype, max(1,k_top)).
  * A T > 0 request's vocabulary passes may be split over several workgroups
- * that exchange partial sums through t->walk_buf / t->walk_sync; they wait
- * for each other with a bounded spin.  If that wait ever runs out (the
- * workgroups were not resident together), the request's accept_len and
- * next_token are set to -1.
+ * that exchange partial sums through t->walk_buf / t->walk_sync and wait for
+ * each other with a bounded spin.  If a wait runs out (the workgroups were
+ * not resident together), workgroup 0 finishes the walk alone over the whole
+ * vocabulary: the outcome is the same, only slower.
+ * Errors: DDT_EINVAL also for a proposal other than the two above.
  */
 int ddt_tree_verify(const ddt_tree* t /*host*/, const ddt_flat* f /*host*/,
                     const ddt_logits* target /*host*/, const ddt_logits* draft /*host or NULL*/,
                     int64_t draft_layer_stride, const float* temperature /*[B]*/,
-                    const float* uniforms /*[B][P][2]*/, int k_top, int32_t* row_topk,
+                    const float* uniforms /*[B][P][2]*/, int proposal, int k_top, int32_t* row_topk,
                     int32_t* row_argmax, int32_t* accept_len, int32_t* accept_path,
                     int32_t* next_token, void* ws, size_t ws_bytes, void* stream);
 
@@ -538,6 +550,15 @@ int ddt_row_topk(const ddt_logits* x /*host*/, int n0, int n1, int K, int32_t* i
  * the previous call.  Process-wide host state; not thread-safe.
  */
 int ddt_set_reduce_events(void* const* events, int n_pairs);
+
+/*
+ * ddt_set_walk_spin_limit -- test and diagnostic hook: the number of polls
+ * after which a T > 0 walk's cross-workgroup wait in ddt_tree_verify gives up
+ * (workgroup 0 then finishes that request alone; see ddt_tree_verify).  0
+ * restores the default (2^22 polls).  Returns the previous value.
+ * Process-wide host state read when a verify is enqueued; not thread-safe.
+ */
+unsigned ddt_set_walk_spin_limit(unsigned polls);
 
 /* Text for a status code. */
 const char* ddt_strerror(int status);

@@ -24,9 +24,22 @@ describe, written in float64, following the pages' steps in their order:
 Where the pages are silent or garbled this module takes one reading and says
 so at the point of use.
 
-Every function that a parity test relies on is pinned by the oracle self-tests
-(closed forms, invariants, brute force, special-case reductions).  None is left
-"parity unpinned".
+Each function a parity test relies on is pinned, in tests/test_oracle_pins.py,
+by something other than itself:
+  * row statistics and top-k: exact sums and brute-force orderings;
+  * path values: the product of confidences recomputed along parent chains;
+  * frontier and rerank: invariants, and brute force over every connected
+    subtree of tiny trees;
+  * flatten, mask, positions, paths: hand-listed visibility and path rules;
+  * greedy verify: the noise-free rank-0-chain closed form;
+  * stochastic verify: the textbook one-child rule, hand-computed thresholds
+    for q- and point-mass proposals (duplicate siblings and T != 1 included),
+    and chi-square losslessness on a 16-token vocabulary;
+  * CAST: the Theorem 4.1 reduction to fixed top-K, a hand-worked round whose
+    cost lookups move through a 4-row grid (context row, verify context,
+    S_T versus S_D, the zero-cost step), and a hand-worked depth-gate FIFO;
+  * Graft: the gather recomputed directly, stages forced by thresholds, and
+    the refresh as a full sort of each target row.
 
 Conventions shared with the library's documented layout (not with its code):
   * node 0 of a row is the root; layer d's children are appended slot-major
@@ -576,29 +589,38 @@ def sample_inverse_cdf(p: np.ndarray, u: float, margins=None) -> int:
 
 
 def verify_stochastic(f: Flat, target_row, draft_row_of, T: float, U: np.ndarray,
-                      margins=None, retrieval=None) -> tuple:
+                      margins=None, retrieval=None, proposal: str = "draft") -> tuple:
     """Speculative sampling over the flattened tree.
 
     Chain rule (EAGLE-2 explainer, ledger section): accept a drafted token x
-    with probability min(1, p(x)/q(x)); on rejection draw from
-    norm(max(0, p - q)).  Reading for a tree (the pages apply the rule "along
-    candidate paths"): at node u, with p the target distribution at u and q the
-    draft distribution u was expanded with, try u's selected children in flat
-    order; child c is accepted when U[c,0] < p(x_c)/q(x_c) (min(1, .) is
-    implicit), and a rejection replaces p by norm(max(0, p - q)) (kept as it was
-    if that residual is all zero) before the next sibling.  When no child is
-    accepted, or u has no selected child, the next token is drawn from the
-    current p by inverse CDF with U[u,1].  p = softmax(target/T), q =
-    softmax(draft/T).
+    with probability min(1, p(x)/q(x)), q being the distribution x was
+    proposed from; on rejection draw from norm(max(0, p - q)).  Reading for a
+    tree (the pages apply the rule "along candidate paths"): at node u, with p
+    the target distribution at u, try u's selected children in flat order;
+    child c is accepted when U[c,0] < p(x_c)/q(x_c) (min(1, .) is implicit),
+    and a rejection replaces p by norm(max(0, p - q)) (kept as it was if that
+    residual is all zero) before the next sibling.  When no child is accepted,
+    or u has no selected child, the next token is drawn from the current p by
+    inverse CDF with U[u,1].  p = softmax(target/T).
+
+    Which q (reading; the losslessness section says the draft distribution
+    only shapes which candidates are proposed, never the output distribution):
+      proposal = "draft": q = softmax(draft/T) of the row u was expanded with.
+        This is the proposal of children drawn i.i.d. from the draft, and the
+        walk is then exactly lossless; on children picked deterministically
+        (top-K) it is not.
+      proposal = "point": every child is a point-mass proposal q = delta_x,
+        the proposal of a deterministically chosen token: accepted with
+        probability p(x), and a rejection leaves norm(max(0, p - delta_x)),
+        i.e. p with x removed and renormalised.  Exactly lossless for any
+        tree, top-K trees included; the draft rows are not read.
 
     Retrieval children (retrieval[c] true: Graft grafted nodes, which no draft
-    row proposed) are tested with a point-mass proposal q = delta_x (reading
-    of the Graft review's step (3), "the acceptance rule is the standard one"):
-    accepted with probability p(x); a rejection removes x from p and
-    renormalises.  This is an exact speculative-sampling step for any
-    deterministic x, so those nodes keep the output distribution p.  Draft
-    children come first in flat order, then retrieval children.
+    row proposed) are point-mass proposals in both modes (Graft review, step
+    (3): the acceptance rule is the standard one).  Draft children come first
+    in flat order, then retrieval children.
     """
+    assert proposal in ("draft", "point")
     n = len([x for x in f.node if x >= 0])
     children = [[] for _ in range(n)]
     for i in range(1, n):
@@ -614,7 +636,7 @@ def verify_stochastic(f: Flat, target_row, draft_row_of, T: float, U: np.ndarray
         acc = None
         for c in children[u]:
             x = f.token[c]
-            if retrieval is not None and retrieval[c]:
+            if proposal == "point" or (retrieval is not None and retrieval[c]):
                 ratio = float(p[x])
                 if margins is not None:
                     margins.append(("accept", abs(float(U[c, 0]) - ratio)))
@@ -682,13 +704,15 @@ def tree_arrays(trees: Sequence[RowTree], cap: int, D: int, R: int) -> dict:
 
 def run_round(*, B, V, dtype, D, K_e, K_n, m_max, root_tok, draft_raw, target_raw_fn,
               temperature, U, prefix=0, cast=None, graft=None, M=None, k_succ=8,
-              tpl=(8, 8)) -> dict:
+              tpl=(8, 8), proposal="point") -> dict:
     """One full round on the CPU.
 
     draft_raw: [D][B][R][V] raw logits; target_raw_fn(flat) -> [B][P][V] raw
     target rows for the flattened tree (the stand-in for the target forward,
     built by the caller from the returned flat layout); temperature [B]
-    (0 = greedy); U [B][P][2].  cast: dict(S_T, S_D, L, M, C1[D], C2, C3[B], R).
+    (0 = greedy); U [B][P][2]; proposal: the T > 0 walk's proposal for draft
+    children ("point" or "draft", see verify_stochastic).
+    cast: dict(S_T, S_D, L, M, C1[D], C2, C3[B], R).
     graft: dict(ck_depth, tau, k_draft, K_max).  M: [B][V][k] successor matrix,
     updated in place when graft is given.  Returns every output of the round.
     """
@@ -749,7 +773,8 @@ def run_round(*, B, V, dtype, D, K_e, K_n, m_max, root_tok, draft_raw, target_ra
 
             ret = [t.src[v] == 1 if v >= 0 else False for v in f.node]
             mb = []
-            L_, path, tok = verify_stochastic(f, trow, qrow, float(temperature[b]), U[b], mb, ret)
+            L_, path, tok = verify_stochastic(f, trow, qrow, float(temperature[b]), U[b], mb, ret,
+                                              proposal)
             margins.extend((k, v, b) for k, v in mb)
         acc_len[b] = L_
         acc_path[b, :len(path)] = path

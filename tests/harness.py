@@ -121,7 +121,8 @@ def oracle_case(w: Workload, seed: int, rnd: int, rows=None, cast=None, graft=No
                           root_tok=roots, draft_raw=draft, target_raw_fn=tfn, temperature=T, U=U,
                           prefix=w.prefix, cast=cst, graft=graft, M=Mc,
                           k_succ=gs.k_succ if gs else 8,
-                          tpl=(gs.tpl_depth, gs.tpl_width) if gs else (8, 8))
+                          tpl=(gs.tpl_depth, gs.tpl_width) if gs else (8, 8),
+                          proposal=w.proposal)
         bad = O.margin_failures(out["margins"])
         if not bad:
             M_after = None
@@ -162,12 +163,14 @@ def runner_for(w: Workload, device="cuda", shared_M=False):
     return RoundRunner(shape, device)
 
 
-def dev_cast(cast: dict, device="cuda"):
+def dev_cast(cast: dict, device="cuda", ctx_verify: int = 0):
+    """CAST parameters on the device; ctx_verify is the verify-cost context
+    (the oracle takes the context prefix)."""
     import torch
     from dynamic_draft_tree_row_amd.api import CastParams
     f = lambda a: torch.tensor(np.asarray(a, np.float32), device=device)
     return CastParams(S_T=f(cast["S_T"]), S_D=f(cast["S_D"]), L=cast["L"], C1=f(cast["C1"]),
-                      C2=float(cast["C2"]), C3=f(cast["C3"]), R=cast["R"], ctx_verify=0)
+                      C2=float(cast["C2"]), C3=f(cast["C3"]), R=cast["R"], ctx_verify=ctx_verify)
 
 
 def dev_gate(graft: dict):
@@ -184,7 +187,7 @@ def gpu_round(case: Case, device="cuda") -> dict:
     run = runner_for(wb, device, case.shared_M)
     arena = to_dev(case.draft, w.dtype, device)
     roots = torch.from_numpy(case.roots).to(device)
-    cast = dev_cast(case.cast, device) if case.cast else None
+    cast = dev_cast(case.cast, device, w.prefix) if case.cast else None
     gate = dev_gate(case.graft) if case.graft else None
     if case.M_before is None:
         M = None
@@ -196,7 +199,7 @@ def gpu_round(case: Case, device="cuda") -> dict:
     target = to_dev(case.target, w.dtype, device)
     T = torch.from_numpy(case.T).to(device)
     U = torch.from_numpy(case.U).to(device)
-    run.verify(target, arena, T, U, M=M)
+    run.verify(target, arena, T, U, M=M, proposal=w.proposal)
     torch.cuda.synchronize()
     t, f = run.tree, run.flat
     g = lambda x: x.cpu().numpy()
@@ -336,7 +339,7 @@ def gpu_round_full(case: Case, device="cuda") -> dict:
                                             rows=others)
     T = torch.from_numpy(synth.temperatures(w, case.seed, case.rnd)).to(device)
     U = torch.from_numpy(synth.uniforms(w, case.seed, case.rnd, att)).to(device)
-    run.verify(to_dev(target, w.dtype, device), arena, T, U)
+    run.verify(to_dev(target, w.dtype, device), arena, T, U, proposal=w.proposal)
     torch.cuda.synchronize()
     t, f = run.tree, run.flat
     g = lambda x: x.cpu().numpy()

@@ -448,12 +448,15 @@ def _cond(seed, ctx, V, floor):
     return _dist(g, V, floor)
 
 
-def _lossless_trial_counts(N, V, sampled, seed=3):
+def _lossless_trial_counts(N, V, sampled, seed=3, proposal="draft"):
     """Joint counts of the first two emitted tokens over N verify calls on a
-    depth-2 tree: 3 root children, 2 children under each."""
+    depth-2 tree: 3 root children, 2 children under each.  Children are drawn
+    i.i.d. from the draft distribution (sampled) or are its top-k tokens."""
     g = np.random.default_rng(seed)
     p = lambda ctx: _cond(seed, ctx, V, 0.03)
     q = lambda ctx: _cond(seed + 1000, ctx, V, 0.01)
+    lp = functools.lru_cache(maxsize=None)(lambda ctx: np.log(p(ctx)))
+    lq = functools.lru_cache(maxsize=None)(lambda ctx: np.log(q(ctx)))
     counts = np.zeros((V, V))
     for _ in range(N):
         tokens, parents, ctxs = [0], [-1], [()]
@@ -470,8 +473,8 @@ def _lossless_trial_counts(N, V, sampled, seed=3):
                 tokens.append(int(x)); parents.append(u); ctxs.append(ctxs[u] + (int(x),))
         f = _mk_flat(tokens, parents)
         U = g.random((len(tokens), 2))
-        L, path, nxt = O.verify_stochastic(f, lambda i: np.log(p(ctxs[i])),
-                                           lambda i: np.log(q(ctxs[i])), 1.0, U)
+        L, path, nxt = O.verify_stochastic(f, lambda i: lp(ctxs[i]), lambda i: lq(ctxs[i]), 1.0, U,
+                                           proposal=proposal)
         emitted = [tokens[i] for i in path[1:]] + [nxt]
         if len(emitted) < 2:       # the next round starts from exact target sampling
             emitted.append(int(g.choice(V, p=p((emitted[0],)))))
@@ -480,22 +483,47 @@ def _lossless_trial_counts(N, V, sampled, seed=3):
     return counts, expect
 
 
-@pytest.mark.slow
-def test_tree_speculative_sampling_is_lossless_with_sampled_children():
-    """Children drawn i.i.d. from q, no pruning: the first two emitted tokens
-    follow the target's joint distribution (losslessness section)."""
-    N, V = 40000, 5
-    counts, expect = _lossless_trial_counts(N, V, sampled=True)
+def _assert_follows_target(counts, expect, N):
     assert stats.chisquare(counts.ravel(), expect.ravel() * N).pvalue > 1e-3
     assert stats.chisquare(counts.sum(1), expect.sum(1) * N).pvalue > 1e-3
 
 
 @pytest.mark.slow
+def test_tree_speculative_sampling_is_lossless_with_sampled_children():
+    """Children drawn i.i.d. from q, no pruning, q-proposal rule: the first two
+    emitted tokens follow the target's joint distribution (losslessness
+    section) on a 16-token vocabulary."""
+    N, V = 100000, 16
+    counts, expect = _lossless_trial_counts(N, V, sampled=True, proposal="draft")
+    _assert_follows_target(counts, expect, N)
+
+
+@pytest.mark.slow
+def test_point_mass_walk_is_lossless_on_topk_children():
+    """The trees the library builds: deterministic top-k children, each
+    verified as a point-mass proposal.  The first two emitted tokens follow
+    the target's joint distribution (losslessness section), V = 16."""
+    N, V = 100000, 16
+    counts, expect = _lossless_trial_counts(N, V, sampled=False, proposal="point")
+    _assert_follows_target(counts, expect, N)
+
+
+@pytest.mark.slow
+def test_point_mass_walk_is_lossless_with_sampled_children():
+    """Point-mass verification does not depend on how the candidates were
+    chosen: sampled children give the target's distribution too."""
+    N, V = 50000, 16
+    counts, expect = _lossless_trial_counts(N, V, sampled=True, proposal="point", seed=4)
+    _assert_follows_target(counts, expect, N)
+
+
+@pytest.mark.slow
 def test_negative_control_topk_children_are_biased():
-    """Deterministic top-k children under the same rule are not exactly
-    lossless (a documented limit of the reading); the bias is detectable."""
-    N, V = 40000, 5
-    counts, expect = _lossless_trial_counts(N, V, sampled=False)
+    """Deterministic top-k children under the q-proposal rule are not exactly
+    lossless (the reason top-k trees take point-mass proposals); the bias is
+    detectable on the same 16-token vocabulary."""
+    N, V = 50000, 16
+    counts, expect = _lossless_trial_counts(N, V, sampled=False, proposal="draft")
     assert stats.chisquare(counts.sum(1), expect.sum(1) * N).pvalue < 1e-6
 
 
@@ -509,17 +537,19 @@ def test_inverse_cdf_sampling_exact_cases():
     assert O.sample_inverse_cdf(p * 4.0, 0.99) == 3    # unnormalised input
 
 
-def test_residual_after_rejection():
+@pytest.mark.parametrize("T", [1.0, 1.6])
+def test_residual_after_rejection(T):
     """A rejected child with p = (.5,.5), q = (.9,.1): the residual puts all
-    mass on token 1, so the emission is token 1 for any uniform."""
-    lp, lq = np.log([0.5, 0.5]), np.log([0.9, 0.1])
+    mass on token 1, so the emission is token 1 for any uniform.  Logits are
+    T log p and T log q, so softmax(logits / T) gives those p and q."""
+    lp, lq = T * np.log([0.5, 0.5]), T * np.log([0.9, 0.1])
     f = _mk_flat([0, 0], [-1, 0])
     for u1 in (0.0, 0.3, 0.99):
         U = np.array([[0.0, u1], [0.99, 0.0]])      # 0.99 > p/q = 0.556: reject
-        L, path, nxt = O.verify_stochastic(f, lambda i: lp, lambda i: lq, 1.0, U)
+        L, path, nxt = O.verify_stochastic(f, lambda i: lp, lambda i: lq, T, U)
         assert L == 0 and nxt == 1
     U = np.array([[0.0, 0.0], [0.5, 0.0]])          # 0.5 < 0.556: accept
-    L, path, nxt = O.verify_stochastic(f, lambda i: lp, lambda i: lq, 1.0, U)
+    L, path, nxt = O.verify_stochastic(f, lambda i: lp, lambda i: lq, T, U)
     assert L == 1 and path == [0, 1]
 
 
@@ -569,37 +599,71 @@ def test_graft_template_under_an_anchor():
     assert len(added) == 2 and all(t2.depth[n] == 11 for n in added)
 
 
-def test_point_mass_children_thresholds():
-    """Retrieval children (point-mass proposals): the k-th is accepted iff
+@pytest.mark.parametrize("T", [1.0, 0.7])
+@pytest.mark.parametrize("mode", ["retrieval", "point"])
+def test_point_mass_children_thresholds(mode, T):
+    """Point-mass proposals (Graft retrieval children, or every child in the
+    "point" mode): the k-th is accepted iff
     U < p(x_k) / (1 - p(x_1) - .. - p(x_{k-1})), i.e. from p with the rejected
-    tokens removed and renormalised; the emission then excludes them."""
+    tokens removed and renormalised; the emission then excludes them.  No
+    draft row is read.  At temperature T the logits are T log p, so that
+    softmax(logits / T) = p and the thresholds are the same."""
     p = np.array([0.1, 0.2, 0.3, 0.15, 0.25])
-    lp = np.log(p)
+    lp = T * np.log(p)
     f = _mk_flat([0, 2, 4, 1], [-1, 0, 0, 0])      # root, then children with tokens 2, 4, 1
-    ret = [False, True, True, True]
+    if mode == "retrieval":
+        ret, prop = [False, True, True, True], "draft"
+    else:
+        ret, prop = None, "point"
     no_q = lambda i: (_ for _ in ()).throw(AssertionError("no draft row is needed"))
     eps = 1e-9
     # first child: threshold p(2) = 0.3
     for u, want in ((0.3 - eps, 1), (0.3 + eps, None)):
         U = np.array([[0.0, 0.0], [u, 0.0], [0.999, 0.0], [0.999, 0.0]])
-        L, path, _ = O.verify_stochastic(f, lambda i: lp, no_q, 1.0, U, retrieval=ret)
+        L, path, _ = O.verify_stochastic(f, lambda i: lp, no_q, T, U, retrieval=ret, proposal=prop)
         assert (path[1] if L else None) == want
     # second child after rejecting token 2: threshold 0.25 / 0.7
     t2 = 0.25 / 0.7
     for u, want in ((t2 - eps, 2), (t2 + eps, None)):
         U = np.array([[0.0, 0.0], [0.999, 0.0], [u, 0.0], [0.999, 0.0]])
-        L, path, _ = O.verify_stochastic(f, lambda i: lp, no_q, 1.0, U, retrieval=ret)
+        L, path, _ = O.verify_stochastic(f, lambda i: lp, no_q, T, U, retrieval=ret, proposal=prop)
         assert (path[1] if L else None) == want
     # third child after rejecting 2 and 4: threshold 0.2 / 0.45
     t3 = 0.2 / 0.45
     for u, want in ((t3 - eps, 3), (t3 + eps, None)):
         U = np.array([[0.0, 0.0], [0.999, 0.0], [0.999, 0.0], [u, 0.0]])
-        L, path, _ = O.verify_stochastic(f, lambda i: lp, no_q, 1.0, U, retrieval=ret)
+        L, path, _ = O.verify_stochastic(f, lambda i: lp, no_q, T, U, retrieval=ret, proposal=prop)
         assert (path[1] if L else None) == want
     # all rejected: the emission draws from {0: 0.1, 3: 0.15} renormalised
     for u1, want in ((0.0, 0), (0.4 - eps, 0), (0.4 + eps, 3), (0.999, 3)):
         U = np.array([[0.0, u1], [0.999, 0.0], [0.999, 0.0], [0.999, 0.0]])
-        L, path, nxt = O.verify_stochastic(f, lambda i: lp, no_q, 1.0, U, retrieval=ret)
+        L, path, nxt = O.verify_stochastic(f, lambda i: lp, no_q, T, U, retrieval=ret, proposal=prop)
+        assert L == 0 and nxt == want
+
+
+def test_point_mass_duplicate_siblings():
+    """Point-mass children with a repeated token: once token 2 is rejected it
+    has no mass left, so its duplicate is rejected for any uniform, the next
+    child's threshold is p(4) / (1 - p(2)), and the emission leaves token 2
+    out once (threshold 0.1 / 0.45 between tokens 0 and 1)."""
+    p = np.array([0.1, 0.2, 0.3, 0.15, 0.25])
+    lp = np.log(p)
+    f = _mk_flat([0, 2, 2, 4], [-1, 0, 0, 0])
+    no_q = lambda i: (_ for _ in ()).throw(AssertionError("no draft row is needed"))
+    eps = 1e-9
+    for u2 in (0.0, 0.5):
+        U = np.array([[0.0, 0.0], [0.999, 0.0], [u2, 0.0], [0.999, 0.0]])
+        L, path, _ = O.verify_stochastic(f, lambda i: lp, no_q, 1.0, U, proposal="point")
+        assert L == 0
+    t3 = 0.25 / 0.7
+    for u, want in ((t3 - eps, 3), (t3 + eps, None)):
+        U = np.array([[0.0, 0.0], [0.999, 0.0], [0.0, 0.0], [u, 0.0]])
+        L, path, _ = O.verify_stochastic(f, lambda i: lp, no_q, 1.0, U, proposal="point")
+        assert (path[1] if L else None) == want
+    # emission over {0: .1, 1: .2, 3: .15} / 0.45
+    for u1, want in ((0.1 / 0.45 - eps, 0), (0.1 / 0.45 + eps, 1), (0.3 / 0.45 + eps, 3)):
+        U = np.array([[0.0, u1], [0.999, 0.0], [0.0, 0.0], [0.999, 0.0]])
+        L, path, nxt = O.verify_stochastic(f, lambda i: lp, no_q, 1.0, U, proposal="point")
         assert L == 0 and nxt == want
 
 
@@ -640,7 +704,7 @@ def test_point_mass_retrieval_nodes_keep_the_tree_lossless():
     """Sampled draft children plus deterministic retrieval nodes (point-mass
     proposals) under the rule: the first two emitted tokens still follow the
     target's joint distribution."""
-    N, V = 40000, 5
+    N, V = 60000, 16
     counts, expect = _mixed_trial_counts(N, V)
     assert stats.chisquare(counts.ravel(), expect.ravel() * N).pvalue > 1e-3
     assert stats.chisquare(counts.sum(1), expect.sum(1) * N).pvalue > 1e-3
@@ -760,6 +824,86 @@ def test_cast_depth_gate_fifo_hand_example():
     assert depth(0.39) == 2 and depth(0.151) == 2
     assert depth(0.149) == 3 and depth(0.127) == 3
     assert depth(0.125) == 4
+
+
+def cast_lookup_example():
+    """The hand-worked CAST round of test_cast_cost_lookup_hand_example: inputs
+    and the values worked out by hand (also run on the GPU)."""
+    V, B, D, K_e, K_n, m_max, prefix = 4, 2, 4, 3, 2, 8, 4
+    probs = {1: [0.5, 0.3, 0.15, 0.05], 2: [0.7, 0.2, 0.06, 0.04],
+             3: [0.5, 0.3, 0.12, 0.08], 4: [0.4, 0.3, 0.2, 0.1]}
+    draft = np.zeros((D, B, K_e, V), np.float32)
+    for d in range(1, D + 1):
+        draft[d - 1] = np.log(np.array(probs[d])).astype(np.float32)
+    k = np.arange(1, 9)
+    S_T = np.zeros((4, 9), np.float32)
+    S_D = np.zeros((4, 9), np.float32)
+    S_T[0, 1:] = 1 + 0.2 * (k - 1)
+    S_T[1, 1:] = 2 * (1 + 0.25 * (k - 1))
+    S_T[2, 1:] = 1 + 0.5 * (k - 1)
+    S_T[3, 1:] = 1 + 1.0 * (k - 1)
+    S_D[0, 1:] = [0.5, 0.5, 0.8, 1.1, 1.4, 1.7, 2.0, 2.3]
+    S_D[1, 1:] = 0.2 + 0.2 * k
+    S_D[2, 1:] = 0.3 * k
+    S_D[3, 1:] = 0.5 * k
+    cast = dict(S_T=S_T, S_D=S_D, L=2, M=4, C1=[2.0, 3.0, 0.8, 0.8], C2=1.0, C3=[0.56, 0.32], R=3)
+    shape = dict(V=V, B=B, D=D, K_e=K_e, K_n=K_n, m_max=m_max, prefix=prefix)
+    expect = dict(widths=[2, 1, 2], depth_built=3, m_rows=[3, 5])
+    return shape, draft, cast, expect
+
+
+def test_cast_cost_lookup_hand_example():
+    """CAST's cost lookup worked by hand (CAST notes, key designs 1, 2 and 4).
+
+    Draft rows are logs of exact probabilities that depend on the layer only,
+    so both requests grow the same tree and every value is a product of the
+    listed numbers.  K_n = 2 children per node, width cap 3, D_max = 4.
+    Grid step L = 2 over M = 4 rows, so select(c) = row min(c // 2, 3); the
+    context prefix is 4 tokens.
+
+    Width costs c_k = S_D[r][k] / S_T[r][1]:
+      row 0: 0.5, 0.5, 0.8, ...   (c_2 = c_1: the second node costs nothing)
+      row 1: 0.2, 0.3, 0.4, ...   (S_T[1][1] = 2)
+      row 2: 0.3, 0.6, 0.9, ...
+
+    Layer 1, context 0 (tree tokens fed so far; neither the root nor the
+    prompt counts) -> row 0.  Candidates 0.5, 0.3: u = 0.5, 0.8.  The cost
+    does not rise from k = 1 to 2 while the utility does, so the anchor moves:
+    n_1 = 2.  (Row 2, reached if the 4 prompt tokens counted, has marginal
+    0.3 / 0.3 = 1.0 < C1 = 2 and gives n_1 = 1; skipping the zero-cost step
+    also gives n_1 = 1.)
+    Layer 2, context 2 -> row 1.  Children of 0.5 and 0.3 under row
+    (0.7, 0.2): 0.35, 0.21, 0.10, 0.06; u = 0.35, 0.56, 0.66 (cap 3).
+    Marginals 0.21 / 0.1 = 2.1 and 0.31 / 0.2 = 1.55 are below C1 = 3: n_2 = 1.
+    Layer 3, context 3 -> row 1.  Children of 0.35 under (0.5, 0.3): 0.175,
+    0.105; marginal 0.105 / 0.1 = 1.05 >= C1 = 0.8: n_3 = 2.  (Counting the
+    root makes the context 4 -> row 2, marginal 0.105 / 0.3 = 0.35: n_3 = 1.)
+
+    Depth gate (R = 3, C2 = 1): layer 1 score 1 * 0.8 / 0.5 = 1.6 (grow);
+    layer 2 pushes 0.35 / 0.8 = 0.4375, score 0.71875 * 0.35 / 0.2 = 1.258
+    (grow); layer 3 pushes 0.28 / 0.35 = 0.8, score
+    (1 + 0.4375 + 0.8) / 3 * 0.28 / 0.3 = 0.696 < 1: stop with 3 layers of 4.
+
+    Verify count: the cost context is the prefix, 4 -> row 2 of S_T,
+    c_k = S_T[2][k] / S_T[2][1] = 1 + 0.5 (k - 1).  Node values in order:
+    0.5, 0.35, 0.3, 0.21, 0.175, 0.105, 0.10, 0.06; with a linear cost the
+    anchor scan keeps node k while v_(k) / 0.5 >= C3.  Request 0 (C3 = 0.56,
+    keep v >= 0.28): m = 3.  Request 1 (C3 = 0.32, keep v >= 0.16): m = 5.
+    (Row 0 of S_T, slope 0.2, gives 5 and 7 (keep v >= 0.112, v >= 0.064);
+    S_D's row 2 read as the verify cost, slope 0.3, also gives 5 and 7.)
+    """
+    shape, draft, cast, expect = cast_lookup_example()
+    B, m_max = shape["B"], shape["m_max"]
+    out = O.run_round(B=B, V=shape["V"], dtype="f32", D=shape["D"], K_e=shape["K_e"],
+                      K_n=shape["K_n"], m_max=m_max, root_tok=[0] * B, draft_raw=draft,
+                      target_raw_fn=lambda dr, fl: np.zeros((B, m_max + 1, shape["V"]), np.float32),
+                      temperature=np.zeros(B, np.float32), U=np.zeros((B, m_max + 1, 2), np.float32),
+                      prefix=shape["prefix"], cast=cast)
+    assert out["draft"].widths == expect["widths"]
+    assert out["draft"].depth_built == expect["depth_built"]
+    assert out["m_rows"].tolist() == expect["m_rows"]
+    vals = sorted(math.exp(s) for s in out["draft"].trees[0].S[1:])[::-1]
+    np.testing.assert_allclose(vals, [0.5, 0.35, 0.3, 0.21, 0.175, 0.105, 0.10, 0.06], rtol=1e-6)
 
 
 def test_cast_verify_count_limits():

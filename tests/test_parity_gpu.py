@@ -135,6 +135,12 @@ SMALL = {
     "cast_b12": configs.shrink(configs.C2, V=9000, B=12),       # more workgroups sharing the layer ticket
     "t1": configs.shrink(configs.C3, V=9001, B=4),            # odd V: unaligned bf16 rows
     "mixed_prefix": configs.shrink(configs.C5, V=4100, B=6),
+    # T > 0 draft children verified with q = the draft row's softmax
+    "t1_draft_q": configs.shrink(configs.C3, V=9001, B=4, proposal="draft"),
+    "mixed_draft_q": configs.shrink(configs.C5, V=4100, B=6, proposal="draft"),
+    # sampling temperatures other than 1: exact normalisers before the first test
+    "tmix": configs.shrink(configs.C3, V=7001, B=8, verify="tmix"),
+    "tmix_draft_q": configs.shrink(configs.C3, V=7001, B=8, verify="tmix", proposal="draft"),
 }
 
 
@@ -184,14 +190,15 @@ def test_graft_small_multi_round():
         M = case.M_after
 
 
-def test_graft_stochastic_verify_point_mass():
+@pytest.mark.parametrize("proposal", ["draft", "point"])
+def test_graft_stochastic_verify_point_mass(proposal):
     # Graft with T > 0: retrieval nodes are verified with point-mass
     # proposals (accepted with probability p(x), rejected tokens leave the
-    # residual), so a T = 1 request's walk can run through grafted chains
-    # (seed 83: the T = 1 walks accept 8 retrieval nodes over the 3 rounds,
-    # a chain of 3 among them, and reject others)
+    # residual), so a T = 1 request's walk can run through grafted chains;
+    # draft children before them take q-proposals or point-mass proposals
     base = configs.shrink(configs.C4, V=6000, B=6)
-    w = configs.Workload(**{**base.__dict__, "verify": "t1", "name": base.name + "_t1"})
+    w = configs.Workload(**{**base.__dict__, "verify": "t1", "name": base.name + "_t1",
+                            "proposal": proposal})
     tau = H.calibrate_tau(w, 83, 4)
     M = synth.succ_matrix0(w, 83)
     M0 = M.copy()
@@ -259,6 +266,124 @@ def test_round_edge_shapes(shape):
     H.compare(case, H.gpu_round(case))
 
 
+def _direct_case(w, draft, target, roots, T, U, cast=None):
+    """A case from inputs given directly (no generator, no re-keying): the
+    oracle's round on exactly these inputs."""
+    B = w.B
+    out = O.run_round(B=B, V=w.V, dtype=w.dtype, D=w.D, K_e=w.K_e, K_n=w.K_n, m_max=w.m_max,
+                      root_tok=roots, draft_raw=draft, target_raw_fn=lambda dr, fl: target,
+                      temperature=T, U=U, prefix=w.prefix, cast=cast, proposal=w.proposal)
+    return H.Case(w, 0, 0, list(range(B)), np.zeros(B, np.int64), draft, target, roots, U, T, out,
+                  cast)
+
+
+def test_cast_cost_lookup_hand_example():
+    # the hand-worked CAST round of the oracle pins: a 4-row cost grid of step
+    # 2 that the widths move through, a zero-cost step, different S_T and S_D
+    # slopes, and a 4-token prefix that picks the verify-cost row
+    from tests.test_oracle_pins import cast_lookup_example
+    shape, draft, cast, expect = cast_lookup_example()
+    B, P, V = shape["B"], shape["m_max"] + 1, shape["V"]
+    w = configs.Workload("cast_lookup", B=B, V=V, dtype="f32", D=shape["D"], K_e=shape["K_e"],
+                         K_n=shape["K_n"], m=shape["m_max"], verify="greedy", sigma=0.0,
+                         prefix=shape["prefix"],
+                         cast=configs.CastSpec(L=cast["L"], M=cast["M"], R=cast["R"]))
+    target = np.random.default_rng(3).standard_normal((B, P, V)).astype(np.float32)
+    case = _direct_case(w, draft, target, np.zeros(B, np.int32), np.zeros(B, np.float32),
+                        np.zeros((B, P, 2), np.float32), cast)
+    assert case.out["draft"].widths == expect["widths"]
+    assert case.out["m_rows"].tolist() == expect["m_rows"]
+    H.compare(case, H.gpu_round(case))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_rerank_exact_ties_take_the_sort_path(dtype):
+    # constant draft rows: every token has confidence 1/V, so the nodes of a
+    # layer tie exactly (32 + 1024 + 1024 nodes).  With m = 255 the 1024 tied
+    # nodes of layer 2 straddle the cut: more candidates than the rank count
+    # holds, so the rerank takes its full-sort path.  Ties go by canonical key
+    # (shallower first, then the rank path), in the frontier too.
+    V, B, D, K, m = 100, 2, 3, 32, 255
+    w = configs.Workload("ties", B=B, V=V, dtype=dtype, D=D, K_e=K, K_n=K, m=m, verify="greedy",
+                         sigma=0.0)
+    row = synth.cast_row(np.full(V, 0.5, np.float32), dtype)
+    draft = np.broadcast_to(row, (D, B, K, V)).copy()
+    g = np.random.default_rng(4)
+    target = np.stack([np.stack([synth.cast_row(g.standard_normal(V).astype(np.float32), dtype)
+                                 for _ in range(m + 1)]) for _ in range(B)])
+    case = _direct_case(w, draft, target, np.array([3, 5], np.int32), np.zeros(B, np.float32),
+                        np.zeros((B, m + 1, 2), np.float32))
+    t = case.out["draft"].trees[0]
+    assert t.n == 1 + K + 2 * K * K
+    say(f"ties dtype={dtype} selected={len(case.out['sels'][0])}")
+    H.compare(case, H.gpu_round(case))
+
+
+@pytest.mark.parametrize("name", ["cast", "mixed_prefix"])
+def test_dense_mask_matches_the_bitmask_with_the_prefix(name):
+    # the optional dense mask: every prefix column visible, then the ancestor
+    # bits of the flat tree (padding rows see the prefix and themselves)
+    from dynamic_draft_tree_row_amd import api
+    w = SMALL[name]
+    case = _case(w, 2, 0)
+    run = H.runner_for(w)
+    cast = H.dev_cast(case.cast, "cuda", w.prefix) if case.cast else None
+    run.draft(H.to_dev(case.draft, w.dtype), torch.from_numpy(case.roots).cuda(), cast=cast)
+    P = w.m_max + 1
+    dense = torch.full((w.B, P, w.prefix + P), 7, dtype=torch.uint8, device="cuda")
+    api.tree_build_mask(run.tree, run.sel, run.m_out, w.prefix, run.flat, dense=dense)
+    torch.cuda.synchronize()
+    d = dense.cpu().numpy()
+    say(f"dense mask {name} prefix={w.prefix} P={P}")
+    for b in range(w.B):
+        f = case.out["flats"][b]
+        bits = np.unpackbits(f.mask.view(np.uint8), axis=1, bitorder="little")[:, :P]
+        want = np.concatenate([np.ones((P, w.prefix), np.uint8), bits], 1)
+        np.testing.assert_array_equal(d[b], want, err_msg=f"row {b}")
+
+
+def test_graft_successor_matrix_resume():
+    # M is the only state a round leaves for the next: a snapshot taken after
+    # two rounds and restored replays the next two rounds bit for bit, and
+    # both replays equal the oracle's rounds
+    w = configs.shrink(configs.C4, V=6000, B=5)
+    tau = H.calibrate_tau(w, 79, 4)
+    M = synth.succ_matrix0(w, 79)
+    M0 = M.copy()
+    cases = []
+    for rnd in range(4):
+        case = H.oracle_case(w, 79, rnd, graft=H.graft_params(w, tau), M=M, M0=M0)
+        cases.append(case)
+        M = case.M_after
+    run = H.runner_for(w)
+    gate = H.dev_gate(cases[0].graft)
+    Md = torch.from_numpy(np.ascontiguousarray(M0)).cuda()
+
+    def play(case):
+        arena = H.to_dev(case.draft, w.dtype)
+        run.draft(arena, torch.from_numpy(case.roots).cuda(), gate=gate, M=Md)
+        run.verify(H.to_dev(case.target, w.dtype), arena, torch.from_numpy(case.T).cuda(),
+                   torch.from_numpy(case.U).cuda(), M=Md)
+        torch.cuda.synchronize()
+        g = lambda x: x.cpu().numpy().copy()
+        return dict(accept_len=g(run.accept_len), accept_path=g(run.accept_path),
+                    next_token=g(run.next_token), flat_token=g(run.flat.token), M=g(Md))
+
+    for c in cases[:2]:
+        play(c)
+    snap = Md.clone()
+    first = [play(c) for c in cases[2:]]
+    Md.copy_(snap)
+    second = [play(c) for c in cases[2:]]
+    for r, (a, b_, c) in enumerate(zip(first, second, cases[2:])):
+        say(f"graft resume round {r + 2} accept={a['accept_len'].tolist()}")
+        for k in a:
+            np.testing.assert_array_equal(a[k], b_[k], err_msg=f"replay differs: {k}")
+        np.testing.assert_array_equal(a["accept_len"], c.out["accept_len"])
+        np.testing.assert_array_equal(a["next_token"], c.out["next_token"])
+        np.testing.assert_array_equal(a["M"], c.M_after)
+
+
 # ---------------------------------------------------------------------------
 # full-size workloads, the bench's launch configuration
 # ---------------------------------------------------------------------------
@@ -267,23 +392,37 @@ def _tau_golden():
     return json.load(open(os.path.join(GOLDEN, "graft_tau.json")))["tau"]
 
 
-@pytest.mark.timeout(900)
+@pytest.mark.timeout(1200)
 @pytest.mark.parametrize("cfg", [configs.C1, configs.C2, configs.C3, configs.C4],
                          ids=lambda c: c.name)
 def test_round_full(cfg):
-    M = synth.succ_matrix0(cfg, 1000) if cfg.graft else None
-    case = _case(cfg, 1000 + configs.ORDER.index(cfg), 0, M=M,
-                 tau=_tau_golden() if cfg.graft else None)
-    say(f"full {cfg.name} tries={case.tries}")
-    H.compare(case, H.gpu_round(case))
+    # three seeds x two consecutive rounds (one seed for the B = 1 workload);
+    # Graft carries its successor matrix from round to round
+    i = configs.ORDER.index(cfg)
+    seeds = [1000 + i] if cfg is configs.C1 else [1000 + i, 2000 + i, 3000 + i]
+    for seed in seeds:
+        M = synth.succ_matrix0(cfg, seed) if cfg.graft else None
+        M0 = None if M is None else M.copy()
+        for rnd in range(2):
+            graft = H.graft_params(cfg, _tau_golden()) if cfg.graft else None
+            cast = H.cast_params(cfg) if cfg.cast else None
+            case = H.oracle_case(cfg, seed, rnd, cast=cast, graft=graft, M=M, M0=M0)
+            say(f"full {cfg.name} seed={seed} round={rnd} tries={case.tries} "
+                f"accept={case.out['accept_len'].tolist()}")
+            H.compare(case, H.gpu_round(case))
+            if cfg.graft:
+                M = case.M_after
 
 
-@pytest.mark.timeout(900)
+@pytest.mark.timeout(1200)
 def test_round_full_b64_sampled_rows():
+    # 16 of the 64 requests compared with the oracle (greedy and T = 1 rows),
+    # every request checked for the method's invariants
     w = configs.C5
-    rows = [0, 13, 27, 41, 63]
+    rows = list(range(0, 64, 4))
     case = _case(w, 1005, 0, rows=rows)
-    say(f"full {w.name} sampled rows {rows} tries={case.tries}")
+    say(f"full {w.name} sampled rows {rows} T={case.T.tolist()} tries={case.tries}")
+    assert (case.T == 0).any() and (case.T > 0).any()
     r = H.gpu_round_full(case)
     sub = {k: (v[rows] if k != "widths" else v) for k, v in r.items()}
     H.compare(case, sub)
