@@ -10,6 +10,7 @@ LIB_PATH = os.path.join(HERE, "libddt.so")
 DDT_OK, DDT_EINVAL, DDT_EDTYPE, DDT_ECAPACITY, DDT_EWORKSPACE, DDT_ELAUNCH = range(6)
 DDT_F32, DDT_BF16 = 0, 1
 DDT_PROPOSAL_DRAFT, DDT_PROPOSAL_POINT = 0, 1
+DDT_NOALLOC_SCRATCH_BYTES = 8 << 20
 MAX_K, MAX_DEPTH, MAX_FRONT, MAX_NODES, MAX_VERIFY, MAX_CHUNKS = 32, 11, 32, 4096, 255, 64
 
 P = C.c_void_p
@@ -94,6 +95,7 @@ SIGNATURES = {
     "ddt_row_topk": (C.c_int, [C.POINTER(Logits), C.c_int, C.c_int, C.c_int, P, P, P, P, P, sz, P]),
     "ddt_set_reduce_events": (C.c_int, [C.POINTER(P), C.c_int]),
     "ddt_set_walk_spin_limit": (C.c_uint, [C.c_uint]),
+    "ddt_row_topk_noalloc": (C.c_int, [C.POINTER(Logits), C.c_int, C.c_int, C.c_int, P, P, P, P, P]),
 }
 
 _lib = None

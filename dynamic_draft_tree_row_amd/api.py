@@ -288,6 +288,17 @@ def row_topk(x: torch.Tensor, K: int, ws: torch.Tensor, ids: Optional[torch.Tens
         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream, x.device)))
 
 
+def row_topk_noalloc(x: torch.Tensor, K: int, ids: Optional[torch.Tensor] = None,
+                     logc: Optional[torch.Tensor] = None, rmax: Optional[torch.Tensor] = None,
+                     rsp: Optional[torch.Tensor] = None, stream=None) -> None:
+    """ddt_row_topk_noalloc: the row reduction with its partials in the
+    library's fixed per-device array (no workspace, nothing allocated)."""
+    d = logits_desc(x)
+    L.check("ddt_row_topk_noalloc", L.load().ddt_row_topk_noalloc(
+        C.byref(d), x.shape[0], x.shape[1], K, _ptr(ids), _ptr(logc), _ptr(rmax), _ptr(rsp),
+        _stream(stream, x.device)))
+
+
 class PagedKV:
     """The caller-owned arrays of a block-paged KV context (ddt_kv_cache) on
     one device: k, v bf16 [n_blocks][block][Hkv][D], table [B][max_blocks],

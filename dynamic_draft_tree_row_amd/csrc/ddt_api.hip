@@ -4,6 +4,7 @@
 #include <hip/hip_ext.h>
 #include <string.h>
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/ddt.h"
 #include "ddt_device.hpp"
@@ -11,6 +12,12 @@
 #include "ddt_tree_kernels.hpp"
 #include "ddt_attention.hpp"
 #include "ddt_kvcache.hpp"
+
+// Chunk partials of ddt_row_topk_noalloc: one fixed array per device (each
+// device that loads the library holds its own copy until the process ends).
+// In host code this name is only a host-side stand-in; kernels and copies
+// get the device address taken by hipGetSymbolAddress (scratch_ptr below).
+static __device__ __align__(256) uint8_t scratch[DDT_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -96,6 +103,35 @@ int g_pairs = 0, g_used = 0;
 
 // polls before a T > 0 walk's cross-workgroup wait gives up (ddt_set_walk_spin_limit)
 unsigned g_walk_spin_limit = WALK_SPIN_LIMIT;
+
+// Device address of `scratch` on the device of `stream` (the current device
+// for the null stream), taken once per device with that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_ptr(void* stream, void** out) {
+    int cur = 0, dev = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return DDT_ELAUNCH;
+    dev = cur;
+    if (stream != nullptr) {
+        hipDevice_t d = 0;
+        if (hipStreamGetDevice((hipStream_t)stream, &d) != hipSuccess) return DDT_EINVAL;
+        dev = (int)d;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return DDT_ECAPACITY;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return DDT_ELAUNCH;
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) (void)hipSetDevice(cur);
+        if (e != hipSuccess || p == nullptr) return DDT_ELAUNCH;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DDT_OK;
+}
 
 // Workgroups of the verify kernel the device holds at once (cached per device).
 int resident_verify_blocks() {
@@ -604,6 +640,23 @@ int ddt_row_topk(const ddt_logits* x, int n0, int n1, int K, int32_t* ids, float
     a.ids = ids; a.logc = logc; a.rmax = rmax; a.rsp = rsp;
     hipLaunchKernelGGL(k_row_finish, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
     return launched();
+}
+
+int ddt_row_topk_noalloc(const ddt_logits* x, int n0, int n1, int K, int32_t* ids, float* logc,
+                         float* rmax, float* rsp, void* stream) {
+    if (!logits_ok(x) || n0 < 0 || n1 < 0) return DDT_EINVAL;
+    if (x->dtype != DDT_F32 && x->dtype != DDT_BF16) return DDT_EDTYPE;
+    if (K < 1 || K > x->V) return DDT_EINVAL;
+    if (K > DDT_MAX_K || chunks_of(x->V, x->dtype) > DDT_MAX_CHUNKS) return DDT_ECAPACITY;
+    const long long rows = (long long)n0 * n1;
+    if (ws_need(rows, x->V, x->dtype, K) > (size_t)DDT_NOALLOC_SCRATCH_BYTES) return DDT_ECAPACITY;
+    if (rows == 0) return DDT_OK;
+    void* ws = nullptr;
+    const int st = scratch_ptr(stream, &ws);
+    if (st) return st;
+    // every partial the finish kernel reads is written by this call first:
+    // nothing in the array has to start at zero
+    return ddt_row_topk(x, n0, n1, K, ids, logc, rmax, rsp, ws, DDT_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

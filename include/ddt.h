@@ -540,6 +540,26 @@ int ddt_row_topk(const ddt_logits* x /*host*/, int n0, int n1, int K, int32_t* i
                  float* rmax, float* rsp, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * ddt_row_topk_noalloc -- ddt_row_topk for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the chunk partials go to a fixed array of
+ * DDT_NOALLOC_SCRATCH_BYTES inside the library, one per device, held until
+ * the process ends, instead of a caller workspace.  Same arguments, outputs
+ * and kernels as ddt_row_topk without ws.  The caller still owns x and the
+ * outputs.  Nothing is allocated or freed; the array's device address is
+ * looked up once per device, on the first call (DDT_ELAUNCH if that fails).
+ * Errors as ddt_row_topk, and DDT_ECAPACITY when the partials would exceed
+ * the array: ddt_workspace_bytes(n0*n1, V, dtype, K) > DDT_NOALLOC_SCRATCH_BYTES
+ * (e.g. 1024 rows of 128256 bf16 logits fit up to K = 32).  All calls on one
+ * device share the array: calls that overlap in time on a device (on
+ * different streams, or from several threads) race and must be ordered by
+ * the caller.
+ */
+#define DDT_NOALLOC_SCRATCH_BYTES (8u << 20)
+int ddt_row_topk_noalloc(const ddt_logits* x /*host*/, int n0, int n1, int K, int32_t* ids,
+                         float* logc, float* rmax, float* rsp, void* stream);
+
+/*
  * ddt_set_reduce_events -- timing hook for the vocabulary-wide row reduction.
  * While set, the i-th launch of that kernel (any call, any stream), i <
  * n_pairs, is launched with events[2i] and events[2i+1] as its start and stop
