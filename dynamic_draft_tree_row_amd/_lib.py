@@ -24,7 +24,7 @@ class Tree(C.Structure):
                 ("layer_base", P), ("n_front", P), ("frontier", P), ("front_S", P), ("front_key", P),
                 ("active", P),
                 ("k_draft", P), ("cont", P), ("widths", P), ("cast_state", P), ("ticket", P),
-                ("walk_buf", P), ("walk_sync", P)]
+                ("walk_buf", P), ("walk_sync", P), ("layer_sync", P)]
 
 
 class Flat(C.Structure):

@@ -10,6 +10,7 @@
 #include "ddt_device.hpp"
 #include "ddt_rowreduce.hpp"
 #include "ddt_tree_kernels.hpp"
+#include "ddt_layer.hpp"
 #include "ddt_attention.hpp"
 #include "ddt_kvcache.hpp"
 
@@ -62,7 +63,7 @@ int check_tree(const ddt_tree* t) {
         t->front_S == nullptr || t->front_key == nullptr ||
         t->active == nullptr || t->k_draft == nullptr || t->cont == nullptr ||
         t->widths == nullptr || t->cast_state == nullptr || t->ticket == nullptr ||
-        t->walk_buf == nullptr || t->walk_sync == nullptr)
+        t->walk_buf == nullptr || t->walk_sync == nullptr || t->layer_sync == nullptr)
         return DDT_EINVAL;
     if (t->B < 1 || t->cap < 2 || t->D_max < 1 || t->R_max < 1) return DDT_EINVAL;
     if (t->cap > DDT_MAX_NODES || t->D_max > DDT_MAX_DEPTH || t->R_max > DDT_MAX_FRONT)
@@ -147,6 +148,21 @@ int resident_verify_blocks() {
     return cache[dev];
 }
 
+// Launch with the reduction timing hook (ddt_set_reduce_events): while it is
+// set, the runtime stamps the next event pair at the kernel's own start and
+// end.
+template <class Kern, class... Args>
+int launch_timed(Kern kern, dim3 grid, dim3 blk, size_t lds, hipStream_t s, Args... args) {
+    if (g_events != nullptr && g_used < g_pairs) {
+        hipEvent_t e0 = (hipEvent_t)g_events[2 * g_used], e1 = (hipEvent_t)g_events[2 * g_used + 1];
+        hipExtLaunchKernelGGL(kern, grid, blk, lds, s, e0, e1, 0, args...);
+        ++g_used;
+        return launched();
+    }
+    hipLaunchKernelGGL(kern, grid, blk, lds, s, args...);
+    return launched();
+}
+
 int launch_partials(const ddt_logits* x, int n0, int n1, const int32_t* count, int count_add,
                     int K, void* ws, hipStream_t s, const float* sum_if = nullptr) {
     RowSrc rs{};
@@ -162,16 +178,7 @@ int launch_partials(const ddt_logits* x, int n0, int n1, const int32_t* count, i
     uint32_t* part = (uint32_t*)ws;
     auto kern = bf16 ? (wide ? &k_row_partial<true, RR_NV_WIDE> : &k_row_partial<true, RR_NV>)
                      : (wide ? &k_row_partial<false, RR_NV_WIDE> : &k_row_partial<false, RR_NV>);
-    if (g_events != nullptr && g_used < g_pairs) {
-        // timed: the runtime stamps the two events at the kernel's own start and end
-        hipEvent_t e0 = (hipEvent_t)g_events[2 * g_used], e1 = (hipEvent_t)g_events[2 * g_used + 1];
-        hipExtLaunchKernelGGL(kern, grid, blk, 0, s, e0, e1, 0, rs, x->V, groups, K, part);
-        ++g_used;
-        return launched();
-    }
-    hipLaunchKernelGGL(kern, grid, blk, 0, s, rs, x->V, groups, K, part);
-    const int st = launched();
-    return st;
+    return launch_timed(kern, grid, blk, 0, s, rs, x->V, groups, K, part);
 }
 
 }  // namespace
@@ -231,6 +238,7 @@ size_t ddt_tree_bytes(int B, int cap, int D_max, int R_max) {
     n += align256(4);                                          // ticket
     n += align256((size_t)B * DDT_WALK_STRIDE * 8);            // walk_buf
     n += align256((size_t)B * 2 * 4);                          // walk_sync
+    n += align256(((size_t)B * R_max + B) * 4);                // layer_sync
     return n;
 }
 
@@ -266,6 +274,7 @@ int ddt_tree_bind(ddt_tree* t, void* base, size_t bytes, int B, int cap, int D_m
     t->ticket = carve<uint32_t>(p, 1);
     t->walk_buf = carve<double>(p, (size_t)B * DDT_WALK_STRIDE);
     t->walk_sync = carve<uint32_t>(p, (size_t)B * 2);
+    t->layer_sync = carve<uint32_t>(p, (size_t)B * R_max + B);
     return DDT_OK;
 }
 
@@ -321,21 +330,30 @@ int ddt_tree_expand(const ddt_tree* t, int layer, const int32_t* root_tok, const
         return DDT_EWORKSPACE;
     hipStream_t s = (hipStream_t)stream;
 
-    st = launch_partials(logits, t->B, R, layer == 1 ? nullptr : t->n_front, 0, K_n, ws, s);
-    if (st) return st;
-
-    AttachArgs a;
-    a.t = *t; a.part = (const uint32_t*)ws; a.root_tok = root_tok; a.layer = layer; a.R = R;
-    a.chunks = groups_of((long long)t->B * R, logits->V, logits->dtype); a.K_n = K_n; a.K_e = K_e;
+    // one kernel: chunk partials, row merges and children, the frontier of
+    // every request, CAST's batch rule
+    const long long rows = (long long)t->B * R;
+    LayerArgs a;
+    a.t = *t;
+    if (cast) a.c = *cast; else memset(&a.c, 0, sizeof(a.c));
+    a.base = logits->data; a.s0 = logits->s0; a.s1 = logits->s1;
+    a.part = (uint32_t*)ws; a.root_tok = root_tok;
+    a.V = logits->V; a.groups = groups_of(rows, logits->V, logits->dtype);
+    a.K_n = K_n; a.K_e = K_e; a.R = R; a.layer = layer;
     a.ck = 0; a.kd_ck = 0; a.tau = 0.f; a.gate_on = gate != nullptr; a.K_max = gate ? gate->K_max : 0;
     a.cast_on = cast != nullptr;
-    if (cast) a.c = *cast; else memset(&a.c, 0, sizeof(a.c));
     if (gate != nullptr)
         for (int i = 0; i < gate->n_ck; ++i)
             if (gate->ck_depth[i] == layer) { a.ck = 1; a.kd_ck = gate->k_draft[i]; a.tau = gate->tau[i]; }
-    hipLaunchKernelGGL(k_attach, dim3(t->B), dim3(AT_NT), 0, s, a);
-    if ((st = launched())) return st;
-    return DDT_OK;
+    const long long total = rows * a.groups;
+    if (total > INT32_MAX) return DDT_ECAPACITY;
+    size_t lds = std::max(sizeof(RRLds), (size_t)MRG_SCR * 8);
+    lds = std::max(lds, layer_lds_c(t->R_max, K_n));
+    if (cast) lds = std::max(lds, layer_lds_c(t->R_max, K_n) + layer_lds_d(t->B, t->R_max, cast->M));
+    const bool bf16 = logits->dtype == DDT_BF16, wide = wide_rows(rows);
+    auto kern = bf16 ? (wide ? &k_expand_layer<true, RR_NV_WIDE> : &k_expand_layer<true, RR_NV>)
+                     : (wide ? &k_expand_layer<false, RR_NV_WIDE> : &k_expand_layer<false, RR_NV>);
+    return launch_timed(kern, dim3((unsigned)total), dim3(RR_NT), lds, s, a);
 }
 
 int ddt_tree_rerank(const ddt_tree* t, int m_max, const ddt_cast* cast, int use_k_draft,

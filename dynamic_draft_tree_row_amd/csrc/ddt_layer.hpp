@@ -1,0 +1,248 @@
+// One draft layer in one kernel: vocabulary reduction, row merge, children,
+// frontier and CAST's batch rule.
+//
+// EAGLE-2 explainer, expansion section: every expanded node gets its draft
+// row's top-K_n tokens as children, value(child) = value(parent) x
+// confidence(child), kept here as S_child = S_parent + log c in fp32 (Graft
+// review step 1, S_{d,j} recursion); the next frontier is the best K_e of the
+// newest layer by value (ties: canonical key).  Graft review step 1: at a
+// checkpoint depth a request stops unless exp(max S of the layer) > tau.
+// CAST notes, key designs 2 and 3: the width and depth rule over the whole
+// batch.
+//
+// Grid: one 256-thread workgroup per (request b, frontier slot j, vocabulary
+// chunk g); workgroups of slots past the request's frontier width leave at
+// once.  Nothing waits: each stage is run by the last workgroup to arrive on
+// a device-scope counter ("ticket"), which then resets it.
+//   A. every workgroup reduces its chunk to a partial record;
+//   B. the last chunk of row (b, j) merges the row's partials (one wave)
+//      and writes its K_n children into the tree, and their sort keys (S,
+//      canonical order) over the row's partials, which are no longer needed;
+//   C. the last row of request b ranks the layer's sort keys of b into the
+//      next frontier and closes b's layer (node count, frontier width,
+//      Graft gate);
+//   D. with CAST, the last request runs the batch rule.
+// Every value one workgroup hands to another within the launch (partial
+// records, the new nodes' values, the frontier values and counts, the
+// frontier width) is written with device-coherent stores and read with
+// device-coherent loads (agent-scope atomic accesses, which bypass the
+// caches that are not coherent across the chip), so no cache write-back or
+// invalidation is needed.  Before counting itself in, every wave waits for
+// its stores to complete (a workgroup barrier alone does not wait for other
+// waves' stores).  Values read only by later kernels use plain stores; no
+// address is written by two workgroups of one launch with plain stores.
+#pragma once
+#include "ddt_device.hpp"
+#include "ddt_rowreduce.hpp"
+#include "ddt_tree_kernels.hpp"
+
+struct LayerArgs {
+    ddt_tree t;
+    ddt_cast c;
+    const void* base;            // logits row (b, j) at base + b*s0 + j*s1 elements
+    int64_t s0, s1;
+    uint32_t* part;              // [B*R][groups][2 + 2 K_n] chunk partials
+    const int32_t* root_tok;     // [B], layer 1
+    int V, groups, K_n, K_e, R, layer;
+    int ck, kd_ck, K_max, gate_on, cast_on;   // ck: this layer is a Graft checkpoint
+    float tau;
+};
+
+// Every wave waits for its device-coherent stores to complete, then thread 0
+// counts the workgroup in on *ctr.  Returns true, in every thread, for the
+// last of n arrivals, which resets the counter; its later loads are issued
+// after the count, so its coherent loads see every arrival's stores.
+__device__ __forceinline__ bool ticket_last(uint32_t* ctr, uint32_t n, int& s_flag) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t old = atomicAdd(ctr, 1u);
+        s_flag = old == n - 1u;
+        if (s_flag) atomicExch(ctr, 0u);
+    }
+    __syncthreads();
+    return s_flag != 0;
+}
+
+__device__ __forceinline__ void st_coh_f32(float* p, float v) { rr_st32((uint32_t*)p, __float_as_uint(v)); }
+__device__ __forceinline__ void st_coh_i32(int32_t* p, int32_t v) { rr_st32((uint32_t*)p, (uint32_t)v); }
+__device__ __forceinline__ float ld_coh_f32(const float* p) { return __uint_as_float(rr_ld32<true>((const uint32_t*)p)); }
+__device__ __forceinline__ int32_t ld_coh_i32(const int32_t* p) { return (int32_t)rr_ld32<true>((const uint32_t*)p); }
+
+// Dynamic LDS of the layer kernel: the stages run one after another in a
+// workgroup, so they share one block sized for the largest.
+__host__ __device__ __forceinline__ size_t layer_lds_c(int R_max, int K_n) {
+    return ((size_t)R_max * K_n + R_max) * 8;                      // sort keys, parents' keys
+}
+__host__ __device__ __forceinline__ size_t layer_lds_d(int B, int R_max, int M) {
+    return (size_t)B * R_max * 8 + 16 * 8 + (((size_t)M * R_max + M) * 4 + 7) / 8 * 8;
+}
+
+template <bool BF16, int NL>
+__global__ __launch_bounds__(RR_NT) void k_expand_layer(LayerArgs a) {
+    extern __shared__ __align__(16) unsigned char dyn[];
+    __shared__ int s_flag;
+    const ddt_tree& t = a.t;
+    const int tid = threadIdx.x, lane = tid & (DDT_WAVE - 1), wid = tid / DDT_WAVE;
+    const int g = blockIdx.x % a.groups;
+    const int rowg = blockIdx.x / a.groups;
+    const int b = rowg / a.R, j = rowg - b * a.R;
+    const int layer = a.layer, du = layer - 1;
+    const int nrows = layer == 1 ? 1 : min(max(t.n_front[b], 0), a.R);
+    if (j >= nrows) return;                                       // block-uniform
+    const int Kn = a.K_n, cap = t.cap, Rm = t.R_max;
+    const int PS = rr_ps(Kn);
+    // the row's parent (frontier slot j of the previous layer; the root at
+    // layer 1) and the request's node count, requested now so that they have
+    // arrived by stage B (scalar loads; the previous kernel wrote them)
+    const int jf = layer == 1 ? 0 : j;
+    const int u0 = t.frontier[(size_t)b * Rm + jf];
+    const float pS0 = t.front_S[(size_t)b * Rm + jf];
+    const uint64_t pk0 = t.front_key[(size_t)b * Rm + jf];
+    const int nn0 = t.n_nodes[b];
+    // wave 0: the other rows' parents' keys (the layer's key order is
+    // (parent key, sibling rank))
+    const uint64_t pkl = t.front_key[(size_t)b * Rm + (lane < nrows && layer > 1 ? lane : 0)];
+
+    // ---- A: this workgroup's chunk of row (b, j) ----------------------------
+    const void* row = (const char*)a.base + ((int64_t)b * a.s0 + (int64_t)j * a.s1) * (BF16 ? 2 : 4);
+    uint32_t* prow = a.part + (size_t)rowg * a.groups * PS;
+    rr_chunk<BF16, NL>(row, a.V, g, Kn, true, prow + (size_t)g * PS, *reinterpret_cast<RRLds*>(dyn));
+    if (!ticket_last(t.layer_sync + rowg, (uint32_t)a.groups, s_flag)) return;
+
+    // ---- B: merge row (b, j), attach its children ----------------------------
+    int32_t* tok = t.token + (size_t)b * cap;
+    int32_t* par = t.parent + (size_t)b * cap;
+    int32_t* dep = t.depth + (size_t)b * cap;
+    int32_t* esl = t.eslot + (size_t)b * cap;
+    uint64_t* key = t.key + (size_t)b * cap;
+    float* S = t.S + (size_t)b * cap;
+    float* lc = t.logc + (size_t)b * cap;
+    const int base = layer == 1 ? 1 : nn0;
+    const bool fits = base >= 1 && base + nrows * Kn <= cap;       // capacity guard
+    if (wid == 0) {
+        MergeIn mi;
+        merge_issue<true>(prow, a.groups, Kn, mi);
+        float M, Sp;
+        const uint64_t mine = merge_finish<true>(mi, prow, a.groups, Kn, M, Sp, (uint64_t*)dyn, true);
+        const int u = layer == 1 ? 0 : ((u0 >= 0 && u0 < base) ? u0 : 0);
+        const float pS = layer == 1 ? 0.f : pS0;
+        const uint64_t pk = layer == 1 ? 0ull : pk0;
+        // rank of this row's parent key among the request's parents
+        int prk = 0;
+        for (int k = 0; k < nrows; ++k) prk += readlane_u64(pkl, k) < pk ? 1 : 0;
+        if (fits) {
+            if (layer == 1 && lane == 0) {
+                tok[0] = a.root_tok[b]; par[0] = -1; dep[0] = 0; key[0] = 0ull;
+                S[0] = 0.f; lc[0] = 0.f;
+            }
+            if (lane < Kn) {
+                const float logc = (vkey_val(mine) - M) - log1pf(Sp);
+                const float Sv = pS + logc;
+                const int node = base + j * Kn + lane;
+                tok[node] = vkey_id(mine); par[node] = u; dep[node] = du + 1; esl[node] = -1;
+                S[node] = Sv; lc[node] = logc; key[node] = key_child(pk, du, lane, 0);
+                // sort key (~code(S), parent's key rank * K_n + r): ascending
+                // is (S desc, canonical key asc) within the layer
+                rr_st64((uint64_t*)prow + lane, ((uint64_t)~ord_f32(Sv) << 32) | (uint32_t)(prk * Kn + lane));
+            }
+            if (lane == 0) {
+                esl[u] = j;
+                const size_t ri = ((size_t)b * t.D_max + du) * Rm + j;
+                t.rmax[ri] = M;
+                t.rsp[ri] = Sp;
+            }
+        }
+    }
+    if (!ticket_last(t.layer_sync + (size_t)t.B * Rm + b, (uint32_t)nrows, s_flag)) return;
+
+    // ---- C: request b's frontier ---------------------------------------------
+    {
+        uint64_t* s_sk = (uint64_t*)dyn;                         // [nrows * Kn]
+        uint64_t* s_pk = s_sk + (size_t)Rm * Kn;                 // [nrows]
+        const int count = fits ? nrows * Kn : 0;
+        // every row's sort keys (over its partials) and parents' keys
+        for (int q = tid; q < count; q += RR_NT) {
+            const int jj = q / Kn, r = q - jj * Kn;
+            s_sk[q] = rr_ld64<true>((const uint64_t*)(a.part + (size_t)(b * a.R + jj) * a.groups * PS) + r);
+        }
+        if (tid < nrows) s_pk[tid] = pkl;
+        __syncthreads();
+        // ranks, each counted by SL lanes; rank < R_max makes a frontier record
+        int32_t* fr = t.frontier + (size_t)b * Rm;
+        float* frS = t.front_S + (size_t)b * Rm;
+        uint64_t* frK = t.front_key + (size_t)b * Rm;
+        const int SL = split_lanes(count, RR_NT);
+        const int lg = __ffs(SL) - 1;
+        for (int cb = 0; cb < count; cb += RR_NT >> lg) {
+            const int q = cb + (tid >> lg), part = tid & (SL - 1);
+            uint64_t sk = 0ull;
+            int r = 0;
+            if (q < count) {
+                sk = s_sk[q];
+#pragma unroll 4
+                for (int p = part; p < count; p += SL) r += s_sk[p] < sk ? 1 : 0;
+            }
+            r = group_sum(r, SL);
+            if (part == 0 && q < count && r < Rm) {
+                const float Sv = unord_f32(~(uint32_t)(sk >> 32));
+                const int jj = q / Kn;
+                fr[r] = base + q; st_coh_f32(frS + r, Sv);
+                frK[r] = key_child(layer == 1 ? 0ull : s_pk[jj], du, q - jj * Kn, 0);
+                if (r == 0) {
+                    st_coh_i32(t.n_nodes + b, base + count);
+                    st_coh_i32(t.layer_base + b, base);
+                    int nf = min(a.K_e, count);
+                    if (layer >= t.D_max) nf = 0;
+                    if (layer == 1) {
+                        t.active[b] = 1;
+                        t.k_draft[b] = a.gate_on ? a.K_max : 0;
+                    }
+                    if (a.ck && !(expf(Sv) > a.tau)) {        // g_d = 1[c_d > tau_d]
+                        t.active[b] = 0;
+                        t.k_draft[b] = a.kd_ck;
+                        nf = 0;
+                    }
+                    st_coh_i32(t.n_front + b, nf);
+                }
+            }
+        }
+        if (count == 0 && tid == 0) {
+            if (layer == 1) { st_coh_i32(t.n_nodes + b, 1); st_coh_i32(t.layer_base + b, 1); }
+            st_coh_i32(t.n_front + b, 0);
+        }
+    }
+    if (!a.cast_on) return;
+
+    // ---- D: CAST's batch rule in the last request of the layer ---------------
+    // (with CAST every request has the same frontier width, so all B take
+    // part in every layer that runs).  The inputs that do not depend on the
+    // layer (state, cost-table entries) are staged before the ticket, in an
+    // LDS region past stage C's.
+    const ddt_cast& cp = a.c;
+    const int B = t.B, Mc = cp.M, N = cp.N;
+    CastView L;
+    L.v = (double*)(dyn + layer_lds_c(Rm, Kn));                   // [B][R_max] e^S of the frontiers
+    L.st = L.v + (size_t)B * Rm;                                 // [16] state
+    L.sd = (float*)(L.st + 16);                                  // [M][R_max] S_D columns 1..R_max
+    L.st1 = L.sd + (size_t)Mc * Rm;                              // [M] S_T column 1
+    for (int q = tid; q < Mc * Rm; q += RR_NT) {
+        const int r = q / Rm, k = q - r * Rm;
+        L.sd[q] = k < N ? cp.S_D[(size_t)r * (N + 1) + k + 1] : 0.f;
+    }
+    if (tid < Mc) L.st1[tid] = cp.S_T[(size_t)tid * (N + 1) + 1];
+    if (tid < 11) {
+        // layer 1 starts the state: FIFO {1}, length 1, no previous u_n, context 0
+        L.st[tid] = layer > 1 ? t.cast_state[tid]
+                              : tid == 0 ? 1.0 : tid == 8 ? 1.0 : tid == 9 ? -1.0 : 0.0;
+    }
+    if (!ticket_last(t.ticket, (uint32_t)B, s_flag)) return;
+    for (int q = tid; q < B * Rm; q += RR_NT) L.v[q] = (double)expf(ld_coh_f32(t.front_S + q));
+    int cnt = 0x7FFFFFFF;
+    if (tid < B) cnt = max(0, ld_coh_i32(t.n_nodes + tid) - ld_coh_i32(t.layer_base + tid));
+    __syncthreads();
+    if (wid == 0) {
+        const int kc = (int)wave_min_u32((uint32_t)cnt);
+        cast_decide(L, t, cp, layer, min(min(a.K_e, Rm), kc));
+    }
+}

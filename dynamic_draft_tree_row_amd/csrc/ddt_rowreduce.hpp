@@ -148,29 +148,58 @@ __device__ __forceinline__ float rr_max3(float a, float b, float c) {
 #define RR_X(r, e) (BF16 ? __uint_as_float(((e) & 1) ? ((r)[(e) >> 1] & 0xFFFF0000u) : ((r)[(e) >> 1] << 16)) \
                          : __uint_as_float((r)[(e)]))
 
-// One workgroup reduces one chunk of one row.
+// The partial record's stores are device-coherent (agent-scope atomic
+// stores write through to the level every compute unit reads), so a
+// workgroup of the same kernel can read them once the writer's stores have
+// completed, with no cache write-back.
+__device__ __forceinline__ void rr_st32(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void rr_st64(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Loads of values another workgroup of the same kernel stored that way
+// (COH) read the coherent level too; plain loads otherwise.
+template <bool COH> __device__ __forceinline__ uint32_t rr_ld32(const uint32_t* p) {
+    if constexpr (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else return *p;
+}
+template <bool COH> __device__ __forceinline__ uint64_t rr_ld64(const uint64_t* p) {
+    if constexpr (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else return *p;
+}
+
+// LDS of one chunk reduction (one workgroup of RR_NT threads).
+struct RRLds {
+    uint32_t wmax[RR_NT / DDT_WAVE], wtau[RR_NT / DDT_WAVE];
+    float wsum[RR_NT / DDT_WAVE];
+    int cnt, ties, amin;
+    uint64_t list[RR_CAP];
+    u32x4 stage[(RR_NT / DDT_WAVE) * RR_SW];
+    int sid[(RR_NT / DDT_WAVE) * RR_SW];
+};
+
+// One workgroup reduces chunk g of one row (base `row`, V elements) and
+// writes its partial record to `out`.  Every thread of the workgroup calls
+// it and every thread returns (no early exit), so a caller can go on after
+// it.
 template <bool BF16, int NL>
-__global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int groups, int K,
-                                                       uint32_t* __restrict__ part) {
+__device__ __forceinline__ void rr_chunk(const void* row, int V, int g, int K, bool sums,
+                                         uint32_t* __restrict__ out, RRLds& L) {
     using SH = RRShape<BF16, NL>;
     constexpr int VEC = SH::VEC, CH = SH::CH, NW = RR_NT / DDT_WAVE;
-    __shared__ uint32_t s_wmax[NW], s_wtau[NW];
-    __shared__ float s_wsum[NW];
-    __shared__ int s_cnt, s_ties, s_amin;
-    __shared__ uint64_t s_list[RR_CAP];
-    __shared__ u32x4 s_stage[NW * RR_SW];
-    __shared__ int s_sid[NW * RR_SW];
-
-    const int g = blockIdx.x % groups;
-    const int rowg = blockIdx.x / groups;
-    const int i0 = rowg / rs.n1, i1 = rowg - i0 * rs.n1;
-    if (rs.count != nullptr && i1 >= rs.count[i0] + rs.count_add) return;   // block-uniform
-    const bool sums = rs.sum_if == nullptr || rs.sum_if[i0] > 0.f;        // block-uniform
+    uint32_t* s_wmax = L.wmax;
+    uint32_t* s_wtau = L.wtau;
+    float* s_wsum = L.wsum;
+    int& s_cnt = L.cnt;
+    int& s_ties = L.ties;
+    int& s_amin = L.amin;
+    uint64_t* s_list = L.list;
+    u32x4* s_stage = L.stage;
+    int* s_sid = L.sid;
     const int tid = threadIdx.x, lane = tid & (DDT_WAVE - 1), wid = tid / DDT_WAVE;
-    const int64_t off = (int64_t)i0 * rs.s0 + (int64_t)i1 * rs.s1;
-    const void* row = (const char*)rs.base + off * (BF16 ? 2 : 4);
     const bool al = (((uintptr_t)row) & 15u) == 0;
-    uint32_t* out = part + ((size_t)rowg * groups + g) * rr_ps(K);
     const int start = g * CH;
     // load i covers ids start + (i*NT + tid)*VEC .. +VEC
 #define RR_ID(i, e) (start + ((i) * RR_NT + tid) * VEC + (e))
@@ -214,7 +243,8 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
         bt = s_wtau[w] > bt ? s_wtau[w] : bt;
     }
     if (bmax == 0u) {                                          // chunk range holds no element
-        if (tid < 2 + 2 * K) out[tid] = tid == 0 ? __float_as_uint(-INFINITY) : 0u;
+        if (tid < 2 + 2 * K) rr_st32(out + tid, tid == 0 ? __float_as_uint(-INFINITY) : 0u);
+        __syncthreads();                                       // LDS free for the caller
         return;
     }
     const float M = unord_f32(bmax);
@@ -338,7 +368,7 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
     const int cnt = s_cnt;
     uint64_t* okeys = (uint64_t*)(out + 2);
     if (K == 1) {
-        if (tid == 0) okeys[0] = vkey(M, s_amin);
+        if (tid == 0) rr_st64(okeys, vkey(M, s_amin));
     } else if (cnt <= RR_CAP) {
         // rank counting, each rank counted by S lanes: keys are unique, so
         // rank < K places the key exactly
@@ -354,9 +384,9 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
                 for (int q = part; q < cnt; q += SL) rank += s_list[q] > k ? 1 : 0;
             }
             rank = group_sum(rank, SL);
-            if (part == 0 && c < cnt && rank < K) okeys[rank] = k;
+            if (part == 0 && c < cnt && rank < K) rr_st64(okeys + rank, k);
         }
-        for (int k = cnt + tid; k < K; k += RR_NT) okeys[k] = 0ull;
+        for (int k = cnt + tid; k < K; k += RR_NT) rr_st64(okeys + k, 0ull);
     } else {
         // list overflow (massive ties): exact K rounds, each reading the
         // chunk again one 16-byte word at a time (keeping every element's key
@@ -383,7 +413,7 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
             best = s_list[0];
 #pragma unroll
             for (int w = 1; w < NW; ++w) best = s_list[w] > best ? s_list[w] : best;
-            if (tid == 0) okeys[k] = best;
+            if (tid == 0) rr_st64(okeys + k, best);
             prev = best;
         }
     }
@@ -391,10 +421,26 @@ __global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int gro
         float st = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) st += s_wsum[w];
-        out[0] = __float_as_uint(M);
-        out[1] = __float_as_uint(sums ? st + (float)(s_ties - 1) : 0.f);
+        rr_st32(out, __float_as_uint(M));
+        rr_st32(out + 1, __float_as_uint(sums ? st + (float)(s_ties - 1) : 0.f));
     }
+    __syncthreads();                                           // LDS free for the caller
 #undef RR_ID
+}
+
+// One workgroup reduces one chunk of one row.
+template <bool BF16, int NL>
+__global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int groups, int K,
+                                                       uint32_t* __restrict__ part) {
+    __shared__ RRLds L;
+    const int g = blockIdx.x % groups;
+    const int rowg = blockIdx.x / groups;
+    const int i0 = rowg / rs.n1, i1 = rowg - i0 * rs.n1;
+    if (rs.count != nullptr && i1 >= rs.count[i0] + rs.count_add) return;   // block-uniform
+    const bool sums = rs.sum_if == nullptr || rs.sum_if[i0] > 0.f;        // block-uniform
+    const int64_t off = (int64_t)i0 * rs.s0 + (int64_t)i1 * rs.s1;
+    const void* row = (const char*)rs.base + off * (BF16 ? 2 : 4);
+    rr_chunk<BF16, NL>(row, V, g, K, sums, part + ((size_t)rowg * groups + g) * rr_ps(K), L);
 }
 
 #define MRG_CAP 128                      // candidate list per wave
@@ -429,6 +475,7 @@ struct MergeIn {
 // Every lane loads, from a clamped address inside the row's partials, so that
 // the loads are straight-line code: a load under a branch ends in a register
 // copy that waits for it.  merge_finish masks the lanes past the data.
+template <bool COH = false>
 __device__ __forceinline__ void merge_issue(const uint32_t* __restrict__ p, int groups, int K,
                                             MergeIn& in) {
     const int lane = threadIdx.x & (DDT_WAVE - 1);
@@ -436,21 +483,22 @@ __device__ __forceinline__ void merge_issue(const uint32_t* __restrict__ p, int 
     const int jth = (K + groups - 1) / groups;         // 1 <= jth <= K
     const int total = groups * K;
     const int gl = lane < groups ? lane : 0;
-    in.mc = __uint_as_float(p[gl * PS]);
-    in.sc = __uint_as_float(p[gl * PS + 1]);
+    in.mc = __uint_as_float(rr_ld32<COH>(p + gl * PS));
+    in.sc = __uint_as_float(rr_ld32<COH>(p + gl * PS + 1));
     // sample: the jth best keys of every group (groups * jth <= 64 lanes)
     const int hl = lane < groups * jth ? lane : 0;
     const int hc = hl / jth, he = hl - hc * jth;
-    in.hv = p[hc * PS + 2 + 2 * he + 1];               // high word (value code)
+    in.hv = rr_ld32<COH>(p + hc * PS + 2 + 2 * he + 1);   // high word (value code)
 #pragma unroll
     for (int r = 0; r < MRG_MR; ++r) {
         const int q = lane + r * DDT_WAVE;
         const int qc = q < total ? q : 0;
         const int c = qc / K, e = qc - c * K;
-        in.kk[r] = *(const uint64_t*)(p + c * PS + 2 + 2 * e);
+        in.kk[r] = rr_ld64<COH>((const uint64_t*)(p + c * PS + 2 + 2 * e));
     }
 }
 
+template <bool COH = false>
 __device__ __forceinline__ uint64_t merge_finish(MergeIn& in, const uint32_t* __restrict__ p,
                                                  int groups, int K, float& M, float& Sp,
                                                  uint64_t* scr, bool live) {
@@ -542,7 +590,7 @@ __device__ __forceinline__ uint64_t merge_finish(MergeIn& in, const uint32_t* __
         } else {
             for (int q = lane; q < total; q += DDT_WAVE) {
                 const int c = q / K, e = q - c * K;
-                const uint64_t v = *(const uint64_t*)(p + c * PS + 2 + 2 * e);
+                const uint64_t v = rr_ld64<COH>((const uint64_t*)(p + c * PS + 2 + 2 * e));
                 if (v < prev && v > best) best = v;
             }
         }

@@ -83,53 +83,17 @@ __device__ int anchor_scan_wave(const double* u, const double* c, double C, int 
     return a;
 }
 
-// CAST's batch rule runs in the last workgroup of a layer.  Every workgroup
-// stages the rule's inputs that do not depend on the layer's results (state,
-// the first R_max entries of every cost-table row, M <= DDT_CAST_MAX_M) in
-// LDS at its start, so the last one only loads the rows' frontier values and
-// counts after the layer ticket.
+// CAST's batch rule runs in the last workgroup of a layer, on inputs staged
+// in LDS: the rows' frontier values, the per-round state, and the first
+// R_max entries of every cost-table row (M <= DDT_CAST_MAX_M).
 #define DDT_CAST_MAX_M 64
 
-struct CastLds {
-    double v[64 * DDT_MAX_FRONT];
-    float sd[DDT_CAST_MAX_M * DDT_MAX_FRONT], st1[DDT_CAST_MAX_M];
-    double st[11];
+struct CastView {
+    double* v;        // [B][R_max] e^S of every row's frontier, by rank
+    double* st;       // [11] state: FIFO [0..7], length, previous u_n, context
+    float* sd;        // [M][R_max] S_D[row][1 .. R_max]
+    float* st1;       // [M] S_T[row][1]
 };
-
-// The staged inputs in registers between their loads and their LDS stores.
-// Every thread loads from a clamped address (straight-line code: a load under
-// a branch ends in a register copy that waits for it); cast_store keeps what
-// is in range.
-struct CastIn {
-    double st;                           // state entry min(tid, 10)
-    float sd0, sd1, st1;                 // cost entries tid and tid + NT, S_T[tid][1]
-};
-
-template <int NT>
-__device__ void cast_issue(CastIn& ci, const ddt_tree& t, const ddt_cast& cp, int layer) {
-    static_assert(2 * NT >= DDT_CAST_MAX_M * DDT_MAX_FRONT, "two cost entries per thread");
-    const int tid = threadIdx.x, R = t.R_max, MR = cp.M * R, N = cp.N;
-    ci.st = t.cast_state[tid < 11 ? tid : 10];
-    const int q0 = tid < MR ? tid : 0, q1 = tid + NT < MR ? tid + NT : 0;
-    const int r0 = q0 / R, k0 = min(q0 - r0 * R, N - 1);
-    const int r1 = q1 / R, k1 = min(q1 - r1 * R, N - 1);
-    ci.sd0 = cp.S_D[(size_t)r0 * (N + 1) + k0 + 1];
-    ci.sd1 = cp.S_D[(size_t)r1 * (N + 1) + k1 + 1];
-    ci.st1 = cp.S_T[(size_t)(tid < cp.M ? tid : 0) * (N + 1) + 1];
-}
-
-template <int NT>
-__device__ void cast_store(CastLds& L, const CastIn& ci, const ddt_tree& t, const ddt_cast& cp,
-                           int layer) {
-    const int tid = threadIdx.x, R = t.R_max, MR = cp.M * R;
-    if (tid < 11) {
-        // layer 1 starts the state: FIFO {1}, length 1, no previous u_n, context 0
-        L.st[tid] = layer > 1 ? ci.st : tid == 0 ? 1.0 : tid == 8 ? 1.0 : tid == 9 ? -1.0 : 0.0;
-    }
-    if (tid < MR) L.sd[tid] = tid % R < cp.N ? ci.sd0 : 0.f;
-    if (tid + NT < MR) L.sd[tid + NT] = (tid + NT) % R < cp.N ? ci.sd1 : 0.f;
-    if (tid < cp.M) L.st1[tid] = ci.st1;
-}
 
 // Wave-level helpers for the batch rule (wave 0, all 64 lanes active).
 // x from lane l (l wave-uniform), through scalar registers.
@@ -200,7 +164,7 @@ __device__ __forceinline__ int anchor_scan_regs(double u, double c, double C, in
 // then the depth gate with the gain FIFO; every row's n_front gets the
 // result.  Item k (1-based) lives in lane k - 1: u_k, c_k in registers; the
 // anchor scan works on ballot masks and the FIFO on lanes 0..7.
-__device__ void cast_decide(CastLds& L, const ddt_tree& t, const ddt_cast& cp, int layer, int kcap) {
+__device__ void cast_decide(const CastView& L, const ddt_tree& t, const ddt_cast& cp, int layer, int kcap) {
     const int lane = threadIdx.x & (DDT_WAVE - 1), B = t.B, R = t.R_max;
     if (layer == 1 && lane < t.D_max) t.widths[lane] = 0;
     const int ctx = (int)L.st[10];
@@ -247,211 +211,16 @@ __device__ void cast_decide(CastLds& L, const ddt_tree& t, const ddt_cast& cp, i
         t.widths[layer - 1] = n;
         t.cont[0] = stop ? 0 : 1;
     }
-    if (lane < B) t.n_front[lane] = stop ? 0 : n;
-}
-
-// The batch rule in the last workgroup of a layer: every thread loads the
-// rows' frontier values, wave 0 the row counts, all together with the
-// batch's continue flag (one round trip); then wave 0 decides, or, when an
-// earlier layer stopped the batch, every row's frontier is cleared.
-template <int NT>
-__device__ void cast_layer(CastLds& L, const ddt_tree& t, const ddt_cast& cp, int layer, int K_e) {
-    const int tid = threadIdx.x, B = t.B, R = t.R_max;
-    const int cont = t.cont[0];
-    for (int q = tid; q < B * R; q += NT) L.v[q] = (double)expf(t.front_S[q]);
-    int cnt = 0x7FFFFFFF;
-    if (tid < B) cnt = max(0, t.n_nodes[tid] - t.layer_base[tid]);
-    __syncthreads();
-    if (!cont) {
-        for (int bb = tid; bb < B; bb += NT) t.n_front[bb] = 0;
-        return;
-    }
-    if (tid < DDT_WAVE) {
-        const int kc = (int)wave_min_u32((uint32_t)cnt);
-        cast_decide(L, t, cp, layer, min(min(K_e, R), kc));
-    }
+    // the frontier width goes out device-coherent: the requests' own stage
+    // of the same launch stored it that way before
+    if (lane < B) __hip_atomic_store(t.n_front + lane, stop ? 0 : n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
-// attach: merge the layer's row partials, create children, pick the frontier
+// the draft layer (reduction, children, frontier, CAST) is k_expand_layer in
+// ddt_layer.hpp; AT_SORT bounds the nodes one layer of a request creates
 // ---------------------------------------------------------------------------
-//
-// EAGLE-2 explainer, expansion section: every expanded node gets its draft
-// row's top-K_n tokens as children, value(child) = value(parent) x
-// confidence(child), kept here as S_child = S_parent + log c in fp32 (Graft
-// review step 1, S_{d,j} recursion).  The next frontier is the best K_e of
-// the newest layer by value (ties: canonical key), found by rank counting.
-// Graft review step 1: at a checkpoint depth the row stops unless
-// exp(max S of the layer) > tau.  With CAST, the last workgroup to finish the
-// layer (device-scope counter) runs the batch-wide width and depth rule.
-//
-// Latency layout: every global input of the layer (the partials of all R
-// slots, merged speculatively, one wave per slot; the row counters; the
-// frontier's node, S and key, stored by the previous layer) is requested in
-// one round before the first barrier; ranks are counted branch-free.
-
-struct AttachArgs {
-    ddt_tree t;
-    ddt_cast c;
-    const uint32_t* part;
-    const int32_t* root_tok;
-    int layer, R, chunks, K_n, K_e;
-    int ck, kd_ck, K_max, gate_on, cast_on;  // ck: 1 if this layer is a Graft checkpoint
-    float tau;
-};
-
-#define AT_NT 1024
 #define AT_SORT 1024
-
-__global__ __launch_bounds__(AT_NT) void k_attach(AttachArgs a) {
-    const ddt_tree& t = a.t;
-    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int cap = t.cap, Rm = t.R_max, Kn = a.K_n;
-    __shared__ float s_M[DDT_MAX_FRONT], s_S[DDT_MAX_FRONT], s_l1p[DDT_MAX_FRONT];
-    __shared__ int s_pn[DDT_MAX_FRONT];
-    __shared__ float s_pS[DDT_MAX_FRONT];
-    __shared__ uint64_t s_pk[DDT_MAX_FRONT];
-    __shared__ uint64_t s_key[DDT_MAX_FRONT * DDT_MAX_K];
-    __shared__ uint64_t s_sk[AT_SORT];
-    __shared__ uint64_t s_scr[AT_NT / 64][MRG_SCR];
-    __shared__ int s_last;
-    __shared__ CastLds s_cast;
-
-    int32_t* tok = t.token + (size_t)b * cap;
-    int32_t* par = t.parent + (size_t)b * cap;
-    int32_t* dep = t.depth + (size_t)b * cap;
-    int32_t* esl = t.eslot + (size_t)b * cap;
-    uint64_t* key = t.key + (size_t)b * cap;
-    float* S = t.S + (size_t)b * cap;
-    float* lc = t.logc + (size_t)b * cap;
-    int32_t* fr = t.frontier + (size_t)b * Rm;
-    float* frS = t.front_S + (size_t)b * Rm;
-    uint64_t* frK = t.front_key + (size_t)b * Rm;
-
-    // first load trip: every global input of the layer is requested before anything
-    // waits on one: the request's counters (scalar), the frontier records, the
-    // CAST inputs and, for wave j, the partials of slot j
-    const int nf0 = a.layer == 1 ? 1 : t.n_front[b];
-    const int nn0 = a.layer == 1 ? 1 : t.n_nodes[b];
-    // (straight-line loads from clamped addresses: a load under a branch ends
-    // in a register copy that waits for it)
-    const int tf = tid < Rm ? tid : 0;
-    const int r_pn = fr[tf];
-    const float r_pS = frS[tf];
-    const uint64_t r_pk = frK[tf];
-    CastIn ci;
-    if (a.cast_on) cast_issue<AT_NT>(ci, t, a.c, a.layer);
-    MergeIn mi;
-    merge_issue(a.part + ((size_t)(b * a.R + (wid < a.R ? wid : 0)) * a.chunks) * rr_ps(Kn), a.chunks, Kn, mi);
-    // LDS staging from registers
-    if (a.layer == 1) {
-        if (tid == 0) {
-            tok[0] = a.root_tok[b]; par[0] = -1; dep[0] = 0; esl[0] = -1; key[0] = 0ull;
-            S[0] = 0.f; lc[0] = 0.f;
-            t.active[b] = 1;
-            t.k_draft[b] = a.gate_on ? a.K_max : 0;
-            if (a.cast_on && b == 0) t.cont[0] = 1;
-            s_pn[0] = 0; s_pS[0] = 0.f; s_pk[0] = 0ull;
-        }
-    } else if (tid < a.R) {
-        s_pn[tid] = r_pn; s_pS[tid] = r_pS; s_pk[tid] = r_pk;
-    }
-    if (a.cast_on) cast_store<AT_NT>(s_cast, ci, t, a.c, a.layer);
-    // merges: wave j takes slot j.  Slots past the row's frontier width hold no
-    // partials of this layer: their loads went out with the others, and the
-    // width stops the merge work there.
-    for (int j = wid; j < a.R; j += AT_NT / 64) {
-        float M, Sp;
-        const uint32_t* p = a.part + ((size_t)(b * a.R + j) * a.chunks) * rr_ps(Kn);
-        const uint64_t mine = j == wid ? merge_finish(mi, p, a.chunks, Kn, M, Sp, s_scr[wid], j < nf0)
-                                       : merge_row_wave(p, a.chunks, Kn, M, Sp, s_scr[wid], j < nf0);
-        if (lane < Kn) s_key[j * Kn + lane] = mine;
-        if (lane == 0) { s_M[j] = M; s_S[j] = Sp; s_l1p[j] = log1pf(Sp); }
-    }
-    __syncthreads();
-    const int base = nn0;
-    int Rd = min(max(nf0, 0), a.R);
-    if (base < 1 || base + Rd * Kn > cap) Rd = 0;          // capacity guard
-    const int count = Rd * Kn;
-    const int du = a.layer - 1;                            // depth of every frontier node
-    for (int q = tid; q < count; q += AT_NT) {
-        const int j = q / Kn, r = q - j * Kn;
-        const int u0 = s_pn[j];
-        const int u = (u0 >= 0 && u0 < base) ? u0 : 0;
-        const uint64_t kk = s_key[j * Kn + r];
-        const float logc = (vkey_val(kk) - s_M[j]) - s_l1p[j];
-        const float Sv = s_pS[j] + logc;
-        const uint64_t pk = s_pk[j];
-        const uint64_t nk = key_child(pk, du, r, 0);
-        const int node = base + q;
-        tok[node] = vkey_id(kk); par[node] = u; dep[node] = du + 1; esl[node] = -1;
-        S[node] = Sv; lc[node] = logc; key[node] = nk;
-        // the layer's canonical-key order is (parent key, sibling rank): the
-        // parent's rank among the slots' keys makes a 64-bit sort key
-        int pr = 0;
-#pragma unroll 8
-        for (int jj = 0; jj < Rd; ++jj) pr += s_pk[jj] < pk ? 1 : 0;
-        s_sk[q] = ((uint64_t)~ord_f32(Sv) << 32) | (uint32_t)(pr * Kn + r);
-        if (r == 0) {
-            esl[u] = j;
-            const size_t ri = ((size_t)b * t.D_max + du) * Rm + j;
-            t.rmax[ri] = s_M[j];
-            t.rsp[ri] = s_S[j];
-        }
-    }
-    __syncthreads();
-    // frontier: the first R_max of the layer by (S desc, key asc), each rank
-    // counted by S lanes; the best node's lane closes the row's layer
-    {
-        const int SL = split_lanes(count, AT_NT);      // count <= R_max * K_n <= AT_NT
-        const int lg = __ffs(SL) - 1;
-        const int q = tid >> lg, part = tid & (SL - 1);
-        uint64_t sk = 0ull;
-        int r = 0;
-        if (q < count) {
-            sk = s_sk[q];
-#pragma unroll 4
-            for (int p = part; p < count; p += SL) r += s_sk[p] < sk ? 1 : 0;
-        }
-        r = group_sum(r, SL);
-        if (part == 0 && q < count && r < Rm) {
-            const float Sv = unord_f32(~(uint32_t)(sk >> 32));
-            const int j = q / Kn;
-            fr[r] = base + q; frS[r] = Sv; frK[r] = key_child(s_pk[j], du, q - j * Kn, 0);
-            if (r == 0) {
-                t.n_nodes[b] = base + count;
-                t.layer_base[b] = base;
-                int nf = min(a.K_e, count);
-                if (a.layer >= t.D_max) nf = 0;
-                if (a.ck && !(expf(Sv) > a.tau)) {       // g_d = 1[c_d > tau_d]
-                    t.active[b] = 0;
-                    t.k_draft[b] = a.kd_ck;
-                    nf = 0;
-                }
-                t.n_front[b] = nf;
-            }
-        }
-    }
-    if (count == 0 && tid == 0) {
-        if (a.layer == 1) { t.n_nodes[b] = 1; t.layer_base[b] = 1; }
-        t.n_front[b] = 0;
-    }
-    if (!a.cast_on) return;
-    // the last workgroup of the layer runs CAST for the batch: the barrier
-    // orders the workgroup's stores before thread 0's device-scope release
-    __syncthreads();
-    if (tid == 0) {
-        __threadfence();
-        s_last = atomicAdd(t.ticket, 1u) == gridDim.x - 1;
-        if (s_last) {
-            __threadfence();
-            atomicExch(t.ticket, 0u);
-        }
-    }
-    __syncthreads();
-    if (!s_last) return;
-    cast_layer<AT_NT>(s_cast, t, a.c, a.layer, a.K_e);
-}
 
 // ---------------------------------------------------------------------------
 // rerank: top-m of all non-root nodes by (S desc, key asc)

@@ -125,6 +125,7 @@ typedef struct ddt_tree {
     uint32_t* ticket;    /* [1] CAST: workgroups of a layer done so far (back to 0 after each layer) */
     double* walk_buf;    /* [B][DDT_WALK_STRIDE] T>0 verify: partial sums shared by a request's workgroups */
     uint32_t* walk_sync; /* [B][2] T>0 verify: arrival and exit counters (back to 0 after each call) */
+    uint32_t* layer_sync; /* [B*R_max + B] expand: per-row and per-request arrival counters (back to 0) */
 } ddt_tree;
 
 /* Bytes of device memory a tree of these sizes needs (256-byte aligned base). */
@@ -133,9 +134,10 @@ size_t ddt_tree_bytes(int B, int cap, int D_max, int R_max);
 /*
  * Fill *t with pointers into `base` (device, >= ddt_tree_bytes, 256-byte
  * aligned).  Host-only: touches no device memory.  The memory must be
- * zero-filled once before its first use (the CAST layer counter and the T>0
- * walk counters start at 0 and every call leaves them at 0); the tree itself
- * is (re)initialised by ddt_tree_expand with layer = 1.
+ * zero-filled once before its first use (the layer counters of
+ * ddt_tree_expand, the CAST layer counter and the T>0 walk counters start at
+ * 0 and every call leaves them at 0); the tree itself is (re)initialised by
+ * ddt_tree_expand with layer = 1.
  */
 int ddt_tree_bind(ddt_tree* t /*host*/, void* base, size_t bytes, int B, int cap, int D_max,
                   int R_max);
@@ -238,8 +240,12 @@ size_t ddt_workspace_bytes(int rows, int V, int dtype, int K);
  * them (CAST: the first n_i), unless the row stops (Graft prune, CAST depth
  * gate, or layer = D_max where no frontier is formed).
  *
- * cast and gate are host pointers or NULL (not both).  With cast, the last
- * kernel of the call updates widths/cont/n_front for the whole batch.
+ * cast and gate are host pointers or NULL (not both).  With cast, the
+ * widths/cont/n_front of the whole batch are updated within the call.
+ * One kernel per call: the chunks of every row are reduced in parallel, and
+ * the last chunk of a row, then the last row of a request, then (CAST) the
+ * last request carry on with the merge, the children and frontier, and the
+ * batch rule, counting themselves in on t->layer_sync and t->ticket.
  * Rows reduced per call: B*1 for layer 1, B*R_max after; ws must hold
  * ddt_workspace_bytes(B*R_max, V, dtype, K_n).
  */
@@ -560,8 +566,10 @@ int ddt_row_topk_noalloc(const ddt_logits* x /*host*/, int n0, int n1, int K, in
                          float* logc, float* rmax, float* rsp, void* stream);
 
 /*
- * ddt_set_reduce_events -- timing hook for the vocabulary-wide row reduction.
- * While set, the i-th launch of that kernel (any call, any stream), i <
+ * ddt_set_reduce_events -- timing hook for the kernels that reduce vocabulary
+ * rows: the layer kernel of ddt_tree_expand and the row reduction of
+ * ddt_tree_verify, ddt_row_topk and ddt_succ_update.  While set, the i-th
+ * launch of those (any call, any stream, in launch order), i <
  * n_pairs, is launched with events[2i] and events[2i+1] as its start and stop
  * events (hipExtLaunchKernelGGL: the runtime stamps them when the kernel
  * itself starts and ends); later launches are not timed.  events are
