@@ -36,8 +36,10 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def pmc_file(workload: str) -> str:
-    return os.path.join(PROFILES, f"k_row_partial_traffic_{workload}.json")
-KERNEL_SRC = os.path.join(ROOT, "dynamic_draft_tree_row_amd", "csrc", "ddt_rowreduce.hpp")
+    return os.path.join(PROFILES, f"k_expand_layer_traffic_{workload}.json")
+CSRC = os.path.join(ROOT, "dynamic_draft_tree_row_amd", "csrc")
+KERNEL_SRC = os.path.join(CSRC, "ddt_rowreduce.hpp")
+LAYER_SRC = os.path.join(CSRC, "ddt_layer.hpp")
 
 
 def log(*a):
@@ -100,20 +102,21 @@ def same(a, b) -> bool:
     return all(torch.equal(a[k], b[k]) for k in a)
 
 
-KERNEL_END = "#undef RR_ID\n}\n"   # the end of k_row_partial in its source file
+KERNEL_END = "#undef RR_ID\n}\n"   # the end of the chunk reduction in its source file
 
 
 def kernel_hash() -> str:
-    """Hash of the row-reduction kernel's source: its file up to the end of
-    k_row_partial, which holds the kernel and every helper it calls (the
-    consumers' merge code that follows does not change its traffic)."""
+    """Hash of the expand layer kernel's source: the chunk reduction's file up
+    to the end of rr_chunk (the reduction and every helper it calls) and the
+    layer kernel's own file."""
     text = open(KERNEL_SRC, "rb").read().decode()
     end = text.index(KERNEL_END) + len(KERNEL_END)
-    return hashlib.sha256(text[:end].encode()).hexdigest()[:16]
+    layer = open(LAYER_SRC, "rb").read().decode()
+    return hashlib.sha256((text[:end] + layer).encode()).hexdigest()[:16]
 
 
 def traffic_per_launch(workload: str):
-    """HBM bytes per row-reduction launch from the committed rocprofv3 counter
+    """HBM bytes per expand-layer launch from the committed rocprofv3 counter
     summary, if it was taken on the current kernel source for this workload."""
     try:
         d = json.load(open(pmc_file(workload)))
@@ -121,7 +124,7 @@ def traffic_per_launch(workload: str):
         return None
     if d.get("kernel_sha") != kernel_hash() or d.get("workload") != workload:
         return None
-    return d.get("bytes_per_launch")
+    return d.get("expand_bytes_per_launch")
 
 
 CAL_BYTES = 256 << 20          # the calibration copy: reads and writes this many bytes
@@ -145,36 +148,79 @@ def ingest_pmc(fetch_csv: str, write_csv: str, workload: str, ring: int) -> None
     f = per_dispatch(fetch_csv, "FETCH_SIZE")
     wr = per_dispatch(write_csv, "WRITE_SIZE")
 
-    # the reduction launches of the pmc run's last two eager passes over the
-    # ring: the same per-round launch mix as the event-timed rounds
-    from gen import configs
-    wl = configs.C2 if workload in ("cast_b8_v128256_bf16", "eagle2_b8_v128256_bf16") \
-        else configs.WORKLOADS[workload]
-    n_last = 2 * ring * (wl.D + 1)
-
-    def split(vals):
-        red = [v for (d, n), v in sorted(vals.items()) if "k_row_partial" in n][-n_last:]
+    # the pmc run's two eager passes over the ring: per round D expand-layer
+    # launches and one verify reduction launch
+    def split(vals, name):
+        ks = [v for (d, n), v in sorted(vals.items()) if name in n]
         cal = [v for (d, n), v in sorted(vals.items()) if "neg" in n.lower()]
-        if not red or not cal:
-            raise SystemExit("counter CSV lacks the reduction or the calibration dispatches")
-        return red, cal[-1]
+        if not ks or not cal:
+            raise SystemExit(f"counter CSV lacks {name} or the calibration dispatches")
+        return ks, cal[-1]
 
-    fr, fcal = split(f)
-    wr_, wcal = split(wr)
+    fe, fcal = split(f, "k_expand_layer")
+    we, wcal = split(wr, "k_expand_layer")
+    fv, _ = split(f, "k_row_partial")
+    wv, _ = split(wr, "k_row_partial")
     ff = (CAL_BYTES / 1024.0) / fcal
     wf = (CAL_BYTES / 1024.0) / wcal
-    fetch_b = float(np.mean(fr)) * 1024.0 * ff
-    write_b = float(np.mean(wr_)) * 1024.0 * wf
+    fetch_b = float(np.mean(fe)) * 1024.0 * ff
+    write_b = float(np.mean(we)) * 1024.0 * wf
+    vfetch_b = float(np.mean(fv)) * 1024.0 * ff
+    vwrite_b = float(np.mean(wv)) * 1024.0 * wf
     out = {"workload": workload, "kernel_sha": kernel_hash(),
-           "bytes_per_launch": round(fetch_b + write_b, 1),
-           "fetch_bytes_per_launch": round(fetch_b, 1), "write_bytes_per_launch": round(write_b, 1),
+           "expand_bytes_per_launch": round(fetch_b + write_b, 1),
+           "expand_fetch_bytes_per_launch": round(fetch_b, 1),
+           "expand_write_bytes_per_launch": round(write_b, 1),
+           "verify_bytes_per_launch": round(vfetch_b + vwrite_b, 1),
            "fetch_scale": round(ff, 4), "write_scale": round(wf, 4),
-           "dispatches": [len(fr), len(wr_)],
+           "dispatches": {"expand": [len(fe), len(we)], "verify": [len(fv), len(wv)]},
            "calibration": f"torch.neg over {CAL_BYTES >> 20} MiB fp32 (reads and writes {CAL_BYTES} bytes)"}
     os.makedirs(PROFILES, exist_ok=True)
     with open(pmc_file(workload), "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out))
+
+
+def expand_b64_detail(api, lib, hip, dev, reps: int = 10) -> dict:
+    """One draft layer at the B = 64 workload's shape through ddt_tree_expand:
+    64 requests x 16 frontier rows of V = 128256 bf16 logits (262.7 MB),
+    K_n = 16 children per row, frontier 16.  Each timed layer 2 follows an
+    untimed layer 1 (64 rows) that sets the frontier.  Rows are N(0, 1)
+    scaled per row by U(0.3, 3), generated on the device.  At this many rows the
+    layer runs as the plain reduction and then one workgroup per request; the
+    time spans both launches."""
+    import torch
+    B, R, V, K = 64, 16, 128256, 16
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    x = torch.randn(2, B, R, V, device=dev, generator=g)
+    x.mul_(0.3 + 2.7 * torch.rand(2, B, R, 1, device=dev, generator=g))
+    x = x.to(torch.bfloat16)
+    tree = api.DeviceTree(B, 1 + K + K * K, 2, R, dev)
+    ws = torch.empty(api.workspace_bytes(B * R, V, torch.bfloat16, K), dtype=torch.uint8, device=dev)
+    roots = torch.zeros(B, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        api.tree_expand(tree, 1, roots, x[0], K, R, ws)
+        api.tree_expand(tree, 2, roots, x[1], K, R, ws)
+    torch.cuda.synchronize()
+    evs = hip.events(4 * reps)
+    arr = (C.c_void_p * len(evs))(*[e.value for e in evs])
+    lib.ddt_set_reduce_events(arr, 2 * reps)
+    for _ in range(reps):
+        api.tree_expand(tree, 1, roots, x[0], K, R, ws)
+        api.tree_expand(tree, 2, roots, x[1], K, R, ws)
+    used = lib.ddt_set_reduce_events(None, 0)
+    torch.cuda.synchronize()
+    assert used == 2 * reps
+    us = np.array([hip.elapsed_ms(evs[4 * i + 2], evs[4 * i + 3]) * 1e3 for i in range(reps)])
+    nbytes = B * R * V * 2
+    gbs = nbytes / (us.mean() * 1e-6) / 1e9
+    assert int(tree.n_nodes.min()) == 1 + K + R * K, "layer 2 did not expand every row"
+    del x, tree, ws
+    return {"kernel": "k_row_partial<bf16,8> + k_expand_finish", "rows": B * R, "V": V, "K_n": K,
+            "mb": round(nbytes / 1e6, 1), "us": round(float(us.mean()), 2),
+            "us_min": round(float(us.min()), 2), "gbs": round(float(gbs), 1),
+            "frac": round(float(gbs / PEAK_HBM_GBS), 4)}
 
 
 def tree_attention_detail(api, dev, seed: int = 7, launches: int = 10, B: int = 64, P: int = 129,
@@ -406,7 +452,7 @@ def cast_calibration_detail(w, run, ring, to_dev, dev, slots: int = 2, replays: 
     }
 
 
-def graft_main(args, w) -> None:
+def graft_main(args, w, child) -> None:
     """The Graft workload: prune-then-graft rounds with the successor matrix.
 
     Checkpoint thresholds come from warm-up rounds drafted on the device
@@ -557,16 +603,19 @@ def graft_main(args, w) -> None:
     assert used == per_round * R, f"expected {per_round * R} timed launches, got {used}"
     torch.cuda.synchronize()
     ebytes = w.V * (2 if w.dtype == "bf16" else 4)
-    durs, nbytes = [], []
+    durs, nbytes, vd, vb = [], [], [], []
     for k_s, st in enumerate(stats):
-        rows = st["rows_per_layer"] + [st["verify_rows"]]
         for k in range(per_round):
             i = k_s * per_round + k
-            durs.append(hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) * 1e-3)
-            nbytes.append(rows[k] * ebytes)
+            d = hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) * 1e-3
+            if k < w.D:
+                durs.append(d); nbytes.append(st["rows_per_layer"][k] * ebytes)
+            else:
+                vd.append(d); vb.append(st["verify_rows"] * ebytes)
     durs, nbytes = np.array(durs), np.array(nbytes, dtype=np.float64)
+    vd, vb = np.array(vd), np.array(vb, dtype=np.float64)
     achieved = nbytes.sum() / durs.sum() / 1e9
-    log(f"row reduction: {len(durs)} launches, mean {durs.mean() * 1e6:.2f} us, {achieved:.0f} GB/s")
+    log(f"expand layers: {len(durs)} launches, mean {durs.mean() * 1e6:.2f} us, {achieved:.0f} GB/s")
     expand_bytes = np.mean([sum(st["rows_per_layer"]) for st in stats]) * ebytes
     verify_bytes = np.mean([st["verify_rows"] for st in stats]) * ebytes
     out = {
@@ -583,59 +632,133 @@ def graft_main(args, w) -> None:
                    "timing": "events around each replay; the successor matrix is reset before each"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                     "kernel": "k_row_partial<bf16> (vocab row reduction)",
+                     "kernel": "k_expand_layer<bf16,4> (one draft layer)",
                      "algorithmic_bytes_per_launch": round(float(nbytes.mean()), 1),
                      "avg_launch_us": round(float(durs.mean() * 1e6), 3), "launches": int(len(durs))},
         "logit_gbs": round((expand_bytes + verify_bytes) / round_s / 1e9, 1),
         "detail": {"round_us_p10_p50_p90": [round(float(np.percentile(us, q)), 2) for q in (10, 50, 90)],
+                   "verify_reduction_launch": {
+                       "kernel": "k_row_partial<bf16,8>, K = 8 (argmax and the refresh's top-8 of every verified row)",
+                       "mb": round(float(vb.mean()) / 1e6, 3), "us": round(float(vd.mean() * 1e6), 3),
+                       "gbs": round(float(vb.sum() / vd.sum() / 1e9), 1)},
                    "k_draft": stats[0]["k_draft"], "accept_len": stats[0]["accept"],
                    "mean_tau": round(float(np.mean([np.mean(st["accept"]) + 1 for st in stats])), 3)},
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = graft_cpu_baseline(w, ring[0], gate, M0_np, args.cpu_seconds)
-    else:
-        out["cpu_baseline"] = None
+    out["cpu_baseline"] = collect_oracle(child, {"tau": tau}) if child is not None else None
     print(json.dumps(out), flush=True)
 
 
-def graft_cpu_baseline(w, slot, gate, M0_np, seconds):
-    """The oracle on one core, on ring slot 0's inputs, each round from the
-    initial successor matrix."""
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle in a child process on one core
+# ---------------------------------------------------------------------------
+
+THREAD_ENV = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "NUMEXPR_NUM_THREADS",
+              "BLIS_NUM_THREADS")
+
+
+def resolve_workload(args):
+    from gen import configs
+    w = configs.C2
+    if args.workload == "fixed":
+        w = configs.Workload(**{**w.__dict__, "cast": None, "name": "eagle2_b8_v128256_bf16"})
+    elif args.workload:
+        w = configs.WORKLOADS[args.workload]
+    if args.break_even and w.cast is not None:
+        w = configs.Workload(**{**w.__dict__, "cast": configs.CastSpec(**configs.BREAK_EVEN)})
+    return w
+
+
+def spawn_oracle(args):
+    """Start the CPU-baseline child before this process touches the GPU: a
+    fresh interpreter with single-threaded BLAS, which builds ring slot 0's
+    inputs itself, waits for one line on stdin (parameters the GPU side
+    calibrated, e.g. Graft thresholds), pins itself to one core and times the
+    oracle.  It never imports torch."""
+    import subprocess
+    env = dict(os.environ)
+    for k in THREAD_ENV:
+        env[k] = "1"
+    cmd = [sys.executable, os.path.abspath(__file__), "--oracle-child", "--cpu-seconds", str(args.cpu_seconds)]
+    if args.workload:
+        cmd += ["--workload", args.workload]
+    if args.break_even:
+        cmd.append("--break-even")
+    return subprocess.Popen(cmd, stdin=subprocess.PIPE, stdout=subprocess.PIPE, env=env, text=True)
+
+
+def collect_oracle(child, params=None, timeout=900):
+    """Send the go line (after every GPU measurement, so the child's timed
+    span never overlaps this process's work) and read the child's JSON."""
+    out, _ = child.communicate(json.dumps(params or {}) + "\n", timeout=timeout)
+    lines = [l for l in out.splitlines() if l.startswith("{")]
+    if child.returncode != 0 or not lines:
+        raise RuntimeError(f"oracle baseline child failed (exit {child.returncode})")
+    return json.loads(lines[-1])
+
+
+def oracle_layout(trees, flats, P):
+    """Per flat position of the oracle's own trees: key, depth, expand slot,
+    token (how the synthetic target rows are laid out)."""
+    B = len(flats)
+    fk = np.full((B, P), -1, np.int64)
+    fd = np.zeros((B, P), np.int32)
+    fs = np.full((B, P), -1, np.int32)
+    ft = np.full((B, P), -1, np.int32)
+    for b, (t, f) in enumerate(zip(trees, flats)):
+        for i, v in enumerate(f.node):
+            if v >= 0:
+                fk[b, i], fd[b, i], fs[b, i], ft[b, i] = t.key[v], t.depth[v], t.eslot[v], t.token[v]
+    return fk, fd, fs, ft
+
+
+def oracle_child(args) -> None:
+    """The child's side of spawn_oracle: the oracle as it stands, single
+    threaded, timed on ring slot 0 of the same workload for about
+    args.cpu_seconds; input generation is outside the timed span."""
+    from gen import synth
     from oracle import ddt_oracle as O
-    gs = w.graft
-    d_np = slot["draft_np"]
-    graft = dict(ck_depth=tuple(gs.ck_depth), tau=list(gate.tau), k_draft=tuple(gs.k_draft), K_max=gs.K_max)
+    w = resolve_workload(args)
+    r = 0
+    d_np = synth.draft_arena(w, SEED, r)
+    roots = synth.root_tokens(w, SEED, r)
+    T = synth.temperatures(w, SEED, r)
+    U = synth.uniforms(w, SEED, r)
+    cast = None
+    if w.cast is not None:
+        S_T, S_D = synth.cost_tables(w)
+        cs = w.cast
+        cast = dict(S_T=S_T, S_D=S_D, L=cs.L, M=cs.M, C1=[cs.C1] * w.D, C2=cs.C2, C3=[cs.C3] * w.B, R=cs.R)
+    params = json.loads(sys.stdin.readline() or "{}")
+    graft, M0, kw = None, None, {}
+    if w.graft is not None:
+        gs = w.graft
+        graft = dict(ck_depth=tuple(gs.ck_depth), tau=list(params["tau"]), k_draft=tuple(gs.k_draft),
+                     K_max=gs.K_max)
+        M0 = synth.succ_matrix0(w, SEED)
+        kw = dict(k_succ=gs.k_succ, tpl=(gs.tpl_depth, gs.tpl_width))
+    held = {}
+
+    def first_target(dr, flats):
+        fk, fd, fs, ft = oracle_layout(dr.trees, flats, w.m_max + 1)
+        held["t"] = synth.target_arena(w, SEED, r, d_np, fk, fd, fs, ft, None, M0)
+        return held["t"]
+
+    def one(tfn):
+        O.run_round(B=w.B, V=w.V, dtype=w.dtype, D=w.D, K_e=w.K_e, K_n=w.K_n, m_max=w.m_max,
+                    root_tok=roots, draft_raw=d_np, target_raw_fn=tfn, temperature=T, U=U,
+                    prefix=w.prefix, cast=cast, graft=graft, M=None if M0 is None else M0.copy(),
+                    proposal=w.proposal, **kw)
+
+    one(first_target)
+    core = min(os.sched_getaffinity(0))
+    os.sched_setaffinity(0, {core})
     t0 = time.perf_counter()
     n = 0
     while True:
-        O.run_round(B=w.B, V=w.V, dtype=w.dtype, D=w.D, K_e=w.K_e, K_n=w.K_n, m_max=w.m_max,
-                    root_tok=slot["roots_np"], draft_raw=d_np, target_raw_fn=lambda dr, flats: slot["target_np"],
-                    temperature=slot["T_np"], U=slot["U_np"], prefix=w.prefix, graft=graft,
-                    M=M0_np.copy(), k_succ=gs.k_succ, tpl=(gs.tpl_depth, gs.tpl_width))
+        one(lambda dr, flats: held["t"])
         n += 1
         el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": n / el, "unit": "rounds/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} rounds of the Graft workload (ring slot 0, {el:.1f} s, single thread, float64 numpy; "
-                      f"input generation excluded)"}
-
-
-def cpu_baseline(w, slot, cast_np, seconds):
-    """The oracle as it stands, on one core, on ring slot 0's inputs."""
-    from oracle import ddt_oracle as O
-    def one():
-        O.run_round(B=w.B, V=w.V, dtype=w.dtype, D=w.D, K_e=w.K_e, K_n=w.K_n, m_max=w.m_max,
-                    root_tok=slot["roots_np"], draft_raw=slot["draft_np"],
-                    target_raw_fn=lambda dr, flats: slot["target_np"],
-                    temperature=slot["T_np"], U=slot["U_np"], prefix=w.prefix, cast=cast_np)
-    t0 = time.perf_counter()
-    n = 0
-    while True:
-        one()
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
+        if el >= args.cpu_seconds:
             break
     cpu = "unknown cpu"
     try:
@@ -645,9 +768,13 @@ def cpu_baseline(w, slot, cast_np, seconds):
                 break
     except OSError:
         pass
-    return {"value": n / el, "unit": "rounds/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} rounds of the same workload (ring slot 0, {el:.1f} s, single thread "
-                      f"of {os.cpu_count()} on {cpu}, float64 numpy; input generation excluded)"}
+    print(json.dumps({
+        "value": round(n / el, 3), "unit": "rounds/s", "cores": 1, "kind": "oracle",
+        "core": core, "cpu": cpu, "host_cpus": os.cpu_count(),
+        "threads_env": {k: os.environ.get(k) for k in THREAD_ENV[:3]},
+        "sample": f"{n} rounds of {w.name} (ring slot 0, seed {SEED}; {el:.1f} s) in a child process "
+                  f"pinned to core {core} with single-threaded BLAS, float64 numpy oracle; input "
+                  f"generation excluded; started after every GPU measurement"}), flush=True)
 
 
 def main():
@@ -675,11 +802,16 @@ def main():
                          "plain 256 MiB copy (torch.neg, fp32) whose counters scale the bytes")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: turn the two --pmc passes' counter CSVs into "
-                         "profiles/k_row_partial_traffic_<workload>.json")
+                         "profiles/k_expand_layer_traffic_<workload>.json")
+    ap.add_argument("--oracle-child", action="store_true",
+                    help="internal: the CPU-baseline child process (no GPU)")
     ap.add_argument("--workload", default=None,
                     help="profile another workload instead (e.g. eagle2_mixed_b64_v128256_bf16, "
                          "graft_b16_v152064_bf16; 'fixed' = the CAST shape with fixed EAGLE-2 widths)")
     args = ap.parse_args()
+    if args.oracle_child:
+        oracle_child(args)
+        return
     if args.ingest_pmc:
         ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.workload or "cast_b8_v128256_bf16", args.ring)
         return
@@ -687,6 +819,11 @@ def main():
         log("bench.py measures one GPU only: there is no multi-GPU path (batch rows "
             "would shard across GPUs, one process each; not built).")
         sys.exit(2)
+
+    # the CPU baseline's child starts before this process touches the GPU
+    child = None
+    if not (args.no_cpu_baseline or args.pmc_run or args.pmc_attention):
+        child = spawn_oracle(args)
 
     import torch
     from gen import configs, synth
@@ -706,15 +843,9 @@ def main():
         log(f"pmc attention run done: 5 launches, then a {CAL_BYTES >> 20} MiB copy (neg)")
         return
 
-    w = configs.C2
-    if args.workload == "fixed":
-        w = configs.Workload(**{**w.__dict__, "cast": None, "name": "eagle2_b8_v128256_bf16"})
-    elif args.workload:
-        w = configs.WORKLOADS[args.workload]
-        if w.graft is not None:
-            return graft_main(args, w)
-    if args.break_even:
-        w = configs.Workload(**{**w.__dict__, "cast": configs.CastSpec(**configs.BREAK_EVEN)})
+    w = resolve_workload(args)
+    if w.graft is not None:
+        return graft_main(args, w, child)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     lib = _lib.load()
@@ -845,12 +976,15 @@ def main():
     torch.cuda.synchronize()
     eager_us = (time.perf_counter() - t0) * 1e6 / ne
 
-    # ---- dominant kernel: the vocabulary-wide row reduction ----------------
-    # Per round: D expand launches + 1 verify launch.  The library launches
-    # them with start/stop events that the runtime stamps at the kernel's own
-    # start and end (ddt_set_reduce_events).  Events inside a captured graph
-    # are not valid timing events on this runtime, so the launches are timed
-    # in eager rounds of the same ring slots, on the same stream.
+    # ---- dominant kernel: the expand layer ----------------------------------
+    # Per round: D expand-layer launches (k_expand_layer: the vocabulary
+    # reduction of the layer's draft rows, their merge and children, the
+    # frontier and CAST's rule), then the verify reduction (k_row_partial,
+    # K = 1 over every flat row).  The library launches them with start/stop
+    # events that the runtime stamps at the kernel's own start and end
+    # (ddt_set_reduce_events).  Events inside a captured graph are not valid
+    # timing events on this runtime, so the launches are timed in eager
+    # rounds of the same ring slots, on the same stream.
     per_round = w.D + 1
     n_pairs = per_round * R * 4
     evs = hip.events(2 * n_pairs)
@@ -861,19 +995,22 @@ def main():
     used = lib.ddt_set_reduce_events(None, 0)
     assert used == per_round * R, f"expected {per_round * R} timed launches, got {used}"
     torch.cuda.synchronize()
-    durs, nbytes = [], []
     ebytes = w.V * (2 if w.dtype == "bf16" else 4)
-    for s, st in enumerate(stats):
-        rows = st["rows_per_layer"] + [st["verify_rows"]]
+    exp_d, exp_b, ver_d, ver_b = [], [], [], []
+    for s_i, st in enumerate(stats):
         for k in range(per_round):
-            i = s * per_round + k
-            durs.append(hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) * 1e-3)
-            nbytes.append(rows[k] * ebytes)
-    durs, nbytes = np.array(durs), np.array(nbytes, dtype=np.float64)
-    achieved = nbytes.sum() / durs.sum() / 1e9
-    big = nbytes >= np.max(nbytes) * 0.5
-    log(f"row reduction: {len(durs)} launches, mean {durs.mean() * 1e6:.2f} us, "
-        f"{nbytes.mean() / 1e6:.2f} MB/launch, {achieved:.0f} GB/s")
+            i = s_i * per_round + k
+            d = hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) * 1e-3
+            if k < w.D:
+                exp_d.append(d); exp_b.append(st["rows_per_layer"][k] * ebytes)
+            else:
+                ver_d.append(d); ver_b.append(st["verify_rows"] * ebytes)
+    exp_d, exp_b = np.array(exp_d), np.array(exp_b, dtype=np.float64)
+    ver_d, ver_b = np.array(ver_d), np.array(ver_b, dtype=np.float64)
+    achieved = exp_b.sum() / exp_d.sum() / 1e9
+    log(f"expand layers: {len(exp_d)} launches, mean {exp_d.mean() * 1e6:.2f} us, "
+        f"{exp_b.mean() / 1e6:.2f} MB/launch, {achieved:.0f} GB/s; verify reduction: "
+        f"{ver_d.mean() * 1e6:.2f} us, {ver_b.mean() / 1e6:.2f} MB/launch")
 
     # ---- per-round spread: replays bracketed one by one ----------------------
     nspread = 100
@@ -930,16 +1067,27 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic_per_launch(w.name),
-                     "kernel": "k_row_partial<bf16> (vocab row reduction: max, sigma', top-k)",
-                     "algorithmic_bytes_per_launch": round(float(nbytes.mean()), 1),
-                     "avg_launch_us": round(float(durs.mean() * 1e6), 3),
-                     "launches": int(len(durs)), "timing": "kernel-stamped HIP start/stop events per launch (hipExtLaunchKernelGGL), eager rounds",
-                     "big_launches_gbs": round(float(nbytes[big].sum() / durs[big].sum() / 1e9), 1)},
+                     "kernel": "k_expand_layer<bf16,4> (one draft layer: vocabulary reduction of the "
+                               "layer's draft rows, row merge and children, frontier, CAST rule)",
+                     "algorithmic_bytes_per_launch": round(float(exp_b.mean()), 1),
+                     "algorithmic_bytes": "the layer's live draft rows x V x 2 bytes (every draft row once)",
+                     "avg_launch_us": round(float(exp_d.mean() * 1e6), 3),
+                     "launches": int(len(exp_d)),
+                     "timing": "kernel-stamped HIP start/stop events per launch (hipExtLaunchKernelGGL), "
+                               "eager rounds; layers after CAST's depth stop are launched too and "
+                               "count with 0 bytes"},
         "logit_gbs": round(logit_gbs, 1),
         "logit_frac_of_peak": round(logit_gbs / PEAK_HBM_GBS, 4),
         "detail": {
             "gpu_event_us_per_round": round(gpu_ms * 1e3 / K, 2),
             "round_us_p10_p50_p90": [round(float(np.percentile(per_round_us, q)), 2) for q in (10, 50, 90)],
+            "verify_reduction_launch": {
+                "kernel": "k_row_partial<bf16,8>, K = 1",
+                "label": "greedy verify reduces every flat row (sum of m_b + 1 rows) to its argmax; "
+                         "the accepted walk needs only sum of accept_len + 1 of them",
+                "mb": round(float(ver_b.mean()) / 1e6, 3), "us": round(float(ver_d.mean() * 1e6), 3),
+                "gbs": round(float(ver_b.sum() / ver_d.sum() / 1e9), 1),
+                "frac": round(float(ver_b.sum() / ver_d.sum() / 1e9 / PEAK_HBM_GBS), 4)},
             "rows_batched_reduction": {"rows": int(nrows), "mb": round(batched_bytes / 1e6, 1),
                                        "us": round(float(bd.mean() * 1e6), 2),
                                        "gbs": round(float(batched_gbs), 1),
@@ -955,6 +1103,7 @@ def main():
             "mean_tau": round(float(np.mean([np.mean(s["accept"]) + 1 for s in stats])), 3),
         },
     }
+    out["detail"]["expand_layer_b64"] = expand_b64_detail(api, lib, hip, dev)
     if not args.no_attention:
         out["detail"]["tree_attention"] = tree_attention_detail(api, dev)
         # the CAST workload's verify shape (8 requests, 61 flat positions) over
@@ -965,10 +1114,7 @@ def main():
     if w.cast is not None and not args.no_calibrate:
         out["detail"]["cast_calibration"] = cast_calibration_detail(w, run, ring, to_dev, dev,
                                                                     save=args.save_tables)
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, ring[0], cast_np, args.cpu_seconds)
-    else:
-        out["cpu_baseline"] = None
+    out["cpu_baseline"] = collect_oracle(child) if child is not None else None
     print(json.dumps(out), flush=True)
 
 

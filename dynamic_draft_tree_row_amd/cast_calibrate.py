@@ -227,17 +227,29 @@ def save_tables(path: str, S_T: np.ndarray, S_D: np.ndarray, B: int, L: int,
                 device: str = "") -> None:
     """Store measured tables with what they were measured for (batch B, grid
     step L, the proxy shapes, the device name): the tables are computed
-    offline once per GPU and batch size and read back at serving time."""
+    offline once per GPU and batch size and read back at serving time.  The
+    file is written at `path` as given (through a handle, so no suffix is
+    added); load_tables reads the same name."""
     S_T, S_D = np.asarray(S_T, np.float32), np.asarray(S_D, np.float32)
     if S_T.shape != S_D.shape or S_T.ndim != 2 or S_T.shape[1] < 2:
         raise ValueError("S_T and S_D must be [M][N+1] tables of the same shape")
-    np.savez(path, S_T=S_T, S_D=S_D, B=np.int64(B), L=np.int64(L),
+    with open(path, "wb") as fh:
+        _savez(fh, S_T, S_D, B, L, target, draft, device)
+
+
+def _savez(fh, S_T, S_D, B, L, target, draft, device) -> None:
+    np.savez(fh, S_T=S_T, S_D=S_D, B=np.int64(B), L=np.int64(L),
              target=np.array(astuple(target), np.int64), draft=np.array(astuple(draft), np.int64),
              device=np.array(device))
 
 
 def load_tables(path: str) -> dict:
-    """Tables stored by save_tables: dict(S_T, S_D, B, L, target, draft, device)."""
+    """Tables stored by save_tables: dict(S_T, S_D, B, L, target, draft, device).
+    A path without the file (as numpy's own savez would have named it
+    `path`.npz) is looked up with that suffix too."""
+    import os
+    if not os.path.exists(path) and os.path.exists(path + ".npz"):
+        path = path + ".npz"
     with np.load(path, allow_pickle=False) as z:
         return {"S_T": z["S_T"], "S_D": z["S_D"], "B": int(z["B"]), "L": int(z["L"]),
                 "target": ProxyModel(*[int(x) for x in z["target"]]),

@@ -150,13 +150,15 @@ int resident_verify_blocks() {
 
 // Launch with the reduction timing hook (ddt_set_reduce_events): while it is
 // set, the runtime stamps the next event pair at the kernel's own start and
-// end.
+// end.  part: 0 = the whole timed span is this launch; 1 = this launch starts
+// a span that the next launch (part 2) ends.
 template <class Kern, class... Args>
-int launch_timed(Kern kern, dim3 grid, dim3 blk, size_t lds, hipStream_t s, Args... args) {
+int launch_timed(int part, Kern kern, dim3 grid, dim3 blk, size_t lds, hipStream_t s, Args... args) {
     if (g_events != nullptr && g_used < g_pairs) {
         hipEvent_t e0 = (hipEvent_t)g_events[2 * g_used], e1 = (hipEvent_t)g_events[2 * g_used + 1];
-        hipExtLaunchKernelGGL(kern, grid, blk, lds, s, e0, e1, 0, args...);
-        ++g_used;
+        hipExtLaunchKernelGGL(kern, grid, blk, lds, s, part == 2 ? nullptr : e0, part == 1 ? nullptr : e1, 0,
+                              args...);
+        if (part != 1) ++g_used;
         return launched();
     }
     hipLaunchKernelGGL(kern, grid, blk, lds, s, args...);
@@ -164,7 +166,7 @@ int launch_timed(Kern kern, dim3 grid, dim3 blk, size_t lds, hipStream_t s, Args
 }
 
 int launch_partials(const ddt_logits* x, int n0, int n1, const int32_t* count, int count_add,
-                    int K, void* ws, hipStream_t s, const float* sum_if = nullptr) {
+                    int K, void* ws, hipStream_t s, const float* sum_if = nullptr, int part = 0) {
     RowSrc rs{};
     rs.base = x->data; rs.s0 = x->s0; rs.s1 = x->s1; rs.n1 = n1;
     rs.count = count; rs.count_add = count_add; rs.sum_if = sum_if;
@@ -175,10 +177,9 @@ int launch_partials(const ddt_logits* x, int n0, int n1, const int32_t* count, i
     if (total > INT32_MAX) return DDT_ECAPACITY;
     const bool bf16 = x->dtype == DDT_BF16, wide = wide_rows(rows);
     const dim3 grid((unsigned)total), blk(RR_NT);
-    uint32_t* part = (uint32_t*)ws;
     auto kern = bf16 ? (wide ? &k_row_partial<true, RR_NV_WIDE> : &k_row_partial<true, RR_NV>)
                      : (wide ? &k_row_partial<false, RR_NV_WIDE> : &k_row_partial<false, RR_NV>);
-    return launch_timed(kern, grid, blk, 0, s, rs, x->V, groups, K, part);
+    return launch_timed(part, kern, grid, blk, 0, s, rs, x->V, groups, K, (uint32_t*)ws);
 }
 
 }  // namespace
@@ -347,13 +348,19 @@ int ddt_tree_expand(const ddt_tree* t, int layer, const int32_t* root_tok, const
             if (gate->ck_depth[i] == layer) { a.ck = 1; a.kd_ck = gate->k_draft[i]; a.tau = gate->tau[i]; }
     const long long total = rows * a.groups;
     if (total > INT32_MAX) return DDT_ECAPACITY;
-    size_t lds = std::max(sizeof(RRLds), (size_t)MRG_SCR * 8);
-    lds = std::max(lds, layer_lds_c(t->R_max, K_n));
-    if (cast) lds = std::max(lds, layer_lds_c(t->R_max, K_n) + layer_lds_d(t->B, t->R_max, cast->M));
     const bool bf16 = logits->dtype == DDT_BF16, wide = wide_rows(rows);
-    auto kern = bf16 ? (wide ? &k_expand_layer<true, RR_NV_WIDE> : &k_expand_layer<true, RR_NV>)
-                     : (wide ? &k_expand_layer<false, RR_NV_WIDE> : &k_expand_layer<false, RR_NV>);
-    return launch_timed(kern, dim3((unsigned)total), dim3(RR_NT), lds, s, a);
+    const size_t cast_lds = cast ? layer_lds_d(t->B, t->R_max, cast->M) : 0;
+    if (wide) {
+        // many rows: the plain reduction, then one workgroup per request
+        st = launch_partials(logits, t->B, R, layer == 1 ? nullptr : t->n_front, 0, K_n, ws, s, nullptr, 1);
+        if (st) return st;
+        const size_t lds = finish_lds(t->R_max, K_n) + cast_lds;
+        return launch_timed(2, &k_expand_finish, dim3((unsigned)t->B), dim3(EF_NT), lds, s, a);
+    }
+    size_t lds = std::max(sizeof(RRLds), (size_t)MRG_SCR * 8);
+    lds = std::max(lds, layer_lds_c(t->R_max, K_n) + cast_lds);
+    auto kern = bf16 ? &k_expand_layer<true, RR_NV> : &k_expand_layer<false, RR_NV>;
+    return launch_timed(0, kern, dim3((unsigned)total), dim3(RR_NT), lds, s, a);
 }
 
 int ddt_tree_rerank(const ddt_tree* t, int m_max, const ddt_cast* cast, int use_k_draft,

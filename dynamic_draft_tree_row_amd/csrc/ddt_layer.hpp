@@ -12,7 +12,12 @@
 //
 // Grid: one 256-thread workgroup per (request b, frontier slot j, vocabulary
 // chunk g); workgroups of slots past the request's frontier width leave at
-// once.  Nothing waits: each stage is run by the last workgroup to arrive on
+// once.  Launches of many rows, which fill the device many times over, run
+// the plain reduction (k_row_partial) and then k_expand_finish, one
+// 1024-thread workgroup per request whose waves merge the request's rows in
+// parallel (a chunk workgroup that waits for its ticket holds a slot the next
+// chunk could use, and the merges and frontier then need no coherent
+// handoffs).  Nothing waits: each stage is run by the last workgroup to arrive on
 // a device-scope counter ("ticket"), which then resets it.
 //   A. every workgroup reduces its chunk to a partial record;
 //   B. the last chunk of row (b, j) merges the row's partials (one wave)
@@ -76,6 +81,96 @@ __host__ __device__ __forceinline__ size_t layer_lds_c(int R_max, int K_n) {
 }
 __host__ __device__ __forceinline__ size_t layer_lds_d(int B, int R_max, int M) {
     return (size_t)B * R_max * 8 + 16 * 8 + (((size_t)M * R_max + M) * 4 + 7) / 8 * 8;
+}
+
+// Request b's next frontier from the layer's sort keys s_sk[count] and the
+// parents' keys s_pk[nrows] (LDS): ranks, each counted by SL lanes; rank <
+// R_max makes a frontier record and rank 0 closes b's layer (node count,
+// frontier width, Graft gate).  The values stage D reads go out
+// device-coherent.  Every thread of the workgroup calls it.
+template <int NT>
+__device__ void layer_frontier(const LayerArgs& a, int b, int base, int count, const uint64_t* s_sk,
+                               const uint64_t* s_pk) {
+    const ddt_tree& t = a.t;
+    const int tid = threadIdx.x, Rm = t.R_max, Kn = a.K_n, layer = a.layer, du = layer - 1;
+    int32_t* fr = t.frontier + (size_t)b * Rm;
+    float* frS = t.front_S + (size_t)b * Rm;
+    uint64_t* frK = t.front_key + (size_t)b * Rm;
+    const int SL = split_lanes(count, NT);
+    const int lg = __ffs(SL) - 1;
+    for (int cb = 0; cb < count; cb += NT >> lg) {
+        const int q = cb + (tid >> lg), part = tid & (SL - 1);
+        uint64_t sk = 0ull;
+        int r = 0;
+        if (q < count) {
+            sk = s_sk[q];
+#pragma unroll 4
+            for (int p = part; p < count; p += SL) r += s_sk[p] < sk ? 1 : 0;
+        }
+        r = group_sum(r, SL);
+        if (part == 0 && q < count && r < Rm) {
+            const float Sv = unord_f32(~(uint32_t)(sk >> 32));
+            const int jj = q / Kn;
+            fr[r] = base + q; st_coh_f32(frS + r, Sv);
+            frK[r] = key_child(layer == 1 ? 0ull : s_pk[jj], du, q - jj * Kn, 0);
+            if (r == 0) {
+                st_coh_i32(t.n_nodes + b, base + count);
+                st_coh_i32(t.layer_base + b, base);
+                int nf = min(a.K_e, count);
+                if (layer >= t.D_max) nf = 0;
+                if (layer == 1) {
+                    t.active[b] = 1;
+                    t.k_draft[b] = a.gate_on ? a.K_max : 0;
+                }
+                if (a.ck && !(expf(Sv) > a.tau)) {            // g_d = 1[c_d > tau_d]
+                    t.active[b] = 0;
+                    t.k_draft[b] = a.kd_ck;
+                    nf = 0;
+                }
+                st_coh_i32(t.n_front + b, nf);
+            }
+        }
+    }
+    if (count == 0 && tid == 0) {
+        if (layer == 1) { st_coh_i32(t.n_nodes + b, 1); st_coh_i32(t.layer_base + b, 1); }
+        st_coh_i32(t.n_front + b, 0);
+    }
+}
+
+// CAST's batch rule (key designs 2 and 3) in the last request of the layer;
+// with CAST every request has the same frontier width, so all B take part in
+// every layer that runs.  The inputs that do not depend on the layer (state,
+// cost-table entries) are staged in `region` (LDS) before the ticket.
+template <int NT>
+__device__ void layer_cast(const LayerArgs& a, unsigned char* region, int& s_flag) {
+    const ddt_tree& t = a.t;
+    const ddt_cast& cp = a.c;
+    const int tid = threadIdx.x, Rm = t.R_max, layer = a.layer;
+    const int B = t.B, Mc = cp.M, N = cp.N;
+    CastView L;
+    L.v = (double*)region;                                       // [B][R_max] e^S of the frontiers
+    L.st = L.v + (size_t)B * Rm;                                 // [16] state
+    L.sd = (float*)(L.st + 16);                                  // [M][R_max] S_D columns 1..R_max
+    L.st1 = L.sd + (size_t)Mc * Rm;                              // [M] S_T column 1
+    for (int q = tid; q < Mc * Rm; q += NT) {
+        const int r = q / Rm, k = q - r * Rm;
+        L.sd[q] = k < N ? cp.S_D[(size_t)r * (N + 1) + k + 1] : 0.f;
+    }
+    if (tid < Mc) L.st1[tid] = cp.S_T[(size_t)tid * (N + 1) + 1];
+    if (tid < 11) {
+        // layer 1 starts the state: FIFO {1}, length 1, no previous u_n, context 0
+        L.st[tid] = layer > 1 ? t.cast_state[tid]
+                              : tid == 0 ? 1.0 : tid == 8 ? 1.0 : tid == 9 ? -1.0 : 0.0;
+    }
+    if (!ticket_last(t.ticket, (uint32_t)B, s_flag)) return;
+    for (int q = tid; q < B * Rm; q += NT) L.v[q] = (double)expf(ld_coh_f32(t.front_S + q));
+    int cnt = 0x7FFFFFFF;
+    if (tid < B) cnt = max(0, ld_coh_i32(t.n_nodes + tid) - ld_coh_i32(t.layer_base + tid));
+    __syncthreads();
+    if (tid < DDT_WAVE) {
+        const int kc = (int)wave_min_u32((uint32_t)cnt);
+        cast_decide(L, t, cp, layer, min(min(a.K_e, Rm), kc));
+    }
 }
 
 template <bool BF16, int NL>
@@ -142,8 +237,9 @@ __global__ __launch_bounds__(RR_NT) void k_expand_layer(LayerArgs a) {
                 const int node = base + j * Kn + lane;
                 tok[node] = vkey_id(mine); par[node] = u; dep[node] = du + 1; esl[node] = -1;
                 S[node] = Sv; lc[node] = logc; key[node] = key_child(pk, du, lane, 0);
-                // sort key (~code(S), parent's key rank * K_n + r): ascending
-                // is (S desc, canonical key asc) within the layer
+                // sort key (~code(S), parent's key rank * K_n + r), ascending
+                // = (S desc, canonical key asc) within the layer; written over
+                // the row's partials, which are no longer needed
                 rr_st64((uint64_t*)prow + lane, ((uint64_t)~ord_f32(Sv) << 32) | (uint32_t)(prk * Kn + lane));
             }
             if (lane == 0) {
@@ -157,92 +253,105 @@ __global__ __launch_bounds__(RR_NT) void k_expand_layer(LayerArgs a) {
     if (!ticket_last(t.layer_sync + (size_t)t.B * Rm + b, (uint32_t)nrows, s_flag)) return;
 
     // ---- C: request b's frontier ---------------------------------------------
-    {
-        uint64_t* s_sk = (uint64_t*)dyn;                         // [nrows * Kn]
-        uint64_t* s_pk = s_sk + (size_t)Rm * Kn;                 // [nrows]
-        const int count = fits ? nrows * Kn : 0;
-        // every row's sort keys (over its partials) and parents' keys
-        for (int q = tid; q < count; q += RR_NT) {
-            const int jj = q / Kn, r = q - jj * Kn;
-            s_sk[q] = rr_ld64<true>((const uint64_t*)(a.part + (size_t)(b * a.R + jj) * a.groups * PS) + r);
-        }
-        if (tid < nrows) s_pk[tid] = pkl;
-        __syncthreads();
-        // ranks, each counted by SL lanes; rank < R_max makes a frontier record
-        int32_t* fr = t.frontier + (size_t)b * Rm;
-        float* frS = t.front_S + (size_t)b * Rm;
-        uint64_t* frK = t.front_key + (size_t)b * Rm;
-        const int SL = split_lanes(count, RR_NT);
-        const int lg = __ffs(SL) - 1;
-        for (int cb = 0; cb < count; cb += RR_NT >> lg) {
-            const int q = cb + (tid >> lg), part = tid & (SL - 1);
-            uint64_t sk = 0ull;
-            int r = 0;
-            if (q < count) {
-                sk = s_sk[q];
-#pragma unroll 4
-                for (int p = part; p < count; p += SL) r += s_sk[p] < sk ? 1 : 0;
-            }
-            r = group_sum(r, SL);
-            if (part == 0 && q < count && r < Rm) {
-                const float Sv = unord_f32(~(uint32_t)(sk >> 32));
-                const int jj = q / Kn;
-                fr[r] = base + q; st_coh_f32(frS + r, Sv);
-                frK[r] = key_child(layer == 1 ? 0ull : s_pk[jj], du, q - jj * Kn, 0);
-                if (r == 0) {
-                    st_coh_i32(t.n_nodes + b, base + count);
-                    st_coh_i32(t.layer_base + b, base);
-                    int nf = min(a.K_e, count);
-                    if (layer >= t.D_max) nf = 0;
-                    if (layer == 1) {
-                        t.active[b] = 1;
-                        t.k_draft[b] = a.gate_on ? a.K_max : 0;
-                    }
-                    if (a.ck && !(expf(Sv) > a.tau)) {        // g_d = 1[c_d > tau_d]
-                        t.active[b] = 0;
-                        t.k_draft[b] = a.kd_ck;
-                        nf = 0;
-                    }
-                    st_coh_i32(t.n_front + b, nf);
-                }
-            }
-        }
-        if (count == 0 && tid == 0) {
-            if (layer == 1) { st_coh_i32(t.n_nodes + b, 1); st_coh_i32(t.layer_base + b, 1); }
-            st_coh_i32(t.n_front + b, 0);
-        }
+    uint64_t* s_sk = (uint64_t*)dyn;                             // [nrows * Kn]
+    uint64_t* s_pk = s_sk + (size_t)Rm * Kn;                     // [nrows]
+    const int count = fits ? nrows * Kn : 0;
+    for (int q = tid; q < count; q += RR_NT) {
+        const int jj = q / Kn, r = q - jj * Kn;
+        s_sk[q] = rr_ld64<true>((const uint64_t*)(a.part + (size_t)(b * a.R + jj) * a.groups * PS) + r);
     }
+    if (tid < nrows) s_pk[tid] = pkl;
+    __syncthreads();
+    layer_frontier<RR_NT>(a, b, base, count, s_sk, s_pk);
     if (!a.cast_on) return;
 
-    // ---- D: CAST's batch rule in the last request of the layer ---------------
-    // (with CAST every request has the same frontier width, so all B take
-    // part in every layer that runs).  The inputs that do not depend on the
-    // layer (state, cost-table entries) are staged before the ticket, in an
-    // LDS region past stage C's.
-    const ddt_cast& cp = a.c;
-    const int B = t.B, Mc = cp.M, N = cp.N;
-    CastView L;
-    L.v = (double*)(dyn + layer_lds_c(Rm, Kn));                   // [B][R_max] e^S of the frontiers
-    L.st = L.v + (size_t)B * Rm;                                 // [16] state
-    L.sd = (float*)(L.st + 16);                                  // [M][R_max] S_D columns 1..R_max
-    L.st1 = L.sd + (size_t)Mc * Rm;                              // [M] S_T column 1
-    for (int q = tid; q < Mc * Rm; q += RR_NT) {
-        const int r = q / Rm, k = q - r * Rm;
-        L.sd[q] = k < N ? cp.S_D[(size_t)r * (N + 1) + k + 1] : 0.f;
+    // ---- D: CAST's batch rule --------------------------------------------------
+    layer_cast<RR_NT>(a, dyn + layer_lds_c(Rm, Kn), s_flag);
+}
+
+// ---------------------------------------------------------------------------
+// the layer of a request after the plain reduction (launches of many rows)
+// ---------------------------------------------------------------------------
+#define EF_NT 1024
+#define EF_NW (EF_NT / DDT_WAVE)
+
+// Dynamic LDS of k_expand_finish: merge scratch per wave, the rows' top keys,
+// the layer's sort keys, per-row statistics and parents; the CAST region
+// follows (layer_lds_d).
+__host__ __device__ __forceinline__ size_t finish_lds(int R_max, int K_n) {
+    return (size_t)EF_NW * MRG_SCR * 8 + (size_t)R_max * K_n * 16 + (size_t)R_max * 24;
+}
+
+__global__ __launch_bounds__(EF_NT) void k_expand_finish(LayerArgs a) {
+    extern __shared__ __align__(16) unsigned char dyn[];
+    __shared__ int s_flag;
+    const ddt_tree& t = a.t;
+    const int tid = threadIdx.x, lane = tid & (DDT_WAVE - 1), wid = tid / DDT_WAVE;
+    const int b = blockIdx.x;
+    const int layer = a.layer, du = layer - 1;
+    const int nrows = layer == 1 ? 1 : min(max(t.n_front[b], 0), a.R);
+    if (nrows == 0) return;                                      // a stopped request
+    const int Kn = a.K_n, cap = t.cap, Rm = t.R_max;
+    const int PS = rr_ps(Kn);
+    uint64_t* scr = (uint64_t*)dyn;                              // [EF_NW][MRG_SCR]
+    uint64_t* s_key = scr + (size_t)EF_NW * MRG_SCR;             // [R_max * K_n]
+    uint64_t* s_sk = s_key + (size_t)Rm * Kn;                    // [R_max * K_n]
+    uint64_t* s_pk = s_sk + (size_t)Rm * Kn;                     // [R_max]
+    float* s_M = (float*)(s_pk + Rm);
+    float* s_Sp = s_M + Rm;
+    float* s_pS = s_Sp + Rm;
+    int* s_pn = (int*)(s_pS + Rm);
+    const int base = layer == 1 ? 1 : t.n_nodes[b];
+    const bool fits = base >= 1 && base + nrows * Kn <= cap;
+    const int count = fits ? nrows * Kn : 0;
+    if (tid < nrows) {
+        const int u0 = t.frontier[(size_t)b * Rm + tid];
+        s_pn[tid] = layer == 1 ? 0 : ((u0 >= 0 && u0 < base) ? u0 : 0);
+        s_pS[tid] = layer == 1 ? 0.f : t.front_S[(size_t)b * Rm + tid];
+        s_pk[tid] = layer == 1 ? 0ull : t.front_key[(size_t)b * Rm + tid];
     }
-    if (tid < Mc) L.st1[tid] = cp.S_T[(size_t)tid * (N + 1) + 1];
-    if (tid < 11) {
-        // layer 1 starts the state: FIFO {1}, length 1, no previous u_n, context 0
-        L.st[tid] = layer > 1 ? t.cast_state[tid]
-                              : tid == 0 ? 1.0 : tid == 8 ? 1.0 : tid == 9 ? -1.0 : 0.0;
+    // wave w merges rows w, w + 16 (plain loads: the previous kernel wrote the
+    // partials)
+    for (int jr = wid; jr < nrows; jr += EF_NW) {
+        float M, Sp;
+        const uint32_t* pr = a.part + (size_t)(b * a.R + jr) * a.groups * PS;
+        const uint64_t mine = merge_row_wave(pr, a.groups, Kn, M, Sp, scr + (size_t)wid * MRG_SCR);
+        if (lane < Kn) s_key[jr * Kn + lane] = mine;
+        if (lane == 0) { s_M[jr] = M; s_Sp[jr] = Sp; }
     }
-    if (!ticket_last(t.ticket, (uint32_t)B, s_flag)) return;
-    for (int q = tid; q < B * Rm; q += RR_NT) L.v[q] = (double)expf(ld_coh_f32(t.front_S + q));
-    int cnt = 0x7FFFFFFF;
-    if (tid < B) cnt = max(0, ld_coh_i32(t.n_nodes + tid) - ld_coh_i32(t.layer_base + tid));
     __syncthreads();
-    if (wid == 0) {
-        const int kc = (int)wave_min_u32((uint32_t)cnt);
-        cast_decide(L, t, cp, layer, min(min(a.K_e, Rm), kc));
+    int32_t* tok = t.token + (size_t)b * cap;
+    int32_t* par = t.parent + (size_t)b * cap;
+    int32_t* dep = t.depth + (size_t)b * cap;
+    int32_t* esl = t.eslot + (size_t)b * cap;
+    uint64_t* key = t.key + (size_t)b * cap;
+    float* S = t.S + (size_t)b * cap;
+    float* lc = t.logc + (size_t)b * cap;
+    if (layer == 1 && tid == 0 && fits) {
+        tok[0] = a.root_tok[b]; par[0] = -1; dep[0] = 0; key[0] = 0ull; S[0] = 0.f; lc[0] = 0.f;
     }
+    for (int q = tid; q < count; q += EF_NT) {
+        const int jj = q / Kn, r = q - jj * Kn;
+        const uint64_t kk = s_key[q];
+        const float logc = (vkey_val(kk) - s_M[jj]) - log1pf(s_Sp[jj]);
+        const float Sv = s_pS[jj] + logc;
+        const uint64_t pk = s_pk[jj];
+        const int u = s_pn[jj];
+        const int node = base + q;
+        tok[node] = vkey_id(kk); par[node] = u; dep[node] = du + 1; esl[node] = -1;
+        S[node] = Sv; lc[node] = logc; key[node] = key_child(pk, du, r, 0);
+        int prk = 0;
+        for (int k = 0; k < nrows; ++k) prk += s_pk[k] < pk ? 1 : 0;
+        s_sk[q] = ((uint64_t)~ord_f32(Sv) << 32) | (uint32_t)(prk * Kn + r);
+        if (r == 0) {
+            esl[u] = jj;
+            const size_t ri = ((size_t)b * t.D_max + du) * Rm + jj;
+            t.rmax[ri] = s_M[jj];
+            t.rsp[ri] = s_Sp[jj];
+        }
+    }
+    __syncthreads();
+    layer_frontier<EF_NT>(a, b, base, count, s_sk, s_pk);
+    if (!a.cast_on) return;
+    layer_cast<EF_NT>(a, dyn + finish_lds(Rm, Kn), s_flag);
 }

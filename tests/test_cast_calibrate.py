@@ -46,6 +46,22 @@ def test_tables_round_trip(tmp_path):
         CC.save_tables(p, S_T, S_D[:, :2], B=8, L=256)
 
 
+def test_tables_round_trip_without_suffix(tmp_path):
+    """A name with no .npz suffix is written and read back as given; a file
+    that numpy's savez wrote as name.npz is found under the bare name too."""
+    S_T = CC.assemble(np.array([[10.0, 11.0], [12.0, 12.5]]), np.array([5.0, 6.0]), 32)
+    S_D = CC.assemble(np.array([[1.0, 1.5], [1.2, 1.6]]), np.array([5.0, 6.0]), 1)
+    p = tmp_path / "tables_b8"
+    CC.save_tables(str(p), S_T, S_D, B=8, L=256)
+    assert p.exists() and not (tmp_path / "tables_b8.npz").exists()
+    np.testing.assert_array_equal(CC.load_tables(str(p))["S_D"], S_D)
+    q = tmp_path / "legacy"
+    np.savez(str(q), S_T=S_T, S_D=S_D, B=np.int64(8), L=np.int64(256),
+             target=np.array(CC.astuple(CC.TARGET_8B), np.int64),
+             draft=np.array(CC.astuple(CC.DRAFT_HEAD), np.int64), device=np.array(""))
+    assert CC.load_tables(str(q))["B"] == 8
+
+
 def test_measure_rejects_bad_grids():
     with pytest.raises(ValueError):
         CC.measure_tables(B=1, L=16, M=1, N=300)

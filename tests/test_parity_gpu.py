@@ -135,6 +135,9 @@ SMALL = {
     "cast_b12": configs.shrink(configs.C2, V=9000, B=12),       # more workgroups sharing the layer ticket
     "t1": configs.shrink(configs.C3, V=9001, B=4),            # odd V: unaligned bf16 rows
     "mixed_prefix": configs.shrink(configs.C5, V=4100, B=6),
+    # 20 requests x 16 frontier rows: layers of 256 rows or more take the
+    # plain reduction and the layer kernel's finishing form
+    "mixed_wide": configs.shrink(configs.C5, V=4100, B=20),
     # T > 0 draft children verified with q = the draft row's softmax
     "t1_draft_q": configs.shrink(configs.C3, V=9001, B=4, proposal="draft"),
     "mixed_draft_q": configs.shrink(configs.C5, V=4100, B=6, proposal="draft"),
