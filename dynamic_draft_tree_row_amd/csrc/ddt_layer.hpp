@@ -25,7 +25,8 @@
 //      canonical order) over the row's partials, which are no longer needed;
 //   C. the last row of request b ranks the layer's sort keys of b into the
 //      next frontier and closes b's layer (node count, frontier width,
-//      Graft gate);
+//      Graft gate); a request with one row skips this ticket and keeps the
+//      sort keys in LDS;
 //   D. with CAST, the last request runs the batch rule.
 // Every value one workgroup hands to another within the launch (partial
 // records, the new nodes' values, the frontier values and counts, the
@@ -239,8 +240,12 @@ __global__ __launch_bounds__(RR_NT) void k_expand_layer(LayerArgs a) {
                 S[node] = Sv; lc[node] = logc; key[node] = key_child(pk, du, lane, 0);
                 // sort key (~code(S), parent's key rank * K_n + r), ascending
                 // = (S desc, canonical key asc) within the layer; written over
-                // the row's partials, which are no longer needed
-                rr_st64((uint64_t*)prow + lane, ((uint64_t)~ord_f32(Sv) << 32) | (uint32_t)(prk * Kn + lane));
+                // the row's partials, which are no longer needed, or, when the
+                // row is the request's only one, kept in LDS (the merge
+                // scratch there is no longer needed either)
+                const uint64_t sk = ((uint64_t)~ord_f32(Sv) << 32) | (uint32_t)(prk * Kn + lane);
+                if (nrows == 1) ((uint64_t*)dyn)[lane] = sk;
+                else rr_st64((uint64_t*)prow + lane, sk);
             }
             if (lane == 0) {
                 esl[u] = j;
@@ -250,15 +255,18 @@ __global__ __launch_bounds__(RR_NT) void k_expand_layer(LayerArgs a) {
             }
         }
     }
-    if (!ticket_last(t.layer_sync + (size_t)t.B * Rm + b, (uint32_t)nrows, s_flag)) return;
-
     // ---- C: request b's frontier ---------------------------------------------
+    // (a request of one row goes on in the same workgroup: its only row's
+    // sort keys are in LDS)
     uint64_t* s_sk = (uint64_t*)dyn;                             // [nrows * Kn]
     uint64_t* s_pk = s_sk + (size_t)Rm * Kn;                     // [nrows]
     const int count = fits ? nrows * Kn : 0;
-    for (int q = tid; q < count; q += RR_NT) {
-        const int jj = q / Kn, r = q - jj * Kn;
-        s_sk[q] = rr_ld64<true>((const uint64_t*)(a.part + (size_t)(b * a.R + jj) * a.groups * PS) + r);
+    if (nrows > 1) {
+        if (!ticket_last(t.layer_sync + (size_t)t.B * Rm + b, (uint32_t)nrows, s_flag)) return;
+        for (int q = tid; q < count; q += RR_NT) {
+            const int jj = q / Kn, r = q - jj * Kn;
+            s_sk[q] = rr_ld64<true>((const uint64_t*)(a.part + (size_t)(b * a.R + jj) * a.groups * PS) + r);
+        }
     }
     if (tid < nrows) s_pk[tid] = pkl;
     __syncthreads();

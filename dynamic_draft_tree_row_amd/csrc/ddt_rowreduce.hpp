@@ -144,6 +144,33 @@ __device__ __forceinline__ float rr_max3(float a, float b, float c) {
     return r;
 }
 
+// Packed maximum of bf16 bit patterns read as fp16.  The reading is monotone
+// (sign, then exponent and mantissa bits in order) for every pattern whose
+// fp16 exponent field is not all ones, i.e. every bf16 value of magnitude
+// below 2^121 and the value 2^121 itself (read as fp16 infinity); larger
+// magnitudes, bf16 infinities and NaNs read as fp16 NaN, which the IEEE
+// maximum3 propagates, so a NaN result flags the one case that needs the
+// fp32 reading.  fp16 denormals are preserved (the kernels' default mode), so
+// tiny values compare exactly.
+//   rr_pkmax3:   lo = max(a.lo, b.lo, c.lo), hi = max(a.hi, b.hi, c.hi)
+//   rr_pkmax3_x: lo = max(a.lo, b.hi, c.hi), hi = max(a.hi, b.lo, c.lo)
+// (each one v_pk_maximum3_f16, the swap folded into its operand selects)
+typedef _Float16 rr_h2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t rr_pkmax3(uint32_t a, uint32_t b, uint32_t c) {
+    const rr_h2 x = __builtin_bit_cast(rr_h2, a), y = __builtin_bit_cast(rr_h2, b),
+                z = __builtin_bit_cast(rr_h2, c);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_maximum(__builtin_elementwise_maximum(x, y), z));
+}
+__device__ __forceinline__ uint32_t rr_pkmax3_x(uint32_t a, uint32_t b, uint32_t c) {
+    const rr_h2 x = __builtin_bit_cast(rr_h2, a), y = __builtin_bit_cast(rr_h2, b),
+                z = __builtin_bit_cast(rr_h2, c);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_maximum(
+        __builtin_elementwise_maximum(x, __builtin_shufflevector(y, y, 1, 0)), __builtin_shufflevector(z, z, 1, 0)));
+}
+__device__ __forceinline__ bool rr_nan16(uint32_t t) {
+    return __builtin_isnan(__builtin_bit_cast(_Float16, (uint16_t)t));
+}
+
 // element e of 16-byte word vector r
 #define RR_X(r, e) (BF16 ? __uint_as_float(((e) & 1) ? ((r)[(e) >> 1] & 0xFFFF0000u) : ((r)[(e) >> 1] << 16)) \
                          : __uint_as_float((r)[(e)]))
@@ -208,19 +235,73 @@ __device__ __forceinline__ void rr_chunk(const void* row, int V, int g, int K, b
     rr_load<BF16, NL>(raw, row, al, start, V, tid);
     if (tid == 0) { s_cnt = 0; s_ties = 0; s_amin = 0x7FFFFFFF; }
 
-    // pass 1: the maximum of every 16-byte word, then of the thread (padding
-    // is -inf); the word maxima let only words holding a candidate be staged
-    float wm[NL];
+    // pass 1: the thread maximum (padding is -inf).  bf16 words take the
+    // packed fp16 maximum, two 32-bit registers per instruction; a wave in
+    // which some lane's result is NaN (a value of magnitude above 2^121, an
+    // infinity or a NaN) takes the fp32 reading instead.
+    bool pk = false;                                           // wave-uniform
+    float tm = -INFINITY;
+    float wm[NL];                                              // word maxima (when needed)
+    // word i's maximum in both halves: three packed maxima
+    auto pk_word = [&](int i) -> uint32_t {
+        const uint32_t m = rr_pkmax3(raw[i][0], raw[i][1], raw[i][2]);
+        const uint32_t h = rr_pkmax3_x(m, m, raw[i][3]);      // lo: all but d3.lo; hi: all but d3.hi
+        return rr_pkmax3_x(h, h, h);
+    };
+    static_assert(!BF16 || NL % 2 == 0, "the packed pass pairs the words");
+    if constexpr (BF16) {
+        // independent packed maxima, three operands each, level by level
+        // (a dependent chain would wait on every result)
+        uint32_t a[NL];
+        if (K > 1) {
+            // every word's maximum (the staging needs them), then the thread's
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-        float a = rr_max3(RR_X(raw[i], 0), RR_X(raw[i], 1), RR_X(raw[i], 2));
+            for (int i = 0; i < NL; ++i) {
+                a[i] = pk_word(i);
+                wm[i] = __uint_as_float(a[i] << 16);
+            }
+        } else {
+            // each word reduced to a packed pair, the fourth registers of odd
+            // words folded into their even neighbours
 #pragma unroll
-        for (int e = 3; e < VEC; e += 2) a = rr_max3(a, RR_X(raw[i], e), RR_X(raw[i], e + 1 < VEC ? e + 1 : e));
-        wm[i] = a;
+            for (int i = 0; i < NL; ++i) a[i] = rr_pkmax3(raw[i][0], raw[i][1], raw[i][2]);
+#pragma unroll
+            for (int i = 0; i + 1 < NL; i += 2) {
+                a[i] = rr_pkmax3(a[i], raw[i][3], raw[i + 1][3]);
+            }
+        }
+        int n = NL;
+#pragma unroll
+        for (int lvl = 0; lvl < 4; ++lvl) {
+            if (n > 1) {
+                int m = 0;
+#pragma unroll
+                for (int j = 0; j < NL; j += 3) {
+                    if (j < n) {
+                        const uint32_t b = a[j], c = j + 1 < n ? a[j + 1] : b, d = j + 2 < n ? a[j + 2] : c;
+                        a[m++] = rr_pkmax3(b, c, d);
+                    }
+                }
+                n = m;
+            }
+        }
+        const uint32_t t = K > 1 ? a[0] : rr_pkmax3_x(a[0], a[0], a[0]);
+        pk = __ballot(rr_nan16(t)) == 0ull;
+        tm = __uint_as_float(t << 16);
     }
-    float tm = wm[0];
+    if (!pk) {
+        // the fp32 reading: every word's maximum, then the thread's
 #pragma unroll
-    for (int i = 1; i < NL; i += 2) tm = rr_max3(tm, wm[i], wm[i + 1 < NL ? i + 1 : i]);
+        for (int i = 0; i < NL; ++i) {
+            float x = rr_max3(RR_X(raw[i], 0), RR_X(raw[i], 1), RR_X(raw[i], 2));
+#pragma unroll
+            for (int e = 3; e < VEC; e += 2) x = rr_max3(x, RR_X(raw[i], e), RR_X(raw[i], e + 1 < VEC ? e + 1 : e));
+            wm[i] = x;
+        }
+        tm = wm[0];
+#pragma unroll
+        for (int i = 1; i < NL; i += 2) tm = rr_max3(tm, wm[i], wm[i + 1 < NL ? i + 1 : i]);
+    }
     // wave maximum and the candidate threshold: the K-th largest lane maximum
     // (exact, bit by bit; bf16 codes differ only in their top 16 bits) bounds
     // the workgroup's K-th largest element from below
@@ -250,6 +331,13 @@ __device__ __forceinline__ void rr_chunk(const void* row, int V, int g, int K, b
     const float M = unord_f32(bmax);
     const float tauf = bt ? unord_f32(bt) : -INFINITY;
     const float ML = M * DDT_LOG2E;
+    // a wave holding the maximum tests for it, word by word, in the words
+    // whose maximum is M
+    const bool mwave = __ballot(tm == M) != 0ull;
+    if (pk && K == 1 && mwave) {
+#pragma unroll
+        for (int i = 0; i < NL; ++i) wm[i] = __uint_as_float(pk_word(i) << 16);
+    }
     // pass 2 unpacks the raw words again: no unpacked copies live across the
     // passes (registers, not instructions, would bound the wide chunks)
 #pragma unroll
@@ -263,25 +351,32 @@ __device__ __forceinline__ void rr_chunk(const void* row, int V, int g, int K, b
     int ties = 0;
     if (!sums) {
         // max and top K only
-    } else if (__ballot(tm == M)) {
-        // a wave holding the maximum: leave out and count the elements equal to M
-#pragma unroll
-        for (int i = 0; i < NL; ++i) {
-#pragma unroll
-            for (int e = 0; e < VEC; e += 2) {
-                const float x0 = RR_X(raw[i], e), x1 = RR_X(raw[i], e + 1);
-                ties += (x0 == M) + (x1 == M);
-                s0 += x0 == M ? 0.f : __builtin_amdgcn_exp2f(fmaf(x0, DDT_LOG2E, -ML));
-                s1 += x1 == M ? 0.f : __builtin_amdgcn_exp2f(fmaf(x1, DDT_LOG2E, -ML));
-            }
-        }
-    } else {
+    } else if (!mwave) {
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
 #pragma unroll
             for (int e = 0; e < VEC; e += 2) {
                 s0 += __builtin_amdgcn_exp2f(fmaf(RR_X(raw[i], e), DDT_LOG2E, -ML));
                 s1 += __builtin_amdgcn_exp2f(fmaf(RR_X(raw[i], e + 1), DDT_LOG2E, -ML));
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            if (__ballot(wm[i] == M)) {
+#pragma unroll
+                for (int e = 0; e < VEC; e += 2) {
+                    const float x0 = RR_X(raw[i], e), x1 = RR_X(raw[i], e + 1);
+                    ties += (x0 == M) + (x1 == M);
+                    s0 += x0 == M ? 0.f : __builtin_amdgcn_exp2f(fmaf(x0, DDT_LOG2E, -ML));
+                    s1 += x1 == M ? 0.f : __builtin_amdgcn_exp2f(fmaf(x1, DDT_LOG2E, -ML));
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < VEC; e += 2) {
+                    s0 += __builtin_amdgcn_exp2f(fmaf(RR_X(raw[i], e), DDT_LOG2E, -ML));
+                    s1 += __builtin_amdgcn_exp2f(fmaf(RR_X(raw[i], e + 1), DDT_LOG2E, -ML));
+                }
             }
         }
     }
@@ -293,9 +388,11 @@ __device__ __forceinline__ void rr_chunk(const void* row, int V, int g, int K, b
             int idm = 0x7FFFFFFF;
 #pragma unroll
             for (int i = NL - 1; i >= 0; --i) {
+                if (wm[i] == M) {
 #pragma unroll
-                for (int e = VEC - 1; e >= 0; --e)
-                    if (RR_X(raw[i], e) == M) idm = RR_ID(i, e);
+                    for (int e = VEC - 1; e >= 0; --e)
+                        if (RR_X(raw[i], e) == M) idm = RR_ID(i, e);
+                }
             }
             atomicMin(&s_amin, idm);
         }
@@ -428,9 +525,11 @@ __device__ __forceinline__ void rr_chunk(const void* row, int V, int g, int K, b
 #undef RR_ID
 }
 
-// One workgroup reduces one chunk of one row.
+// One workgroup reduces one chunk of one row.  Seven workgroups per compute
+// unit (72 VGPRs) keep the wide chunks' waves resident seven to a SIMD; the
+// register allocator would otherwise take a few more and leave six.
 template <bool BF16, int NL>
-__global__ __launch_bounds__(RR_NT) void k_row_partial(RowSrc rs, int V, int groups, int K,
+__global__ __launch_bounds__(RR_NT, 7) void k_row_partial(RowSrc rs, int V, int groups, int K,
                                                        uint32_t* __restrict__ part) {
     __shared__ RRLds L;
     const int g = blockIdx.x % groups;

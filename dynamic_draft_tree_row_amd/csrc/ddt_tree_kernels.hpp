@@ -250,6 +250,7 @@ struct RerankArgs {
 #define RK_PER (DDT_MAX_NODES / RK_NT)   // nodes per thread
 #define RK_SORT DDT_MAX_NODES
 #define RK_CAND 1024
+#define RK_SMALL 256                     // rows of at most this many nodes skip the select
 
 // In-LDS bitonic sort of n2 (power of two) 64-bit keys, ascending.
 template <int NT>
@@ -346,9 +347,11 @@ __global__ __launch_bounds__(RK_NT) void k_rerank(RerankArgs a) {
     if (a.cast_on && tid < kmax) s_c[tid + 1] = (double)c_num / (double)c_den;
     if (tid == 0) { s_need = kmax; s_ngt = 0; s_ntie = 0; s_slot = 0; }
 
-    // radix select: T = code of the kmax-th largest value (0 when every node is kept)
+    // radix select: T = code of the kmax-th largest value (0 when every node
+    // is kept, or when the row is small enough that ranking all its nodes
+    // costs less than the select's four passes)
     uint32_t T = 0u;
-    if (kmax > 0 && kmax < N) {
+    if (kmax > 0 && kmax < N && N > RK_SMALL) {
         uint32_t prefix = 0u, pmask = 0u;
         for (int pass = 0; pass < 4; ++pass) {
             const int shift = 24 - 8 * pass;
