@@ -4,8 +4,8 @@
 A step is one full speculative-decoding round of the hot path on the CAST
 workload (B=8, V=128256, bf16 draft and target logits, depth 8, expand 10,
 60 verify tokens, CAST width / depth / verify-count selection, greedy verify):
-8 ddt_tree_expand layers, ddt_tree_rerank, ddt_tree_build_mask and
-ddt_tree_verify.  Inputs are seeded synthetic logits resident in HBM before the
+8 ddt_tree_expand layers, ddt_tree_select (rerank and flat layout in one
+launch) and ddt_tree_verify.  Inputs are seeded synthetic logits resident in HBM before the
 timed region, in a ring of rounds whose distinct logit bytes exceed 1 GB (more
 than twice the 256 MB last-level cache).  Each ring slot's round is captured
 once as a HIP graph (the kernels take every size from device memory, so no host

@@ -78,6 +78,8 @@ SIGNATURES = {
     "ddt_succ_gather": (C.c_int, [C.POINTER(Tree), P, i64, C.c_int, C.c_int, C.c_int, C.c_int,
                                   C.c_int, C.c_int, P, P, P]),
     "ddt_tree_build_mask": (C.c_int, [C.POINTER(Tree), P, P, C.c_int, C.POINTER(Flat), P, P]),
+    "ddt_tree_select": (C.c_int, [C.POINTER(Tree), C.c_int, C.POINTER(Cast), C.c_int, P, P, C.c_int,
+                                  C.POINTER(Flat), P, P]),
     "ddt_tree_verify": (C.c_int, [C.POINTER(Tree), C.POINTER(Flat), C.POINTER(Logits),
                                   C.POINTER(Logits), i64, P, P, C.c_int, C.c_int, P, P, P, P, P,
                                   P, sz, P]),

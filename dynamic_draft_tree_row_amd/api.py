@@ -197,6 +197,16 @@ def tree_build_mask(tree: DeviceTree, sel: torch.Tensor, m: torch.Tensor, prefix
         _stream(stream, sel.device)))
 
 
+def tree_select(tree: DeviceTree, m_max: int, sel: torch.Tensor, m_out: torch.Tensor, prefix_len: int,
+                flat: DeviceFlat, cast: Optional[CastParams] = None, use_k_draft: bool = False,
+                dense: Optional[torch.Tensor] = None, stream=None) -> None:
+    """ddt_tree_select: tree_rerank and tree_build_mask in one launch."""
+    cs = C.byref(cast.struct()) if cast is not None else None
+    L.check("ddt_tree_select", L.load().ddt_tree_select(
+        C.byref(tree.c), m_max, cs, int(use_k_draft), _ptr(sel), _ptr(m_out), prefix_len,
+        C.byref(flat.c), _ptr(dense), _stream(stream, sel.device)))
+
+
 PROPOSALS = {"draft": L.DDT_PROPOSAL_DRAFT, "point": L.DDT_PROPOSAL_POINT}
 
 

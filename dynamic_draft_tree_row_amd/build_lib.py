@@ -16,7 +16,7 @@ SOURCES = [
     ("ddt_attention.hip", ["-fno-honor-nans", "-mno-amdgpu-ieee"]),
 ]
 DEPS = ["ddt_api.hip", "ddt_attention.hip", "ddt_device.hpp", "ddt_rowreduce.hpp",
-        "ddt_tree_kernels.hpp", "ddt_attention.hpp"]
+        "ddt_tree_kernels.hpp", "ddt_layer.hpp", "ddt_kvcache.hpp", "ddt_attention.hpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -419,6 +419,29 @@ int ddt_tree_build_mask(const ddt_tree* t, const int32_t* sel, const int32_t* m,
     return launched();
 }
 
+int ddt_tree_select(const ddt_tree* t, int m_max, const ddt_cast* cast, int use_k_draft,
+                    int32_t* sel, int32_t* m_out, int prefix_len, const ddt_flat* f, uint8_t* dense,
+                    void* stream) {
+    int st = check_tree(t);
+    if (st) return st;
+    if (sel == nullptr || m_out == nullptr || m_max < 0) return DDT_EINVAL;
+    if (m_max > DDT_MAX_VERIFY) return DDT_ECAPACITY;
+    if (cast != nullptr && (st = check_cast(cast, t->B))) return st;
+    if (cast != nullptr && m_max > cast->N) return DDT_EINVAL;
+    if ((st = check_flat(f, t->B))) return st;
+    if (prefix_len < 0) return DDT_EINVAL;
+    if (f->P > MK_NT || f->W > 8) return DDT_ECAPACITY;
+    RerankArgs ra;
+    ra.t = *t;
+    if (cast) ra.c = *cast; else memset(&ra.c, 0, sizeof(ra.c));
+    ra.cast_on = cast != nullptr; ra.use_k_draft = use_k_draft != 0; ra.m_max = m_max;
+    ra.sel = sel; ra.m_out = m_out;
+    MaskArgs ma;
+    ma.t = *t; ma.f = *f; ma.sel = sel; ma.m = m_out; ma.prefix = prefix_len; ma.dense = dense;
+    hipLaunchKernelGGL(k_select, dim3(t->B), dim3(RK_NT), 0, (hipStream_t)stream, ra, ma);
+    return launched();
+}
+
 int ddt_tree_verify(const ddt_tree* t, const ddt_flat* f, const ddt_logits* target,
                     const ddt_logits* draft, int64_t draft_layer_stride, const float* temperature,
                     const float* uniforms, int proposal, int k_top, int32_t* row_topk,

@@ -140,29 +140,42 @@ __device__ void layer_frontier(const LayerArgs& a, int b, int base, int count, c
 
 // CAST's batch rule (key designs 2 and 3) in the last request of the layer;
 // with CAST every request has the same frontier width, so all B take part in
-// every layer that runs.  The inputs that do not depend on the layer (state,
-// cost-table entries) are staged in `region` (LDS) before the ticket.
-template <int NT>
-__device__ void layer_cast(const LayerArgs& a, unsigned char* region, int& s_flag) {
-    const ddt_tree& t = a.t;
-    const ddt_cast& cp = a.c;
-    const int tid = threadIdx.x, Rm = t.R_max, layer = a.layer;
-    const int B = t.B, Mc = cp.M, N = cp.N;
+// every layer that runs.  The inputs that do not depend on this layer's
+// frontiers (state, the layer's C1, cost-table entries) are staged in
+// `region` (LDS) beforehand by threads i0, i0 + stride, ... (cast_stage);
+// cast_finish then takes the batch ticket and, in the last request, reads the
+// frontiers and decides.
+__device__ __forceinline__ CastView cast_view(unsigned char* region, int B, int R_max, int M) {
     CastView L;
     L.v = (double*)region;                                       // [B][R_max] e^S of the frontiers
-    L.st = L.v + (size_t)B * Rm;                                 // [16] state
+    L.st = L.v + (size_t)B * R_max;                              // [16] state, [11] = C1 of the layer
     L.sd = (float*)(L.st + 16);                                  // [M][R_max] S_D columns 1..R_max
-    L.st1 = L.sd + (size_t)Mc * Rm;                              // [M] S_T column 1
-    for (int q = tid; q < Mc * Rm; q += NT) {
+    L.st1 = L.sd + (size_t)M * R_max;                            // [M] S_T column 1
+    return L;
+}
+
+__device__ void cast_stage(const LayerArgs& a, unsigned char* region, int i0, int stride) {
+    const ddt_tree& t = a.t;
+    const ddt_cast& cp = a.c;
+    const int Rm = t.R_max, layer = a.layer, Mc = cp.M, N = cp.N;
+    const CastView L = cast_view(region, t.B, Rm, Mc);
+    for (int q = i0; q < Mc * Rm; q += stride) {
         const int r = q / Rm, k = q - r * Rm;
         L.sd[q] = k < N ? cp.S_D[(size_t)r * (N + 1) + k + 1] : 0.f;
     }
-    if (tid < Mc) L.st1[tid] = cp.S_T[(size_t)tid * (N + 1) + 1];
-    if (tid < 11) {
+    for (int q = i0; q < Mc; q += stride) L.st1[q] = cp.S_T[(size_t)q * (N + 1) + 1];
+    for (int q = i0; q < 12; q += stride) {
         // layer 1 starts the state: FIFO {1}, length 1, no previous u_n, context 0
-        L.st[tid] = layer > 1 ? t.cast_state[tid]
-                              : tid == 0 ? 1.0 : tid == 8 ? 1.0 : tid == 9 ? -1.0 : 0.0;
+        L.st[q] = q == 11 ? (double)cp.C1[layer - 1]
+                : layer > 1 ? t.cast_state[q] : q == 0 ? 1.0 : q == 8 ? 1.0 : q == 9 ? -1.0 : 0.0;
     }
+}
+
+template <int NT>
+__device__ void cast_finish(const LayerArgs& a, unsigned char* region, int& s_flag) {
+    const ddt_tree& t = a.t;
+    const int tid = threadIdx.x, Rm = t.R_max, B = t.B;
+    const CastView L = cast_view(region, B, Rm, a.c.M);
     if (!ticket_last(t.ticket, (uint32_t)B, s_flag)) return;
     for (int q = tid; q < B * Rm; q += NT) L.v[q] = (double)expf(ld_coh_f32(t.front_S + q));
     int cnt = 0x7FFFFFFF;
@@ -170,7 +183,7 @@ __device__ void layer_cast(const LayerArgs& a, unsigned char* region, int& s_fla
     __syncthreads();
     if (tid < DDT_WAVE) {
         const int kc = (int)wave_min_u32((uint32_t)cnt);
-        cast_decide(L, t, cp, layer, min(min(a.K_e, Rm), kc));
+        cast_decide(L, t, a.c, a.layer, min(min(a.K_e, Rm), kc));
     }
 }
 
@@ -274,7 +287,10 @@ __global__ __launch_bounds__(RR_NT) void k_expand_layer(LayerArgs a) {
     if (!a.cast_on) return;
 
     // ---- D: CAST's batch rule --------------------------------------------------
-    layer_cast<RR_NT>(a, dyn + layer_lds_c(Rm, Kn), s_flag);
+    // (staging the inputs while wave 0 merges measured slower: the loads
+    // compete with the merge's)
+    cast_stage(a, dyn + layer_lds_c(Rm, Kn), tid, RR_NT);
+    cast_finish<RR_NT>(a, dyn + layer_lds_c(Rm, Kn), s_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -312,6 +328,7 @@ __global__ __launch_bounds__(EF_NT) void k_expand_finish(LayerArgs a) {
     const int base = layer == 1 ? 1 : t.n_nodes[b];
     const bool fits = base >= 1 && base + nrows * Kn <= cap;
     const int count = fits ? nrows * Kn : 0;
+    if (a.cast_on) cast_stage(a, dyn + finish_lds(Rm, Kn), tid, EF_NT);
     if (tid < nrows) {
         const int u0 = t.frontier[(size_t)b * Rm + tid];
         s_pn[tid] = layer == 1 ? 0 : ((u0 >= 0 && u0 < base) ? u0 : 0);
@@ -361,5 +378,5 @@ __global__ __launch_bounds__(EF_NT) void k_expand_finish(LayerArgs a) {
     __syncthreads();
     layer_frontier<EF_NT>(a, b, base, count, s_sk, s_pk);
     if (!a.cast_on) return;
-    layer_cast<EF_NT>(a, dyn + finish_lds(Rm, Kn), s_flag);
+    cast_finish<EF_NT>(a, dyn + finish_lds(Rm, Kn), s_flag);
 }

@@ -571,6 +571,15 @@ struct MergeIn {
     uint64_t kk[MRG_MR];                 // keys lane + 64 r, when they fit
 };
 
+// q / d for 0 <= q < 2^12 and 1 <= d <= 64, given rd = 1/d to within two
+// ulp: q * rd is then within 2^-11 of q/d (exact for d = 1), and a quotient
+// that is not an integer is at least 1/d >= 2^-6 below the next one, so
+// adding 2^-10 before truncating gives floor(q / d) exactly.  Three
+// instructions instead of an integer division's fifteen or so.
+__device__ __forceinline__ int small_div(int q, float rd) {
+    return (int)fmaf((float)q, rd, 0x1p-10f);
+}
+
 // Every lane loads, from a clamped address inside the row's partials, so that
 // the loads are straight-line code: a load under a branch ends in a register
 // copy that waits for it.  merge_finish masks the lanes past the data.
@@ -579,20 +588,21 @@ __device__ __forceinline__ void merge_issue(const uint32_t* __restrict__ p, int 
                                             MergeIn& in) {
     const int lane = threadIdx.x & (DDT_WAVE - 1);
     const int PS = rr_ps(K);
-    const int jth = (K + groups - 1) / groups;         // 1 <= jth <= K
+    const int jth = (K + groups - 1) / groups;         // 1 <= jth <= K (wave-uniform)
     const int total = groups * K;
+    const float rK = 1.0f / (float)K, rj = 1.0f / (float)jth;
     const int gl = lane < groups ? lane : 0;
     in.mc = __uint_as_float(rr_ld32<COH>(p + gl * PS));
     in.sc = __uint_as_float(rr_ld32<COH>(p + gl * PS + 1));
     // sample: the jth best keys of every group (groups * jth <= 64 lanes)
     const int hl = lane < groups * jth ? lane : 0;
-    const int hc = hl / jth, he = hl - hc * jth;
+    const int hc = small_div(hl, rj), he = hl - hc * jth;
     in.hv = rr_ld32<COH>(p + hc * PS + 2 + 2 * he + 1);   // high word (value code)
 #pragma unroll
     for (int r = 0; r < MRG_MR; ++r) {
         const int q = lane + r * DDT_WAVE;
         const int qc = q < total ? q : 0;
-        const int c = qc / K, e = qc - c * K;
+        const int c = small_div(qc, rK), e = qc - c * K;
         in.kk[r] = rr_ld64<COH>((const uint64_t*)(p + c * PS + 2 + 2 * e));
     }
 }

@@ -90,7 +90,7 @@ __device__ int anchor_scan_wave(const double* u, const double* c, double C, int 
 
 struct CastView {
     double* v;        // [B][R_max] e^S of every row's frontier, by rank
-    double* st;       // [11] state: FIFO [0..7], length, previous u_n, context
+    double* st;       // [12] state: FIFO [0..7], length, previous u_n, context; C1 of the layer
     float* sd;        // [M][R_max] S_D[row][1 .. R_max]
     float* st1;       // [M] S_T[row][1]
 };
@@ -178,7 +178,7 @@ __device__ void cast_decide(const CastView& L, const ddt_tree& t, const ddt_cast
     }
     const double u = wave_incl_scan_f64(mean);
     const double c = item ? (double)L.sd[row * R + lane] / (double)L.st1[row] : 0.0;
-    const int n = anchor_scan_regs(u, c, (double)cp.C1[layer - 1], kcap);
+    const int n = anchor_scan_regs(u, c, L.st[11], kcap);           // C1 of the layer
     const double un = n > 0 ? readlane_f64(u, n - 1) : 0.0;
     const double cn = n > 0 ? readlane_f64(c, n - 1) : 0.0;
     // gain FIFO (entries 0..7 of the state, one per lane), length, previous u_n
@@ -300,7 +300,10 @@ __device__ void rerank_sort_all(const float* S, const uint64_t* key, int N, int 
     __syncthreads();
 }
 
-__global__ __launch_bounds__(RK_NT) void k_rerank(RerankArgs a) {
+// Request blockIdx.x's selection (one workgroup of RK_NT threads): writes sel
+// and m_out, and leaves the selected nodes in rank order in LDS
+// (*nodes_lds[k] for k < m).  Returns m.
+__device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds) {
     const ddt_tree& t = a.t;
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     __shared__ int s_hist[256];
@@ -493,6 +496,13 @@ __global__ __launch_bounds__(RK_NT) void k_rerank(RerankArgs a) {
     for (int k = tid; k <= a.m_max; k += RK_NT)
         sel[k] = k == 0 ? 0 : (k <= m ? s_node[k - 1] : -1);
     if (tid == 0) a.m_out[b] = m;
+    *nodes_lds = s_node;
+    return m;
+}
+
+__global__ __launch_bounds__(RK_NT) void k_rerank(RerankArgs a) {
+    const int32_t* nodes;
+    rerank_row(a, &nodes);
 }
 
 // ---------------------------------------------------------------------------
@@ -608,11 +618,15 @@ struct MaskArgs {
 
 #define MK_NT 256
 
-// One workgroup per row, P <= MK_NT.  Two rounds of global loads (the
-// selection, then the selected nodes' key, token, parent and depth); flat
-// indices by rank counting on the keys; a node -> flat index table in LDS
-// gives each node's flat parent; leaves are numbered by a ballot prefix sum.
-__global__ __launch_bounds__(MK_NT) void k_build_mask(MaskArgs a) {
+// Request blockIdx.x's flat layout by one workgroup of NT >= MK_NT threads,
+// P <= MK_NT.  The selection comes from sel (global) or, when nodes_lds is
+// given, from the rerank of the same workgroup (node of selection index k >= 1
+// at nodes_lds[k - 1], m given).  One round of global loads for the selected
+// nodes' key, token, parent and depth; flat indices by rank counting on the
+// keys; a node -> flat index table in LDS gives each node's flat parent;
+// leaves are numbered by a ballot prefix sum.
+template <int NT>
+__device__ void mask_row(const MaskArgs& a, int m_in, const int32_t* nodes_lds) {
     const ddt_tree& t = a.t;
     const ddt_flat& f = a.f;
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -622,16 +636,16 @@ __global__ __launch_bounds__(MK_NT) void k_build_mask(MaskArgs a) {
     __shared__ int32_t s_fnode[MK_NT], s_ftok[MK_NT], s_fpn[MK_NT], s_fdep[MK_NT];
     __shared__ int s_fp[MK_NT], s_hc[MK_NT], s_lidx[MK_NT];
     __shared__ int16_t s_inv[DDT_MAX_NODES];
-    __shared__ int s_woff[MK_NT / 64];
-    const int m = min(max(a.m[b], 0), P - 1);
+    __shared__ int s_woff[NT / 64];
+    const int m = min(max(m_in, 0), P - 1);
     const int n = m + 1;
     const size_t o = (size_t)b * cap;
     const int32_t* sel = a.sel + (size_t)b * P;
     // the selection (issued with the count), then the selected nodes' records:
     // straight-line loads from clamped addresses, masked afterwards (a load
     // under a branch ends in a register copy that waits for it)
-    for (int q = tid; q < P; q += MK_NT) {
-        const int raw = sel[q];
+    for (int q = tid; q < P; q += NT) {
+        const int raw = nodes_lds == nullptr ? sel[q] : (q == 0 ? 0 : nodes_lds[q - 1]);
         int node = q <= m ? raw : -1;
         if (node < 0 || node >= cap) node = -1;
         const int nc = node >= 0 ? node : 0;
@@ -644,10 +658,10 @@ __global__ __launch_bounds__(MK_NT) void k_build_mask(MaskArgs a) {
         s_dep[q] = node >= 0 ? dv : 0;
         s_hc[q] = 0;
     }
-    for (int i = tid; i < cap; i += MK_NT) s_inv[i] = -1;
+    for (int i = tid; i < cap; i += NT) s_inv[i] = -1;
     __syncthreads();
     // flat index = rank of the key among the selected keys (keys are unique)
-    for (int q = tid; q < n; q += MK_NT) {
+    for (int q = tid; q < n; q += NT) {
         const uint64_t k = s_key[q];
         int r = 0;
 #pragma unroll 8
@@ -657,7 +671,7 @@ __global__ __launch_bounds__(MK_NT) void k_build_mask(MaskArgs a) {
     }
     __syncthreads();
     const size_t fo = (size_t)b * P;
-    for (int i = tid; i < P; i += MK_NT) {
+    for (int i = tid; i < P; i += NT) {
         int node = -1, tk = -1, fp = -1, d = 0;
         if (i < n && s_fnode[i] >= 0) {
             node = s_fnode[i];
@@ -682,7 +696,7 @@ __global__ __launch_bounds__(MK_NT) void k_build_mask(MaskArgs a) {
         __syncthreads();
         int off = 0, tot = 0;
 #pragma unroll
-        for (int w = 0; w < MK_NT / 64; ++w) { off += w < wid ? s_woff[w] : 0; tot += s_woff[w]; }
+        for (int w = 0; w < NT / 64; ++w) { off += w < wid ? s_woff[w] : 0; tot += s_woff[w]; }
         if (tid < P)
             s_lidx[tid] = leaf ? off + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u)) : -1;
@@ -691,7 +705,7 @@ __global__ __launch_bounds__(MK_NT) void k_build_mask(MaskArgs a) {
     }
     // ancestor mask: one thread per (row, word), walking the parent chain
     const int cols = a.prefix + P;
-    for (int q = tid; q < P * W; q += MK_NT) {
+    for (int q = tid; q < P * W; q += NT) {
         const int i = q / W, k = q - i * W;
         uint32_t word = 0u;
         int j = i, guard = 0;
@@ -712,8 +726,8 @@ __global__ __launch_bounds__(MK_NT) void k_build_mask(MaskArgs a) {
     int32_t* ret = f.retrieve + (size_t)b * L * (Dp + 1);
     int nl = 0;
 #pragma unroll
-    for (int w = 0; w < MK_NT / 64; ++w) nl += s_woff[w];
-    for (int i = tid; i < n; i += MK_NT) {
+    for (int w = 0; w < NT / 64; ++w) nl += s_woff[w];
+    for (int i = tid; i < n; i += NT) {
         const int li = s_lidx[i];
         if (li < 0 || li >= L) continue;
         int32_t* row = ret + (size_t)li * (Dp + 1);
@@ -725,7 +739,19 @@ __global__ __launch_bounds__(MK_NT) void k_build_mask(MaskArgs a) {
             j = j >= 0 ? s_fp[j] : -1;
         }
     }
-    for (int q = nl * (Dp + 1) + tid; q < L * (Dp + 1); q += MK_NT) ret[q] = -1;
+    for (int q = nl * (Dp + 1) + tid; q < L * (Dp + 1); q += NT) ret[q] = -1;
+}
+
+__global__ __launch_bounds__(MK_NT) void k_build_mask(MaskArgs a) {
+    mask_row<MK_NT>(a, a.m[blockIdx.x], nullptr);
+}
+
+// rerank and flat layout of one request in one workgroup (no Graft template
+// between them): the selection stays in LDS
+__global__ __launch_bounds__(RK_NT) void k_select(RerankArgs ra, MaskArgs ma) {
+    const int32_t* nodes;
+    const int m = rerank_row(ra, &nodes);
+    mask_row<RK_NT>(ma, m, nodes);
 }
 
 // ---------------------------------------------------------------------------

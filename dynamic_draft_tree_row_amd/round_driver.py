@@ -1,8 +1,8 @@
 """One speculative-decoding round composed from the library calls.
 
 draft(): layers 1..D of ddt_tree_expand (EAGLE-2 expansion; CAST width/depth or
-the Graft gate when given), ddt_tree_rerank, ddt_succ_gather (Graft) and
-ddt_tree_build_mask.  verify(): ddt_tree_verify and, for Graft,
+the Graft gate when given), then ddt_tree_select (rerank and flat layout in one
+launch), or for Graft ddt_tree_rerank, ddt_succ_gather and ddt_tree_build_mask.  verify(): ddt_tree_verify and, for Graft,
 ddt_succ_update.  Between the two a serving engine runs the target forward over
 the flattened tree; here the caller supplies the target logits.
 
@@ -86,12 +86,15 @@ class RoundRunner:
         for d in range(1, s.D + 1):
             api.tree_expand(self.tree, d, root_tok, draft_arena[d - 1], s.K_n, s.K_e, self.ws,
                             cast=cast, gate=gate, stream=stream)
+        if not s.graft:
+            api.tree_select(self.tree, s.m_max, self.sel, self.m_out, s.prefix, self.flat, cast=cast,
+                            use_k_draft=gate is not None, stream=stream)
+            return
         api.tree_rerank(self.tree, s.m_max, self.sel, self.m_out, cast=cast,
                         use_k_draft=gate is not None, stream=stream)
-        if s.graft:
-            api.succ_gather(self.tree, M, s.k_succ, s.tpl_depth, s.tpl_width, s.m_max, s.m_max,
-                            self.sel, self.m_out, shared=s.shared_M, anchor=s.graft_anchor,
-                            stream=stream)
+        api.succ_gather(self.tree, M, s.k_succ, s.tpl_depth, s.tpl_width, s.m_max, s.m_max,
+                        self.sel, self.m_out, shared=s.shared_M, anchor=s.graft_anchor,
+                        stream=stream)
         api.tree_build_mask(self.tree, self.sel, self.m_out, s.prefix, self.flat, stream=stream)
 
     def verify(self, target: torch.Tensor, draft_arena: Optional[torch.Tensor],

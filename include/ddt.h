@@ -315,6 +315,20 @@ int ddt_tree_build_mask(const ddt_tree* t /*host*/, const int32_t* sel, const in
                         void* stream);
 
 /*
+ * ddt_tree_select -- ddt_tree_rerank followed by ddt_tree_build_mask, for a
+ * round with no Graft template between them, in one launch: the selection
+ * goes from the rerank to the flattening in on-chip memory.  sel and m_out
+ * are written as ddt_tree_rerank writes them, and f (and dense) as
+ * ddt_tree_build_mask writes them from those; the results are the same as
+ * calling the two in turn.  Arguments and errors are those of the two calls
+ * ([E2] reranking section and engineering difficulty one; [CAST] key
+ * design 4).
+ */
+int ddt_tree_select(const ddt_tree* t /*host*/, int m_max, const ddt_cast* cast, int use_k_draft,
+                    int32_t* sel, int32_t* m_out, int prefix_len, const ddt_flat* f /*host*/,
+                    uint8_t* dense, void* stream);
+
+/*
  * ddt_tree_verify -- accept walk over the flattened tree ([E2] ledger and
  * losslessness sections, decode-step flow step 3).
  *

@@ -133,6 +133,10 @@ def test_calls_reject_bad_arguments_before_launch(lib):
                                None) == L.DDT_EINVAL
     f = L.Flat()
     assert lib.ddt_tree_build_mask(C.byref(t), dummy, dummy, 0, C.byref(f), None, None) == L.DDT_EINVAL
+    sl = lib.ddt_tree_select
+    assert sl(C.byref(t), 300, None, 0, dummy, dummy, 0, C.byref(f), None, None) == L.DDT_ECAPACITY
+    assert sl(C.byref(t), 10, None, 0, None, dummy, 0, C.byref(f), None, None) == L.DDT_EINVAL
+    assert sl(C.byref(t), 10, None, 0, dummy, dummy, 0, C.byref(f), None, None) == L.DDT_EINVAL
     assert lib.ddt_row_topk(C.byref(lg), 2, 3, 0, None, None, None, None, ws, 1 << 20, None) == L.DDT_EINVAL
     assert lib.ddt_row_topk(C.byref(lg), 2, 3, 40, None, None, None, None, ws, 1 << 20,
                             None) == L.DDT_ECAPACITY

@@ -345,6 +345,33 @@ def test_dense_mask_matches_the_bitmask_with_the_prefix(name):
         np.testing.assert_array_equal(d[b], want, err_msg=f"row {b}")
 
 
+@pytest.mark.parametrize("name", ["cast", "mixed_prefix", "eagle2_f32"])
+def test_select_equals_rerank_then_mask(name):
+    # ddt_tree_select (one launch) against ddt_tree_rerank + ddt_tree_build_mask
+    # on the same drafted trees: every output equal bit for bit
+    from dynamic_draft_tree_row_amd import api
+    w = SMALL[name]
+    case = _case(w, 3, 1)
+    run = H.runner_for(w)
+    cast = H.dev_cast(case.cast, "cuda", w.prefix) if case.cast else None
+    run.draft(H.to_dev(case.draft, w.dtype), torch.from_numpy(case.roots).cuda(), cast=cast)
+    P = w.m_max + 1
+    dense = torch.full((w.B, P, w.prefix + P), 7, dtype=torch.uint8, device="cuda")
+    api.tree_select(run.tree, w.m_max, run.sel, run.m_out, w.prefix, run.flat, cast=cast, dense=dense)
+    sel2 = torch.full_like(run.sel, -5)
+    m2 = torch.full_like(run.m_out, -5)
+    flat2 = api.DeviceFlat(w.B, w.m_max, run.shape.Dp, "cuda")
+    dense2 = torch.full_like(dense, 9)
+    api.tree_rerank(run.tree, w.m_max, sel2, m2, cast=cast)
+    api.tree_build_mask(run.tree, sel2, m2, w.prefix, flat2, dense=dense2)
+    torch.cuda.synchronize()
+    say(f"select vs rerank+mask {name}: m={m2.tolist()}")
+    assert torch.equal(run.sel, sel2) and torch.equal(run.m_out, m2)
+    assert torch.equal(dense, dense2)
+    for k in ("node", "token", "parent", "pos", "mask", "retrieve", "n_leaves", "m"):
+        assert torch.equal(getattr(run.flat, k), getattr(flat2, k)), k
+
+
 def test_graft_successor_matrix_resume():
     # M is the only state a round leaves for the next: a snapshot taken after
     # two rounds and restored replays the next two rounds bit for bit, and
