@@ -94,25 +94,23 @@ def test_measured_tables_on_device():
 
 @pytest.mark.gpu
 def test_cast_round_on_measured_tables():
+    # tables measured on this GPU are inputs like the logits: the oracle, fed
+    # the same S_T and S_D, must reproduce the library's round exactly (CAST
+    # key design 1: the tables are measured per GPU and batch size)
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no ROCm device")
-    from dynamic_draft_tree_row_amd import api
     from tests import harness as H
     w = configs.shrink(configs.C2, V=17000)
     cs = w.cast
     print(f"calibrate B={w.B} L={cs.L} M=2 N=64 for a CAST round", flush=True)
     S_T, S_D = CC.measure_tables(w.B, cs.L, 2, 64, reps=2)
-    f = lambda a: torch.tensor(np.asarray(a, np.float32), device="cuda")
-    cast = api.CastParams(S_T=f(S_T), S_D=f(S_D), L=cs.L, C1=f([cs.C1] * w.D), C2=cs.C2,
-                          C3=f([cs.C3] * w.B), R=cs.R, ctx_verify=w.prefix)
-    run = H.runner_for(w)
-    draft = H.to_dev(synth.draft_arena(w, 5, 0), w.dtype)
-    roots = torch.from_numpy(synth.root_tokens(w, 5, 0)).to("cuda")
-    run.draft(draft, roots, cast=cast)
-    torch.cuda.synchronize()
-    m = run.m_out.cpu().numpy()
-    n_nodes = run.tree.n_nodes.cpu().numpy()
-    print(f"measured S_T[0][1] {S_T[0, 1]:.1f} us, S_D[0][1] {S_D[0, 1]:.1f} us, "
-          f"nodes {n_nodes.tolist()}, verify counts {m.tolist()}", flush=True)
-    assert (n_nodes >= 1).all() and ((m >= 1) & (m <= w.m_max)).all() and (m < n_nodes).all()
+    cast = dict(S_T=S_T, S_D=S_D, L=cs.L, M=2, C1=[cs.C1] * w.D, C2=cs.C2, C3=[cs.C3] * w.B, R=cs.R)
+    for rnd in range(2):
+        case = H.oracle_case(w, 5, rnd, cast=cast)
+        r = H.gpu_round(case)
+        print(f"round {rnd}: measured S_T[0][1] {S_T[0, 1]:.1f} us, S_D[0][1] {S_D[0, 1]:.1f} us, "
+              f"widths {r['widths'].tolist()}, verify counts {r['m_out'].tolist()}", flush=True)
+        H.compare(case, r)
+        m, n_nodes = r["m_out"], r["n_nodes"]
+        assert (n_nodes >= 1).all() and ((m >= 1) & (m <= w.m_max)).all() and (m < n_nodes).all()
