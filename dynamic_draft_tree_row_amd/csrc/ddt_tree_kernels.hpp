@@ -257,8 +257,9 @@ template <int NT>
 __device__ void bitonic_sort_u64(uint64_t* v, int n2) {
     for (int k = 2; k <= n2; k <<= 1) {
         for (int j = k >> 1; j > 0; j >>= 1) {
+            const int lj = __ffs(j) - 1;                     // j is a power of two
             for (int t = threadIdx.x; t < (n2 >> 1); t += NT) {
-                const int i = ((t / j) * (j << 1)) + (t % j);
+                const int i = ((t >> lj) << (lj + 1)) + (t & (j - 1));
                 const int l = i + j;
                 const uint64_t x = v[i], y = v[l];
                 if ((x > y) == ((i & k) == 0)) { v[i] = y; v[l] = x; }
@@ -268,18 +269,11 @@ __device__ void bitonic_sort_u64(uint64_t* v, int n2) {
     }
 }
 
-// Fallback: full sort of the row's N non-root nodes by (~code, node), runs of
-// equal value re-ordered by canonical key; writes the first kmax nodes to
-// out_node in order.
+// Runs of equal value in sv[0 .. N) (sorted by (~code, node)) re-ordered by
+// canonical key, one thread per run (runs are rare outside degenerate rows).
 template <int NT>
-__device__ void rerank_sort_all(const float* S, const uint64_t* key, int N, int kmax, uint64_t* sv,
-                                int32_t* out_node) {
+__device__ void rerank_fix_ties(const uint64_t* key, int N, uint64_t* sv) {
     const int tid = threadIdx.x;
-    const int n2 = next_pow2(N > 0 ? N : 1);
-    for (int q = tid; q < n2; q += NT)
-        sv[q] = q < N ? ((uint64_t)~ord_f32(S[1 + q]) << 32) | (uint32_t)(1 + q) : ~0ull;
-    __syncthreads();
-    bitonic_sort_u64<NT>(sv, n2);
     for (int q = tid; q < N; q += NT) {
         const uint32_t hv = (uint32_t)(sv[q] >> 32);
         if ((q > 0 && (uint32_t)(sv[q - 1] >> 32) == hv) || q + 1 >= N ||
@@ -296,6 +290,21 @@ __device__ void rerank_sort_all(const float* S, const uint64_t* key, int N, int 
         }
     }
     __syncthreads();
+}
+
+// Fallback: full sort of the row's N non-root nodes by (~code, node), runs of
+// equal value re-ordered by canonical key; writes the first kmax nodes to
+// out_node in order.
+template <int NT>
+__device__ void rerank_sort_all(const float* S, const uint64_t* key, int N, int kmax, uint64_t* sv,
+                                int32_t* out_node) {
+    const int tid = threadIdx.x;
+    const int n2 = next_pow2(N > 0 ? N : 1);
+    for (int q = tid; q < n2; q += NT)
+        sv[q] = q < N ? ((uint64_t)~ord_f32(S[1 + q]) << 32) | (uint32_t)(1 + q) : ~0ull;
+    __syncthreads();
+    bitonic_sort_u64<NT>(sv, n2);
+    rerank_fix_ties<NT>(key, N, sv);
     for (int k = tid; k < kmax; k += NT) out_node[k] = (int32_t)(uint32_t)sv[k];
     __syncthreads();
 }
@@ -341,6 +350,7 @@ __device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds) {
     const float* ST = S;
     if (a.cast_on) ST = a.c.S_T + (size_t)cast_sel_row(a.c.ctx_verify, a.c.L, a.c.M) * (a.c.N + 1);
     const float c_num = ST[kc + 1], c_den = ST[1];
+    const float C3 = a.cast_on ? a.c.C3[b] : 0.f;       // requested with the rest
 #pragma unroll
     for (int i = 0; i < RK_PER; ++i) {
         const int q = tid + i * RK_NT;
@@ -352,7 +362,9 @@ __device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds) {
 
     // radix select: T = code of the kmax-th largest value (0 when every node
     // is kept, or when the row is small enough that ranking all its nodes
-    // costs less than the select's four passes)
+    // costs less than the select's four passes; sorting mid-sized rows whole
+    // measured slower: a barrier of the 1024-thread workgroup costs about
+    // 0.2 us, and a bitonic sort of 512 nodes takes 45 of them)
     uint32_t T = 0u;
     if (kmax > 0 && kmax < N && N > RK_SMALL) {
         uint32_t prefix = 0u, pmask = 0u;
@@ -363,7 +375,20 @@ __device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds) {
 #pragma unroll
             for (int i = 0; i < RK_PER; ++i) {
                 const int q = tid + i * RK_NT;
-                if (q < N && (o[i] & pmask) == prefix) atomicAdd(&s_hist[(o[i] >> shift) & 255], 1);
+                const bool act = q < N && (o[i] & pmask) == prefix;
+                const int bin = (int)((o[i] >> shift) & 255u);
+                // the wave's most common bins first, one atomic each (many
+                // nodes share the top byte of their code, and atomics on one
+                // LDS word serialize); the rest one by one
+                uint64_t pend = __ballot(act);
+                for (int rd = 0; rd < 2 && pend; ++rd) {
+                    const int leader = __ffsll((unsigned long long)pend) - 1;
+                    const int lb = __builtin_amdgcn_readlane(bin, leader);
+                    const uint64_t same = __ballot(act && bin == lb) & pend;
+                    if (lane == leader) atomicAdd(&s_hist[lb], (int)__popcll(same));
+                    pend &= ~same;
+                }
+                if ((pend >> lane) & 1ull) atomicAdd(&s_hist[bin], 1);
             }
             __syncthreads();
             if (wid == 0) {
@@ -372,12 +397,7 @@ __device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds) {
                 int h[4], loc = 0;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) { h[i] = s_hist[255 - 4 * lane - i]; loc += h[i]; }
-                int incl = loc;
-#pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const int v = __shfl_up(incl, d);
-                    if (lane >= d) incl += v;
-                }
+                const int incl = wave_incl_scan_i32(loc);
                 int ex = incl - loc;
                 if (ex < need && need <= incl) {
 #pragma unroll
@@ -393,7 +413,9 @@ __device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds) {
         }
         T = prefix;
     }
-    // candidates: every node strictly above T, and the ties at T
+    // candidates: every node strictly above T, and the ties at T (counted
+    // per wave: one LDS atomic per wave, since atomics on one LDS word from
+    // every thread serialize)
     {
         int ngt = 0, ntie = 0;
 #pragma unroll
@@ -402,8 +424,10 @@ __device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds) {
             ngt += (q < N) & (o[i] > T);
             ntie += (q < N) & (o[i] == T);
         }
-        if (ngt) atomicAdd(&s_ngt, ngt);
-        if (ntie) atomicAdd(&s_ntie, ntie);
+        const int wgt = __builtin_amdgcn_readlane(wave_incl_scan_i32(ngt), DDT_WAVE - 1);
+        const int wtie = __builtin_amdgcn_readlane(wave_incl_scan_i32(ntie), DDT_WAVE - 1);
+        if (lane == 0 && wgt) atomicAdd(&s_ngt, wgt);
+        if (lane == 0 && wtie) atomicAdd(&s_ntie, wtie);
     }
     __syncthreads();
     const int nc = s_ngt + s_ntie;
@@ -414,7 +438,12 @@ __device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds) {
         int mine = 0;
 #pragma unroll
         for (int i = 0; i < RK_PER; ++i) mine += (tid + i * RK_NT < N) & (o[i] >= T);
-        int slot = mine ? atomicAdd(&s_slot, mine) : 0;
+        // slots: a wave prefix of the counts and one LDS atomic per wave
+        const int incl = wave_incl_scan_i32(mine);
+        const int wtot = __builtin_amdgcn_readlane(incl, DDT_WAVE - 1);
+        int wbase = 0;
+        if (lane == 0 && wtot) wbase = atomicAdd(&s_slot, wtot);
+        int slot = __builtin_amdgcn_readfirstlane(wbase) + incl - mine;
 #pragma unroll
         for (int i = 0; i < RK_PER; ++i) {
             const int q = tid + i * RK_NT;
@@ -431,6 +460,8 @@ __device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds) {
         if (c < nc) {
             ca = s_ca[c];
             ck = s_ck[c];
+            // branch-free: equal value codes are common (bf16 logits repeat),
+            // and a branch per tie measured slower than the second load
 #pragma unroll 4
             for (int p = part; p < nc; p += SL) {
                 const uint32_t pa = s_ca[p];
@@ -456,7 +487,7 @@ __device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds) {
             const double v = item ? (double)expf(s_sv[lane]) : 0.0;
             const double u = wave_incl_scan_f64(v);
             const double c = item ? s_c[lane + 1] : 0.0;
-            const int m = anchor_scan_regs(u, c, (double)a.c.C3[b], kmax);
+            const int m = anchor_scan_regs(u, c, (double)C3, kmax);
             if (lane == 0) s_m = m;
         }
     } else if (a.cast_on) {
@@ -485,7 +516,7 @@ __device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds) {
             }
             if (lane == 0) { s_u[0] = 0.0; s_c[0] = 0.0; }
             wave_lds_sync();
-            const int m = anchor_scan_wave(s_u, s_c, (double)a.c.C3[b], kmax);
+            const int m = anchor_scan_wave(s_u, s_c, (double)C3, kmax);
             if (lane == 0) s_m = m;
         }
     } else if (tid == 0) {
