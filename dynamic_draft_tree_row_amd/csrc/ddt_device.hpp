@@ -37,19 +37,9 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
     }
     return v;
 }
-__device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-    return v;
-}
 __device__ __forceinline__ int wave_min_i32(int v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v = min(v, __shfl_xor(v, m));
-    return v;
-}
-__device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
     return v;
 }
 __device__ __forceinline__ double wave_sum_f64(double v) {

@@ -1,24 +1,12 @@
-// Tree kernels: attach + frontier, CAST width/depth, rerank, retrieval graft,
-// flatten + mask, accept walk, successor refresh.  One workgroup per batch row
+// Tree kernels: CAST's width/depth decision (run by the draft layer kernel),
+// rerank, retrieval graft, flatten + mask, the select (rerank and flatten in
+// one launch), accept walk, successor refresh.  One workgroup per batch row
 // unless noted; every index derived from device state is bounded by the
 // capacities passed in, so corrupt state cannot push an access out of range.
 #pragma once
 #include "ddt_device.hpp"
 #include "ddt_rowreduce.hpp"
 #include "../../include/ddt.h"
-
-// Rank of (a, k) among n entries of (sa, sb) in ascending (sa, sb) order: the
-// number of entries that precede it.  Entries are unique (keys differ).
-__device__ __forceinline__ int rank_among(const uint32_t* sa, const uint64_t* sb, int n, uint32_t a,
-                                          uint64_t k) {
-    int r = 0;
-#pragma unroll 8
-    for (int p = 0; p < n; ++p) {
-        const uint32_t ap = sa[p];
-        r += (ap < a) || (ap == a && sb[p] < k);
-    }
-    return r;
-}
 
 // ---------------------------------------------------------------------------
 // CAST width and depth for the whole batch
