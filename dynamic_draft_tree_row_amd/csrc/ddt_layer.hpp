@@ -81,7 +81,8 @@ __host__ __device__ __forceinline__ size_t layer_lds_c(int R_max, int K_n) {
     return ((size_t)R_max * K_n + R_max) * 8;                      // sort keys, parents' keys
 }
 __host__ __device__ __forceinline__ size_t layer_lds_d(int B, int R_max, int M) {
-    return (size_t)B * R_max * 8 + 16 * 8 + (((size_t)M * R_max + M) * 4 + 7) / 8 * 8;
+    (void)M;
+    return (size_t)B * R_max * 8 + 16 * 8 + (size_t)R_max * 8;
 }
 
 // Request b's next frontier from the layer's sort keys s_sk[count] and the
@@ -145,29 +146,36 @@ __device__ void layer_frontier(const LayerArgs& a, int b, int base, int count, c
 // `region` (LDS) beforehand by threads i0, i0 + stride, ... (cast_stage);
 // cast_finish then takes the batch ticket and, in the last request, reads the
 // frontiers and decides.
-__device__ __forceinline__ CastView cast_view(unsigned char* region, int B, int R_max, int M) {
+__device__ __forceinline__ CastView cast_view(unsigned char* region, int B, int R_max) {
     CastView L;
     L.v = (double*)region;                                       // [B][R_max] e^S of the frontiers
-    L.st = L.v + (size_t)B * R_max;                              // [16] state, [11] = C1 of the layer
-    L.sd = (float*)(L.st + 16);                                  // [M][R_max] S_D columns 1..R_max
-    L.st1 = L.sd + (size_t)M * R_max;                            // [M] S_T column 1
+    L.st = L.v + (size_t)B * R_max;                              // [16] state, C1, 1/B
+    L.c = L.st + 16;                                             // [R_max] width costs
     return L;
 }
 
+// The state (layer 1 starts it: FIFO {1}, length 1, no previous u_n,
+// context 0), the layer's C1, 1/B, and the width costs of this layer's
+// context row, c_k = S_D[sel(ctx)][k] / S_T[sel(ctx)][1] (the context is the
+// previous layer's state; each cost thread reads it itself).
 __device__ void cast_stage(const LayerArgs& a, unsigned char* region, int i0, int stride) {
     const ddt_tree& t = a.t;
     const ddt_cast& cp = a.c;
-    const int Rm = t.R_max, layer = a.layer, Mc = cp.M, N = cp.N;
-    const CastView L = cast_view(region, t.B, Rm, Mc);
-    for (int q = i0; q < Mc * Rm; q += stride) {
-        const int r = q / Rm, k = q - r * Rm;
-        L.sd[q] = k < N ? cp.S_D[(size_t)r * (N + 1) + k + 1] : 0.f;
-    }
-    for (int q = i0; q < Mc; q += stride) L.st1[q] = cp.S_T[(size_t)q * (N + 1) + 1];
-    for (int q = i0; q < 12; q += stride) {
-        // layer 1 starts the state: FIFO {1}, length 1, no previous u_n, context 0
-        L.st[q] = q == 11 ? (double)cp.C1[layer - 1]
-                : layer > 1 ? t.cast_state[q] : q == 0 ? 1.0 : q == 8 ? 1.0 : q == 9 ? -1.0 : 0.0;
+    const int Rm = t.R_max, layer = a.layer, N = cp.N;
+    const CastView L = cast_view(region, t.B, Rm);
+    for (int q = i0; q < 16 + Rm; q += stride) {
+        if (q < 12) {
+            L.st[q] = q == 11 ? (double)cp.C1[layer - 1]
+                    : layer > 1 ? t.cast_state[q] : q == 0 ? 1.0 : q == 8 ? 1.0 : q == 9 ? -1.0 : 0.0;
+        } else if (q == 12) {
+            L.st[12] = 1.0 / (double)t.B;
+        } else if (q >= 16) {
+            const int k = q - 16;
+            const int ctx = layer > 1 ? (int)t.cast_state[10] : 0;
+            const float* rowp = cp.S_D + (size_t)cast_sel_row(ctx, cp.L, cp.M) * (N + 1);
+            const float* rowt = cp.S_T + (size_t)cast_sel_row(ctx, cp.L, cp.M) * (N + 1);
+            L.c[k] = k < N ? (double)rowp[k + 1] / (double)rowt[1] : 0.0;
+        }
     }
 }
 
@@ -175,7 +183,7 @@ template <int NT>
 __device__ void cast_finish(const LayerArgs& a, unsigned char* region, int& s_flag) {
     const ddt_tree& t = a.t;
     const int tid = threadIdx.x, Rm = t.R_max, B = t.B;
-    const CastView L = cast_view(region, B, Rm, a.c.M);
+    const CastView L = cast_view(region, B, Rm);
     if (!ticket_last(t.ticket, (uint32_t)B, s_flag)) return;
     for (int q = tid; q < B * Rm; q += NT) L.v[q] = (double)expf(ld_coh_f32(t.front_S + q));
     int cnt = 0x7FFFFFFF;

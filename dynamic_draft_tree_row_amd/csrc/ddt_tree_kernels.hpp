@@ -72,15 +72,15 @@ __device__ int anchor_scan_wave(const double* u, const double* c, double C, int 
 }
 
 // CAST's batch rule runs in the last workgroup of a layer, on inputs staged
-// in LDS: the rows' frontier values, the per-round state, and the first
-// R_max entries of every cost-table row (M <= DDT_CAST_MAX_M).
+// in LDS: the rows' frontier values, the per-round state and the width costs
+// of the layer's context row.  Cost tables hold at most DDT_CAST_MAX_M rows.
 #define DDT_CAST_MAX_M 64
 
 struct CastView {
     double* v;        // [B][R_max] e^S of every row's frontier, by rank
-    double* st;       // [12] state: FIFO [0..7], length, previous u_n, context; C1 of the layer
-    float* sd;        // [M][R_max] S_D[row][1 .. R_max]
-    float* st1;       // [M] S_T[row][1]
+    double* st;       // [16] state: FIFO [0..7], length, previous u_n, context; [11] C1 of
+                      // the layer, [12] 1/B
+    double* c;        // [R_max] width costs c_k = S_D[sel(ctx)][k] / S_T[sel(ctx)][1], k = 1..
 };
 
 // Wave-level helpers for the batch rule (wave 0, all 64 lanes active).
@@ -156,16 +156,15 @@ __device__ void cast_decide(const CastView& L, const ddt_tree& t, const ddt_cast
     const int lane = threadIdx.x & (DDT_WAVE - 1), B = t.B, R = t.R_max;
     if (layer == 1 && lane < t.D_max) t.widths[lane] = 0;
     const int ctx = (int)L.st[10];
-    const int row = cast_sel_row(ctx, cp.L, cp.M);
     const bool item = lane < kcap;
     // column means of e^S, prefix-summed across lanes
     double mean = 0.0;
     if (item) {
         for (int b = 0; b < B; ++b) mean += L.v[b * R + lane];
-        mean *= 1.0 / (double)B;
+        mean *= L.st[12];                                   // 1.0 / B
     }
     const double u = wave_incl_scan_f64(mean);
-    const double c = item ? (double)L.sd[row * R + lane] / (double)L.st1[row] : 0.0;
+    const double c = item ? L.c[lane] : 0.0;
     const int n = anchor_scan_regs(u, c, L.st[11], kcap);           // C1 of the layer
     const double un = n > 0 ? readlane_f64(u, n - 1) : 0.0;
     const double cn = n > 0 ? readlane_f64(c, n - 1) : 0.0;
