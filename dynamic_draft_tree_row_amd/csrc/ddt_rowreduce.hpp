@@ -98,10 +98,25 @@ __device__ __forceinline__ int wave_incl_scan_i32(int v) {
     return v;
 }
 
+// Padding of a ragged bf16 chunk.  Wide chunks pad with -2^121, the smallest
+// bf16 value that pass 1's packed fp16 reading orders (it reads as fp16
+// -inf), so that their ragged chunks (one in eight of a row's chunks) stay on
+// the packed path; -inf padding reads as NaN and would send every wave of the
+// chunk to the fp32 reading.  A lane maximum equal to -2^121 is ambiguous and
+// takes the fp32 reading, which first restores -inf past V; on the packed path
+// the padding lies below the maximum, adds exp(-2^121 - M) = 0 to sigma' and
+// never reaches the (finite) threshold.  Short chunks keep -inf: there the
+// ragged chunk is one in sixteen and the extra code costs more than it saves.
+template <bool BF16, int NL> struct RRPad {
+    static constexpr bool low = BF16 && NL >= RR_NV_WIDE;
+    static constexpr uint32_t pad16 = low ? 0xFC00u : 0xFF80u;
+};
+
 template <bool BF16, int NL>
 __device__ __forceinline__ void rr_load(u32x4 (&raw)[NL], const void* row, bool al, int start,
                                         int V, int tid) {
     using SH = RRShape<BF16, NL>;
+    constexpr uint32_t pad16 = RRPad<BF16, NL>::pad16;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
         const int e0 = start + (i * RR_NT + tid) * SH::VEC;
@@ -109,14 +124,14 @@ __device__ __forceinline__ void rr_load(u32x4 (&raw)[NL], const void* row, bool 
             raw[i] = __builtin_nontemporal_load(
                 (const u32x4*)((const char*)row + (size_t)e0 * (BF16 ? 2 : 4)));
         } else {
-            // ragged tail or unaligned row: element-wise, -inf past V
+            // ragged tail or unaligned row: element-wise, padding past V
             uint32_t w[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 if constexpr (BF16) {
                     const int a = e0 + 2 * q, b = a + 1;
-                    const uint32_t lo = a < V ? (uint32_t)((const uint16_t*)row)[a] : 0xFF80u;
-                    const uint32_t hi = b < V ? (uint32_t)((const uint16_t*)row)[b] : 0xFF80u;
+                    const uint32_t lo = a < V ? (uint32_t)((const uint16_t*)row)[a] : pad16;
+                    const uint32_t hi = b < V ? (uint32_t)((const uint16_t*)row)[b] : pad16;
                     w[q] = lo | (hi << 16);
                 } else {
                     const int a = e0 + q;
@@ -235,10 +250,11 @@ __device__ __forceinline__ void rr_chunk(const void* row, int V, int g, int K, b
     rr_load<BF16, NL>(raw, row, al, start, V, tid);
     if (tid == 0) { s_cnt = 0; s_ties = 0; s_amin = 0x7FFFFFFF; }
 
-    // pass 1: the thread maximum (padding is -inf).  bf16 words take the
-    // packed fp16 maximum, two 32-bit registers per instruction; a wave in
-    // which some lane's result is NaN (a value of magnitude above 2^121, an
-    // infinity or a NaN) takes the fp32 reading instead.
+    // pass 1: the thread maximum (padding is -inf, or -2^121: RRPad).  bf16
+    // words take the packed fp16 maximum, two 32-bit registers per
+    // instruction; a wave in which some lane's result is NaN (a value of
+    // magnitude above 2^121, an infinity or a NaN) takes the fp32 reading
+    // instead.
     bool pk = false;                                           // wave-uniform
     float tm = -INFINITY;
     float wm[NL];                                              // word maxima (when needed)
@@ -286,11 +302,25 @@ __device__ __forceinline__ void rr_chunk(const void* row, int V, int g, int K, b
             }
         }
         const uint32_t t = K > 1 ? a[0] : rr_pkmax3_x(a[0], a[0], a[0]);
-        pk = __ballot(rr_nan16(t)) == 0ull;
+        pk = __ballot(rr_nan16(t) | (RRPad<BF16, NL>::low && (t & 0xFFFFu) == 0xFC00u)) == 0ull;
         tm = __uint_as_float(t << 16);
     }
     if (!pk) {
-        // the fp32 reading: every word's maximum, then the thread's
+        // the fp32 reading: every word's maximum, then the thread's (a ragged
+        // chunk's -2^121 padding set to -inf first)
+        if (RRPad<BF16, NL>::low && start + CH > V) {
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int a = RR_ID(i, 2 * q);
+                    uint32_t x = raw[i][q];
+                    if (a >= V) x = (x & 0xFFFF0000u) | 0xFF80u;
+                    if (a + 1 >= V) x = (x & 0x0000FFFFu) | 0xFF800000u;
+                    raw[i][q] = x;
+                }
+            }
+        }
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             float x = rr_max3(RR_X(raw[i], 0), RR_X(raw[i], 1), RR_X(raw[i], 2));
@@ -401,7 +431,8 @@ __device__ __forceinline__ void rr_chunk(const void* row, int V, int g, int K, b
         // of a wave whose maximum reaches the threshold (usually a few) stage
         // their loaded words in LDS; the whole wave then tests those elements,
         // one per lane, and appends the ones that qualify.  Ids need checking
-        // only in a ragged chunk or when the threshold is -inf (padding is -inf).
+        // only in a ragged chunk or when the threshold is -inf (padding
+        // qualifies only against a threshold of -inf).
         const bool chk = !(tauf > -INFINITY) || start + CH > V;
         const uint64_t pm = __ballot(tm >= tauf);
         if (pm) {

@@ -118,6 +118,75 @@ def test_row_topk_parity_wide_launch(dtype, V):
             np.testing.assert_allclose(sp_h[i], s_, rtol=1e-5, atol=1e-30)
 
 
+def _rows_special(V, dtype, seed):
+    """Rows with values the packed bf16 reading of the reduction cannot order:
+    masked (-inf) entries, whole masked chunks, the bf16 value -2^121 that the
+    kernels use as padding (as data, and filling the ragged last chunk), and
+    a value of magnitude 2^125 (read as fp16 NaN)."""
+    g = np.random.default_rng(seed)
+    rows = []
+    r = (g.standard_normal(V) * 2).astype(np.float32)
+    r[g.random(V) < 0.3] = -np.inf                                          # masked entries
+    r[g.integers(0, V, size=40)] = 5.0                                       # >= 32 finite survivors
+    rows.append(r)
+    r = (g.standard_normal(V) * 1.5).astype(np.float32)
+    r[: min(V - 40, 20000)] = -np.inf                                        # whole masked chunks
+    rows.append(r)
+    r = g.standard_normal(V).astype(np.float32)
+    r[g.integers(0, V, size=min(V, 50))] = -(2.0 ** 121)                     # the padding value as data
+    rows.append(r)
+    r = g.standard_normal(V).astype(np.float32)
+    r[V - min(V, 20000):] = -(2.0 ** 121)                                    # ...filling the last chunks
+    r[: min(V, 40)] = 3.0
+    rows.append(r)
+    rows.append(np.full(V, -(2.0 ** 121), np.float32))                       # ...everywhere
+    r = g.standard_normal(V).astype(np.float32)
+    r[g.integers(0, V, size=3)] = 2.0 ** 125                                 # fp16 reading: NaN
+    r[g.integers(0, V, size=5)] = -(2.0 ** 124)
+    rows.append(r)
+    return np.stack([synth.cast_row(x, dtype) for x in rows])
+
+
+def _check_rows(raw, dtype, n, K, ids, lc, mx, sp):
+    ids_h, lc_h, mx_h, sp_h = ids.cpu().numpy(), lc.cpu().numpy(), mx.cpu().numpy(), sp.cpu().numpy()
+    for i in range(n):
+        l = O.decode(raw[i], dtype)
+        m, _, s_ = O.row_stats(l)
+        want = O.topk_ids(l, K)
+        assert ids_h[i].tolist() == want.tolist(), f"row {i} K={K}"
+        np.testing.assert_allclose(lc_h[i], O.log_conf(l, want, m, s_), rtol=1e-5, atol=1e-30)
+        assert mx_h[i] == np.float32(m)
+        np.testing.assert_allclose(sp_h[i], s_, rtol=1e-5, atol=1e-30)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [8193, 33001, 128256])
+@pytest.mark.parametrize("wide", [False, True])
+def test_row_topk_parity_special_values(dtype, V, wide):
+    # wide: 260 rows, so that the chunks are twice as long
+    from dynamic_draft_tree_row_amd import api
+    raw = _rows_special(V, dtype, V + 7)
+    if wide:
+        g = np.random.default_rng(V)
+        extra = np.stack([synth.cast_row((g.standard_normal(V) * g.uniform(0.3, 3)).astype(np.float32), dtype)
+                          for _ in range(260 - raw.shape[0])])
+        raw = np.concatenate([raw, extra])
+    n = raw.shape[0]
+    host = np.zeros((1, n, V + 3), raw.dtype)
+    host[0, :, :V] = raw
+    x = H.to_dev(host, dtype)[:, :, :V]
+    for K in (1, 10, 32):
+        say(f"row_topk special dtype={dtype} V={V} wide={wide} K={K}")
+        ws = torch.empty(api.workspace_bytes(n, V, x.dtype, K), dtype=torch.uint8, device="cuda")
+        ids = torch.empty((n, K), dtype=torch.int32, device="cuda")
+        lc = torch.empty((n, K), dtype=torch.float32, device="cuda")
+        mx = torch.empty(n, dtype=torch.float32, device="cuda")
+        sp = torch.empty(n, dtype=torch.float32, device="cuda")
+        api.row_topk(x, K, ws, ids, lc, mx, sp)
+        torch.cuda.synchronize()
+        _check_rows(raw, dtype, min(n, 12), K, ids, lc, mx, sp)
+
+
 # ---------------------------------------------------------------------------
 # whole rounds, small vocabularies
 # ---------------------------------------------------------------------------
