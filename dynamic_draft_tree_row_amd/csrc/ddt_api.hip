@@ -24,8 +24,12 @@ namespace {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Launches of RR_WIDE_ROWS rows or more reduce wide chunks.
-inline bool wide_rows(long long rows) { return rows >= RR_WIDE_ROWS; }
+// Launches of RR_WIDE_ROWS rows or more reduce wide chunks; launches over the
+// flat verify rows from RR_WIDE_FLAT_ROWS rows on (only each request's first
+// m_b + 1 of its P rows are live, so fewer chunks are actually reduced).
+inline bool wide_rows(long long rows, bool flat = false) {
+    return rows >= (flat ? RR_WIDE_FLAT_ROWS : RR_WIDE_ROWS);
+}
 
 inline int chunk_elems(int dtype, bool wide) {
     if (dtype == DDT_BF16) return wide ? RRShape<true, RR_NV_WIDE>::CH : RRShape<true, RR_NV>::CH;
@@ -40,8 +44,8 @@ inline int chunks_of(int V, int dtype) {
 
 // Partials per row (one per chunk) of a launch over `rows` rows; the producer
 // and its consumers call this with the same rows, so they agree.
-inline int groups_of(long long rows, int V, int dtype) {
-    const int ch = chunk_elems(dtype, wide_rows(rows));
+inline int groups_of(long long rows, int V, int dtype, bool flat = false) {
+    const int ch = chunk_elems(dtype, wide_rows(rows, flat));
     return (V + ch - 1) / ch;
 }
 
@@ -166,16 +170,17 @@ int launch_timed(int part, Kern kern, dim3 grid, dim3 blk, size_t lds, hipStream
 }
 
 int launch_partials(const ddt_logits* x, int n0, int n1, const int32_t* count, int count_add,
-                    int K, void* ws, hipStream_t s, const float* sum_if = nullptr, int part = 0) {
+                    int K, void* ws, hipStream_t s, const float* sum_if = nullptr, int part = 0,
+                    bool flat = false) {
     RowSrc rs{};
     rs.base = x->data; rs.s0 = x->s0; rs.s1 = x->s1; rs.n1 = n1;
     rs.count = count; rs.count_add = count_add; rs.sum_if = sum_if;
     const long long rows = (long long)n0 * n1;
-    const int groups = groups_of(rows, x->V, x->dtype);
+    const int groups = groups_of(rows, x->V, x->dtype, flat);
     const long long total = rows * groups;
     if (total <= 0) return DDT_OK;
     if (total > INT32_MAX) return DDT_ECAPACITY;
-    const bool bf16 = x->dtype == DDT_BF16, wide = wide_rows(rows);
+    const bool bf16 = x->dtype == DDT_BF16, wide = wide_rows(rows, flat);
     const dim3 grid((unsigned)total), blk(RR_NT);
     auto kern = bf16 ? (wide ? &k_row_partial<true, RR_NV_WIDE> : &k_row_partial<true, RR_NV>)
                      : (wide ? &k_row_partial<false, RR_NV_WIDE> : &k_row_partial<false, RR_NV>);
@@ -469,11 +474,11 @@ int ddt_tree_verify(const ddt_tree* t, const ddt_flat* f, const ddt_logits* targ
         return DDT_EWORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     // greedy requests (temperature 0) use only the rows' argmax and top k
-    st = launch_partials(target, t->B, f->P, f->m, 1, Kp, ws, s, temperature);
+    st = launch_partials(target, t->B, f->P, f->m, 1, Kp, ws, s, temperature, 0, true);
     if (st) return st;
     VerifyArgs a;
     a.t = *t; a.f = *f; a.part = (const uint32_t*)ws;
-    a.chunks = groups_of((long long)t->B * f->P, target->V, target->dtype); a.Kp = Kp;
+    a.chunks = groups_of((long long)t->B * f->P, target->V, target->dtype, true); a.Kp = Kp;
     a.tgt = target->data; a.bf16 = target->dtype == DDT_BF16; a.V = target->V;
     a.ts0 = target->s0; a.ts1 = target->s1;
     a.point = proposal == DDT_PROPOSAL_POINT;
@@ -663,9 +668,9 @@ int ddt_succ_update(int32_t* M, int64_t M_bstride, int V, int k_succ, const ddt_
         if (target->dtype != DDT_F32 && target->dtype != DDT_BF16) return DDT_EDTYPE;
         if (chunks_of(V, target->dtype) > DDT_MAX_CHUNKS) return DDT_ECAPACITY;
         if (ws_bytes < ws_need((long long)f->B * f->P, V, target->dtype, k_succ)) return DDT_EWORKSPACE;
-        st = launch_partials(target, f->B, f->P, f->m, 1, k_succ, ws, s);
+        st = launch_partials(target, f->B, f->P, f->m, 1, k_succ, ws, s, nullptr, 0, true);
         if (st) return st;
-        a.part = (const uint32_t*)ws; a.chunks = groups_of((long long)f->B * f->P, V, target->dtype);
+        a.part = (const uint32_t*)ws; a.chunks = groups_of((long long)f->B * f->P, V, target->dtype, true);
     }
     hipLaunchKernelGGL(k_succ_update, dim3(a.shared ? 1 : f->B), dim3(UP_NT), 0, s, a);
     return launched();

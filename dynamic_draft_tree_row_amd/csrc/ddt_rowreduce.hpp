@@ -24,6 +24,7 @@
 #define RR_NV 4             // 16-byte loads per thread per chunk (small launches)
 #define RR_NV_WIDE 8        // the same for launches of RR_WIDE_ROWS rows or more
 #define RR_WIDE_ROWS 256
+#define RR_WIDE_FLAT_ROWS 512
 #define RR_CAP 1024         // LDS candidate list
 #define RR_SW 64            // words per wave staged at a time
 

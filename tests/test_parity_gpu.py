@@ -262,6 +262,22 @@ def test_graft_small_multi_round():
         M = case.M_after
 
 
+def test_graft_wide_flat_rows():
+    # 18 requests x 61 flat rows: launches over the flat verify rows of 512
+    # rows or more reduce wide chunks, in the verify and in the successor
+    # refresh alike
+    w = configs.shrink(configs.C4, V=4100, B=18)
+    assert w.B * (w.m_max + 1) >= 512
+    tau = H.calibrate_tau(w, 79, 4)
+    M = synth.succ_matrix0(w, 79)
+    M0 = M.copy()
+    for rnd in range(2):
+        case = H.oracle_case(w, 79, rnd, cast=None, graft=H.graft_params(w, tau), M=M, M0=M0)
+        say(f"graft wide flat round {rnd} k_draft={case.out['draft'].k_draft}")
+        H.compare(case, H.gpu_round(case))
+        M = case.M_after
+
+
 @pytest.mark.parametrize("proposal", ["draft", "point"])
 def test_graft_stochastic_verify_point_mass(proposal):
     # Graft with T > 0: retrieval nodes are verified with point-mass
