@@ -81,8 +81,8 @@ __host__ __device__ __forceinline__ size_t layer_lds_c(int R_max, int K_n) {
     return ((size_t)R_max * K_n + R_max) * 8;                      // sort keys, parents' keys
 }
 __host__ __device__ __forceinline__ size_t layer_lds_d(int B, int R_max, int M) {
-    (void)M;
-    return (size_t)B * R_max * 8 + 16 * 8 + (size_t)R_max * 8;
+    (void)B; (void)M;
+    return 16 * 8 + (size_t)R_max * 8;
 }
 
 // Request b's next frontier from the layer's sort keys s_sk[count] and the
@@ -144,12 +144,12 @@ __device__ void layer_frontier(const LayerArgs& a, int b, int base, int count, c
 // every layer that runs.  The inputs that do not depend on this layer's
 // frontiers (state, the layer's C1, cost-table entries) are staged in
 // `region` (LDS) beforehand by threads i0, i0 + stride, ... (cast_stage);
-// cast_finish then takes the batch ticket and, in the last request, reads the
-// frontiers and decides.
-__device__ __forceinline__ CastView cast_view(unsigned char* region, int B, int R_max) {
+// cast_finish then takes the batch ticket and, in the last request, wave 0
+// reads the frontiers (lane k the k-th node of every request) and decides.
+__device__ __forceinline__ CastView cast_view(unsigned char* region, int R_max) {
+    (void)R_max;
     CastView L;
-    L.v = (double*)region;                                       // [B][R_max] e^S of the frontiers
-    L.st = L.v + (size_t)B * R_max;                              // [16] state, C1, 1/B
+    L.st = (double*)region;                                      // [16] state, C1, 1/B
     L.c = L.st + 16;                                             // [R_max] width costs
     return L;
 }
@@ -162,7 +162,7 @@ __device__ void cast_stage(const LayerArgs& a, unsigned char* region, int i0, in
     const ddt_tree& t = a.t;
     const ddt_cast& cp = a.c;
     const int Rm = t.R_max, layer = a.layer, N = cp.N;
-    const CastView L = cast_view(region, t.B, Rm);
+    const CastView L = cast_view(region, Rm);
     for (int q = i0; q < 16 + Rm; q += stride) {
         if (q < 12) {
             L.st[q] = q == 11 ? (double)cp.C1[layer - 1]
@@ -182,17 +182,26 @@ __device__ void cast_stage(const LayerArgs& a, unsigned char* region, int i0, in
 template <int NT>
 __device__ void cast_finish(const LayerArgs& a, unsigned char* region, int& s_flag) {
     const ddt_tree& t = a.t;
-    const int tid = threadIdx.x, Rm = t.R_max, B = t.B;
-    const CastView L = cast_view(region, B, Rm);
+    const int tid = threadIdx.x, lane = tid & (DDT_WAVE - 1), Rm = t.R_max, B = t.B;
+    const CastView L = cast_view(region, Rm);
     if (!ticket_last(t.ticket, (uint32_t)B, s_flag)) return;
-    for (int q = tid; q < B * Rm; q += NT) L.v[q] = (double)expf(ld_coh_f32(t.front_S + q));
-    int cnt = 0x7FFFFFFF;
-    if (tid < B) cnt = max(0, ld_coh_i32(t.n_nodes + tid) - ld_coh_i32(t.layer_base + tid));
-    __syncthreads();
-    if (tid < DDT_WAVE) {
-        const int kc = (int)wave_min_u32((uint32_t)cnt);
-        cast_decide(L, t, a.c, a.layer, min(min(a.K_e, Rm), kc));
+    if (tid >= DDT_WAVE) return;                                 // wave 0 decides
+    // every request's node count and this lane's column of frontier values,
+    // requested together (straight-line loads from clamped addresses)
+    const int lb = lane < B ? lane : 0, kl = lane < Rm ? lane : 0;
+    const int nn = ld_coh_i32(t.n_nodes + lb), lbase = ld_coh_i32(t.layer_base + lb);
+    double mean = 0.0;                                           // column sum of e^S, b ascending
+    for (int b0 = 0; b0 < B; b0 += 8) {
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = ld_coh_f32(t.front_S + (size_t)min(b0 + j, B - 1) * Rm + kl);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (b0 + j < B) mean += (double)expf(x[j]);
     }
+    const int cnt = lane < B ? max(0, nn - lbase) : 0x7FFFFFFF;
+    const int kcap = min(min(a.K_e, Rm), (int)wave_min_u32((uint32_t)cnt));
+    cast_decide(L, t, a.c, a.layer, kcap, lane < kcap ? mean * L.st[12] : 0.0);
 }
 
 template <bool BF16, int NL>

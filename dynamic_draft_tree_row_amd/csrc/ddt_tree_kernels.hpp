@@ -77,7 +77,6 @@ __device__ int anchor_scan_wave(const double* u, const double* c, double C, int 
 #define DDT_CAST_MAX_M 64
 
 struct CastView {
-    double* v;        // [B][R_max] e^S of every row's frontier, by rank
     double* st;       // [16] state: FIFO [0..7], length, previous u_n, context; [11] C1 of
                       // the layer, [12] 1/B
     double* c;        // [R_max] width costs c_k = S_D[sel(ctx)][k] / S_T[sel(ctx)][1], k = 1..
@@ -146,23 +145,19 @@ __device__ __forceinline__ int anchor_scan_regs(double u, double c, double C, in
     return a;
 }
 
-// The batch rule, run by wave 0 of the layer's last workgroup once
-// L.v[b * R_max + k] = e^S of row b's k-th frontier node is in LDS (k < kcap
-// <= 32): width by the anchor scan on the batch-averaged cumulative utility,
+// The batch rule, run by wave 0 of the layer's last workgroup with mean (lane
+// k - 1) = the batch average of e^S over every row's k-th frontier node (k <=
+// kcap <= 32): width by the anchor scan on the batch-averaged cumulative utility,
 // then the depth gate with the gain FIFO; every row's n_front gets the
 // result.  Item k (1-based) lives in lane k - 1: u_k, c_k in registers; the
 // anchor scan works on ballot masks and the FIFO on lanes 0..7.
-__device__ void cast_decide(const CastView& L, const ddt_tree& t, const ddt_cast& cp, int layer, int kcap) {
-    const int lane = threadIdx.x & (DDT_WAVE - 1), B = t.B, R = t.R_max;
+__device__ void cast_decide(const CastView& L, const ddt_tree& t, const ddt_cast& cp, int layer, int kcap,
+                            double mean) {
+    const int lane = threadIdx.x & (DDT_WAVE - 1), B = t.B;
     if (layer == 1 && lane < t.D_max) t.widths[lane] = 0;
     const int ctx = (int)L.st[10];
     const bool item = lane < kcap;
-    // column means of e^S, prefix-summed across lanes
-    double mean = 0.0;
-    if (item) {
-        for (int b = 0; b < B; ++b) mean += L.v[b * R + lane];
-        mean *= L.st[12];                                   // 1.0 / B
-    }
+    // column means of e^S (lane k - 1: item k), prefix-summed across lanes
     const double u = wave_incl_scan_f64(mean);
     const double c = item ? L.c[lane] : 0.0;
     const int n = anchor_scan_regs(u, c, L.st[11], kcap);           // C1 of the layer
