@@ -299,6 +299,7 @@ __device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds) {
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     __shared__ int s_hist[256];
     __shared__ int s_bin, s_need, s_ngt, s_ntie, s_slot, s_m;
+    __shared__ uint32_t s_T;
     __shared__ uint32_t s_ca[RK_CAND];
     __shared__ uint64_t s_ck[RK_CAND];
     __shared__ int32_t s_cn[RK_CAND];
@@ -343,12 +344,43 @@ __device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds) {
     if (tid == 0) { s_need = kmax; s_ngt = 0; s_ntie = 0; s_slot = 0; }
 
     // radix select: T = code of the kmax-th largest value (0 when every node
-    // is kept, or when the row is small enough that ranking all its nodes
-    // costs less than the select's four passes; sorting mid-sized rows whole
-    // measured slower: a barrier of the 1024-thread workgroup costs about
-    // 0.2 us, and a bitonic sort of 512 nodes takes 45 of them)
+    // is kept; sorting mid-sized rows whole measured slower: a barrier of the
+    // 1024-thread workgroup costs about 0.2 us, and a bitonic sort of 512
+    // nodes takes 45 of them).  Small rows take a lower bound instead: wave 0
+    // holds all their codes (four per lane) and finds, bit by bit over the top
+    // 16 bits, the largest 16-bit prefix p with at least kmax codes >= p << 16;
+    // then T' = p << 16 <= T (T's own prefix qualifies, and a larger T' would
+    // leave fewer than kmax codes above T), and the few codes below T in T's
+    // 16-bit bucket join the candidates.  Ranking every node of a 150-node row
+    // cost 2.2 us against about 0.3 us for the search.
+    const bool small = N <= RK_SMALL;
     uint32_t T = 0u;
-    if (kmax > 0 && kmax < N && N > RK_SMALL) {
+    if (small) {
+        // (the barrier also orders the counters' initialisation before the
+        // listing's atomics)
+        if (wid == 0) {
+            uint32_t p = 0u;
+            if (kmax > 0 && kmax < N) {
+                uint32_t oc[RK_SMALL / DDT_WAVE];
+#pragma unroll
+                for (int j = 0; j < RK_SMALL / DDT_WAVE; ++j) {
+                    const int q = lane + j * DDT_WAVE;
+                    const float sv = S[1 + (q < N ? q : 0)];
+                    oc[j] = q < N ? ord_f32(sv) : 0u;
+                }
+                for (int bit = 31; bit >= 16; --bit) {
+                    const uint32_t cand = p | (1u << bit);
+                    int c = 0;
+#pragma unroll
+                    for (int j = 0; j < RK_SMALL / DDT_WAVE; ++j) c += __popcll(__ballot(oc[j] >= cand));
+                    if (c >= kmax) p = cand;
+                }
+            }
+            if (lane == 0) s_T = p;
+        }
+        __syncthreads();
+        T = s_T;
+    } else if (kmax > 0 && kmax < N) {
         uint32_t prefix = 0u, pmask = 0u;
         for (int pass = 0; pass < 4; ++pass) {
             const int shift = 24 - 8 * pass;
@@ -397,8 +429,9 @@ __device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds) {
     }
     // candidates: every node strictly above T, and the ties at T (counted
     // per wave: one LDS atomic per wave, since atomics on one LDS word from
-    // every thread serialize)
-    {
+    // every thread serialize).  Small rows skip the count: all their nodes
+    // fit the candidate list, and the listing's slot counter gives nc.
+    if (!small) {
         int ngt = 0, ntie = 0;
 #pragma unroll
         for (int i = 0; i < RK_PER; ++i) {
@@ -410,13 +443,13 @@ __device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds) {
         const int wtie = __builtin_amdgcn_readlane(wave_incl_scan_i32(ntie), DDT_WAVE - 1);
         if (lane == 0 && wgt) atomicAdd(&s_ngt, wgt);
         if (lane == 0 && wtie) atomicAdd(&s_ntie, wtie);
+        __syncthreads();
     }
-    __syncthreads();
-    const int nc = s_ngt + s_ntie;
+    int nc = small ? 0 : s_ngt + s_ntie;
     int32_t* sel = a.sel + (size_t)b * (a.m_max + 1);
     if (kmax == 0) {
         // nothing to rank
-    } else if (nc <= RK_CAND) {
+    } else if (small || nc <= RK_CAND) {
         int mine = 0;
 #pragma unroll
         for (int i = 0; i < RK_PER; ++i) mine += (tid + i * RK_NT < N) & (o[i] >= T);
@@ -432,6 +465,7 @@ __device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds) {
             if (q < N && o[i] >= T) { s_ca[slot] = ~o[i]; s_ck[slot] = kk[i]; s_cn[slot] = 1 + q; ++slot; }
         }
         __syncthreads();
+        if (small) nc = s_slot;
         // rank of candidate c, counted by S lanes (nc <= RK_CAND = RK_NT)
         const int SL = split_lanes(nc, RK_NT);
         const int lg = __ffs(SL) - 1;
