@@ -291,10 +291,19 @@ __device__ void rerank_sort_all(const float* S, const uint64_t* key, int N, int 
     __syncthreads();
 }
 
+// Node records of a small row (at most RK_SMALL nodes besides the root), left
+// in LDS by the rerank for the flat layout of the same workgroup; indexed by
+// node id.
+struct NodeRecs {
+    const uint64_t* key;
+    const int32_t *tok, *par, *dep;
+    bool ok;                             // the row was small: the tables are filled
+};
+
 // Request blockIdx.x's selection (one workgroup of RK_NT threads): writes sel
 // and m_out, and leaves the selected nodes in rank order in LDS
 // (*nodes_lds[k] for k < m).  Returns m.
-__device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds) {
+__device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds, NodeRecs* recs) {
     const ddt_tree& t = a.t;
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     __shared__ int s_hist[256];
@@ -307,6 +316,8 @@ __device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds) {
     __shared__ float s_sv[DDT_MAX_VERIFY];
     __shared__ double s_u[DDT_MAX_VERIFY + 1], s_c[DDT_MAX_VERIFY + 1];
     __shared__ uint64_t s_sort[RK_SORT];
+    __shared__ uint64_t s_nkey[RK_SMALL + 1];
+    __shared__ int32_t s_ntok[RK_SMALL + 1], s_npar[RK_SMALL + 1], s_ndep[RK_SMALL + 1];
     const int nn = min(max(t.n_nodes[b], 1), t.cap);
     const int N = nn - 1;
     const int kmax = min(a.m_max, N);
@@ -327,6 +338,11 @@ __device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds) {
         sraw[i] = S[1 + qc];
         kk[i] = key[1 + qc];
     }
+    // records of node tid (root included) for the flat layout of a small row
+    const int rn = tid < nn ? tid : 0;
+    const uint64_t r_key = key[rn];
+    const int32_t r_tok = t.token[(size_t)b * t.cap + rn], r_par = t.parent[(size_t)b * t.cap + rn],
+                  r_dep = t.depth[(size_t)b * t.cap + rn];
     // verify costs c_k = S_T[row][k] / S_T[row][1] for k = tid + 1 (without
     // CAST the loads read the row's own values and are not used)
     const int kc = tid < kmax ? tid : 0;
@@ -354,6 +370,8 @@ __device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds) {
     // 16-bit bucket join the candidates.  Ranking every node of a 150-node row
     // cost 2.2 us against about 0.3 us for the search.
     const bool small = N <= RK_SMALL;
+    if (small && tid <= N) { s_nkey[tid] = r_key; s_ntok[tid] = r_tok; s_npar[tid] = r_par; s_ndep[tid] = r_dep; }
+    recs->key = s_nkey; recs->tok = s_ntok; recs->par = s_npar; recs->dep = s_ndep; recs->ok = small;
     uint32_t T = 0u;
     if (small) {
         // (the barrier also orders the counters' initialisation before the
@@ -549,7 +567,8 @@ __device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds) {
 
 __global__ __launch_bounds__(RK_NT) void k_rerank(RerankArgs a) {
     const int32_t* nodes;
-    rerank_row(a, &nodes);
+    NodeRecs recs;
+    rerank_row(a, &nodes, &recs);
 }
 
 // ---------------------------------------------------------------------------
@@ -793,11 +812,109 @@ __global__ __launch_bounds__(MK_NT) void k_build_mask(MaskArgs a) {
     mask_row<MK_NT>(a, a.m[blockIdx.x], nullptr);
 }
 
+// The flat layout of a small selection (m + 1 <= P <= 64 positions, no dense
+// mask) by wave 0 alone, from the rerank's LDS: the node records were loaded
+// with the values, so no second round of global loads.  Lane q holds
+// selection row q, then lane i flat row i.  Same outputs as mask_row: flat
+// index = rank of the canonical key among the selected keys; parents through
+// a node -> flat index table; the ancestor sets (mask rows) by pointer
+// doubling over the flat parents (six steps reach depth 63); leaves by ballot;
+// a leaf's retrieve row lists its ancestor set's flat indices in ascending
+// order (a parent precedes its children in key order).
+__device__ void flat_small(const MaskArgs& a, int m_in, const int32_t* nodes_lds, const NodeRecs& r,
+                           int N) {
+    const ddt_flat& f = a.f;
+    const int b = blockIdx.x, lane = threadIdx.x & 63;
+    const int P = f.P, W = f.W, Dp = f.Dp, L = f.L;
+    __shared__ int32_t s_fnode[DDT_WAVE], s_ftok[DDT_WAVE], s_fpn[DDT_WAVE], s_fdep[DDT_WAVE];
+    __shared__ int s_hc[DDT_WAVE];
+    __shared__ int16_t s_inv[RK_SMALL + 1];
+    const int m = min(max(m_in, 0), P - 1);
+    const int n = m + 1;
+    // selection row q = lane: its node (row 0 the root) and key
+    const int nq = lane == 0 ? 0 : (lane < n ? nodes_lds[lane - 1] : 0);
+    const int nqc = nq >= 0 && nq <= N ? nq : 0;
+    const uint64_t kq = lane < n ? r.key[nqc] : ~0ull;
+    // flat index: the number of selected keys below this row's
+    int rk = 0;
+    for (int p = 0; p < n; ++p) rk += readlane_u64(kq, p) < kq ? 1 : 0;
+    for (int i = lane; i <= N; i += DDT_WAVE) s_inv[i] = -1;
+    s_hc[lane] = 0;
+    wave_lds_sync();
+    if (lane < n) {
+        s_fnode[rk] = nq; s_ftok[rk] = r.tok[nqc]; s_fpn[rk] = r.par[nqc]; s_fdep[rk] = r.dep[nqc];
+        if (nq >= 0 && nq <= N) s_inv[nq] = (int16_t)rk;
+    }
+    wave_lds_sync();
+    // flat row i = lane
+    const int i = lane;
+    int node = -1, tk = -1, fp = -1, d = 0;
+    if (i < n) {
+        node = s_fnode[i];
+        tk = s_ftok[i];
+        const int pn = s_fpn[i];
+        fp = (pn >= 0 && pn <= N) ? (int)s_inv[pn] : -1;
+        d = s_fdep[i];
+    }
+    const size_t fo = (size_t)b * P;
+    if (i < P) {
+        f.node[fo + i] = node;
+        f.token[fo + i] = tk;
+        f.parent[fo + i] = fp;
+        f.pos[fo + i] = a.prefix + d;
+    }
+    if (i >= 1 && i < n && fp >= 0) s_hc[fp] = 1;
+    // ancestor sets: M_i = {i} and the ancestors within 2^k - 1 steps,
+    // anc = the ancestor 2^k steps up (-1 past the root)
+    uint64_t M = 1ull << i;
+    int anc = (i < n && fp >= 0 && fp < i) ? fp : -1;
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+        const int src = anc >= 0 ? anc : lane;
+        const uint64_t Ma = ((uint64_t)(uint32_t)__shfl((int)(uint32_t)(M >> 32), src) << 32) |
+                            (uint32_t)__shfl((int)(uint32_t)M, src);
+        const int aa = __shfl(anc, src);
+        if (anc >= 0) { M |= Ma; anc = aa; }
+    }
+    if (i < P)
+        for (int k = 0; k < W; ++k) f.mask[(fo + i) * W + k] = (uint32_t)(M >> (32 * k));
+    wave_lds_sync();
+    // leaves (no selected child), numbered in flat order
+    const bool leaf = i < n && !s_hc[i];
+    const uint64_t bal = __ballot(leaf);
+    const int nl = (int)__popcll(bal);
+    if (lane == 0) { f.n_leaves[b] = nl; f.m[b] = m; }
+    int32_t* ret = f.retrieve + (size_t)b * L * (Dp + 1);
+    const int li = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    if (leaf && li < L) {
+        int32_t* row = ret + (size_t)li * (Dp + 1);
+        const int dd = min(d, Dp);
+        uint64_t x = M;
+        for (int s2 = Dp; s2 >= 0; --s2) {
+            int v = -1;
+            if (s2 <= dd && x) {
+                v = 63 - __clzll((long long)x);
+                x &= ~(1ull << v);
+            }
+            row[s2] = v;
+        }
+    }
+    for (int q = nl * (Dp + 1) + lane; q < L * (Dp + 1); q += DDT_WAVE) ret[q] = -1;
+}
+
 // rerank and flat layout of one request in one workgroup (no Graft template
 // between them): the selection stays in LDS
 __global__ __launch_bounds__(RK_NT) void k_select(RerankArgs ra, MaskArgs ma) {
     const int32_t* nodes;
-    const int m = rerank_row(ra, &nodes);
+    NodeRecs recs;
+    const int m = rerank_row(ra, &nodes, &recs);
+    if (recs.ok && ma.f.P <= DDT_WAVE && ma.dense == nullptr) {
+        if (threadIdx.x < DDT_WAVE) {
+            const int N = min(max(ra.t.n_nodes[blockIdx.x], 1), ra.t.cap) - 1;
+            flat_small(ma, m, nodes, recs, N);
+        }
+        return;
+    }
     mask_row<RK_NT>(ma, m, nodes);
 }
 
