@@ -509,7 +509,7 @@ __device__ __forceinline__ void rr_chunk(const void* row, int V, int g, int K, b
             int rank = 0;
             if (c < cnt) {
                 k = s_list[c];
-#pragma unroll 4
+#pragma unroll 8
                 for (int q = part; q < cnt; q += SL) rank += s_list[q] > k ? 1 : 0;
             }
             rank = group_sum(rank, SL);
