@@ -343,6 +343,14 @@ __device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds, NodeRe
     const uint64_t r_key = key[rn];
     const int32_t r_tok = t.token[(size_t)b * t.cap + rn], r_par = t.parent[(size_t)b * t.cap + rn],
                   r_dep = t.depth[(size_t)b * t.cap + rn];
+    // every value of a small row in each lane set lane + 64 j (wave 0's
+    // threshold search), requested with the rest
+    float s_all[RK_SMALL / DDT_WAVE];
+#pragma unroll
+    for (int j = 0; j < RK_SMALL / DDT_WAVE; ++j) {
+        const int q = lane + j * DDT_WAVE;
+        s_all[j] = S[1 + (q < N ? q : 0)];
+    }
     // verify costs c_k = S_T[row][k] / S_T[row][1] for k = tid + 1 (without
     // CAST the loads read the row's own values and are not used)
     const int kc = tid < kmax ? tid : 0;
@@ -381,11 +389,8 @@ __device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds, NodeRe
             if (kmax > 0 && kmax < N) {
                 uint32_t oc[RK_SMALL / DDT_WAVE];
 #pragma unroll
-                for (int j = 0; j < RK_SMALL / DDT_WAVE; ++j) {
-                    const int q = lane + j * DDT_WAVE;
-                    const float sv = S[1 + (q < N ? q : 0)];
-                    oc[j] = q < N ? ord_f32(sv) : 0u;
-                }
+                for (int j = 0; j < RK_SMALL / DDT_WAVE; ++j)
+                    oc[j] = lane + j * DDT_WAVE < N ? ord_f32(s_all[j]) : 0u;
                 for (int bit = 31; bit >= 16; --bit) {
                     const uint32_t cand = p | (1u << bit);
                     int c = 0;
@@ -828,6 +833,7 @@ __device__ void flat_small(const MaskArgs& a, int m_in, const int32_t* nodes_lds
     const int P = f.P, W = f.W, Dp = f.Dp, L = f.L;
     __shared__ int32_t s_fnode[DDT_WAVE], s_ftok[DDT_WAVE], s_fpn[DDT_WAVE], s_fdep[DDT_WAVE];
     __shared__ int s_hc[DDT_WAVE];
+    __shared__ uint64_t s_selk[DDT_WAVE];
     __shared__ int16_t s_inv[RK_SMALL + 1];
     const int m = min(max(m_in, 0), P - 1);
     const int n = m + 1;
@@ -835,12 +841,15 @@ __device__ void flat_small(const MaskArgs& a, int m_in, const int32_t* nodes_lds
     const int nq = lane == 0 ? 0 : (lane < n ? nodes_lds[lane - 1] : 0);
     const int nqc = nq >= 0 && nq <= N ? nq : 0;
     const uint64_t kq = lane < n ? r.key[nqc] : ~0ull;
-    // flat index: the number of selected keys below this row's
-    int rk = 0;
-    for (int p = 0; p < n; ++p) rk += readlane_u64(kq, p) < kq ? 1 : 0;
+    // flat index: the number of selected keys below this row's (broadcast
+    // LDS reads, eight in flight)
+    s_selk[lane] = kq;
     for (int i = lane; i <= N; i += DDT_WAVE) s_inv[i] = -1;
     s_hc[lane] = 0;
     wave_lds_sync();
+    int rk = 0;
+#pragma unroll 8
+    for (int p = 0; p < n; ++p) rk += s_selk[p] < kq ? 1 : 0;
     if (lane < n) {
         s_fnode[rk] = nq; s_ftok[rk] = r.tok[nqc]; s_fpn[rk] = r.par[nqc]; s_fdep[rk] = r.dep[nqc];
         if (nq >= 0 && nq <= N) s_inv[nq] = (int16_t)rk;
@@ -865,11 +874,14 @@ __device__ void flat_small(const MaskArgs& a, int m_in, const int32_t* nodes_lds
     }
     if (i >= 1 && i < n && fp >= 0) s_hc[fp] = 1;
     // ancestor sets: M_i = {i} and the ancestors within 2^k - 1 steps,
-    // anc = the ancestor 2^k steps up (-1 past the root)
+    // anc = the ancestor 2^k steps up (-1 past the root); 2^steps exceeds the
+    // deepest selected row's depth (a chain of selected rows is at most that
+    // long: a parent precedes its child in flat order)
     uint64_t M = 1ull << i;
     int anc = (i < n && fp >= 0 && fp < i) ? fp : -1;
-#pragma unroll
-    for (int k = 0; k < 6; ++k) {
+    const int dmax = (int)wave_max_u32(i < n ? (uint32_t)max(d, 0) : 0u);
+    const int steps = dmax > 0 ? min(32 - __clz(dmax), 6) : 0;
+    for (int k = 0; k < steps; ++k) {
         const int src = anc >= 0 ? anc : lane;
         const uint64_t Ma = ((uint64_t)(uint32_t)__shfl((int)(uint32_t)(M >> 32), src) << 32) |
                             (uint32_t)__shfl((int)(uint32_t)M, src);
