@@ -758,10 +758,19 @@ __device__ __forceinline__ void merge1_issue(const uint32_t* __restrict__ p, int
     in.k0 = *(const uint64_t*)(p + gl * PS + 2);
 }
 
-// The K = 1 merge_finish: lane 0 returns the row's best key.
-__device__ __forceinline__ uint64_t merge1_finish(const MergeIn1& in, int groups, float& M, float& Sp) {
+// The K = 1 merge_finish: lane 0 returns the row's best key; with stats =
+// false (a greedy row: only its argmax is read) M and sigma' are not formed
+// and read -inf and 0.
+__device__ __forceinline__ uint64_t merge1_finish(const MergeIn1& in, int groups, float& M, float& Sp,
+                                                  bool stats = true) {
     const int lane = threadIdx.x & (DDT_WAVE - 1);
     const bool on = lane < groups;
+    if (!stats) {
+        M = -INFINITY;
+        Sp = 0.f;
+        const uint64_t best = wave_max_key(on ? in.k0 : 0ull);
+        return lane == 0 ? best : 0ull;
+    }
     const float mc = on ? in.mc : -INFINITY;
     M = unord_f32(wave_max_u32(on ? ord_f32(mc) : 0u));
     const uint64_t mm = __ballot(on && mc == M);

@@ -1378,7 +1378,7 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
                 const int i = i0 + r * NWV;
                 if (i >= n) break;
                 float M, Sp;
-                const uint64_t mine = merge1_finish(in1[r], a.chunks, M, Sp);
+                const uint64_t mine = merge1_finish(in1[r], a.chunks, M, Sp, T > 0.f);
                 if (lane == 0) {
                     const int am = vkey_id(mine);
                     s_am[i] = am; s_M[i] = M; s_S[i] = Sp;
