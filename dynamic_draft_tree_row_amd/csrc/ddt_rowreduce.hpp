@@ -666,11 +666,17 @@ __device__ __forceinline__ uint64_t merge_finish(MergeIn& in, const uint32_t* __
     for (int r = 0; r < MR; ++r) kk[r] = fits && lane + r * DDT_WAVE < total ? in.kk[r] : 0ull;
     M = unord_f32(wave_max_u32(lane < groups ? ord_f32(mc) : 0u));
     // T: the K-th largest sampled value code, bit by bit over the top 16 bits
-    // (a lower T only admits a few more candidates); K = 1 needs none
+    // (a lower T only admits a few more candidates); K = 1 needs none.  With
+    // exactly K samples (groups * jth = K) it is the smallest sample's top 16
+    // bits, the same value the search finds.
     uint32_t T = 0u;
-    for (int bit = 31; K > 1 && bit >= 16; --bit) {
-        const uint32_t cand = T | (1u << bit);
-        if (__popcll(__ballot(hv >= cand)) >= (unsigned)K) T = cand;
+    if (K > 1 && groups * jth == K) {
+        T = wave_min_u32(lane < K ? hv : 0xFFFFFFFFu) & 0xFFFF0000u;
+    } else {
+        for (int bit = 31; K > 1 && bit >= 16; --bit) {
+            const uint32_t cand = T | (1u << bit);
+            if (__popcll(__ballot(hv >= cand)) >= (unsigned)K) T = cand;
+        }
     }
     const uint64_t mm = __ballot(lane < groups && mc == M);
     const int cstar = mm ? __ffsll((unsigned long long)mm) - 1 : -1;
