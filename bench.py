@@ -1082,7 +1082,8 @@ def main():
             "gpu_event_us_per_round": round(gpu_ms * 1e3 / K, 2),
             "round_us_p10_p50_p90": [round(float(np.percentile(per_round_us, q)), 2) for q in (10, 50, 90)],
             "verify_reduction_launch": {
-                "kernel": "k_row_partial<bf16,8>, K = 1",
+                # short chunks below 512 flat rows, as the library launches them
+                "kernel": f"k_row_partial<{w.dtype},{8 if w.B * (w.m_max + 1) >= 512 else 4}>, K = 1",
                 "label": "greedy verify reduces every flat row (sum of m_b + 1 rows) to its argmax; "
                          "the accepted walk needs only sum of accept_len + 1 of them",
                 "mb": round(float(ver_b.mean()) / 1e6, 3), "us": round(float(ver_d.mean() * 1e6), 3),
