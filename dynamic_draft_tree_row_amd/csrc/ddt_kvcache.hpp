@@ -88,64 +88,77 @@ __device__ __forceinline__ int kv_block_scan(int v, int* s_w) {
     return r;
 }
 
-// bookkeeping of a commit: thread b plans request b
+// bookkeeping of a commit: thread b plans request b.  Its loads come in three
+// rounds: the free count with each request's own inputs, then the top of the
+// free stack with the tail block's id, then that block's holder count.
 __global__ __launch_bounds__(KV_NT) void k_kv_plan(KvCommitArgs a) {
     __shared__ int s_w[KV_NT / 64];
     __shared__ int s_x[KV_MAXB];                        // old block of each admitted copier, else -1
+    __shared__ int s_need[KV_NT];                       // blocks each request needs (0 past B)
     __shared__ int s_red[2];
     __shared__ int s_free[KV_STAGE];                    // free_ids[nf - win .. nf)
     const KvCache& c = a.c;
     const int b = threadIdx.x;
     const int bs = c.block, mb = c.max_blocks;
-    // the free count first, then the top of the stack, while the requests'
-    // own loads are in flight
-    const int nf = min(max(*c.n_free, 0), c.n_blocks);
-    const int win = min(nf, KV_STAGE);
-    for (int i = b; i < win; i += KV_NT) s_free[i] = c.free_ids[nf - win + i];
-    auto pop = [&](int idx) { return idx >= nf - win ? s_free[idx - (nf - win)] : c.free_ids[idx]; };
-    int st = 0, n = 0, L0 = 0, off = 0, first = 0, last = -1, X = -1, r = 0, need = 0;
-    bool live = false;
+    const int nf_in = *c.n_free;
+    int acc = -1, L0 = 0;
+    int pe[DDT_MAX_DEPTH + 1];                          // the path entries (Dp <= DDT_MAX_DEPTH)
     if (b < c.B) {
-        const int acc = a.accept_len[b];
+        acc = a.accept_len[b];
         L0 = c.len[b];
-        if (acc >= 0) {
-            n = acc + 1;
-            // the path entries in one round of loads (Dp <= DDT_MAX_DEPTH; an
-            // early exit would make each load wait for the one before)
-            bool bad = n > a.Dp + 1;
-            int pe[DDT_MAX_DEPTH + 1];
 #pragma unroll
-            for (int j = 0; j <= DDT_MAX_DEPTH; ++j) pe[j] = a.accept_path[(size_t)b * (a.Dp + 1) + min(j, a.Dp)];
+        for (int j = 0; j <= DDT_MAX_DEPTH; ++j) pe[j] = a.accept_path[(size_t)b * (a.Dp + 1) + min(j, a.Dp)];
+    }
+    const int nf = min(max(nf_in, 0), c.n_blocks);
+    const int win = min(nf, KV_STAGE);
+    int stg[KV_STAGE / KV_NT];
 #pragma unroll
-            for (int j = 0; j <= DDT_MAX_DEPTH; ++j)
-                if (j < n && (pe[j] < 0 || pe[j] >= a.P)) bad = true;
-            if (bad) {
-                st = -3;
-            } else if (L0 < 0 || L0 + n > mb * bs) {
-                st = -1;
-            } else {
-                live = true;
-                off = L0 % bs;
-                first = L0 / bs;
-                last = (L0 + n - 1) / bs;
-                if (off > 0) {
-                    X = c.table[(size_t)b * mb + first];
-                    r = (unsigned)X < (unsigned)c.n_blocks ? c.ref[X] : 0;
-                }
-                const bool cow = off > 0 && r > 1;
-                need = (last - first + 1) - (off > 0 ? 1 : 0) + (cow ? 1 : 0);
-                if (!cow) X = -1;
+    for (int u = 0; u < KV_STAGE / KV_NT; ++u) {
+        const int i = b + u * KV_NT;
+        stg[u] = i < win ? c.free_ids[nf - win + i] : 0;
+    }
+    auto pop = [&](int idx) { return idx >= nf - win ? s_free[idx - (nf - win)] : c.free_ids[idx]; };
+    int st = 0, n = 0, off = 0, first = 0, last = -1, X = -1, r = 0, need = 0;
+    bool live = false;
+    if (b < c.B && acc >= 0) {
+        n = acc + 1;
+        bool bad = n > a.Dp + 1;
+#pragma unroll
+        for (int j = 0; j <= DDT_MAX_DEPTH; ++j)
+            if (j < n && (pe[j] < 0 || pe[j] >= a.P)) bad = true;
+        if (bad) {
+            st = -3;
+        } else if (L0 < 0 || L0 + n > mb * bs) {
+            st = -1;
+        } else {
+            live = true;
+            off = L0 % bs;
+            first = L0 / bs;
+            last = (L0 + n - 1) / bs;
+            if (off > 0) {
+                X = c.table[(size_t)b * mb + first];
+                r = (unsigned)X < (unsigned)c.n_blocks ? c.ref[X] : 0;
             }
+            const bool cow = off > 0 && r > 1;
+            need = (last - first + 1) - (off > 0 ? 1 : 0) + (cow ? 1 : 0);
+            if (!cow) X = -1;
         }
     }
+#pragma unroll
+    for (int u = 0; u < KV_STAGE / KV_NT; ++u)
+        if (b + u * KV_NT < win) s_free[b + u * KV_NT] = stg[u];
+    s_need[b] = need;
+    if (b == 0) { s_red[0] = 0; s_red[1] = 0; }
     // admission in index order while the free stack lasts
     const int pre = kv_block_scan(need, s_w);
     const bool adm = live && pre <= nf;
     if (live) st = adm ? n : -2;
-    if (b == 0) { s_red[0] = 0; s_red[1] = 0; }
+    // blocks taken: the prefix at the last request whose prefix fits (the
+    // prefixes never decrease, so exactly one thread finds itself there, or
+    // none when the first request does not fit)
+    if (pre <= nf && (b == KV_NT - 1 || pre + s_need[b + 1] > nf)) s_red[0] = pre;
     s_x[b] = adm ? X : -1;
     __syncthreads();
-    if (adm) atomicMax(&s_red[0], pre);                 // blocks taken = the largest admitted prefix
     // copiers of one old block: the lowest-index one settles its holder count
     // and, when no holder is left, pushes it
     int cnt = 0;
@@ -196,15 +209,15 @@ __global__ __launch_bounds__(KV_CT) void k_kv_copy(KvCommitArgs a) {
     __shared__ size_t s_src[DDT_MAX_DEPTH + 1], s_dst[DDT_MAX_DEPTH + 1];
     const KvCache& c = a.c;
     const int b = blockIdx.x;
+    const int j = threadIdx.x;
     const int4 pl = *(const int4*)(c.plan + 4 * b);
+    const int p = j <= a.Dp ? a.accept_path[(size_t)b * (a.Dp + 1) + j] : 0;  // with the plan: n <= Dp + 1
     const int L0 = pl.x, n = pl.y, X = pl.z, nbk = pl.w;
     if (n == 0) return;
     const int HD = c.Hkv * c.D;                         // elements per token, a multiple of 8
     const int V8 = HD / 8;                              // 16-byte words per token
     const int bs = c.block;
-    if (threadIdx.x < n) {
-        const int j = threadIdx.x;
-        const int p = a.accept_path[(size_t)b * (a.Dp + 1) + j];
+    if (j < n) {
         const int t = L0 + j;
         const int blk = c.table[(size_t)b * c.max_blocks + t / bs];
         s_src[j] = ((size_t)b * a.P + p) * HD;
@@ -221,11 +234,11 @@ __global__ __launch_bounds__(KV_CT) void k_kv_copy(KvCommitArgs a) {
     }
     __syncthreads();
     for (int e = e0; e < n * V8; e += KV_CT * KV_SPLIT) {
-        const int j = e / V8, w = e - (e / V8) * V8;
-        const size_t src = s_src[j] + 8 * (size_t)w;
+        const int tok = e / V8, w = e - tok * V8;
+        const size_t src = s_src[tok] + 8 * (size_t)w;
         const u32x4 kd = *(const u32x4*)(a.kt + src);   // loads outside the store's guard
         const u32x4 vd = *(const u32x4*)(a.vt + src);
-        const size_t dst = s_dst[j];
+        const size_t dst = s_dst[tok];
         if (dst != ~(size_t)0) {
             *(u32x4*)(c.k + dst + 8 * (size_t)w) = kd;
             *(u32x4*)(c.v + dst + 8 * (size_t)w) = vd;

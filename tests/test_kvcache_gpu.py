@@ -152,3 +152,43 @@ def test_kv_shared_tails_copied_by_every_holder():
     KV.release(st, np.arange(B))
     _compare(kv, st, "release all")
     assert st["n_free"] == 64
+
+
+def test_kv_admission_boundaries():
+    # the blocks a commit takes are the prefix sum at the last request whose
+    # prefix fits: exercised with a stack that runs out part-way, with the
+    # first request not fitting (nothing taken; the requests after it that
+    # need no block are refused too, admission being in index order), and
+    # with admitted requests that take no block before a refused one
+    from dynamic_draft_tree_row_amd import api
+    rng = np.random.default_rng(33)
+    B, P, Dp, Hkv, D, block = 4, 12, 10, 1, 8, 4
+    kv = api.PagedKV(B, 8, 3, block, Hkv, D, "cuda")
+    st = KV.new_state(B, 8, 3, block, Hkv, D)
+
+    def commit(acc, want_status):
+        kt = rng.integers(0, 1 << 16, size=(B, P, Hkv, D), dtype=np.uint16)
+        vt = rng.integers(0, 1 << 16, size=(B, P, Hkv, D), dtype=np.uint16)
+        acc = np.asarray(acc, np.int32)
+        path = np.full((B, Dp + 1), -1, np.int32)
+        for b in range(B):
+            if acc[b] >= 0:
+                path[b, :acc[b] + 1] = rng.permutation(P)[:acc[b] + 1]
+        status = torch.full((B,), 99, dtype=torch.int32, device="cuda")
+        kv.commit(_i32(acc), _i32(path), _bits(kt), _bits(vt), status)
+        want = KV.commit(st, acc, path, kt, vt)
+        torch.cuda.synchronize()
+        assert list(want) == want_status
+        assert (status.cpu().numpy() == want).all(), f"status {status.cpu().numpy()} vs {want}"
+        _compare(kv, st, f"commit {list(acc)}")
+
+    commit([1, 1, 1, 1], [2, 2, 2, -2])                 # one block each; the stack runs out at request 3
+    assert st["n_free"] == 0
+    commit([9, 0, 0, -1], [-2, -2, -2, 0])              # 0 does not fit: nothing is taken, and 1 and 2,
+                                                        # which need no block, come after a refusal
+    commit([1, 0, 0, 0], [2, 1, 1, -2])                 # 0..2 fit in their tails: the last fitting prefix is 0
+    kv.release(_i32(np.array([1], np.int32)))
+    KV.release(st, np.array([1], np.int32))
+    _compare(kv, st, "release 1")
+    assert st["n_free"] == 1
+    commit([0, -1, 5, 0], [1, 0, -2, -2])               # 0 takes the one block; 2 needs two more
