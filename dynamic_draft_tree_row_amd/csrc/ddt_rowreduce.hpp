@@ -118,6 +118,21 @@ __device__ __forceinline__ void rr_load(u32x4 (&raw)[NL], const void* row, bool 
                                         int V, int tid) {
     using SH = RRShape<BF16, NL>;
     constexpr uint32_t pad16 = RRPad<BF16, NL>::pad16;
+    if (al && start + SH::CH <= V) {
+        // the whole chunk lies inside the row (every chunk but a ragged
+        // last one): a uniform base plus a 32-bit per-lane offset, one add
+        // per load instead of a range test and a 64-bit address each
+        const char* base = (const char*)row + (size_t)start * (BF16 ? 2 : 4);
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            // (opaque to the compiler, so that the address stays a scalar
+            // base plus a 32-bit vector offset rather than a 64-bit sum)
+            uint32_t off = (uint32_t)((i * RR_NT + tid) * 16);
+            asm volatile("" : "+v"(off));
+            raw[i] = __builtin_nontemporal_load((const u32x4*)(base + off));
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
         const int e0 = start + (i * RR_NT + tid) * SH::VEC;
@@ -223,6 +238,32 @@ struct RRLds {
     int sid[(RR_NT / DDT_WAVE) * RR_SW];
 };
 
+typedef unsigned long long rr_u64x2 __attribute__((ext_vector_type(2)));
+
+// Ranks of the first cnt keys of the candidate list (unique, nonzero; the
+// list is zero past them up to RR_NT entries) by counting the larger keys:
+// candidate c = tid / S is counted by the S adjacent lanes c*S .. c*S + S - 1,
+// lane part over the contiguous slice [part * NC/S, (part + 1) * NC/S) of the
+// first NC = RR_NT / S entries, read 16 bytes at a time (the slice address
+// depends on the lane's part only, so a wave's reads are broadcasts).  cnt
+// <= NC.  Rank < K puts the key at out[rank].
+template <int S>
+__device__ __forceinline__ void rr_rank_fixed(const uint64_t* s_list, int cnt, int K,
+                                              uint64_t* __restrict__ out) {
+    constexpr int NC = RR_NT / S, SLICE = NC / S;
+    const int tid = threadIdx.x, c = tid / S, part = tid % S;
+    const uint64_t k = s_list[c];
+    const rr_u64x2* sl = (const rr_u64x2*)(s_list + part * SLICE);
+    int r = 0;
+#pragma unroll 8
+    for (int j = 0; j < SLICE / 2; ++j) {
+        const rr_u64x2 w = sl[j];
+        r += (w.x > k ? 1 : 0) + (w.y > k ? 1 : 0);
+    }
+    r = group_sum(r, S);
+    if (part == 0 && c < cnt && r < K) rr_st64(out + r, k);
+}
+
 // One workgroup reduces chunk g of one row (base `row`, V elements) and
 // writes its partial record to `out`.  Every thread of the workgroup calls
 // it and every thread returns (no early exit), so a caller can go on after
@@ -250,6 +291,10 @@ __device__ __forceinline__ void rr_chunk(const void* row, int V, int g, int K, b
     u32x4 raw[NL];
     rr_load<BF16, NL>(raw, row, al, start, V, tid);
     if (tid == 0) { s_cnt = 0; s_ties = 0; s_amin = 0x7FFFFFFF; }
+    // the candidate list's first RR_NT entries start at 0 (key 0 is no
+    // element and never outranks one), so that the ranking can read a
+    // zero-padded list with fixed trip counts
+    if (K > 1) s_list[tid] = 0ull;
 
     // pass 1: the thread maximum (padding is -inf, or -2^121: RRPad).  bf16
     // words take the packed fp16 maximum, two 32-bit registers per
@@ -469,9 +514,14 @@ __device__ __forceinline__ void rr_chunk(const void* row, int V, int g, int K, b
                     if (q < nq) {
                         w = st[q];
                         id0 = sid[q];
+                        if (!chk) {                      // (block-uniform)
 #pragma unroll
-                        for (int e = 0; e < VEC; ++e)
-                            hit |= (uint32_t)((RR_X(w, e) >= tauf) & (!chk | (id0 + e < V))) << e;
+                            for (int e = 0; e < VEC; ++e) hit |= (uint32_t)(RR_X(w, e) >= tauf) << e;
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < VEC; ++e)
+                                hit |= (uint32_t)((RR_X(w, e) >= tauf) & (id0 + e < V)) << e;
+                        }
                     }
                     const int nh = __popc(hit);
                     const int incl = wave_incl_scan_i32(nh);
@@ -498,6 +548,13 @@ __device__ __forceinline__ void rr_chunk(const void* row, int V, int g, int K, b
     uint64_t* okeys = (uint64_t*)(out + 2);
     if (K == 1) {
         if (tid == 0) rr_st64(okeys, vkey(M, s_amin));
+    } else if (cnt <= RR_NT) {
+        // the usual case (a few dozen candidates): fixed trip counts over the
+        // zero-padded list, no remainder loops
+        if (cnt <= RR_NT / 4) rr_rank_fixed<4>(s_list, cnt, K, okeys);
+        else if (cnt <= RR_NT / 2) rr_rank_fixed<2>(s_list, cnt, K, okeys);
+        else rr_rank_fixed<1>(s_list, cnt, K, okeys);
+        for (int k = cnt + tid; k < K; k += RR_NT) rr_st64(okeys + k, 0ull);
     } else if (cnt <= RR_CAP) {
         // rank counting, each rank counted by S lanes: keys are unique, so
         // rank < K places the key exactly
