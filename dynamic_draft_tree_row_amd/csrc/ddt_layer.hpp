@@ -85,19 +85,67 @@ __host__ __device__ __forceinline__ size_t layer_lds_d(int B, int R_max, int M) 
     return 16 * 8 + (size_t)R_max * 8;
 }
 
-// Request b's next frontier from the layer's sort keys s_sk[count] and the
-// parents' keys s_pk[nrows] (LDS): ranks, each counted by SL lanes; rank <
+// Request b's next frontier from the layer's sort keys s_sk[count] (nrows
+// rows of K_n, row-major) and the parents' keys s_pk[nrows] (LDS): rank <
 // R_max makes a frontier record and rank 0 closes b's layer (node count,
 // frontier width, Graft gate).  The values stage D reads go out
 // device-coherent.  Every thread of the workgroup calls it.
+//
+// One row's children come out of the merge in (value desc, id asc) order
+// and S = S_parent + log c keeps that order, so the sort keys of a request
+// with one row usually ascend already: then a key's rank is its position
+// (each wave checks the order on its own, over the same LDS words, so every
+// wave decides alike).  Otherwise each rank is counted over all keys by SL
+// lanes.  (A bound from each row's first keys, then ranks among the keys
+// below it, measured slower at 100 and 256 keys: its sampling and two more
+// barriers cost more than the shorter counting saved.)
 template <int NT>
 __device__ void layer_frontier(const LayerArgs& a, int b, int base, int count, const uint64_t* s_sk,
-                               const uint64_t* s_pk) {
+                               const uint64_t* s_pk, int nrows) {
     const ddt_tree& t = a.t;
-    const int tid = threadIdx.x, Rm = t.R_max, Kn = a.K_n, layer = a.layer, du = layer - 1;
+    const int tid = threadIdx.x, lane = tid & (DDT_WAVE - 1), Rm = t.R_max, Kn = a.K_n,
+              layer = a.layer, du = layer - 1;
     int32_t* fr = t.frontier + (size_t)b * Rm;
     float* frS = t.front_S + (size_t)b * Rm;
     uint64_t* frK = t.front_key + (size_t)b * Rm;
+    auto emit = [&](int q, uint64_t sk, int r) {
+        const float Sv = unord_f32(~(uint32_t)(sk >> 32));
+        const int jj = q / Kn;
+        fr[r] = base + q; st_coh_f32(frS + r, Sv);
+        frK[r] = key_child(layer == 1 ? 0ull : s_pk[jj], du, q - jj * Kn, 0);
+        if (r == 0) {
+            st_coh_i32(t.n_nodes + b, base + count);
+            st_coh_i32(t.layer_base + b, base);
+            int nf = min(a.K_e, count);
+            if (layer >= t.D_max) nf = 0;
+            if (layer == 1) {
+                t.active[b] = 1;
+                t.k_draft[b] = a.gate_on ? a.K_max : 0;
+            }
+            if (a.ck && !(expf(Sv) > a.tau)) {                // g_d = 1[c_d > tau_d]
+                t.active[b] = 0;
+                t.k_draft[b] = a.kd_ck;
+                nf = 0;
+            }
+            st_coh_i32(t.n_front + b, nf);
+        }
+    };
+    if (count == 0) {
+        if (tid == 0) {
+            if (layer == 1) { st_coh_i32(t.n_nodes + b, 1); st_coh_i32(t.layer_base + b, 1); }
+            st_coh_i32(t.n_front + b, 0);
+        }
+        return;
+    }
+    // one row: each wave checks the order on its own (the same LDS words, so
+    // every wave decides alike)
+    if (nrows == 1 && count <= DDT_WAVE) {
+        const uint64_t x = lane < count ? s_sk[lane] : 0ull, xp = lane >= 1 && lane < count ? s_sk[lane - 1] : 0ull;
+        if (__ballot(lane >= 1 && lane < count && !(xp < x)) == 0ull) {
+            if (tid < count && tid < Rm) emit(tid, x, tid);
+            return;
+        }
+    }
     const int SL = split_lanes(count, NT);
     const int lg = __ffs(SL) - 1;
     for (int cb = 0; cb < count; cb += NT >> lg) {
@@ -110,32 +158,7 @@ __device__ void layer_frontier(const LayerArgs& a, int b, int base, int count, c
             for (int p = part; p < count; p += SL) r += s_sk[p] < sk ? 1 : 0;
         }
         r = group_sum(r, SL);
-        if (part == 0 && q < count && r < Rm) {
-            const float Sv = unord_f32(~(uint32_t)(sk >> 32));
-            const int jj = q / Kn;
-            fr[r] = base + q; st_coh_f32(frS + r, Sv);
-            frK[r] = key_child(layer == 1 ? 0ull : s_pk[jj], du, q - jj * Kn, 0);
-            if (r == 0) {
-                st_coh_i32(t.n_nodes + b, base + count);
-                st_coh_i32(t.layer_base + b, base);
-                int nf = min(a.K_e, count);
-                if (layer >= t.D_max) nf = 0;
-                if (layer == 1) {
-                    t.active[b] = 1;
-                    t.k_draft[b] = a.gate_on ? a.K_max : 0;
-                }
-                if (a.ck && !(expf(Sv) > a.tau)) {            // g_d = 1[c_d > tau_d]
-                    t.active[b] = 0;
-                    t.k_draft[b] = a.kd_ck;
-                    nf = 0;
-                }
-                st_coh_i32(t.n_front + b, nf);
-            }
-        }
-    }
-    if (count == 0 && tid == 0) {
-        if (layer == 1) { st_coh_i32(t.n_nodes + b, 1); st_coh_i32(t.layer_base + b, 1); }
-        st_coh_i32(t.n_front + b, 0);
+        if (part == 0 && q < count && r < Rm) emit(q, sk, r);
     }
 }
 
@@ -177,6 +200,50 @@ __device__ void cast_stage(const LayerArgs& a, unsigned char* region, int i0, in
             L.c[k] = k < N ? (double)rowp[k + 1] / (double)rowt[1] : 0.0;
         }
     }
+}
+
+// The same inputs for the one-kernel layer, requested early from registers:
+// thread q < 12 the state entry or C1 at the kernel's start; thread
+// CAST_CT + k (wave 1, idle while wave 0 merges) the context at the start
+// and cost k of its row once the row's merge begins, so that stage D finds
+// them in registers instead of waiting on two dependent loads.
+#define CAST_CT 64
+static_assert(CAST_CT + DDT_MAX_FRONT <= RR_NT, "cost threads inside the workgroup");
+struct CastPre {
+    double v;         // state entry / C1 (q < 12)
+    int ctx;          // context (cost threads)
+    float num, den;   // S_D[row][k + 1], S_T[row][1] (cost threads)
+};
+
+__device__ __forceinline__ void cast_prefetch(const LayerArgs& a, CastPre& p) {
+    const ddt_tree& t = a.t;
+    const int q = threadIdx.x, layer = a.layer;
+    p.v = 0.0; p.ctx = 0; p.num = 0.f; p.den = 1.f;
+    if (q < 12) {
+        p.v = q == 11 ? (double)a.c.C1[layer - 1]
+            : layer > 1 ? t.cast_state[q] : q == 0 ? 1.0 : q == 8 ? 1.0 : q == 9 ? -1.0 : 0.0;
+    } else if (q >= CAST_CT && q < CAST_CT + t.R_max && layer > 1) {
+        p.ctx = (int)t.cast_state[10];
+    }
+}
+
+__device__ __forceinline__ void cast_cost_loads(const LayerArgs& a, CastPre& p) {
+    const ddt_cast& cp = a.c;
+    const int k = (int)threadIdx.x - CAST_CT, N = cp.N;
+    if (k >= 0 && k < a.t.R_max) {
+        const size_t row = (size_t)cast_sel_row(p.ctx, cp.L, cp.M) * (N + 1);
+        p.num = k < N ? cp.S_D[row + k + 1] : 0.f;
+        p.den = cp.S_T[row + 1];
+    }
+}
+
+// cast_stage from the prefetched registers (every thread of the workgroup)
+__device__ __forceinline__ void cast_stage_pre(const LayerArgs& a, unsigned char* region, const CastPre& p) {
+    const CastView L = cast_view(region, a.t.R_max);
+    const int q = threadIdx.x, k = q - CAST_CT;
+    if (q < 12) L.st[q] = p.v;
+    else if (q == 12) L.st[12] = 1.0 / (double)a.t.B;
+    else if (k >= 0 && k < a.t.R_max) L.c[k] = k < a.c.N ? (double)p.num / (double)p.den : 0.0;
 }
 
 template <int NT>
@@ -229,6 +296,8 @@ __global__ __launch_bounds__(RR_NT) void k_expand_layer(LayerArgs a) {
     // wave 0: the other rows' parents' keys (the layer's key order is
     // (parent key, sibling rank))
     const uint64_t pkl = t.front_key[(size_t)b * Rm + (lane < nrows && layer > 1 ? lane : 0)];
+    CastPre cpre;
+    if (a.cast_on) cast_prefetch(a, cpre);
 
     // ---- A: this workgroup's chunk of row (b, j) ----------------------------
     const void* row = (const char*)a.base + ((int64_t)b * a.s0 + (int64_t)j * a.s1) * (BF16 ? 2 : 4);
@@ -246,6 +315,7 @@ __global__ __launch_bounds__(RR_NT) void k_expand_layer(LayerArgs a) {
     float* lc = t.logc + (size_t)b * cap;
     const int base = layer == 1 ? 1 : nn0;
     const bool fits = base >= 1 && base + nrows * Kn <= cap;       // capacity guard
+    if (a.cast_on) cast_cost_loads(a, cpre);
     if (wid == 0) {
         MergeIn mi;
         merge_issue<true>(prow, a.groups, Kn, mi);
@@ -300,13 +370,11 @@ __global__ __launch_bounds__(RR_NT) void k_expand_layer(LayerArgs a) {
     }
     if (tid < nrows) s_pk[tid] = pkl;
     __syncthreads();
-    layer_frontier<RR_NT>(a, b, base, count, s_sk, s_pk);
+    layer_frontier<RR_NT>(a, b, base, count, s_sk, s_pk, nrows);
     if (!a.cast_on) return;
 
     // ---- D: CAST's batch rule --------------------------------------------------
-    // (staging the inputs while wave 0 merges measured slower: the loads
-    // compete with the merge's)
-    cast_stage(a, dyn + layer_lds_c(Rm, Kn), tid, RR_NT);
+    cast_stage_pre(a, dyn + layer_lds_c(Rm, Kn), cpre);
     cast_finish<RR_NT>(a, dyn + layer_lds_c(Rm, Kn), s_flag);
 }
 
@@ -393,7 +461,7 @@ __global__ __launch_bounds__(EF_NT) void k_expand_finish(LayerArgs a) {
         }
     }
     __syncthreads();
-    layer_frontier<EF_NT>(a, b, base, count, s_sk, s_pk);
+    layer_frontier<EF_NT>(a, b, base, count, s_sk, s_pk, nrows);
     if (!a.cast_on) return;
     cast_finish<EF_NT>(a, dyn + finish_lds(Rm, Kn), s_flag);
 }

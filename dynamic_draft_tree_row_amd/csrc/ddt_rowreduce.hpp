@@ -679,7 +679,8 @@ __device__ __forceinline__ void merge_issue(const uint32_t* __restrict__ p, int 
     const int PS = rr_ps(K);
     const int jth = (K + groups - 1) / groups;         // 1 <= jth <= K (wave-uniform)
     const int total = groups * K;
-    const float rK = 1.0f / (float)K, rj = 1.0f / (float)jth;
+    // (the hardware reciprocal: within one ulp, which small_div allows)
+    const float rK = __builtin_amdgcn_rcpf((float)K), rj = __builtin_amdgcn_rcpf((float)jth);
     const int gl = lane < groups ? lane : 0;
     in.mc = __uint_as_float(rr_ld32<COH>(p + gl * PS));
     in.sc = __uint_as_float(rr_ld32<COH>(p + gl * PS + 1));

@@ -151,42 +151,53 @@ __device__ __forceinline__ int anchor_scan_regs(double u, double c, double C, in
 // then the depth gate with the gain FIFO; every row's n_front gets the
 // result.  Item k (1-based) lives in lane k - 1: u_k, c_k in registers; the
 // anchor scan works on ballot masks and the FIFO on lanes 0..7.
+//
+// The depth gate is evaluated in every lane as if the width were n = lane + 1
+// (push the gain ratio u_n / prev, drop the oldest entry when the FIFO then
+// holds more than R, score = mean(FIFO) * u_n / c_n): the same operations, in
+// the same order, as for the chosen n alone, but independent of the anchor
+// scan, so that its divisions overlap the scan instead of following it; the
+// chosen lane's values are then read.
 __device__ void cast_decide(const CastView& L, const ddt_tree& t, const ddt_cast& cp, int layer, int kcap,
                             double mean) {
     const int lane = threadIdx.x & (DDT_WAVE - 1), B = t.B;
     if (layer == 1 && lane < t.D_max) t.widths[lane] = 0;
+    // state (FIFO entries 0..7 one per lane, oldest first; length; previous
+    // u_n, negative before the first layer's; context), C1, costs
+    const double f = lane < 8 ? L.st[lane] : 0.0;
+    const int len = (int)L.st[8];
+    const double prev = L.st[9];
     const int ctx = (int)L.st[10];
+    const double C1 = L.st[11];
     const bool item = lane < kcap;
+    const double c = item ? L.c[lane] : 0.0;
     // column means of e^S (lane k - 1: item k), prefix-summed across lanes
     const double u = wave_incl_scan_f64(mean);
-    const double c = item ? L.c[lane] : 0.0;
-    const int n = anchor_scan_regs(u, c, L.st[11], kcap);           // C1 of the layer
+    // FIFO after the push: the entries kept (len <= R always, so a push drops
+    // the oldest exactly when len == R) and their sum, oldest first; the new
+    // ratio is added last
+    const bool push = prev >= 0.0;
+    const int drop = push && len >= cp.R ? 1 : 0;
+    const int len2 = len + (push ? 1 : 0) - drop;
+    double base = 0.0;
+    for (int i = drop; i < len; ++i) base += readlane_f64(f, i);
+    const double phi_l = push && prev > 0.0 ? u / prev : 0.0;
+    const double fm_l = (push ? base + phi_l : base) / (double)len2;
+    const double sc_l = fm_l * u / c;
+    const int n = anchor_scan_regs(u, c, C1, kcap);
     const double un = n > 0 ? readlane_f64(u, n - 1) : 0.0;
-    const double cn = n > 0 ? readlane_f64(c, n - 1) : 0.0;
-    // gain FIFO (entries 0..7 of the state, one per lane), length, previous u_n
-    double f = lane < 8 ? L.st[lane] : 0.0;
-    int len = (int)L.st[8];
-    const double prev = L.st[9];
-    if (prev >= 0.0) {                                  // push the previous layer's gain ratio
-        const double phi = prev > 0.0 ? un / prev : 0.0;
-        if (len < 8) {
-            if (lane == len) f = phi;
-            ++len;
-        }
-        if (len > cp.R) {
-            const double g = __shfl_down(f, 1);
-            if (lane < len - 1) f = g;
-            --len;
-        }
-    }
-    double fm = 0.0;
-    for (int i = 0; i < len; ++i) fm += readlane_f64(f, i);
-    fm /= (double)len;
-    const double score = n > 0 ? fm * un / cn : 0.0;
+    const double score = n > 0 ? readlane_f64(sc_l, n - 1) : 0.0;
+    const double phi = n > 0 ? readlane_f64(phi_l, n - 1) : 0.0;    // 0 / prev = 0 for n = 0
     const bool stop = (layer >= t.D_max) || !(score >= (double)cp.C2);
+    // the new FIFO: entries shifted down by one when the oldest is dropped
+    // (lane i takes lane i + 1, within the first row of 16 lanes), the new
+    // ratio in entry len2 - 1
+    const double fsh = dpp_f64<0x101, 0xF>(f);
+    double fn = drop ? fsh : f;
+    if (push && lane == len2 - 1) fn = phi;
     double* st = t.cast_state;
-    if (lane < 8) st[lane] = f;
-    if (lane == 8) st[8] = (double)len;
+    if (lane < 8) st[lane] = fn;
+    if (lane == 8) st[8] = (double)len2;
     if (lane == 9) st[9] = un;
     if (lane == 10) st[10] = (double)(ctx + n);
     if (lane == 0) {

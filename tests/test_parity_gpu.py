@@ -250,6 +250,22 @@ def test_cast_roofline_cost_table(table_B, C1, C2, C3):
         H.compare(case, H.gpu_round(case))
 
 
+@pytest.mark.parametrize("C2", [0.001, 0.002])
+def test_cast_gain_fifo_full_length(C2):
+    # R = 8, the longest gain FIFO the state holds, and 11 layers: from layer 9
+    # on a push meets a full FIFO and drops the oldest ratio (CAST notes, key
+    # design 3).  At these thresholds the depth gate stops the tree at layer 9
+    # or 10, so the decisions read the full-length FIFO.
+    cs = configs.CastSpec(C1=0.05, C2=C2, C3=0.02, R=8)
+    base = configs.shrink(configs.C2, V=3000, B=3)
+    w = configs.Workload(**{**base.__dict__, "D": 11, "m": 120, "cast": cs, "name": "cast_fifo8"})
+    cast = H.cast_params(w)
+    for seed in (1, 2, 3):
+        case = H.oracle_case(w, seed, 0, cast=cast)
+        say(f"cast FIFO R=8 C2={C2} seed={seed} depth={case.out['draft'].depth_built}")
+        H.compare(case, H.gpu_round(case))
+
+
 def test_graft_small_multi_round():
     w = configs.shrink(configs.C4, V=6000, B=5)
     tau = H.calibrate_tau(w, 77, 4)
