@@ -338,19 +338,22 @@ __device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds, NodeRe
     // one round of loads: values and keys of this thread's nodes, verify costs.
     // Straight-line loads from clamped addresses (a load under a branch ends in
     // a register copy that waits for it); the values past the data are masked
-    // after the loads.
+    // after the loads.  The addresses are clamped to the row's capacity, not
+    // to its node count, so that the loads go out together with the count's
+    // instead of after it.
+    const int cap1 = t.cap - 1;
     uint32_t o[RK_PER];
     uint64_t kk[RK_PER];
     float sraw[RK_PER];
 #pragma unroll
     for (int i = 0; i < RK_PER; ++i) {
         const int q = tid + i * RK_NT;
-        const int qc = q < N ? q : 0;
+        const int qc = q < cap1 ? q : 0;
         sraw[i] = S[1 + qc];
         kk[i] = key[1 + qc];
     }
     // records of node tid (root included) for the flat layout of a small row
-    const int rn = tid < nn ? tid : 0;
+    const int rn = tid <= cap1 ? tid : 0;
     const uint64_t r_key = key[rn];
     const int32_t r_tok = t.token[(size_t)b * t.cap + rn], r_par = t.parent[(size_t)b * t.cap + rn],
                   r_dep = t.depth[(size_t)b * t.cap + rn];
@@ -360,11 +363,11 @@ __device__ int rerank_row(const RerankArgs& a, const int32_t** nodes_lds, NodeRe
 #pragma unroll
     for (int j = 0; j < RK_SMALL / DDT_WAVE; ++j) {
         const int q = lane + j * DDT_WAVE;
-        s_all[j] = S[1 + (q < N ? q : 0)];
+        s_all[j] = S[1 + (q < cap1 ? q : 0)];
     }
     // verify costs c_k = S_T[row][k] / S_T[row][1] for k = tid + 1 (without
     // CAST the loads read the row's own values and are not used)
-    const int kc = tid < kmax ? tid : 0;
+    const int kc = tid < min(a.m_max, cap1) ? tid : 0;             // (kmax <= both)
     const float* ST = S;
     if (a.cast_on) ST = a.c.S_T + (size_t)cast_sel_row(a.c.ctx_verify, a.c.L, a.c.M) * (a.c.N + 1);
     const float c_num = ST[kc + 1], c_den = ST[1];
@@ -1339,15 +1342,19 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
     // the first batch of argmax merges are requested before anything waits
     // (straight-line loads from clamped addresses: a load under a branch ends
     // in a register copy that waits for it)
+    // (clamped to the arrays' capacities rather than to m and the leaf count,
+    // so that these loads go out together with the first trip's; everything
+    // past the data is masked below)
     const int32_t* ret = f.retrieve + (size_t)b * f.L * (Dp + 1);
     const int nret = greedy && ret_lds ? Lr * (Dp + 1) : 0;
+    const int ret_cap = f.L * (Dp + 1);
     int32_t r_ret[VF_RET / VF_NT];
 #pragma unroll
     for (int k = 0; k < VF_RET / VF_NT; ++k) {
         const int q = tid + k * VF_NT;
-        r_ret[k] = ret[q < nret ? q : 0];
+        r_ret[k] = ret[q < ret_cap ? q : 0];
     }
-    const int tn = tid < n ? tid : 0;                  // P <= MK_NT <= VF_NT
+    const int tn = tid < P ? tid : 0;                  // P <= MK_NT <= VF_NT
     const int r_fp = f.parent[fo + tn], r_ft = f.token[fo + tn];
     const bool k1 = a.Kp == 1;
     constexpr int VB = 4, NWV = VF_NT / 64;           // rows per wave per batch, waves
@@ -1355,7 +1362,7 @@ __global__ __launch_bounds__(VF_NT) void k_verify(VerifyArgs a) {
     if (k1) {
 #pragma unroll
         for (int r = 0; r < VB; ++r) {
-            const int i = min(wid + r * NWV, n - 1);
+            const int i = min(wid + r * NWV, P - 1);
             merge1_issue(a.part + ((size_t)(b * P + i) * a.chunks) * rr_ps(1), a.chunks, in1[r]);
         }
     }
