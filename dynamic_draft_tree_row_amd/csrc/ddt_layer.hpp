@@ -97,8 +97,8 @@ __host__ __device__ __forceinline__ size_t layer_lds_d(int B, int R_max, int M) 
 // (each wave checks the order on its own, over the same LDS words, so every
 // wave decides alike).  Otherwise each rank is counted over all keys by SL
 // lanes.  (A bound from each row's first keys, then ranks among the keys
-// below it, measured slower at 100 and 256 keys: its sampling and two more
-// barriers cost more than the shorter counting saved.)
+// below it, measured slower in the 1024-thread finish at 256 keys: its
+// sampling and two more barriers cost more than the shorter counting saved.)
 template <int NT>
 __device__ void layer_frontier(const LayerArgs& a, int b, int base, int count, const uint64_t* s_sk,
                                const uint64_t* s_pk, int nrows) {
